@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the gated delta-rule forward pass.
+
+This module only draws and stores random tensors; it holds none of the
+method's arithmetic, so both the GPU path and the oracle can take their
+inputs from it.
+
+Distributions (one layer, one head group):
+  * q ~ N(0,1) then L2-normalised over the key dimension of each (b, t, h);
+  * k ~ N(0,1) then L2-normalised the same way, except for the Kaczmarz
+    workload, whose keys keep their norm: k = N(0,1) * LogNormal(0, 0.5),
+    one log-normal factor per (b, t, h) scaling the whole key vector;
+  * v ~ N(0,1);
+  * scalar decay alpha = exp(-softplus(N(0,1)) * s) per (b, t, h), or one such
+    value per key channel for the channel-wise variants;
+  * beta, eta, erase gate b and write gate w = sigmoid(N(0,1)).
+
+Draw order from ``numpy.random.default_rng(seed)``: q, k (and the log-normal
+key scale), v, then the gates in the order alpha, beta/eta, b, w.  Values are
+drawn in float32; q, k, v are then stored in the requested dtype (bf16 by
+round-to-nearest-even through torch) and gates stay float32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+VARIANTS = ("deltanet", "gated_deltanet", "kda", "gdn2", "kla")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    variant: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    dtype: str          # "fp32" or "bf16": storage type of q, k, v and o
+    seed: int
+    alpha_scale: float = 0.1
+    eps: float = 0.0
+    unnormalised_keys: bool = False
+    decode: dict = field(default_factory=dict)
+
+
+# The five layer shapes measured here.
+WORKLOADS = {
+    1: Workload("deltanet_fp32_B1_H2_T256_d64", "deltanet", 1, 2, 256, 64, 64,
+                "fp32", 85001),
+    2: Workload("gated_deltanet_bf16_B4_H8_T4096_d128", "gated_deltanet", 4, 8,
+                4096, 128, 128, "bf16", 85002, alpha_scale=0.1),
+    3: Workload("kda_bf16_B4_H8_T4096_d128", "kda", 4, 8, 4096, 128, 128,
+                "bf16", 85003, alpha_scale=0.05),
+    4: Workload("gdn2_bf16_B2_H16_T8192_d128", "gdn2", 2, 16, 8192, 128, 128,
+                "bf16", 85004, alpha_scale=0.05),
+    5: Workload("kla_bf16_B1_H16_T65536_d128_decode_B64x1024", "kla", 1, 16,
+                65536, 128, 128, "bf16", 85005, alpha_scale=0.1, eps=1e-6,
+                unnormalised_keys=True,
+                decode=dict(B=64, steps=1024, seed=85105)),
+}
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def _l2norm_last(x):
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+
+
+def _store(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def make_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0,
+                alpha_scale=0.1, eps=None, unnormalised_keys=None,
+                state_scale=0.0):
+    """Draw one problem.  Returns a dict of CPU torch tensors:
+    q, k [B,T,H,dk], v [B,T,H,dv] in ``dtype``; alpha, beta, erase_b, write_w
+    float32 (None where the variant has no such gate); eps (float); state_in
+    float32 [B,H,dk,dv] drawn N(0,1)*state_scale, or None when state_scale==0.
+    """
+    if variant not in VARIANTS:
+        raise ValueError(variant)
+    if unnormalised_keys is None:
+        unnormalised_keys = variant == "kla"
+    if eps is None:
+        eps = 1e-6 if variant == "kla" else 0.0
+    rng = np.random.default_rng(seed)
+    q = _l2norm_last(_normal(rng, (B, T, H, dk)))
+    k = _normal(rng, (B, T, H, dk))
+    if unnormalised_keys:
+        scale = np.exp(0.5 * _normal(rng, (B, T, H, 1)))
+        k = (k * scale).astype(np.float32)
+    else:
+        k = _l2norm_last(k)
+    v = _normal(rng, (B, T, H, dv))
+    out = dict(q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype),
+               alpha=None, beta=None, erase_b=None, write_w=None, eps=float(eps),
+               state_in=None)
+    if variant in ("gated_deltanet", "kla"):
+        out["alpha"] = torch.from_numpy(
+            np.exp(-_softplus(_normal(rng, (B, T, H))) * alpha_scale).astype(np.float32))
+    elif variant in ("kda", "gdn2"):
+        out["alpha"] = torch.from_numpy(
+            np.exp(-_softplus(_normal(rng, (B, T, H, dk))) * alpha_scale).astype(np.float32))
+    if variant != "gdn2":
+        out["beta"] = torch.from_numpy(_sigmoid(_normal(rng, (B, T, H))).astype(np.float32))
+    else:
+        out["erase_b"] = torch.from_numpy(_sigmoid(_normal(rng, (B, T, H, dk))).astype(np.float32))
+        out["write_w"] = torch.from_numpy(_sigmoid(_normal(rng, (B, T, H, dv))).astype(np.float32))
+    if state_scale:
+        out["state_in"] = torch.from_numpy(
+            (_normal(rng, (B, H, dk, dv)) * state_scale).astype(np.float32))
+    return out
+
+
+def make_workload(wl: Workload, T=None, B=None, H=None):
+    """Inputs of a named workload, optionally cut to a shorter sequence or
+    fewer batch rows / heads (the draw keeps the workload's seed)."""
+    return make_inputs(wl.variant, B or wl.B, T or wl.T, H or wl.H, wl.dk, wl.dv,
+                       wl.dtype, wl.seed, alpha_scale=wl.alpha_scale,
+                       eps=wl.eps, unnormalised_keys=wl.unnormalised_keys)
+
+
+def make_decode_inputs(wl: Workload, steps=None, B=None):
+    """Per-step decode inputs for a workload with a decode phase: tensors with
+    a leading step axis, q, k [S,B,1,H,dk], v [S,B,1,H,dv], gates [S,B,1,H(,d)]."""
+    d = wl.decode
+    S = steps or d["steps"]
+    Bd = B or d["B"]
+    rng = np.random.default_rng(d["seed"])
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    q = _l2norm_last(_normal(rng, (S, Bd, 1, H, dk)))
+    k = _normal(rng, (S, Bd, 1, H, dk))
+    if wl.unnormalised_keys:
+        k = (k * np.exp(0.5 * _normal(rng, (S, Bd, 1, H, 1)))).astype(np.float32)
+    else:
+        k = _l2norm_last(k)
+    v = _normal(rng, (S, Bd, 1, H, dv))
+    out = dict(q=_store(q, wl.dtype), k=_store(k, wl.dtype), v=_store(v, wl.dtype),
+               alpha=None, beta=None, erase_b=None, write_w=None, eps=float(wl.eps))
+    variant = wl.variant
+    if variant in ("gated_deltanet", "kla"):
+        out["alpha"] = torch.from_numpy(
+            np.exp(-_softplus(_normal(rng, (S, Bd, 1, H))) * wl.alpha_scale).astype(np.float32))
+    elif variant in ("kda", "gdn2"):
+        out["alpha"] = torch.from_numpy(
+            np.exp(-_softplus(_normal(rng, (S, Bd, 1, H, dk))) * wl.alpha_scale).astype(np.float32))
+    if variant != "gdn2":
+        out["beta"] = torch.from_numpy(_sigmoid(_normal(rng, (S, Bd, 1, H))).astype(np.float32))
+    else:
+        out["erase_b"] = torch.from_numpy(_sigmoid(_normal(rng, (S, Bd, 1, H, dk))).astype(np.float32))
+        out["write_w"] = torch.from_numpy(_sigmoid(_normal(rng, (S, Bd, 1, H, dv))).astype(np.float32))
+    return out

@@ -1,0 +1,146 @@
+"""Parity oracle for the gated delta-rule forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The GPU library never calls it and it
+never calls the GPU library: the two share no code.
+
+It wraps ``gdr_oracle.c`` (plain sequential double-precision recurrences, one
+function per variant) with ctypes and runs independent heads (b, h) on a
+thread pool.  Inputs are the exact stored values (bf16 or fp32) upcast to
+float64; results come back as float64 numpy arrays.
+
+Parity status: every variant is pinned by the tests in ``tests/test_oracle_*``
+(exact rational brute force on short sequences, the Kaczmarz projection and
+line-search properties, variant reductions, closed forms); none is unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+VARIANTS = ("deltanet", "gated_deltanet", "kda", "gdn2", "kla")
+_ENTRY = {
+    "deltanet": "oracle_deltanet_head",
+    "gated_deltanet": "oracle_gated_deltanet_head",
+    "kda": "oracle_kda_head",
+    "gdn2": "oracle_gdn2_head",
+    "kla": "oracle_kla_head",
+}
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_long), ("T", ctypes.c_long), ("H", ctypes.c_long),
+        ("dk", ctypes.c_long), ("dv", ctypes.c_long),
+        ("q", _dp), ("k", _dp), ("v", _dp),
+        ("alpha", _dp), ("beta", _dp), ("erase_b", _dp), ("write_w", _dp),
+        ("eps", ctypes.c_double),
+        ("state_in", _dp), ("state_out", _dp), ("o", _dp),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", out, src]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    with _lib_lock:
+        if path is not None:
+            lib = ctypes.CDLL(path)
+        else:
+            if _lib is not None:
+                return _lib
+            if (not os.path.exists(_LIB)
+                    or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+            lib = ctypes.CDLL(_LIB)
+        for name in _ENTRY.values():
+            fn = getattr(lib, name)
+            fn.argtypes = [ctypes.POINTER(_Problem), ctypes.c_long, ctypes.c_long]
+            fn.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: exact upcast of bf16/fp32 values
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
+            write_w=None, eps: float = 0.0, state_in=None, heads=None,
+            threads: int | None = None, lib=None):
+    """Run the sequential recurrence for ``variant``.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; gates as documented in
+    ``gdr_oracle.c``.  ``heads`` optionally restricts the work to a list of
+    (b, h) pairs; outputs of other heads are left as NaN.  Returns
+    ``(o [B,T,H,dv], state_out [B,H,dk,dv])`` in float64.
+    """
+    if variant not in _ENTRY:
+        raise ValueError(f"unknown variant {variant!r}")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    arrays = dict(alpha=_f64(alpha), beta=_f64(beta), erase_b=_f64(erase_b),
+                  write_w=_f64(write_w), state_in=_f64(state_in))
+    o = np.full((B, T, H, dv), np.nan)
+    s_out = np.full((B, H, dk, dv), np.nan)
+    prob = _Problem(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                    _ptr(arrays["alpha"]), _ptr(arrays["beta"]),
+                    _ptr(arrays["erase_b"]), _ptr(arrays["write_w"]),
+                    float(eps), _ptr(arrays["state_in"]), _ptr(s_out), _ptr(o))
+    lib = lib if lib is not None else load()
+    fn = getattr(lib, _ENTRY[variant])
+    todo = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def run(bh):
+        rc = fn(ctypes.byref(prob), bh[0], bh[1])
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+
+    n = max(1, min(threads or default_threads(), len(todo)))
+    if n == 1:
+        for bh in todo:
+            run(bh)
+    else:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(run, todo))
+    # keep the argument arrays alive until the calls are done
+    del arrays
+    return o, s_out
