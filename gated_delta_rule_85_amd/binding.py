@@ -1,0 +1,199 @@
+"""Python binding of the C ABI in include/gdr.h -- argument marshalling only.
+
+The functions named like the C entry points (``gdr_forward_chunked``,
+``gdr_decode_step``, ...) take a ``GdrArgs`` structure and raw device
+pointers exactly as the C functions do.  ``make_args`` fills that structure
+from torch tensors (shapes, dtypes and ``data_ptr()``), and ``forward`` /
+``decode_step`` allocate outputs and workspace with torch and call the
+library.  Every step of the computation runs in the HIP kernels of
+``libgdr.so``; if the library is missing, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdr.so")
+
+VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "gdn2": 3, "kla": 4}
+GDR_F32, GDR_BF16 = 0, 1
+STATUS = {0: "GDR_OK", 1: "GDR_ERR_INVALID_ARGUMENT", 2: "GDR_ERR_UNSUPPORTED",
+          3: "GDR_ERR_WORKSPACE", 4: "GDR_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+
+
+class GdrArgs(ctypes.Structure):
+    """Mirror of ``struct gdr_args``."""
+    _fields_ = [
+        ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q", _vp), ("k", _vp), ("v", _vp),
+        ("alpha", _vp), ("beta", _vp), ("erase_b", _vp), ("write_w", _vp),
+        ("eps", ctypes.c_float), ("reserved_f", ctypes.c_float),
+        ("state_in", _vp), ("state_out", _vp), ("o", _vp),
+    ]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib(path: str | None = None):
+    """Load libgdr.so (built by ``gated_delta_rule_85_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m gated_delta_rule_85_amd.build`")
+    L = ctypes.CDLL(p)
+    A = ctypes.POINTER(GdrArgs)
+    L.gdr_check_args.argtypes = [A, ctypes.c_int]
+    L.gdr_check_args.restype = ctypes.c_int
+    L.gdr_forward_workspace_size.argtypes = [A]
+    L.gdr_forward_workspace_size.restype = ctypes.c_size_t
+    L.gdr_forward_chunked.argtypes = [A, _vp, ctypes.c_size_t, _vp]
+    L.gdr_forward_chunked.restype = ctypes.c_int
+    L.gdr_decode_step.argtypes = [A, _vp]
+    L.gdr_decode_step.restype = ctypes.c_int
+    L.gdr_status_string.argtypes = [ctypes.c_int]
+    L.gdr_status_string.restype = ctypes.c_char_p
+    L.gdr_last_error_detail.argtypes = []
+    L.gdr_last_error_detail.restype = ctypes.c_char_p
+    if path is None:
+        _lib = L
+    return L
+
+
+# ---- the C entry points, one to one ----------------------------------------------
+
+def gdr_check_args(args: GdrArgs, for_decode: int) -> int:
+    return lib().gdr_check_args(ctypes.byref(args), int(for_decode))
+
+
+def gdr_forward_workspace_size(args: GdrArgs) -> int:
+    return lib().gdr_forward_workspace_size(ctypes.byref(args))
+
+
+def gdr_forward_chunked(args: GdrArgs, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().gdr_forward_chunked(ctypes.byref(args), workspace or None, ws_bytes,
+                                     stream or None)
+
+
+def gdr_decode_step(args: GdrArgs, stream: int) -> int:
+    return lib().gdr_decode_step(ctypes.byref(args), stream or None)
+
+
+def gdr_status_string(status: int) -> str:
+    return lib().gdr_status_string(int(status)).decode()
+
+
+def gdr_last_error_detail() -> str:
+    return lib().gdr_last_error_detail().decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise GdrError(status, gdr_last_error_detail())
+
+
+# ---- marshalling from torch tensors ----------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_args(variant: str, q, k, v, o, alpha=None, beta=None, erase_b=None,
+              write_w=None, eps: float = 0.0, state_in=None, state_out=None,
+              chunk: int = 0) -> GdrArgs:
+    """Fill GdrArgs from contiguous tensors q, k [B,T,H,dk], v, o [B,T,H,dv]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("alpha", alpha),
+                    ("beta", beta), ("erase_b", erase_b), ("write_w", write_w),
+                    ("state_in", state_in), ("state_out", state_out)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype == torch.bfloat16:
+        dt = GDR_BF16
+    elif q.dtype == torch.float32:
+        dt = GDR_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    return GdrArgs(VARIANTS[variant], dt, B, T, H, dk, dv, chunk, 0,
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                   _ptr(erase_b), _ptr(write_w), float(eps), 0.0,
+                   _ptr(state_in), _ptr(state_out), _ptr(o))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
+            write_w=None, eps: float = 0.0, state_in=None, output_state: bool = True,
+            o=None, state_out=None, workspace=None, stream=None):
+    """Chunked forward on device tensors.  Returns (o, state_out or None)."""
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if output_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
+                  state_in, state_out)
+    check(gdr_check_args(a, 0))
+    need = gdr_forward_workspace_size(a)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check(gdr_forward_chunked(a, workspace.data_ptr(), workspace.numel(),
+                              _stream_handle(stream)))
+    return o, state_out
+
+
+def workspace_bytes(variant: str, q, k, v) -> int:
+    """Workspace size gdr_forward_chunked needs for these shapes."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    a = GdrArgs(VARIANTS[variant], GDR_BF16 if q.dtype == torch.bfloat16 else GDR_F32,
+                B, T, H, dk, dv, 0, 0, 16, 16, 16,
+                16 if variant != "deltanet" else None,
+                16 if variant != "gdn2" else None,
+                16 if variant == "gdn2" else None, 16 if variant == "gdn2" else None,
+                1e-6 if variant == "kla" else 0.0, 0.0, None, None, 32)
+    return gdr_forward_workspace_size(a)
+
+
+def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=None,
+                write_w=None, eps: float = 0.0, o=None, state_out=None, stream=None):
+    """One decode step: q, k [B,1,H,dk], v [B,1,H,dv]; updates ``state`` in
+    place unless ``state_out`` is given.  Returns o [B,1,H,dv]."""
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
+                  state, state if state_out is None else state_out)
+    check(gdr_decode_step(a, _stream_handle(stream)))
+    return o

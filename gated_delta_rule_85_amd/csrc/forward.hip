@@ -1,0 +1,614 @@
+// forward.hip -- chunkwise-parallel prefill of the gated delta rule on gfx950.
+//
+// The sequence of every (b, h) is cut into chunks of C = 64 tokens.  Inside a
+// chunk, with g_r = sum_{j<=r} log alpha_j (inclusive, per key channel i for
+// channel-wise decay) and the chunk's incoming state S, the recurrence
+//     S_t = (I - k_t a_t^T) D_t S_{t-1} + k_t u_t^T,   o_t = S_t^T q_t
+// unrolls to the closed form (an algebraic identity, not an approximation):
+//     A[r][s] = sum_i a_r[i] k_s[i] e^{g_r[i] - g_s[i]}      (s <  r)
+//     P[r][s] = sum_i q_r[i] k_s[i] e^{g_r[i] - g_s[i]}      (s <= r)
+//     T = (I + A)^{-1}              (unit lower triangular)
+//     W = T (a (.) e^{g}),   U~ = T U
+//     Delta = U~ - W S
+//     O = (q (.) e^{g}) S + P Delta
+//     S' = Diag(e^{g_C}) S + (k (.) e^{g_C - g})^T Delta
+// This is the chunk-wise parallel form that the pages keep for every variant
+// ("Kaczmarz Linear Attention", Implementation section: only the per-chunk
+// diagonal coefficient matrix Diag(beta_1..beta_C) changes; "Gated
+// DeltaNet-2", technical core: a chunkwise WY algorithm in which the
+// channel-wise decay is absorbed into an asymmetric erase factor -- here the
+// left factor a (.) e^{g} differs from the right factor k (.) e^{-g}).  The
+// derivation and the kernel design are our own.
+//
+// Two kernels:
+//   chunk_prep  one workgroup per (chunk, h, b), fully parallel.  Gate prefix
+//               sums, the two 64x64 Gram products A and P on bf16 matrix cores
+//               (fp32 accumulate), the unit-lower-triangular inverse T in LDS
+//               (fp32; 16x16 diagonal blocks by substitution, off-diagonal
+//               blocks by block recursion), then W and U~ on matrix cores.
+//               It writes per-chunk factors W, U~^T, q(.)e^{g}, K-bar^T, P and
+//               e^{g_C} to the workspace.
+//   chunk_scan  one workgroup per (slice of 16*NJ value columns, h, b): the
+//               sequential pass over chunks.  Columns of S evolve independently
+//               given the chunk factors, so the state is split by value
+//               columns; each wave keeps its rows of S in fp32 MFMA
+//               accumulators for the whole sequence and a bf16 copy of S^T in
+//               LDS feeds the products.  The next chunk's factors are loaded
+//               while the current one is computed.
+//
+// All products are written as D = A * B^T over a K-contiguous pair of
+// operands, so every fragment is one 16-byte load; operand order is chosen so
+// that each lane's four accumulator values are four consecutive elements of
+// the row-major destination.
+#include "gdr_device.hpp"
+
+namespace gdr {
+namespace {
+
+constexpr int C = 64;              // chunk length
+constexpr int kPrepThreads = 256;
+constexpr int kScanThreads = 256;
+
+template <typename TI> struct WsPtrs {
+    TI *W;     // [nch][C][DK]   T (a (.) e^{g})
+    TI *Ut;    // [nch][DV][C]   (T U)^T
+    TI *Qt;    // [nch][C][DK]   q (.) e^{g}
+    TI *Kbt;   // [nch][DK][C]   (k (.) e^{g_C - g})^T
+    TI *P;     // [nch][C][C]    decayed q k^T, lower triangle incl. diagonal
+    float *gam;// [nch][DK]      e^{g_C}
+};
+
+struct WsLayout {
+    size_t W, Ut, Qt, Kbt, P, gam, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const Problem &p) {
+    const size_t es = p.bf16 ? 2 : 4;
+    const size_t nch = (size_t)p.B * p.H * ((p.T + C - 1) / C);
+    WsLayout L;
+    size_t o = 0;
+    L.W = o;   o = align256(o + nch * C * p.dk * es);
+    L.Ut = o;  o = align256(o + nch * C * p.dv * es);
+    L.Qt = o;  o = align256(o + nch * C * p.dk * es);
+    L.Kbt = o; o = align256(o + nch * C * p.dk * es);
+    L.P = o;   o = align256(o + nch * C * C * es);
+    L.gam = o; o = align256(o + nch * p.dk * 4);
+    L.total = o;
+    return L;
+}
+
+template <typename TI> WsPtrs<TI> ws_ptrs(const Problem &p, void *base) {
+    WsLayout L = ws_layout(p);
+    char *b = static_cast<char *>(base);
+    return WsPtrs<TI>{reinterpret_cast<TI *>(b + L.W), reinterpret_cast<TI *>(b + L.Ut),
+                      reinterpret_cast<TI *>(b + L.Qt), reinterpret_cast<TI *>(b + L.Kbt),
+                      reinterpret_cast<TI *>(b + L.P), reinterpret_cast<float *>(b + L.gam)};
+}
+
+// ---- small vector stores ------------------------------------------------------
+
+__device__ __forceinline__ void store8(bf16 *dst, const float *x) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+    *reinterpret_cast<bf16x8 *>(dst) = v;
+}
+__device__ __forceinline__ void store8(float *dst, const float *x) {
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void store4(bf16 *dst, f32x4 x) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+    *reinterpret_cast<bf16x4 *>(dst) = v;
+}
+__device__ __forceinline__ void store4(float *dst, f32x4 x) {
+    *reinterpret_cast<f32x4 *>(dst) = x;
+}
+__device__ __forceinline__ f32x4 load4(const bf16 *src) {
+    bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 load4(const float *src) {
+    return *reinterpret_cast<const f32x4 *>(src);
+}
+// kPerLane consecutive input elements as floats (8 for bf16, 1 for fp32).
+__device__ __forceinline__ void load_lane(const bf16 *src, float *x) {
+    bf16x8 v = *reinterpret_cast<const bf16x8 *>(src);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load_lane(const float *src, float *x) { x[0] = *src; }
+
+// The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix, spread so
+// that four waves get 3, 3, 2, 2 of them.
+__constant__ int8_t kLowerR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int8_t kLowerS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// The six strictly upper 16x16 tiles.
+__constant__ int8_t kUpperR[6] = {0, 0, 0, 1, 1, 2};
+__constant__ int8_t kUpperS[6] = {1, 2, 3, 2, 3, 3};
+
+// ============================================================================
+// chunk_prep
+// ============================================================================
+template <int V, typename TI, int DK, int DV>
+__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsPtrs<TI> ws) {
+    using VT = VariantTraits<V>;
+    using M = Mma<TI>;
+    constexpr int PT = 8;                                  // pad (elements) of TI tiles
+    constexpr int PF = 4;                                  // pad of fp32 tiles
+    constexpr int GW = VT::kChannelDecay ? DK : 1;         // width of a g row
+    constexpr int NL = M::kPerLane;
+
+    __shared__ float sG[C][GW];
+    __shared__ float sBeta[C];
+    __shared__ __attribute__((aligned(16))) TI sAt[DK][C + PT];   // (a (.) e^{g})^T
+    __shared__ __attribute__((aligned(16))) TI sUt[DV][C + PT];   // U^T
+    __shared__ __attribute__((aligned(16))) float sAm[C][C + PF]; // A (strictly lower)
+    __shared__ __attribute__((aligned(16))) float sT[C][C + PF];  // T = (I + A)^{-1}
+    __shared__ float sX[3][16][17];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const long T = p.T;
+    const int H = (int)p.H;
+    const long t0 = (long)c * C;
+    const int nvalid = (int)min((long)C, T - t0);
+    const long NC = (T + C - 1) / C;
+    const long ch = ((long)b * H + h) * NC + c;
+    const TI *q = static_cast<const TI *>(p.q);
+    const TI *k = static_cast<const TI *>(p.k);
+    const TI *v = static_cast<const TI *>(p.v);
+    auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
+
+    // ---- phase 0: decay prefix sums and per-token write strength ------------
+    if constexpr (VT::kChannelDecay) {
+        if (tid < DK) {
+            float g = 0.f;
+            for (int r = 0; r < C; ++r) {
+                if (r < nvalid) g += logf(p.alpha[tok(r) * DK + tid]);
+                sG[r][tid] = g;
+            }
+        }
+    } else if constexpr (VT::kHasDecay) {
+        if (wave == 0) {
+            float g = lane < nvalid ? logf(p.alpha[tok(lane)]) : 0.f;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                float y = __shfl_up(g, off, kWave);
+                if (lane >= off) g += y;
+            }
+            sG[lane][0] = g;
+        }
+    } else {
+        if (tid < C) sG[tid][0] = 0.f;
+    }
+    if constexpr (VT::kScalarBeta) {
+        if constexpr (VT::kKaczmarz) {
+            // beta_r = eta_r / (||k_r||^2 + eps), from the stored keys.
+            for (int r = wave; r < C; r += kPrepThreads / kWave) {
+                float s = 0.f;
+                if (r < nvalid)
+                    for (int i = lane; i < DK; i += kWave) {
+                        float x = to_f32(k[tok(r) * DK + i]);
+                        s += x * x;
+                    }
+                s = wave_sum(s);
+                if (lane == 0) sBeta[r] = r < nvalid ? p.beta[tok(r)] / (s + p.eps) : 0.f;
+            }
+        } else {
+            if (tid < C) sBeta[tid] = tid < nvalid ? p.beta[tok(tid)] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 1: element-wise factors ------------------------------------
+    // Thread -> key channel i and groups of 8 consecutive rows, so that the
+    // transposed tiles get 16-byte writes and the global reads of a row are
+    // coalesced across lanes.
+    {
+        const int i = tid % DK;
+        const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
+        if (tid < DK) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
+        for (int r0 = 8 * (tid / DK); r0 < C; r0 += 8 * (kPrepThreads / DK)) {
+            float at[8], kb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = r0 + e;
+                float kk = 0.f, qq = 0.f, a = 0.f;
+                if (r < nvalid) {
+                    kk = to_f32(k[tok(r) * DK + i]);
+                    qq = to_f32(q[tok(r) * DK + i]);
+                    if constexpr (VT::kGates) a = p.erase_b[tok(r) * DK + i] * kk;
+                    else a = sBeta[r] * kk;
+                }
+                float eg = 1.f, egc = 1.f;
+                if constexpr (VT::kHasDecay) {
+                    const float g = sG[r][VT::kChannelDecay ? i : 0];
+                    eg = __expf(g);
+                    egc = __expf(gC - g);
+                }
+                at[e] = a * eg;
+                kb[e] = kk * egc;
+                ws.Qt[(ch * C + r) * DK + i] = from_f32<TI>(qq * eg);
+            }
+            store8(&sAt[i][r0], at);
+            store8(&ws.Kbt[(ch * DK + i) * C + r0], kb);
+        }
+        const int j = tid % DV;
+        for (int r0 = 8 * (tid / DV); r0 < C; r0 += 8 * (kPrepThreads / DV)) {
+            float u[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = r0 + e;
+                float uu = 0.f;
+                if (r < nvalid) {
+                    const float vv = to_f32(v[tok(r) * DV + j]);
+                    if constexpr (VT::kGates) uu = p.write_w[tok(r) * DV + j] * vv;
+                    else uu = sBeta[r] * vv;
+                }
+                u[e] = uu;
+            }
+            store8(&sUt[j][r0], u);
+        }
+    }
+
+    // ---- phase 2: A and P on matrix cores -----------------------------------
+    // Computed transposed, D'(s, r) = sum_i Kr[s][i] L[r][i], so a lane holds
+    // four consecutive s of one row r.  Channel-wise decay is split between
+    // the operands around the mid-chunk reference g_ref = g_{C/2-1}; scalar
+    // decay is applied to the product as e^{g_r - g_s} <= 1.
+    for (int tl = wave; tl < 10; tl += kPrepThreads / kWave) {
+        const int R = kLowerR[tl], S = kLowerS[tl];
+        const int rs = 16 * S + l16;   // row supplying the K_R operand
+        const int rr = 16 * R + l16;   // row supplying the A_L / Q_L operands
+        f32x4 accA = zero4(), accP = zero4();
+        float br = 0.f;
+        if constexpr (VT::kScalarBeta) br = sBeta[rr];
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += M::kK) {
+            const int kb = k0 + NL * lg;   // first key channel of this lane's slice
+            float kr[NL], ar[NL], qr[NL];
+            if (rs < nvalid) load_lane(&k[tok(rs) * DK + kb], kr);
+            else {
+#pragma unroll
+                for (int e = 0; e < NL; ++e) kr[e] = 0.f;
+            }
+            if (rr < nvalid) {
+                load_lane(&k[tok(rr) * DK + kb], ar);
+                load_lane(&q[tok(rr) * DK + kb], qr);
+            } else {
+#pragma unroll
+                for (int e = 0; e < NL; ++e) ar[e] = qr[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < NL; ++e) {
+                float a;
+                if constexpr (VT::kGates)
+                    a = rr < nvalid ? p.erase_b[tok(rr) * DK + kb + e] * ar[e] : 0.f;
+                else
+                    a = br * ar[e];
+                if constexpr (VT::kChannelDecay) {
+                    const float gref = sG[C / 2 - 1][kb + e];
+                    const float fl = __expf(sG[rr][kb + e] - gref);
+                    kr[e] *= __expf(gref - sG[rs][kb + e]);
+                    a *= fl;
+                    qr[e] *= fl;
+                }
+                ar[e] = a;
+            }
+            const typename M::frag fk = M::from_f32x8(kr);
+            accA = M::mma(fk, M::from_f32x8(ar), accA);
+            accP = M::mma(fk, M::from_f32x8(qr), accP);
+        }
+        // lane: row r = rr, columns s = 16 S + 4 lg + m
+        const int r = rr;
+        f32x4 Av, Pv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int s = 16 * S + 4 * lg + m;
+            float f = 1.f;
+            if constexpr (VT::kHasDecay && !VT::kChannelDecay)
+                f = s <= r ? __expf(sG[r][0] - sG[s][0]) : 0.f;
+            Av[m] = s < r ? accA[m] * f : 0.f;
+            Pv[m] = s <= r ? accP[m] * f : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(&sAm[r][16 * S + 4 * lg]) = Av;
+        store4(&ws.P[(ch * C + r) * C + 16 * S + 4 * lg], Pv);
+    }
+    for (int idx = tid; idx < 6 * 16 * 4; idx += kPrepThreads) {
+        // zero the strictly upper tiles of P (4 values per thread-step)
+        const int t6 = idx / 64, e = idx % 64;
+        const int r = 16 * kUpperR[t6] + e / 4;
+        const int s = 16 * kUpperS[t6] + 4 * (e % 4);
+        store4(&ws.P[(ch * C + r) * C + s], zero4());
+    }
+    __syncthreads();
+
+    // ---- phase 3: T = (I + A)^{-1} ------------------------------------------
+    if (wave == 0) {
+        // Diagonal blocks by forward substitution; lane = (block, column).
+        const int R = lg, cc = l16;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc += sAm[16 * R + r][16 * R + j] * x[j];
+            x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[16 * R + r][16 * R + cc] = x[r];
+    } else {
+        for (int idx = tid - kWave; idx < 6 * 256; idx += kPrepThreads - kWave) {
+            const int t6 = idx >> 8, e = idx & 255;
+            sT[16 * kUpperR[t6] + (e >> 4)][16 * kUpperS[t6] + (e & 15)] = 0.f;
+        }
+    }
+    __syncthreads();
+    // Off-diagonal blocks by distance d = R - S:
+    //   T_RS = -T_RR * sum_{J=S}^{R-1} A_RJ T_JS
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;
+        for (int idx = tid; idx < nb * 256; idx += kPrepThreads) {
+            const int blk = idx >> 8, e = idx & 255;
+            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            float acc = 0.f;
+            for (int J = S; J < R; ++J)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                    acc += sAm[16 * R + r][16 * J + jj] * sT[16 * J + jj][16 * S + cc];
+            sX[blk][r][cc] = acc;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nb * 256; idx += kPrepThreads) {
+            const int blk = idx >> 8, e = idx & 255;
+            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                acc += sT[16 * R + r][16 * R + jj] * sX[blk][jj][cc];
+            sT[16 * R + r][16 * S + cc] = -acc;
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: W = T (a (.) e^{g}) and U~ = T U on matrix cores -----------
+    {
+        const int R = wave;                                   // row tile of T
+        const int nK = (16 * (R + 1) + M::kK - 1) / M::kK;    // K-steps covering s <= r
+        typename M::frag Tf[C / M::kK];
+#pragma unroll
+        for (int ks = 0; ks < C / M::kK; ++ks) {
+            if (ks < nK) {
+                float tmp[8];
+#pragma unroll
+                for (int e = 0; e < NL; ++e) tmp[e] = sT[16 * R + l16][ks * M::kK + NL * lg + e];
+                Tf[ks] = M::from_f32x8(tmp);
+            }
+        }
+        // W'(i, r) = sum_s At[i][s] T[r][s]: lane holds W[r][i .. i+3].
+#pragma unroll 2
+        for (int mi = 0; mi < DK / 16; ++mi) {
+            f32x4 acc = zero4();
+            const TI *arow = &sAt[16 * mi + l16][0];
+#pragma unroll
+            for (int ks = 0; ks < C / M::kK; ++ks)
+                if (ks < nK) acc = M::mma(M::load(arow, ks * M::kK, lane), Tf[ks], acc);
+            store4(&ws.W[(ch * C + 16 * R + l16) * DK + 16 * mi + 4 * lg], acc);
+        }
+        // U~(r, j) = sum_s T[r][s] Ut[j][s]: lane holds U~^T[j][r .. r+3].
+#pragma unroll 2
+        for (int nj = 0; nj < DV / 16; ++nj) {
+            f32x4 acc = zero4();
+            const TI *urow = &sUt[16 * nj + l16][0];
+#pragma unroll
+            for (int ks = 0; ks < C / M::kK; ++ks)
+                if (ks < nK) acc = M::mma(Tf[ks], M::load(urow, ks * M::kK, lane), acc);
+            store4(&ws.Ut[(ch * DV + 16 * nj + l16) * C + 16 * R + 4 * lg], acc);
+        }
+    }
+}
+
+// ============================================================================
+// chunk_scan
+// ============================================================================
+template <typename TI, int DK, int NJ> struct ScanOperands {
+    using M = Mma<TI>;
+    static constexpr int KS_D = DK / M::kK;
+    static constexpr int KS_C = C / M::kK;
+    static constexpr int NI = DK / 64;       // 16-row key tiles per wave
+    typename M::frag Wf[KS_D], Qf[KS_D], Pf[KS_C], Kf[NI][KS_C];
+    f32x4 U[NJ], gam[NI];
+
+    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0,
+                                         int wave, int lane) {
+        const int l16 = lane & 15, lg = lane >> 4;
+        const int r = 16 * wave + l16;
+        const TI *wrow = ws.W + (ch * C + r) * DK;
+        const TI *qrow = ws.Qt + (ch * C + r) * DK;
+        const TI *prow = ws.P + (ch * C + r) * C;
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) {
+            Wf[ks] = M::load(wrow, ks * M::kK, lane);
+            Qf[ks] = M::load(qrow, ks * M::kK, lane);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = M::load(prow, ks * M::kK, lane);
+#pragma unroll
+        for (int a = 0; a < NI; ++a) {
+            const TI *krow = ws.Kbt + (ch * DK + 16 * (wave * NI + a) + l16) * C;
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) Kf[a][ks] = M::load(krow, ks * M::kK, lane);
+            gam[a] = load4(ws.gam + ch * DK + 16 * (wave * NI + a) + 4 * lg);
+        }
+#pragma unroll
+        for (int n = 0; n < NJ; ++n)
+            U[n] = load4(ws.Ut + (ch * DV + col0 + 16 * n + l16) * C + 16 * wave + 4 * lg);
+    }
+};
+
+template <typename TI, int DK, int NJ, bool PREFETCH>
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsPtrs<TI> ws) {
+    using M = Mma<TI>;
+    using Ops = ScanOperands<TI, DK, NJ>;
+    constexpr int KS_D = Ops::KS_D, KS_C = Ops::KS_C, NI = Ops::NI;
+    constexpr int JW = 16 * NJ;
+    constexpr int PT = 8;
+    __shared__ __attribute__((aligned(16))) TI sSt[JW][DK + PT];   // S^T (operand copy)
+    __shared__ __attribute__((aligned(16))) TI sDt[JW][C + PT];    // Delta^T
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int H = (int)p.H, DV = (int)p.dv;
+    const long T = p.T;
+    const long NC = (T + C - 1) / C;
+    const long bh = (long)b * H + h;
+    const int col0 = blockIdx.x * JW;
+    TI *out = static_cast<TI *>(p.o);
+    // K-steps of P Delta that cover s <= r for this wave's rows.
+    const int nKP = (16 * (wave + 1) + M::kK - 1) / M::kK;
+
+    // S rows i = 16 (wave*NI + a) + 4 lg + m, column j = col0 + 16 n + l16.
+    f32x4 S[NI][NJ];
+#pragma unroll
+    for (int a = 0; a < NI; ++a)
+#pragma unroll
+        for (int n = 0; n < NJ; ++n)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = 16 * (wave * NI + a) + 4 * lg + m;
+                S[a][n][m] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + 16 * n + l16] : 0.f;
+            }
+    auto write_st = [&]() {
+#pragma unroll
+        for (int a = 0; a < NI; ++a)
+#pragma unroll
+            for (int n = 0; n < NJ; ++n)
+                store4(&sSt[16 * n + l16][16 * (wave * NI + a) + 4 * lg], S[a][n]);
+    };
+    write_st();
+    __syncthreads();
+
+    Ops cur;
+    cur.load(ws, bh * NC, DV, col0, wave, lane);
+    for (long c = 0; c < NC; ++c) {
+        Ops nxt;
+        if constexpr (PREFETCH)
+            if (c + 1 < NC) nxt.load(ws, bh * NC + c + 1, DV, col0, wave, lane);
+
+        // Delta(r, j) = U~ - sum_i W[r][i] S^T[j][i];  O'(j, r) = sum_i S^T[j][i] Qt[r][i]
+        f32x4 Dl[NJ], Ov[NJ];
+#pragma unroll
+        for (int n = 0; n < NJ; ++n) {
+            Dl[n] = zero4();
+            Ov[n] = zero4();
+            const TI *srow = &sSt[16 * n + l16][0];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) {
+                const typename M::frag sf = M::load(srow, ks * M::kK, lane);
+                Dl[n] = M::mma(cur.Wf[ks], sf, Dl[n]);
+                Ov[n] = M::mma(sf, cur.Qf[ks], Ov[n]);
+            }
+            Dl[n] = cur.U[n] - Dl[n];
+            store4(&sDt[16 * n + l16][16 * wave + 4 * lg], Dl[n]);
+        }
+        __syncthreads();
+
+        const long t0 = c * C;
+        const int r = 16 * wave + l16;
+#pragma unroll
+        for (int n = 0; n < NJ; ++n) {
+            const TI *drow = &sDt[16 * n + l16][0];
+            typename M::frag Df[KS_C];
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(drow, ks * M::kK, lane);
+            // O'(j, r) += sum_s Delta^T[j][s] P[r][s]
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks)
+                if (ks < nKP) Ov[n] = M::mma(Df[ks], cur.Pf[ks], Ov[n]);
+            if (t0 + r < T)
+                store4(&out[((b * T + t0 + r) * H + h) * (long)DV + col0 + 16 * n + 4 * lg], Ov[n]);
+            // S(i, j) <- e^{g_C[i]} S + sum_s Kbar^T[i][s] Delta^T[j][s]
+#pragma unroll
+            for (int a = 0; a < NI; ++a) {
+                f32x4 acc = S[a][n] * cur.gam[a];
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(cur.Kf[a][ks], Df[ks], acc);
+                S[a][n] = acc;
+            }
+        }
+        write_st();
+        __syncthreads();
+        if constexpr (PREFETCH) {
+            cur = nxt;
+        } else {
+            if (c + 1 < NC) cur.load(ws, bh * NC + c + 1, DV, col0, wave, lane);
+        }
+    }
+    if (p.state_out) {
+#pragma unroll
+        for (int a = 0; a < NI; ++a)
+#pragma unroll
+            for (int n = 0; n < NJ; ++n)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * (wave * NI + a) + 4 * lg + m;
+                    p.state_out[(bh * DK + i) * DV + col0 + 16 * n + l16] = S[a][n][m];
+                }
+    }
+}
+
+// ---- dispatch -----------------------------------------------------------------
+
+template <int V, typename TI, int DK, int DV>
+hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
+    const WsPtrs<TI> w = ws_ptrs<TI>(p, ws);
+    const long NC = (p.T + C - 1) / C;
+    hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>),
+                       dim3((unsigned)NC, (unsigned)p.H, (unsigned)p.B), dim3(kPrepThreads), 0,
+                       stream, p, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int NJ = 1;
+    constexpr bool PF = sizeof(TI) == 2;
+    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, PF>),
+                       dim3((unsigned)(DV / (16 * NJ)), (unsigned)p.H, (unsigned)p.B),
+                       dim3(kScanThreads), 0, stream, p, w);
+    return hipGetLastError();
+}
+
+template <int V, typename TI>
+hipError_t launch_t(const Problem &p, void *ws, hipStream_t stream) {
+    if (p.dk == 128 && p.dv == 128) return launch_shape<V, TI, 128, 128>(p, ws, stream);
+    if (p.dk == 128 && p.dv == 64) return launch_shape<V, TI, 128, 64>(p, ws, stream);
+    if (p.dk == 64 && p.dv == 128) return launch_shape<V, TI, 64, 128>(p, ws, stream);
+    return launch_shape<V, TI, 64, 64>(p, ws, stream);
+}
+
+template <int V>
+hipError_t launch_v(const Problem &p, void *ws, hipStream_t stream) {
+    return p.bf16 ? launch_t<V, bf16>(p, ws, stream) : launch_t<V, float>(p, ws, stream);
+}
+
+}  // namespace
+
+size_t forward_workspace_bytes(const Problem &p) { return ws_layout(p).total; }
+
+hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream) {
+    switch (p.variant) {
+    case kDeltaNet: return launch_v<kDeltaNet>(p, workspace, stream);
+    case kGatedDeltaNet: return launch_v<kGatedDeltaNet>(p, workspace, stream);
+    case kKDA: return launch_v<kKDA>(p, workspace, stream);
+    case kGDN2: return launch_v<kGDN2>(p, workspace, stream);
+    case kKLA: return launch_v<kKLA>(p, workspace, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdr

@@ -1,0 +1,81 @@
+// gdr_device.hpp -- device-side helpers shared by the gfx950 kernels:
+// element types, vector loads/stores, wave reductions and the matrix-core
+// (MFMA) fragment operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdr_kernels.hpp"
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Sum over the 64 lanes of a wave; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// ----------------------------------------------------------------------------
+// Matrix-core tiles.  One wave computes a 16x16 fp32 tile D += A * B^T where
+// A is 16 x K and B is 16 x K, both "K-contiguous" (row-major along K).  The
+// accumulator fragment holds, in lane l, column (l % 16) and rows
+// 4*(l / 16) + {0,1,2,3}.
+//
+// bf16: v_mfma_f32_16x16x32_bf16 consumes K = 32 per instruction; lane l
+//   supplies row (l % 16) and K-elements 8*(l / 16) + {0..7} of each operand.
+// fp32: v_mfma_f32_16x16x4_f32 consumes K = 4; lane l supplies row (l % 16)
+//   and K-element (l / 16).
+// ----------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    static constexpr int kK = 32;          // K per instruction
+    static constexpr int kPerLane = 8;     // operand elements per lane
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Fragment from a K-contiguous row: elements row[k0 + 8*(lane/16) + 0..7].
+    __device__ __forceinline__ static frag load(const bf16 *row, int k0, int lane) {
+        return *reinterpret_cast<const frag *>(row + k0 + 8 * (lane >> 4));
+    }
+    __device__ __forceinline__ static frag from_f32x8(const float *x) {
+        frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (bf16)x[i];
+        return f;
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int kK = 4;
+    static constexpr int kPerLane = 1;
+    typedef float frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static frag load(const float *row, int k0, int lane) {
+        return row[k0 + (lane >> 4)];
+    }
+    __device__ __forceinline__ static frag from_f32x8(const float *x) { return x[0]; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace gdr

@@ -1,0 +1,148 @@
+// gdr_host.cpp -- the C ABI declared in include/gdr.h: argument validation
+// (pure host code, no HIP call before it passes), workspace sizing and
+// dispatch to the gfx950 kernels.
+#include <stdio.h>
+#include <stdarg.h>
+#include <string.h>
+
+#include "gdr.h"
+#include "gdr_kernels.hpp"
+
+namespace {
+
+thread_local char g_detail[512];
+
+gdr_status fail(gdr_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gdr_status check(const gdr_args *a, int for_decode) {
+    if (!a) return fail(GDR_ERR_INVALID_ARGUMENT, "args is NULL");
+    if (a->variant < GDR_DELTANET || a->variant > GDR_KLA)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "unknown variant %d", a->variant);
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "unknown dtype %d", a->dtype);
+    if (a->reserved != 0 || a->reserved_f != 0.f)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "reserved fields must be zero");
+    if (a->B < 1 || a->T < 1 || a->H < 1)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "B, T, H must be >= 1 (got %lld, %lld, %lld)",
+                    (long long)a->B, (long long)a->T, (long long)a->H);
+    if (a->dk < 1 || a->dv < 1)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "dk, dv must be >= 1");
+    if ((a->dk != 64 && a->dk != 128) || (a->dv != 64 && a->dv != 128))
+        return fail(GDR_ERR_UNSUPPORTED, "dk and dv must each be 64 or 128 (got %lld, %lld)",
+                    (long long)a->dk, (long long)a->dv);
+    if (a->B > (1 << 20) || a->H > (1 << 16) || a->T > (int64_t(1) << 31))
+        return fail(GDR_ERR_UNSUPPORTED, "B, H or T beyond the supported range");
+    if (for_decode) {
+        if (a->T != 1) return fail(GDR_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
+                                   (long long)a->T);
+        if (!a->state_in || !a->state_out)
+            return fail(GDR_ERR_INVALID_ARGUMENT, "decode needs state_in and state_out");
+    } else {
+        if (a->chunk != 0 && a->chunk != 64)
+            return fail(GDR_ERR_UNSUPPORTED, "chunk must be 0 or 64 (got %d)", a->chunk);
+    }
+    if (!a->q || !a->k || !a->v || !a->o)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "q, k, v and o are required");
+
+    const int v = a->variant;
+    const bool needs_alpha = v != GDR_DELTANET;
+    const bool needs_beta = v != GDR_GDN2;
+    const bool needs_gates = v == GDR_GDN2;
+    if (needs_alpha != (a->alpha != nullptr))
+        return fail(GDR_ERR_INVALID_ARGUMENT, needs_alpha ? "alpha is required for this variant"
+                                                          : "alpha must be NULL for DeltaNet");
+    if (needs_beta != (a->beta != nullptr))
+        return fail(GDR_ERR_INVALID_ARGUMENT, needs_beta ? "beta (eta for KLA) is required"
+                                                         : "beta must be NULL for GDN-2");
+    if (needs_gates != (a->erase_b != nullptr) || needs_gates != (a->write_w != nullptr))
+        return fail(GDR_ERR_INVALID_ARGUMENT, needs_gates
+                        ? "erase_b and write_w are required for GDN-2"
+                        : "erase_b and write_w are only used by GDN-2");
+    if (v == GDR_KLA && !(a->eps >= 0.f))
+        return fail(GDR_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+
+    const void *ptrs[] = {a->q, a->k, a->v, a->o, a->alpha, a->beta, a->erase_b,
+                          a->write_w, a->state_in, a->state_out};
+    const char *names[] = {"q", "k", "v", "o", "alpha", "beta", "erase_b",
+                           "write_w", "state_in", "state_out"};
+    for (int i = 0; i < 10; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i]))
+            return fail(GDR_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+    if (a->o == a->q || a->o == a->k || a->o == a->v)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "o must not alias an input");
+    return GDR_OK;
+}
+
+gdr::Problem to_problem(const gdr_args *a) {
+    gdr::Problem p;
+    p.variant = a->variant;
+    p.bf16 = a->dtype == GDR_BF16;
+    p.B = a->B; p.T = a->T; p.H = a->H; p.dk = a->dk; p.dv = a->dv;
+    p.chunk = a->chunk ? a->chunk : 64;
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.alpha = a->alpha; p.beta = a->beta; p.erase_b = a->erase_b; p.write_w = a->write_w;
+    p.eps = a->eps;
+    p.state_in = a->state_in; p.state_out = a->state_out;
+    p.o = a->o;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_check_args(const gdr_args *a, int for_decode) { return check(a, for_decode); }
+
+size_t gdr_forward_workspace_size(const gdr_args *a) {
+    if (check(a, 0) != GDR_OK) return 0;
+    return gdr::forward_workspace_bytes(to_problem(a));
+}
+
+gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
+                               void *hip_stream) {
+    gdr_status s = check(a, 0);
+    if (s != GDR_OK) return s;
+    gdr::Problem p = to_problem(a);
+    size_t need = gdr::forward_workspace_bytes(p);
+    if (need > 0) {
+        if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        if (ws_bytes < need)
+            return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    }
+    hipError_t e = gdr::launch_forward(p, workspace, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status gdr_decode_step(const gdr_args *a, void *hip_stream) {
+    gdr_status s = check(a, 1);
+    if (s != GDR_OK) return s;
+    hipError_t e = gdr::launch_decode(to_problem(a), reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+const char *gdr_status_string(int status) {
+    switch (status) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARGUMENT: return "GDR_ERR_INVALID_ARGUMENT";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+    default: return "unknown gdr_status";
+    }
+}
+
+const char *gdr_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// gdr_kernels.hpp -- internal interface between the C-ABI host layer
+// (gdr_host.cpp) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+enum Variant { kDeltaNet = 0, kGatedDeltaNet = 1, kKDA = 2, kGDN2 = 3, kKLA = 4 };
+
+// Compile-time facts of a variant.
+template <int V> struct VariantTraits {
+    static constexpr bool kHasDecay = V != kDeltaNet;
+    static constexpr bool kChannelDecay = V == kKDA || V == kGDN2;
+    static constexpr bool kScalarBeta = V != kGDN2;     // beta (or eta) per token
+    static constexpr bool kKaczmarz = V == kKLA;        // beta = eta / (||k||^2 + eps)
+    static constexpr bool kGates = V == kGDN2;          // erase b [dk], write w [dv]
+};
+
+// Everything a kernel needs about one call; pointers are device memory.
+struct Problem {
+    int variant;
+    int bf16;            // 1: q, k, v, o are bfloat16; 0: float32
+    int64_t B, T, H, dk, dv;
+    int chunk;
+    const void *q, *k, *v;
+    const float *alpha, *beta, *erase_b, *write_w;
+    float eps;
+    const float *state_in;
+    float *state_out;
+    void *o;
+};
+
+// Decode step (T == 1).  Returns the launch status.
+hipError_t launch_decode(const Problem &p, hipStream_t stream);
+
+// Chunked forward.
+size_t forward_workspace_bytes(const Problem &p);
+hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream);
+
+}  // namespace gdr

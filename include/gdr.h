@@ -1,0 +1,151 @@
+/*
+ * gdr.h -- C ABI of the gated delta-rule linear-attention forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Per batch row b and head h, a fast-weight state
+ * S in R^{dk x dv} (rows = key channels, columns = value channels; "Kaczmarz
+ * Linear Attention", Implementation section, which keeps the state shape
+ * S in R^{d_k x d_v}) is carried along the sequence.  Token t first decays the
+ * state, S~ = D_t S_{t-1}, then reads it along an erase key a_t and writes the
+ * residual along k_t, and the output reads the updated state:
+ *
+ *     S_t = (I - k_t a_t^T) D_t S_{t-1} + k_t u_t^T,       o_t = S_t^T q_t.
+ *
+ * Equivalently delta_t = u_t - S~^T a_t and S_t = S~ + k_t delta_t^T, which is
+ * the KLA update of "Kaczmarz Linear Attention" (KLA update rule: residual
+ * e_t = v_t - S~_{t-1}^T k_t, step S_t = S~_{t-1} + beta_t k_t e_t^T).
+ * The variants differ only in D_t, a_t and u_t:
+ *
+ *   GDR_DELTANET        D = I            a = beta k     u = beta v
+ *   GDR_GATED_DELTANET  D = alpha I      a = beta k     u = beta v
+ *   GDR_KDA             D = Diag(alpha)  a = beta k     u = beta v
+ *   GDR_GDN2            D = Diag(alpha)  a = b (.) k    u = w (.) v
+ *   GDR_KLA             D = alpha I      a = beta k     u = beta v,
+ *                       beta = eta / (||k||^2 + eps)
+ *
+ * ("Linear Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer
+ * Routing": DeltaNet writes the difference, Gated DeltaNet adds a scalar forget
+ * gate, Kimi Delta Attention makes the forget gate channel-wise, Gated
+ * DeltaNet-2 separates erase and write; "Gated DeltaNet-2: Decoupling Erase and
+ * Write in Linear Attention", novelty section: a channel-wise erase gate b_t on
+ * the key side and a channel-wise write gate w_t on the value side, reducing to
+ * KDA when both collapse to one scalar; "Kaczmarz Linear Attention", KLA update
+ * rule: the key-norm-normalised step size.)  Channel-wise decay acts on the key
+ * rows of S.
+ *
+ * Two entry points compute it: a chunkwise-parallel prefill over a whole
+ * sequence ("Kaczmarz Linear Attention", Implementation section: the
+ * chunk-wise parallel algorithm is kept and only the per-chunk diagonal
+ * coefficient matrix Diag(beta_1..beta_C) changes; "Gated DeltaNet-2", technical
+ * core: a chunkwise WY algorithm with the decay folded into the erase factor)
+ * and a single-token recurrent decode step ("Gated DeltaNet-2", introduction:
+ * a fixed-size recurrent state gives linear-time mixing and constant decode
+ * memory).
+ *
+ * Conventions (all entry points):
+ *   - Every tensor pointer is device memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; work is enqueued on the HIP
+ *     stream passed as `hip_stream` (a hipStream_t; NULL = the null stream).
+ *   - Layouts are dense row-major:
+ *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
+ *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
+ *                DELTANET: must be NULL.  Linear decay in (0, 1].
+ *       beta     DELTANET, GATED_DELTANET, KDA: beta [B, T, H];
+ *                KLA: eta [B, T, H];  GDN2: must be NULL.
+ *       erase_b  GDN2: [B, T, H, dk], else NULL.
+ *       write_w  GDN2: [B, T, H, dv], else NULL.
+ *       state_in, state_out  [B, H, dk, dv] float32.
+ *     q, k, v and o share one element type (`dtype`); gates and state are
+ *     float32.  Every pointer must be 16-byte aligned.
+ *   - Arguments are validated before any HIP call; a rejected call enqueues
+ *     nothing.  Gate values are device data and are not checked: NaN or Inf
+ *     propagate.  Launch failures return GDR_ERR_HIP; faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - The functions keep no state between calls and may be called from several
+ *     threads; a thread-local message explains the last failure.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARGUMENT = 1, /* null/extra pointer, bad size, misalignment */
+    GDR_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement */
+    GDR_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    GDR_ERR_HIP = 4               /* a HIP launch or query failed */
+} gdr_status;
+
+typedef enum {
+    GDR_DELTANET = 0,
+    GDR_GATED_DELTANET = 1,
+    GDR_KDA = 2,
+    GDR_GDN2 = 3,
+    GDR_KLA = 4
+} gdr_variant;
+
+typedef enum {
+    GDR_F32 = 0, /* q, k, v, o in float32 */
+    GDR_BF16 = 1 /* q, k, v, o in bfloat16; products on bf16 matrix cores, fp32 accumulation */
+} gdr_dtype;
+
+typedef struct gdr_args {
+    int32_t variant;   /* gdr_variant */
+    int32_t dtype;     /* gdr_dtype */
+    int64_t B, T, H;   /* batch rows, tokens, heads; all >= 1 */
+    int64_t dk, dv;    /* key and value head sizes: 64 or 128 each */
+    int32_t chunk;     /* chunk length of the prefill; 0 = default (64); decode ignores it */
+    int32_t reserved;  /* must be 0 */
+    const void *q, *k, *v;
+    const float *alpha;
+    const float *beta;
+    const float *erase_b;
+    const float *write_w;
+    float eps;         /* KLA stabiliser added to ||k||^2; ignored otherwise */
+    float reserved_f;  /* must be 0 */
+    const float *state_in; /* NULL = zero initial state */
+    float *state_out;      /* NULL = final state not written; may equal state_in */
+    void *o;               /* required */
+} gdr_args;
+
+/* Validate `a` for gdr_forward_chunked (for_decode = 0) or gdr_decode_step
+ * (for_decode = 1) without touching the GPU.  Returns GDR_OK or the error the
+ * entry point would return (GDR_ERR_WORKSPACE is never returned here). */
+gdr_status gdr_check_args(const gdr_args *a, int for_decode);
+
+/* Bytes of device workspace gdr_forward_chunked needs for `a` (0 if `a` is
+ * invalid).  The workspace holds per-chunk intermediate factors; its content
+ * is undefined before and after a call. */
+size_t gdr_forward_workspace_size(const gdr_args *a);
+
+/* Chunkwise-parallel forward over T tokens for every (b, h): writes o and,
+ * if state_out != NULL, the final state.  state_out may alias state_in; no
+ * other output may overlap an input.  `workspace` must be 256-byte aligned and
+ * at least gdr_forward_workspace_size(a) bytes.  Calls that share a workspace
+ * must be ordered on one stream. */
+gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
+                               void *hip_stream);
+
+/* One recurrent decode step (requires T == 1) for every (b, h): reads
+ * state_in (required), writes o and state_out (required; may equal state_in
+ * for an in-place update). */
+gdr_status gdr_decode_step(const gdr_args *a, void *hip_stream);
+
+/* Static description of a status code. */
+const char *gdr_status_string(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * (empty string if none). */
+const char *gdr_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */
