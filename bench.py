@@ -1,0 +1,284 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  * the chunked forward (prefill) of the Kaczmarz layer, B=1, H=16, T=65536,
+    d_k = d_v = 128, bf16 q/k/v, fp32 gates and state, writing o and S_T;
+  * 1024 single-token decode steps at batch 64 (16 heads), each a
+    read-modify-write of the 64 x 16 x 128 x 128 fp32 state in HBM, each with
+    its own pre-generated q, k, v, eta, alpha.
+
+The JSON line reports whole-step throughput (prefill tokens + decode tokens per
+second), the prefill and decode figures separately, a roofline entry for the
+dominant kernel (decode: HBM-bound) timed with HIP events on the launch stream,
+and the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 matrix cores
+C = 64                     # chunk length
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def forward_flops_per_head_token(dk, dv, c=C):
+    """Algorithmic FLOPs of the chunked method per head-token: the needed
+    triangles of A, P, W, U~, P Delta, the three state products and the
+    triangular solve."""
+    return 2 * ((c - 1) / 2 * dk + (c + 1) / 2 * dk + (c + 1) / 2 * dk + (c + 1) / 2 * dv
+                + (c + 1) / 2 * dv + 3 * dk * dv + c * c / 6)
+
+
+def forward_bytes(B, T, H, dk, dv, in_bytes=2, channel_decay=False):
+    """Algorithmic HBM bytes of one forward: q, k, v read and o written once,
+    gates read once, S_0 absent (zeros), S_T written."""
+    tok = B * T * H
+    gates = 4 * (dk if channel_decay else 1) + 4  # alpha + eta
+    return tok * (in_bytes * (2 * dk + 2 * dv) + gates) + B * H * dk * dv * 4
+
+
+def decode_bytes(B, H, dk, dv, in_bytes=2):
+    """Algorithmic HBM bytes of one decode step: state read + write, q, k, v
+    read, o written, two scalar gates."""
+    return B * H * (2 * dk * dv * 4 + in_bytes * (dk + dk + dv + dv) + 8)
+
+
+def git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                              capture_output=True, text=True).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, T_sample, decode_steps_sample, threads):
+    """Time the oracle on a bounded sample: the first T_sample tokens of the
+    prefill (all heads) and decode_steps_sample decode steps (all 64 x 16
+    heads), then scale to one full step of the workload."""
+    import numpy as np
+
+    from gated_delta_rule_85_amd.inputs import make_decode_inputs, make_inputs
+    from oracle import oracle
+
+    oracle.load()
+    inp = make_inputs(wl.variant, 1, T_sample, wl.H, wl.dk, wl.dv, wl.dtype, seed=wl.seed,
+                      alpha_scale=wl.alpha_scale, eps=wl.eps,
+                      unnormalised_keys=wl.unnormalised_keys)
+    t0 = time.perf_counter()
+    _, s_T = oracle.forward(wl.variant, inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                            beta=inp["beta"], eps=inp["eps"], threads=threads)
+    t_pre = time.perf_counter() - t0
+    dec = make_decode_inputs(wl, steps=decode_steps_sample)
+    Bd = wl.decode["B"]
+    state = np.broadcast_to(s_T, (Bd,) + s_T.shape[1:]).copy()
+    t0 = time.perf_counter()
+    for s in range(decode_steps_sample):
+        _, state = oracle.forward(wl.variant, dec["q"][s], dec["k"][s], dec["v"][s],
+                                  alpha=dec["alpha"][s], beta=dec["beta"][s], eps=dec["eps"],
+                                  state_in=state, threads=threads)
+    t_dec = time.perf_counter() - t0
+    t_step = t_pre * (wl.T / T_sample) + t_dec * (wl.decode["steps"] / decode_steps_sample)
+    tokens = wl.B * wl.T + Bd * wl.decode["steps"]
+    return dict(value=tokens / t_step, unit="tokens/s", cores=min(threads, Bd * wl.H),
+                kind="oracle",
+                sample=(f"float64 oracle: prefill of the first {T_sample} of {wl.T} tokens "
+                        f"(16 heads, {min(threads, wl.H)} threads, {t_pre:.1f} s) and "
+                        f"{decode_steps_sample} of {wl.decode['steps']} decode steps at batch "
+                        f"{Bd} ({min(threads, Bd * wl.H)} threads, {t_dec:.1f} s), scaled "
+                        f"linearly to one full step"),
+                prefill_tokens_per_s=wl.B * T_sample / t_pre,
+                decode_tokens_per_s=Bd * decode_steps_sample / t_dec)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--cpu-decode-steps", type=int, default=192)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs every (b, h) head on one "
+              "device and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import WORKLOADS, make_decode_inputs, make_workload
+
+    wl = WORKLOADS[5]
+    L = binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # ---- inputs (untimed), resident in HBM ----------------------------------
+    log("generating prefill inputs")
+    inp = make_workload(wl)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    del inp
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    fa = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"],
+                           None, None, d["eps"], None, s_T)
+    binding.check(binding.gdr_check_args(fa, 0))
+    ws_bytes = binding.gdr_forward_workspace_size(fa)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    log(f"prefill workspace {ws_bytes / 2**20:.1f} MiB")
+
+    log("generating decode inputs")
+    Sd = wl.decode["steps"]
+    Bd = wl.decode["B"]
+    dec = make_decode_inputs(wl)
+    dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in dec.items()}
+    del dec
+    state = torch.empty((Bd, H, dk, dv), dtype=torch.float32, device=dev)
+    o_dec = torch.empty((Sd, Bd, 1, H, dv), dtype=torch.bfloat16, device=dev)
+    dargs = [binding.make_args(wl.variant, dd["q"][s], dd["k"][s], dd["v"][s], o_dec[s],
+                               dd["alpha"][s], dd["beta"][s], None, None, dd["eps"],
+                               state, state) for s in range(Sd)]
+    for a in dargs:
+        binding.check(binding.gdr_check_args(a, 1))
+    fa_ref = ctypes.byref(fa)
+    dargs_ref = [ctypes.byref(a) for a in dargs]
+    fwd_fn, dec_fn = L.gdr_forward_chunked, L.gdr_decode_step
+    ws_ptr = ws.data_ptr()
+
+    # Decode starts from the prefill's final state, broadcast over the batch.
+    binding.check(fwd_fn(fa_ref, ws_ptr, ws_bytes, sh))
+    state.copy_(s_T.expand(Bd, H, dk, dv))
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(timers=None):
+        if timers is not None:
+            timers["f0"].record(stream)
+        rc = fwd_fn(fa_ref, ws_ptr, ws_bytes, sh)
+        if rc:
+            binding.check(rc)
+        if timers is not None:
+            timers["f1"].record(stream)
+            ds, de = timers["ds"], timers["de"]
+            for s in range(Sd):
+                ds[s].record(stream)
+                rc = dec_fn(dargs_ref[s], sh)
+                de[s].record(stream)
+                if rc:
+                    binding.check(rc)
+        else:
+            for s in range(Sd):
+                rc = dec_fn(dargs_ref[s], sh)
+                if rc:
+                    binding.check(rc)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timers = [dict(f0=ev(), f1=ev(), ds=[ev() for _ in range(Sd)], de=[ev() for _ in range(Sd)])
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed region done")
+
+    fwd_ms = [t["f0"].elapsed_time(t["f1"]) for t in timers]
+    dec_us = [t["ds"][s].elapsed_time(t["de"][s]) * 1e3 for t in timers for s in range(Sd)]
+    fwd_s = sum(fwd_ms) / len(fwd_ms) / 1e3
+    dec_s = sum(dec_us) / len(dec_us) / 1e6
+
+    tokens_step = B * T + Bd * Sd
+    ms_step = wall / args.steps * 1e3
+    value = tokens_step * args.steps / wall
+
+    head_tokens = B * T * H
+    fl = forward_flops_per_head_token(dk, dv) * head_tokens
+    fb = forward_bytes(B, T, H, dk, dv)
+    db = decode_bytes(Bd, H, dk, dv)
+    dec_bw = db / dec_s
+    prefill = dict(tokens_per_s=B * T / fwd_s, ms=fwd_s * 1e3,
+                   tflops=fl / fwd_s / 1e12, mfma_frac=fl / fwd_s / PEAK_BF16,
+                   hbm_GBps=fb / fwd_s / 1e9, hbm_frac=fb / fwd_s / PEAK_HBM,
+                   algorithmic_flop=fl, algorithmic_bytes=fb)
+    decode = dict(tokens_per_s=Bd / dec_s, us_per_step=dec_s * 1e6,
+                  GBps=dec_bw / 1e9, hbm_frac=dec_bw / PEAK_HBM, algorithmic_bytes=db,
+                  steps_per_bench_step=Sd, batch=Bd)
+    t_dec_total = dec_s * Sd
+    dominant = "decode" if t_dec_total >= fwd_s else "prefill"
+    if dominant == "decode":
+        roofline = dict(kernel="decode_kernel<KLA,bf16,128,64>", bound="hbm",
+                        achieved=dec_bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
+                        frac=dec_bw / PEAK_HBM, traffic=None,
+                        per_launch_bytes=db, avg_launch_us=dec_s * 1e6)
+    else:
+        roofline = dict(kernel="chunked forward", bound="hbm", achieved=fb / fwd_s / 1e9,
+                        peak=PEAK_HBM / 1e9, unit="GB/s", frac=fb / fwd_s / PEAK_HBM,
+                        traffic=None)
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = 16
+        cpu = cpu_baseline(wl, args.cpu_tokens, args.cpu_decode_steps, threads)
+
+    out = {
+        "metric": "chunked-forward tokens/s + %MFMA peak; decode tokens/s + HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"Kaczmarz LA layer: prefill B={B} H={H} T={T} d_k=d_v={dk} bf16 "
+                         f"(fp32 gates/state) + {Sd} decode steps at batch {Bd}"),
+            "variant": wl.variant, "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": C,
+            "decode_batch": Bd, "decode_steps": Sd,
+            "tokens_per_step": tokens_step,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+        "decode": decode,
+        "git": git_sha(),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

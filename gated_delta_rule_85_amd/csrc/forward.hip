@@ -40,6 +40,8 @@
 // operands, so every fragment is one 16-byte load; operand order is chosen so
 // that each lane's four accumulator values are four consecutive elements of
 // the row-major destination.
+#include <type_traits>
+
 #include "gdr_device.hpp"
 
 namespace gdr {
@@ -48,6 +50,7 @@ namespace {
 constexpr int C = 64;              // chunk length
 constexpr int kPrepThreads = 256;
 constexpr int kScanThreads = 256;
+constexpr int kXcds = 8;           // accelerator complex dies per MI355X
 
 template <typename TI> struct WsPtrs {
     TI *W;     // [nch][C][DK]   T (a (.) e^{g})
@@ -115,6 +118,10 @@ __device__ __forceinline__ f32x4 load4(const bf16 *src) {
 __device__ __forceinline__ f32x4 load4(const float *src) {
     return *reinterpret_cast<const f32x4 *>(src);
 }
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 to_f32x4(f32x4 v) { return v; }
 // kPerLane consecutive input elements as floats (8 for bf16, 1 for fp32).
 __device__ __forceinline__ void load_lane(const bf16 *src, float *x) {
     bf16x8 v = *reinterpret_cast<const bf16x8 *>(src);
@@ -415,6 +422,362 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 }
 
 // ============================================================================
+// chunk_prep, bf16 inputs: the same factors as chunk_prep_kernel, restructured
+// for memory-level parallelism.  All global reads of the chunk (q, k, v and the
+// gates) are issued at once into LDS before any arithmetic, eight waves share
+// the work, and LDS regions are reused as the phases retire them.
+// ============================================================================
+constexpr int kPrep2Threads = 512;
+
+template <int V, int DK, int DV>
+__global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem p,
+                                                                       WsPtrs<bf16> ws) {
+    using VT = VariantTraits<V>;
+    using M = Mma<bf16>;
+    constexpr int NT = kPrep2Threads, NW = NT / kWave;
+    constexpr int PT = 8, PF = 4;
+    constexpr int KP = DK + PT, VP = DV + PT, CP = C + PT, FP = C + PF;
+    constexpr int GW = VT::kChannelDecay ? DK : 1;
+    constexpr int R1 = C * KP * 2;                                         // k   -> sX
+    constexpr int R2 = C * KP * 2 > C * FP * 4 ? C * KP * 2 : C * FP * 4;  // q   -> T
+    constexpr int R3 = C * VP * 2 > C * FP * 4 ? C * VP * 2 : C * FP * 4;  // u   -> A
+    static_assert(3 * 16 * 17 * 4 <= R1, "sX fits in the k region");
+
+    __shared__ __attribute__((aligned(16))) char smem1[R1];
+    __shared__ __attribute__((aligned(16))) char smem2[R2];
+    __shared__ __attribute__((aligned(16))) char smem3[R3];
+    __shared__ __attribute__((aligned(16))) bf16 sAg[VT::kGates ? C : 1][KP];  // b (.) k
+    __shared__ __attribute__((aligned(16))) float sG[C][GW];
+    __shared__ float sBeta[C];
+    __shared__ __attribute__((aligned(16))) bf16 sAt[DK][CP];   // (a (.) e^{g})^T
+    __shared__ __attribute__((aligned(16))) bf16 sUt[DV][CP];   // U^T
+    auto sK = reinterpret_cast<bf16 (*)[KP]>(smem1);
+    auto sQ = reinterpret_cast<bf16 (*)[KP]>(smem2);
+    auto sV = reinterpret_cast<bf16 (*)[VP]>(smem3);
+    auto sX = reinterpret_cast<float (*)[16][17]>(smem1);
+    auto sT = reinterpret_cast<float (*)[FP]>(smem2);
+    auto sAm = reinterpret_cast<float (*)[FP]>(smem3);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const long T = p.T;
+    const int H = (int)p.H;
+    const long t0 = (long)c * C;
+    const int nvalid = (int)min((long)C, T - t0);
+    const long NC = (T + C - 1) / C;
+    const long ch = ((long)b * H + h) * NC + c;
+    const bf16 *q = static_cast<const bf16 *>(p.q);
+    const bf16 *k = static_cast<const bf16 *>(p.k);
+    const bf16 *v = static_cast<const bf16 *>(p.v);
+    auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
+
+    // ---- load: every global read of the chunk, issued together --------------
+    constexpr int PK = DK / 8, PV = DV / 8;
+#pragma unroll
+    for (int idx = tid; idx < C * PK; idx += NT) {
+        const int r = idx / PK, pc = idx % PK;
+        bf16x8 kv, qv;
+        if (r < nvalid) {
+            kv = *reinterpret_cast<const bf16x8 *>(&k[tok(r) * DK + 8 * pc]);
+            qv = *reinterpret_cast<const bf16x8 *>(&q[tok(r) * DK + 8 * pc]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kv[e] = qv[e] = (bf16)0.f;
+        }
+        *reinterpret_cast<bf16x8 *>(&sK[r][8 * pc]) = kv;
+        *reinterpret_cast<bf16x8 *>(&sQ[r][8 * pc]) = qv;
+        if constexpr (VT::kGates) {
+            bf16x8 av;
+            if (r < nvalid) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    av[e] = (bf16)(b0[e] * (float)kv[e]);
+                    av[e + 4] = (bf16)(b1[e] * (float)kv[e + 4]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) av[e] = (bf16)0.f;
+            }
+            *reinterpret_cast<bf16x8 *>(&sAg[r][8 * pc]) = av;
+        }
+    }
+#pragma unroll
+    for (int idx = tid; idx < C * PV; idx += NT) {
+        const int r = idx / PV, pc = idx % PV;
+        bf16x8 vv;
+        if (r < nvalid) {
+            vv = *reinterpret_cast<const bf16x8 *>(&v[tok(r) * DV + 8 * pc]);
+            if constexpr (VT::kGates) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc + 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vv[e] = (bf16)(w0[e] * (float)vv[e]);
+                    vv[e + 4] = (bf16)(w1[e] * (float)vv[e + 4]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = (bf16)0.f;
+        }
+        *reinterpret_cast<bf16x8 *>(&sV[r][8 * pc]) = vv;
+    }
+    if constexpr (VT::kChannelDecay) {
+#pragma unroll
+        for (int idx = tid; idx < C * DK / 4; idx += NT) {
+            const int r = idx / (DK / 4), i4 = 4 * (idx % (DK / 4));
+            f32x4 a = f32x4{1.f, 1.f, 1.f, 1.f};
+            if (r < nvalid) a = *reinterpret_cast<const f32x4 *>(&p.alpha[tok(r) * DK + i4]);
+            *reinterpret_cast<f32x4 *>(&sG[r][i4]) = a;
+        }
+    } else if constexpr (VT::kHasDecay) {
+        if (wave == 0) sG[lane][0] = lane < nvalid ? p.alpha[tok(lane)] : 1.f;
+    } else {
+        if (tid < C) sG[tid][0] = 0.f;
+    }
+    if constexpr (VT::kScalarBeta)
+        if (tid >= NT - C) {
+            const int r = tid - (NT - C);
+            sBeta[r] = r < nvalid ? p.beta[tok(r)] : 0.f;
+        }
+    __syncthreads();
+
+    // ---- gates: decay prefix sums; KLA step size ------------------------------
+    if constexpr (VT::kChannelDecay) {
+        if (tid < DK) {
+            float g = 0.f;
+            for (int r = 0; r < C; ++r) {
+                g += logf(sG[r][tid]);
+                sG[r][tid] = g;
+            }
+        }
+    } else if constexpr (VT::kHasDecay) {
+        if (wave == 0) {
+            float g = logf(sG[lane][0]);
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_up(g, off, kWave);
+                if (lane >= off) g += y;
+            }
+            sG[lane][0] = g;
+        }
+    }
+    if constexpr (VT::kKaczmarz) {
+        // beta_r = eta_r / (||k_r||^2 + eps), from the stored keys: eight lanes
+        // per row, all 64 rows at once.
+        static_assert(NT == 8 * C, "eight lanes per row");
+        const int r = tid >> 3, part = tid & 7;
+        float s2 = 0.f;
+#pragma unroll
+        for (int i = 8 * part; i < DK; i += 64) {
+            const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(&sK[r][i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s2 += (float)kv[e] * (float)kv[e];
+        }
+        s2 += __shfl_xor(s2, 1, kWave);
+        s2 += __shfl_xor(s2, 2, kWave);
+        s2 += __shfl_xor(s2, 4, kWave);
+        if (part == 0) sBeta[r] = r < nvalid ? sBeta[r] / (s2 + p.eps) : 0.f;
+    }
+    __syncthreads();
+
+    // ---- phase 1: element-wise factors ------------------------------------
+    {
+        // q (.) e^{g}, row-major, 16-byte pieces
+#pragma unroll
+        for (int idx = tid; idx < C * PK; idx += NT) {
+            const int r = idx / PK, pc = idx % PK;
+            const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(&sQ[r][8 * pc]);
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float eg = 1.f;
+                if constexpr (VT::kHasDecay) eg = __expf(sG[r][VT::kChannelDecay ? 8 * pc + e : 0]);
+                o[e] = (bf16)((float)qv[e] * eg);
+            }
+            *reinterpret_cast<bf16x8 *>(&ws.Qt[(ch * C + r) * DK + 8 * pc]) = o;
+        }
+        // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace
+#pragma unroll
+        for (int idx = tid; idx < DK * (C / 8); idx += NT) {
+            const int i = idx % DK, r0 = 8 * (idx / DK);
+            const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
+            float at[8], kb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = r0 + e;
+                const float kk = (float)sK[r][i];
+                float a;
+                if constexpr (VT::kGates) a = (float)sAg[r][i];
+                else a = sBeta[r] * kk;
+                float eg = 1.f, egc = 1.f;
+                if constexpr (VT::kHasDecay) {
+                    const float g = sG[r][VT::kChannelDecay ? i : 0];
+                    eg = __expf(g);
+                    egc = __expf(gC - g);
+                }
+                at[e] = a * eg;
+                kb[e] = kk * egc;
+            }
+            store8(&sAt[i][r0], at);
+            store8(&ws.Kbt[(ch * DK + i) * C + r0], kb);
+            if (idx < DK) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
+        }
+        // U^T into LDS
+#pragma unroll
+        for (int idx = tid; idx < DV * (C / 8); idx += NT) {
+            const int j = idx % DV, r0 = 8 * (idx / DV);
+            float u[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float vv = (float)sV[r0 + e][j];
+                if constexpr (VT::kGates) u[e] = vv;
+                else u[e] = sBeta[r0 + e] * vv;
+            }
+            store8(&sUt[j][r0], u);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: A and P on matrix cores (operands from LDS) -----------------
+    for (int tl = wave; tl < 10; tl += NW) {
+        const int R = kLowerR[tl], S = kLowerS[tl];
+        const int rs = 16 * S + l16;
+        const int rr = 16 * R + l16;
+        f32x4 accA = zero4(), accP = zero4();
+        float br = 0.f;
+        if constexpr (VT::kScalarBeta) br = sBeta[rr];
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += M::kK) {
+            const int kb = k0 + 8 * lg;
+            const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[rs][kb]);
+            const bf16x8 qr8 = *reinterpret_cast<const bf16x8 *>(&sQ[rr][kb]);
+            bf16x8 ar8;
+            if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[rr][kb]);
+            else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[rr][kb]);
+            float kr[8], ar[8], qr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kr[e] = (float)kr8[e];
+                qr[e] = (float)qr8[e];
+                ar[e] = VT::kGates ? (float)ar8[e] : br * (float)ar8[e];
+                if constexpr (VT::kChannelDecay) {
+                    const float gref = sG[C / 2 - 1][kb + e];
+                    const float fl = __expf(sG[rr][kb + e] - gref);
+                    kr[e] *= __expf(gref - sG[rs][kb + e]);
+                    ar[e] *= fl;
+                    qr[e] *= fl;
+                }
+            }
+            const M::frag fk = M::from_f32x8(kr);
+            accA = M::mma(fk, M::from_f32x8(ar), accA);
+            accP = M::mma(fk, M::from_f32x8(qr), accP);
+        }
+        const int r = rr;
+        f32x4 Av, Pv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int s2 = 16 * S + 4 * lg + m;
+            float f = 1.f;
+            if constexpr (VT::kHasDecay && !VT::kChannelDecay)
+                f = s2 <= r ? __expf(sG[r][0] - sG[s2][0]) : 0.f;
+            Av[m] = s2 < r ? accA[m] * f : 0.f;
+            Pv[m] = s2 <= r ? accP[m] * f : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(&sAm[r][16 * S + 4 * lg]) = Av;
+        store4(&ws.P[(ch * C + r) * C + 16 * S + 4 * lg], Pv);
+    }
+    for (int idx = tid; idx < 6 * 16 * 4; idx += NT) {
+        const int t6 = idx / 64, e = idx % 64;
+        const int r = 16 * kUpperR[t6] + e / 4;
+        const int s2 = 16 * kUpperS[t6] + 4 * (e % 4);
+        store4(&ws.P[(ch * C + r) * C + s2], zero4());
+    }
+    __syncthreads();
+
+    // ---- phase 3: T = (I + A)^{-1} ------------------------------------------
+    if (wave == 0) {
+        const int R = lg, cc = l16;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc += sAm[16 * R + r][16 * R + j] * x[j];
+            x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[16 * R + r][16 * R + cc] = x[r];
+    } else {
+        for (int idx = tid - kWave; idx < 6 * 256; idx += NT - kWave) {
+            const int t6 = idx >> 8, e = idx & 255;
+            sT[16 * kUpperR[t6] + (e >> 4)][16 * kUpperS[t6] + (e & 15)] = 0.f;
+        }
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        const int nb = 4 - d;
+        for (int idx = tid; idx < nb * 256; idx += NT) {
+            const int blk = idx >> 8, e = idx & 255;
+            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            float acc = 0.f;
+            for (int J = S; J < R; ++J)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                    acc += sAm[16 * R + r][16 * J + jj] * sT[16 * J + jj][16 * S + cc];
+            sX[blk][r][cc] = acc;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nb * 256; idx += NT) {
+            const int blk = idx >> 8, e = idx & 255;
+            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            float acc = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) acc += sT[16 * R + r][16 * R + jj] * sX[blk][jj][cc];
+            sT[16 * R + r][16 * S + cc] = -acc;
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: W and U~ on matrix cores --------------------------------------
+    {
+        const int R = wave & 3, half = wave >> 2;
+        const int nK = R / 2 + 1;                 // K-steps of 32 covering s <= r
+        M::frag Tf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks < nK) {
+                float tmp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tmp[e] = sT[16 * R + l16][32 * ks + 8 * lg + e];
+                Tf[ks] = M::from_f32x8(tmp);
+            }
+        }
+#pragma unroll
+        for (int mi = half * (DK / 32); mi < (half + 1) * (DK / 32); ++mi) {
+            f32x4 acc = zero4();
+            const bf16 *arow = &sAt[16 * mi + l16][0];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < nK) acc = M::mma(M::load(arow, 32 * ks, lane), Tf[ks], acc);
+            store4(&ws.W[(ch * C + 16 * R + l16) * DK + 16 * mi + 4 * lg], acc);
+        }
+#pragma unroll
+        for (int nj = half * (DV / 32); nj < (half + 1) * (DV / 32); ++nj) {
+            f32x4 acc = zero4();
+            const bf16 *urow = &sUt[16 * nj + l16][0];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < nK) acc = M::mma(Tf[ks], M::load(urow, 32 * ks, lane), acc);
+            store4(&ws.Ut[(ch * DV + 16 * nj + l16) * C + 16 * R + 4 * lg], acc);
+        }
+    }
+}
+
+// ============================================================================
 // chunk_scan
 // ============================================================================
 template <typename TI, int DK, int NJ> struct ScanOperands {
@@ -422,8 +785,12 @@ template <typename TI, int DK, int NJ> struct ScanOperands {
     static constexpr int KS_D = DK / M::kK;
     static constexpr int KS_C = C / M::kK;
     static constexpr int NI = DK / 64;       // 16-row key tiles per wave
+    // Raw loaded values only: a conversion here would make the compiler wait
+    // for the load at once and defeat the prefetch.
+    typedef typename std::conditional<sizeof(TI) == 2, bf16x4, f32x4>::type raw4;
     typename M::frag Wf[KS_D], Qf[KS_D], Pf[KS_C], Kf[NI][KS_C];
-    f32x4 U[NJ], gam[NI];
+    raw4 U[NJ];
+    f32x4 gam[NI];
 
     __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0,
                                          int wave, int lane) {
@@ -448,11 +815,12 @@ template <typename TI, int DK, int NJ> struct ScanOperands {
         }
 #pragma unroll
         for (int n = 0; n < NJ; ++n)
-            U[n] = load4(ws.Ut + (ch * DV + col0 + 16 * n + l16) * C + 16 * wave + 4 * lg);
+            U[n] = *reinterpret_cast<const raw4 *>(ws.Ut + (ch * DV + col0 + 16 * n + l16) * C +
+                                                   16 * wave + 4 * lg);
     }
 };
 
-template <typename TI, int DK, int NJ, bool PREFETCH>
+template <typename TI, int DK, int NJ, int DEPTH, int LOOK>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsPtrs<TI> ws) {
     using M = Mma<TI>;
     using Ops = ScanOperands<TI, DK, NJ>;
@@ -464,12 +832,20 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsP
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int h = blockIdx.y, b = blockIdx.z;
     const int H = (int)p.H, DV = (int)p.dv;
     const long T = p.T;
     const long NC = (T + C - 1) / C;
-    const long bh = (long)b * H + h;
-    const int col0 = blockIdx.x * JW;
+    // Workgroups are dispatched round-robin over the 8 XCDs.  Remap so that
+    // the column slices of one head, which read the same chunk factors, run
+    // on the same XCD and share its L2.
+    const int nslice = DV / JW;
+    const long nwg = p.B * p.H * nslice;
+    const long per_xcd = (nwg + kXcds - 1) / kXcds;
+    const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical >= nwg) return;
+    const long bh = logical / nslice;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int col0 = (int)(logical % nslice) * JW;
     TI *out = static_cast<TI *>(p.o);
     // K-steps of P Delta that cover s <= r for this wave's rows.
     const int nKP = (16 * (wave + 1) + M::kK - 1) / M::kK;
@@ -495,60 +871,141 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsP
     write_st();
     __syncthreads();
 
-    Ops cur;
-    cur.load(ws, bh * NC, DV, col0, wave, lane);
-    for (long c = 0; c < NC; ++c) {
-        Ops nxt;
-        if constexpr (PREFETCH)
-            if (c + 1 < NC) nxt.load(ws, bh * NC + c + 1, DV, col0, wave, lane);
-
-        // Delta(r, j) = U~ - sum_i W[r][i] S^T[j][i];  O'(j, r) = sum_i S^T[j][i] Qt[r][i]
-        f32x4 Dl[NJ], Ov[NJ];
+    // One chunk of the sequential pass with the factors held in `op`.  The
+    // state recurrence (Delta, then S) is the critical path; the output
+    // products are issued where they overlap its latencies.
+    auto step = [&](const Ops &op, long c) __attribute__((always_inline)) {
+        typename M::frag Sf[NJ][KS_D];
+#pragma unroll
+        for (int n = 0; n < NJ; ++n)
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) Sf[n][ks] = M::load(&sSt[16 * n + l16][0], ks * M::kK, lane);
+        // Delta(r, j) = U~ - sum_i W[r][i] S^T[j][i], two interleaved partial sums
+        f32x4 Ov[NJ];
 #pragma unroll
         for (int n = 0; n < NJ; ++n) {
-            Dl[n] = zero4();
-            Ov[n] = zero4();
-            const TI *srow = &sSt[16 * n + l16][0];
+            f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) {
-                const typename M::frag sf = M::load(srow, ks * M::kK, lane);
-                Dl[n] = M::mma(cur.Wf[ks], sf, Dl[n]);
-                Ov[n] = M::mma(sf, cur.Qf[ks], Ov[n]);
+            for (int ks = 0; ks < KS_D; ks += 2) {
+                d0 = M::mma(op.Wf[ks], Sf[n][ks], d0);
+                if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[n][ks + 1], d1);
             }
-            Dl[n] = cur.U[n] - Dl[n];
-            store4(&sDt[16 * n + l16][16 * wave + 4 * lg], Dl[n]);
+            const f32x4 Dl = to_f32x4(op.U[n]) - (d0 + d1);
+            store4(&sDt[16 * n + l16][16 * wave + 4 * lg], Dl);
+        }
+        // O'(j, r) = sum_i S^T[j][i] Qt[r][i]   (overlaps the barrier below)
+#pragma unroll
+        for (int n = 0; n < NJ; ++n) {
+            Ov[n] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) Ov[n] = M::mma(Sf[n][ks], op.Qf[ks], Ov[n]);
         }
         __syncthreads();
 
+        typename M::frag Df[NJ][KS_C];
+#pragma unroll
+        for (int n = 0; n < NJ; ++n)
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) Df[n][ks] = M::load(&sDt[16 * n + l16][0], ks * M::kK, lane);
+        // S(i, j) <- e^{g_C[i]} S + sum_s Kbar^T[i][s] Delta^T[j][s]
+#pragma unroll
+        for (int n = 0; n < NJ; ++n)
+#pragma unroll
+            for (int a = 0; a < NI; ++a) {
+                f32x4 acc = S[a][n] * op.gam[a];
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[n][ks], acc);
+                S[a][n] = acc;
+            }
+        write_st();
+        // O'(j, r) += sum_s Delta^T[j][s] P[r][s], then the output rows
         const long t0 = c * C;
         const int r = 16 * wave + l16;
 #pragma unroll
         for (int n = 0; n < NJ; ++n) {
-            const TI *drow = &sDt[16 * n + l16][0];
-            typename M::frag Df[KS_C];
-#pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(drow, ks * M::kK, lane);
-            // O'(j, r) += sum_s Delta^T[j][s] P[r][s]
 #pragma unroll
             for (int ks = 0; ks < KS_C; ++ks)
-                if (ks < nKP) Ov[n] = M::mma(Df[ks], cur.Pf[ks], Ov[n]);
+                if (ks < nKP) Ov[n] = M::mma(Df[n][ks], op.Pf[ks], Ov[n]);
             if (t0 + r < T)
                 store4(&out[((b * T + t0 + r) * H + h) * (long)DV + col0 + 16 * n + 4 * lg], Ov[n]);
-            // S(i, j) <- e^{g_C[i]} S + sum_s Kbar^T[i][s] Delta^T[j][s]
-#pragma unroll
-            for (int a = 0; a < NI; ++a) {
-                f32x4 acc = S[a][n] * cur.gam[a];
-#pragma unroll
-                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(cur.Kf[a][ks], Df[ks], acc);
-                S[a][n] = acc;
-            }
         }
-        write_st();
         __syncthreads();
-        if constexpr (PREFETCH) {
-            cur = nxt;
-        } else {
-            if (c + 1 < NC) cur.load(ws, bh * NC + c + 1, DV, col0, wave, lane);
+    };
+
+    const long ch0 = bh * NC;
+    const long last = NC - 1;
+    // Past the end the loads re-read the last chunk, so the number of loads in
+    // flight is the same on every path and the waits stay exact.
+    auto chunk = [&](long c) { return ch0 + (c < last ? c : last); };
+    if constexpr (DEPTH == 3) {
+        // Three register sets in rotation: chunk c + 2 in flight while chunk
+        // c is computed, with no register copies.
+        Ops A, Bq, Cq;
+        A.load(ws, chunk(0), DV, col0, wave, lane);
+        Bq.load(ws, chunk(1), DV, col0, wave, lane);
+        for (long c = 0; c < NC; c += 3) {
+            Cq.load(ws, chunk(c + 2), DV, col0, wave, lane);
+            step(A, c);
+            if (c + 1 >= NC) break;
+            A.load(ws, chunk(c + 3), DV, col0, wave, lane);
+            step(Bq, c + 1);
+            if (c + 2 >= NC) break;
+            Bq.load(ws, chunk(c + 4), DV, col0, wave, lane);
+            step(Cq, c + 2);
+        }
+    } else if constexpr (DEPTH == 2) {
+        // Two register sets in rotation, plus an L2 prefetch of the chunk
+        // LOOK chunks ahead: one 4-byte read per 128-byte line of the factors
+        // this workgroup will stream, whose result is only folded into a sink
+        // after a later wait has retired it, so it never stalls.
+        unsigned sink = 0;
+        constexpr int LW = C * DK * (int)sizeof(TI) / 128;   // lines of one W, Qt or Kbar^T tile
+        constexpr int LP = C * C * (int)sizeof(TI) / 128;    // lines of one P tile
+        constexpr int LU = JW * C * (int)sizeof(TI) / 128;   // lines of this slice of U~^T
+        constexpr int LT = 3 * LW + LP + LU;
+        auto touch = [&](long c) -> uint2 {
+            const long ch = chunk(c);
+            uint2 t;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                int li = tid + u * kScanThreads;
+                li = li < LT ? li : LT - 1;
+                const char *base;
+                if (li < LW)
+                    base = reinterpret_cast<const char *>(ws.W + ch * C * DK) + 128 * li;
+                else if (li < 2 * LW)
+                    base = reinterpret_cast<const char *>(ws.Qt + ch * C * DK) + 128 * (li - LW);
+                else if (li < 3 * LW)
+                    base = reinterpret_cast<const char *>(ws.Kbt + ch * C * DK) + 128 * (li - 2 * LW);
+                else if (li < 3 * LW + LP)
+                    base = reinterpret_cast<const char *>(ws.P + ch * C * C) + 128 * (li - 3 * LW);
+                else
+                    base = reinterpret_cast<const char *>(ws.Ut + (ch * DV + col0) * C) +
+                           128 * (li - 3 * LW - LP);
+                t[u] = *reinterpret_cast<const unsigned *>(base);
+            }
+            return t;
+        };
+        Ops A, Bq;
+        A.load(ws, chunk(0), DV, col0, wave, lane);
+        uint2 tA = make_uint2(0, 0), tB = make_uint2(0, 0);
+        for (long c = 0; c < NC; c += 2) {
+            if constexpr (LOOK > 0) tA = touch(c + LOOK);
+            Bq.load(ws, chunk(c + 1), DV, col0, wave, lane);
+            step(A, c);
+            sink ^= tB.x ^ tB.y;
+            if (c + 1 >= NC) break;
+            if constexpr (LOOK > 0) tB = touch(c + 1 + LOOK);
+            A.load(ws, chunk(c + 2), DV, col0, wave, lane);
+            step(Bq, c + 1);
+            sink ^= tA.x ^ tA.y;
+        }
+        if (sink == 0x9e3779b9u && T < 0) out[0] = from_f32<TI>(0.f);   // keeps the reads alive
+    } else {
+        Ops cur;
+        for (long c = 0; c < NC; ++c) {
+            cur.load(ws, ch0 + c, DV, col0, wave, lane);
+            step(cur, c);
         }
     }
     if (p.state_out) {
@@ -570,15 +1027,20 @@ template <int V, typename TI, int DK, int DV>
 hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     const WsPtrs<TI> w = ws_ptrs<TI>(p, ws);
     const long NC = (p.T + C - 1) / C;
-    hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>),
-                       dim3((unsigned)NC, (unsigned)p.H, (unsigned)p.B), dim3(kPrepThreads), 0,
-                       stream, p, w);
+    const dim3 pgrid((unsigned)NC, (unsigned)p.H, (unsigned)p.B);
+    if constexpr (sizeof(TI) == 2)
+        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), pgrid, dim3(kPrep2Threads), 0,
+                           stream, p, w);
+    else
+        hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>), pgrid, dim3(kPrepThreads), 0,
+                           stream, p, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int NJ = 1;
-    constexpr bool PF = sizeof(TI) == 2;
-    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, PF>),
-                       dim3((unsigned)(DV / (16 * NJ)), (unsigned)p.H, (unsigned)p.B),
+    constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
+    const long nwg = p.B * p.H * (DV / (16 * NJ));
+    const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, DEPTH, 0>), dim3((unsigned)grid),
                        dim3(kScanThreads), 0, stream, p, w);
     return hipGetLastError();
 }

@@ -38,8 +38,10 @@ gdr_status check(const gdr_args *a, int for_decode) {
     if ((a->dk != 64 && a->dk != 128) || (a->dv != 64 && a->dv != 128))
         return fail(GDR_ERR_UNSUPPORTED, "dk and dv must each be 64 or 128 (got %lld, %lld)",
                     (long long)a->dk, (long long)a->dv);
-    if (a->B > (1 << 20) || a->H > (1 << 16) || a->T > (int64_t(1) << 31))
-        return fail(GDR_ERR_UNSUPPORTED, "B, H or T beyond the supported range");
+    if (a->B > 65535 || a->H > 65535 || a->B * a->H > (int64_t(1) << 26) ||
+        a->T > (int64_t(1) << 31))
+        return fail(GDR_ERR_UNSUPPORTED, "B, H or T beyond the supported range "
+                    "(B, H <= 65535, B*H <= 2^26, T <= 2^31)");
     if (for_decode) {
         if (a->T != 1) return fail(GDR_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
                                    (long long)a->T);
