@@ -58,6 +58,25 @@ def decode_bytes(B, H, dk, dv, in_bytes=2):
     return B * H * (2 * dk * dv * 4 + in_bytes * (dk + dk + dv + dv) + 8)
 
 
+def measured_traffic(kernel: str, source: str):
+    """HBM bytes per dispatch of `kernel` from the committed counter summary,
+    or None if the kernel source has changed since the counters were taken."""
+    import glob
+    import hashlib
+    try:
+        sha = hashlib.sha1(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:12]
+    except OSError:
+        return None
+    for path in glob.glob(os.path.join(ROOT, "profiles", "hbm_counters_*.txt")):
+        for line in open(path):
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
+                kv = dict(x.split("=", 1) for x in parts[2:])
+                if kv.get("source_sha1") == sha:
+                    return int(kv["bytes_per_dispatch"])
+    return None
+
+
 def git_sha():
     try:
         return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
@@ -262,7 +281,11 @@ def main():
     if dominant == "decode":
         roofline = dict(kernel="decode_wave_kernel<KLA,bf16,128,32,4>", bound="hbm",
                         achieved=dec_bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
-                        frac=dec_bw / PEAK_HBM, traffic=None,
+                        frac=dec_bw / PEAK_HBM,
+                        traffic=measured_traffic("decode_wave_kernel",
+                                                 "gated_delta_rule_85_amd/csrc/decode.hip"),
+                        traffic_unit="bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
                         per_launch_bytes=db, avg_launch_us=dec_s * 1e6)
     else:
         roofline = dict(kernel="chunked forward", bound="hbm", achieved=fb / fwd_s / 1e9,

@@ -1,0 +1,85 @@
+"""Summaries of rocprofv3 result databases (rocpd SQLite) for this library.
+
+    python -m gated_delta_rule_85_amd.rocpd_summary trace RUN_results.db
+        per-kernel dispatch count and duration (from --kernel-trace --stats)
+
+    python -m gated_delta_rule_85_amd.rocpd_summary pmc FETCH.db WRITE.db [COPY_BYTES]
+        mean FETCH_SIZE / WRITE_SIZE per dispatch (KiB) from two --pmc runs,
+        and bytes per dispatch after calibration against the plain device copy
+        of COPY_BYTES bytes found in the same runs (its counters divided by its
+        known size give the factor that turns a counter into bytes)
+"""
+from __future__ import annotations
+
+import collections
+import sqlite3
+import sys
+
+PREFIX = "_ZN3gdr12_GLOBAL__N_1"
+
+
+def _short(name: str, width: int = 70) -> str:
+    return name.replace(PREFIX, "")[:width]
+
+
+def trace(db: str) -> str:
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select name, count(*), avg(duration), sum(duration), min(duration), max(duration) "
+        "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[3] for r in rows) or 1
+    out = ["| kernel | calls | avg us | min us | max us | total us | % |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for n, c, avg, tot, mn, mx in rows:
+        out.append(f"| `{_short(n)}` | {c} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
+                   f"{tot / 1e3:.1f} | {100 * tot / total:.1f} |")
+    return "\n".join(out)
+
+
+def _pmc(db: str):
+    con = sqlite3.connect(db)
+    agg = collections.defaultdict(list)
+    for name, counter, value in con.execute(
+            "select kernel_name, counter_name, value from counters_collection"):
+        agg[(name, counter)].append(value)
+    return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
+
+
+def pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 28) -> str:
+    f, fn = _pmc(fetch_db)
+    w, _ = _pmc(write_db)
+    copy = [k for k in f if "copyBuffer" in k[0]]
+    fr = wr = None
+    if copy:
+        name = copy[0][0]
+        fr = f[(name, "FETCH_SIZE")] * 1024 / copy_bytes
+        wr = w.get((name, "WRITE_SIZE"), 0) * 1024 / copy_bytes
+    lines = [f"calibration (plain device copy of {copy_bytes} bytes): "
+             f"FETCH_SIZE reads {fr:.4f} x bytes, WRITE_SIZE reads {wr:.4f} x bytes"
+             if fr else "calibration: no copy kernel found"]
+    lines.append("kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | write bytes | "
+                 "total bytes (calibrated, per dispatch)")
+    for (name, counter), val in sorted(f.items(), key=lambda kv: -kv[1]):
+        if counter != "FETCH_SIZE":
+            continue
+        wv = w.get((name, "WRITE_SIZE"), float("nan"))
+        rb = val * 1024 / fr if fr else float("nan")
+        wb = wv * 1024 / wr if wr else float("nan")
+        lines.append(f"{_short(name)} | {fn[(name, counter)]} | {val:.1f} | {wv:.1f} | "
+                     f"{rb:.4g} | {wb:.4g} | {rb + wb:.4g}")
+    return "\n".join(lines)
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "trace":
+        print(trace(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "pmc":
+        print(pmc(argv[1], argv[2], int(argv[3]) if len(argv) > 3 else 1 << 28))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
