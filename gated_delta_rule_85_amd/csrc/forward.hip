@@ -39,7 +39,8 @@
 // All products are written as D = A * B^T over a K-contiguous pair of
 // operands, so every fragment is one 16-byte load; operand order is chosen so
 // that each lane's four accumulator values are four consecutive elements of
-// the row-major destination.
+// the destination.  The chunk factors are stored fragment-major, so the scan
+// reads each operand tile as one contiguous 1 KB block.
 #include <type_traits>
 
 #include "gdr_device.hpp"
@@ -52,13 +53,15 @@ constexpr int kPrepThreads = 256;
 constexpr int kScanThreads = 256;
 constexpr int kXcds = 8;           // accelerator complex dies per MI355X
 
+// Per chunk-head factors, each block contiguous; the operand factors are
+// stored fragment-major (frag_off / ufrag_off below).
 template <typename TI> struct WsPtrs {
-    TI *W;     // [nch][C][DK]   T (a (.) e^{g})
-    TI *Ut;    // [nch][DV][C]   (T U)^T
-    TI *Qt;    // [nch][C][DK]   q (.) e^{g}
-    TI *Kbt;   // [nch][DK][C]   (k (.) e^{g_C - g})^T
-    TI *P;     // [nch][C][C]    decayed q k^T, lower triangle incl. diagonal
-    float *gam;// [nch][DK]      e^{g_C}
+    TI *W;     // [nch] C x DK    T (a (.) e^{g})
+    TI *Ut;    // [nch] DV x C    (T U)^T, accumulator layout
+    TI *Qt;    // [nch] C x DK    q (.) e^{g}
+    TI *Kbt;   // [nch] DK x C    (k (.) e^{g_C - g})^T
+    TI *P;     // [nch] C x C     decayed q k^T, lower triangle incl. diagonal
+    float *gam;// [nch][DK]       e^{g_C}
 };
 
 struct WsLayout {
@@ -129,6 +132,40 @@ __device__ __forceinline__ void load_lane(const bf16 *src, float *x) {
     for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
 }
 __device__ __forceinline__ void load_lane(const float *src, float *x) { x[0] = *src; }
+
+
+// ---- fragment-major workspace layout ------------------------------------------
+// Each rows x K operand factor is stored as 16-row tiles by K-steps of the
+// matrix-core instruction, and inside a tile in MFMA lane order, so that one
+// wave's fragment load of a tile is one contiguous 1 KB (bf16) read: whole
+// cache lines, no half-used lines.
+template <typename TI> __device__ __forceinline__ long frag_off(int r, int k, int K) {
+    using M = Mma<TI>;
+    const int tile = (r >> 4) * (K / M::kK) + k / M::kK;
+    const int ln = (r & 15) + 16 * ((k % M::kK) / M::kPerLane);
+    return ((long)tile * kWave + ln) * M::kPerLane + (k % M::kPerLane);
+}
+// Four (bf16: one 8-byte store) or eight (one 16-byte store) consecutive k.
+__device__ __forceinline__ void store_frag4(bf16 *base, int r, int k, int K, f32x4 x) {
+    store4(base + frag_off<bf16>(r, k, K), x);
+}
+__device__ __forceinline__ void store_frag4(float *base, int r, int k, int K, f32x4 x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) base[frag_off<float>(r, k + e, K)] = x[e];
+}
+__device__ __forceinline__ void store_frag8(bf16 *base, int r, int k, int K, const float *x) {
+    store8(base + frag_off<bf16>(r, k, K), x);
+}
+__device__ __forceinline__ void store_frag8(float *base, int r, int k, int K, const float *x) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) base[frag_off<float>(r, k + e, K)] = x[e];
+}
+// U~^T is consumed in accumulator layout: for value tile j/16 and row tile
+// r/16, lane (j % 16) + 16 ((r % 16) / 4) holds rows r .. r+3 of column j.
+__device__ __forceinline__ long ufrag_off(int j, int r) {
+    return ((long)((j >> 4) * (C / 16) + (r >> 4)) * kWave + (j & 15) + 16 * ((r & 15) >> 2)) * 4 +
+           (r & 3);
+}
 
 // The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix, spread so
 // that four waves get 3, 3, 2, 2 of them.
@@ -241,10 +278,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
                 }
                 at[e] = a * eg;
                 kb[e] = kk * egc;
-                ws.Qt[(ch * C + r) * DK + i] = from_f32<TI>(qq * eg);
+                ws.Qt[ch * C * DK + frag_off<TI>(r, i, DK)] = from_f32<TI>(qq * eg);
             }
             store8(&sAt[i][r0], at);
-            store8(&ws.Kbt[(ch * DK + i) * C + r0], kb);
+            store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
         }
         const int j = tid % DV;
         for (int r0 = 8 * (tid / DV); r0 < C; r0 += 8 * (kPrepThreads / DV)) {
@@ -325,14 +362,14 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
             Pv[m] = s <= r ? accP[m] * f : 0.f;
         }
         *reinterpret_cast<f32x4 *>(&sAm[r][16 * S + 4 * lg]) = Av;
-        store4(&ws.P[(ch * C + r) * C + 16 * S + 4 * lg], Pv);
+        store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }
     for (int idx = tid; idx < 6 * 16 * 4; idx += kPrepThreads) {
         // zero the strictly upper tiles of P (4 values per thread-step)
         const int t6 = idx / 64, e = idx % 64;
         const int r = 16 * kUpperR[t6] + e / 4;
         const int s = 16 * kUpperS[t6] + 4 * (e % 4);
-        store4(&ws.P[(ch * C + r) * C + s], zero4());
+        store_frag4(ws.P + ch * C * C, r, s, C, zero4());
     }
     __syncthreads();
 
@@ -406,7 +443,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 #pragma unroll
             for (int ks = 0; ks < C / M::kK; ++ks)
                 if (ks < nK) acc = M::mma(M::load(arow, ks * M::kK, lane), Tf[ks], acc);
-            store4(&ws.W[(ch * C + 16 * R + l16) * DK + 16 * mi + 4 * lg], acc);
+            store_frag4(ws.W + ch * C * DK, 16 * R + l16, 16 * mi + 4 * lg, DK, acc);
         }
         // U~(r, j) = sum_s T[r][s] Ut[j][s]: lane holds U~^T[j][r .. r+3].
 #pragma unroll 2
@@ -416,7 +453,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 #pragma unroll
             for (int ks = 0; ks < C / M::kK; ++ks)
                 if (ks < nK) acc = M::mma(Tf[ks], M::load(urow, ks * M::kK, lane), acc);
-            store4(&ws.Ut[(ch * DV + 16 * nj + l16) * C + 16 * R + 4 * lg], acc);
+            store4(ws.Ut + ch * DV * C + ufrag_off(16 * nj + l16, 16 * R + 4 * lg), acc);
         }
     }
 }
@@ -598,7 +635,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
                 if constexpr (VT::kHasDecay) eg = __expf(sG[r][VT::kChannelDecay ? 8 * pc + e : 0]);
                 o[e] = (bf16)((float)qv[e] * eg);
             }
-            *reinterpret_cast<bf16x8 *>(&ws.Qt[(ch * C + r) * DK + 8 * pc]) = o;
+            *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace
 #pragma unroll
@@ -623,7 +660,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
                 kb[e] = kk * egc;
             }
             store8(&sAt[i][r0], at);
-            store8(&ws.Kbt[(ch * DK + i) * C + r0], kb);
+            store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
             if (idx < DK) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
         }
         // U^T into LDS
@@ -688,13 +725,13 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
         *reinterpret_cast<f32x4 *>(&sAm[r][16 * S + 4 * lg]) = Av;
-        store4(&ws.P[(ch * C + r) * C + 16 * S + 4 * lg], Pv);
+        store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }
     for (int idx = tid; idx < 6 * 16 * 4; idx += NT) {
         const int t6 = idx / 64, e = idx % 64;
         const int r = 16 * kUpperR[t6] + e / 4;
         const int s2 = 16 * kUpperS[t6] + 4 * (e % 4);
-        store4(&ws.P[(ch * C + r) * C + s2], zero4());
+        store_frag4(ws.P + ch * C * C, r, s2, C, zero4());
     }
     __syncthreads();
 
@@ -763,7 +800,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < nK) acc = M::mma(M::load(arow, 32 * ks, lane), Tf[ks], acc);
-            store4(&ws.W[(ch * C + 16 * R + l16) * DK + 16 * mi + 4 * lg], acc);
+            store_frag4(ws.W + ch * C * DK, 16 * R + l16, 16 * mi + 4 * lg, DK, acc);
         }
 #pragma unroll
         for (int nj = half * (DV / 32); nj < (half + 1) * (DV / 32); ++nj) {
@@ -772,7 +809,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < nK) acc = M::mma(Tf[ks], M::load(urow, 32 * ks, lane), acc);
-            store4(&ws.Ut[(ch * DV + 16 * nj + l16) * C + 16 * R + 4 * lg], acc);
+            store4(ws.Ut + ch * DV * C + ufrag_off(16 * nj + l16, 16 * R + 4 * lg), acc);
         }
     }
 }
@@ -794,33 +831,35 @@ template <typename TI, int DK, int NJ> struct ScanOperands {
 
     __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0,
                                          int wave, int lane) {
-        const int l16 = lane & 15, lg = lane >> 4;
-        const int r = 16 * wave + l16;
-        const TI *wrow = ws.W + (ch * C + r) * DK;
-        const TI *qrow = ws.Qt + (ch * C + r) * DK;
-        const TI *prow = ws.P + (ch * C + r) * C;
+        const int lg = lane >> 4;
+        auto frag = [&](const TI *base, int tile) {
+            return *reinterpret_cast<const typename M::frag *>(base + ((long)tile * kWave + lane) *
+                                                                   M::kPerLane);
+        };
+        const TI *wb = ws.W + ch * C * DK, *qb = ws.Qt + ch * C * DK;
+        const TI *pb = ws.P + ch * C * C, *kb = ws.Kbt + ch * DK * C;
 #pragma unroll
         for (int ks = 0; ks < KS_D; ++ks) {
-            Wf[ks] = M::load(wrow, ks * M::kK, lane);
-            Qf[ks] = M::load(qrow, ks * M::kK, lane);
+            Wf[ks] = frag(wb, wave * KS_D + ks);
+            Qf[ks] = frag(qb, wave * KS_D + ks);
         }
 #pragma unroll
-        for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = M::load(prow, ks * M::kK, lane);
+        for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = frag(pb, wave * KS_C + ks);
 #pragma unroll
         for (int a = 0; a < NI; ++a) {
-            const TI *krow = ws.Kbt + (ch * DK + 16 * (wave * NI + a) + l16) * C;
 #pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks) Kf[a][ks] = M::load(krow, ks * M::kK, lane);
+            for (int ks = 0; ks < KS_C; ++ks) Kf[a][ks] = frag(kb, (wave * NI + a) * KS_C + ks);
             gam[a] = load4(ws.gam + ch * DK + 16 * (wave * NI + a) + 4 * lg);
         }
 #pragma unroll
         for (int n = 0; n < NJ; ++n)
-            U[n] = *reinterpret_cast<const raw4 *>(ws.Ut + (ch * DV + col0 + 16 * n + l16) * C +
-                                                   16 * wave + 4 * lg);
+            U[n] = *reinterpret_cast<const raw4 *>(ws.Ut + ch * (long)DV * C +
+                                                   ufrag_off(col0 + 16 * n + (lane & 15),
+                                                             16 * wave + 4 * lg));
     }
 };
 
-template <typename TI, int DK, int NJ, int DEPTH, int LOOK>
+template <typename TI, int DK, int NJ, int DEPTH>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsPtrs<TI> ws) {
     using M = Mma<TI>;
     using Ops = ScanOperands<TI, DK, NJ>;
@@ -954,53 +993,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsP
             step(Cq, c + 2);
         }
     } else if constexpr (DEPTH == 2) {
-        // Two register sets in rotation, plus an L2 prefetch of the chunk
-        // LOOK chunks ahead: one 4-byte read per 128-byte line of the factors
-        // this workgroup will stream, whose result is only folded into a sink
-        // after a later wait has retired it, so it never stalls.
-        unsigned sink = 0;
-        constexpr int LW = C * DK * (int)sizeof(TI) / 128;   // lines of one W, Qt or Kbar^T tile
-        constexpr int LP = C * C * (int)sizeof(TI) / 128;    // lines of one P tile
-        constexpr int LU = JW * C * (int)sizeof(TI) / 128;   // lines of this slice of U~^T
-        constexpr int LT = 3 * LW + LP + LU;
-        auto touch = [&](long c) -> uint2 {
-            const long ch = chunk(c);
-            uint2 t;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                int li = tid + u * kScanThreads;
-                li = li < LT ? li : LT - 1;
-                const char *base;
-                if (li < LW)
-                    base = reinterpret_cast<const char *>(ws.W + ch * C * DK) + 128 * li;
-                else if (li < 2 * LW)
-                    base = reinterpret_cast<const char *>(ws.Qt + ch * C * DK) + 128 * (li - LW);
-                else if (li < 3 * LW)
-                    base = reinterpret_cast<const char *>(ws.Kbt + ch * C * DK) + 128 * (li - 2 * LW);
-                else if (li < 3 * LW + LP)
-                    base = reinterpret_cast<const char *>(ws.P + ch * C * C) + 128 * (li - 3 * LW);
-                else
-                    base = reinterpret_cast<const char *>(ws.Ut + (ch * DV + col0) * C) +
-                           128 * (li - 3 * LW - LP);
-                t[u] = *reinterpret_cast<const unsigned *>(base);
-            }
-            return t;
-        };
         Ops A, Bq;
         A.load(ws, chunk(0), DV, col0, wave, lane);
-        uint2 tA = make_uint2(0, 0), tB = make_uint2(0, 0);
         for (long c = 0; c < NC; c += 2) {
-            if constexpr (LOOK > 0) tA = touch(c + LOOK);
             Bq.load(ws, chunk(c + 1), DV, col0, wave, lane);
             step(A, c);
-            sink ^= tB.x ^ tB.y;
             if (c + 1 >= NC) break;
-            if constexpr (LOOK > 0) tB = touch(c + 1 + LOOK);
             A.load(ws, chunk(c + 2), DV, col0, wave, lane);
             step(Bq, c + 1);
-            sink ^= tA.x ^ tA.y;
         }
-        if (sink == 0x9e3779b9u && T < 0) out[0] = from_f32<TI>(0.f);   // keeps the reads alive
     } else {
         Ops cur;
         for (long c = 0; c < NC; ++c) {
@@ -1040,7 +1041,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
     const long nwg = p.B * p.H * (DV / (16 * NJ));
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, DEPTH, 0>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, DEPTH>), dim3((unsigned)grid),
                        dim3(kScanThreads), 0, stream, p, w);
     return hipGetLastError();
 }
