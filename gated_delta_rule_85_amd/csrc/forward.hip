@@ -50,7 +50,6 @@ namespace {
 
 constexpr int C = 64;              // chunk length
 constexpr int kPrepThreads = 256;
-constexpr int kScanThreads = 256;
 constexpr int kXcds = 8;           // accelerator complex dies per MI355X
 
 // Per chunk-head factors, each block contiguous; the operand factors are
@@ -165,6 +164,32 @@ __device__ __forceinline__ void store_frag8(float *base, int r, int k, int K, co
 __device__ __forceinline__ long ufrag_off(int j, int r) {
     return ((long)((j >> 4) * (C / 16) + (r >> 4)) * kWave + (j & 15) + 16 * ((r & 15) >> 2)) * 4 +
            (r & 3);
+}
+
+
+// ---- buffer loads ------------------------------------------------------------
+// The scan addresses each chunk's factors through a buffer descriptor built in
+// scalar registers from the chunk's block address, plus a per-lane offset that
+// never changes: the per-chunk address arithmetic stays scalar, so no vector
+// register that may still be the target of a load in flight is rewritten.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    if constexpr (sizeof(T) == 16) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return __builtin_bit_cast(T, v);
+    } else if constexpr (sizeof(T) == 8) {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return __builtin_bit_cast(T, v);
+    } else {
+        static_assert(sizeof(T) == 4, "4, 8 or 16 bytes");
+        unsigned v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        return __builtin_bit_cast(T, v);
+    }
 }
 
 // The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix, spread so
@@ -815,210 +840,243 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 }
 
 // ============================================================================
-// chunk_scan
+// chunk_scan, split roles: eight waves per workgroup.  Waves 0-3 run only the
+// state recurrence (Delta = U~ - W S, then S <- Gamma S + Kbar^T Delta) and
+// load only W, Kbar^T, U~ and e^{g_C}; waves 4-7 produce the output of the
+// previous chunk, O = Qt S + P Delta, from double-buffered copies of S^T and
+// Delta^T in LDS, and load only Qt and P.  The state chain per chunk is then
+// two short matrix-core steps between two barriers, and the output work runs
+// beside it on the same SIMDs.
 // ============================================================================
-template <typename TI, int DK, int NJ> struct ScanOperands {
+template <typename TI, int DK> struct ChainOps {
     using M = Mma<TI>;
-    static constexpr int KS_D = DK / M::kK;
-    static constexpr int KS_C = C / M::kK;
-    static constexpr int NI = DK / 64;       // 16-row key tiles per wave
-    // Raw loaded values only: a conversion here would make the compiler wait
-    // for the load at once and defeat the prefetch.
+    static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK, NI = DK / 64;
+    static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);   // bytes per fragment tile
     typedef typename std::conditional<sizeof(TI) == 2, bf16x4, f32x4>::type raw4;
-    typename M::frag Wf[KS_D], Qf[KS_D], Pf[KS_C], Kf[NI][KS_C];
-    raw4 U[NJ];
+    typename M::frag Wf[KS_D], Kf[NI][KS_C];
+    raw4 U;
     f32x4 gam[NI];
-
-    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0,
-                                         int wave, int lane) {
-        const int lg = lane >> 4;
-        auto frag = [&](const TI *base, int tile) {
-            return *reinterpret_cast<const typename M::frag *>(base + ((long)tile * kWave + lane) *
-                                                                   M::kPerLane);
-        };
-        const TI *wb = ws.W + ch * C * DK, *qb = ws.Qt + ch * C * DK;
-        const TI *pb = ws.P + ch * C * C, *kb = ws.Kbt + ch * DK * C;
+    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0, int w,
+                                         int lane) {
+        const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
+        const auto rw = make_rsrc(reinterpret_cast<const char *>(ws.W + ch * C * DK) + w * KS_D * FB);
+        const auto rk = make_rsrc(reinterpret_cast<const char *>(ws.Kbt + ch * DK * C) +
+                                  w * NI * KS_C * FB);
+        const auto rg = make_rsrc(ws.gam + ch * DK + 16 * NI * w);
+        const auto ru = make_rsrc(reinterpret_cast<const char *>(ws.Ut + ch * (long)DV * C) +
+                                  ((col0 / 16) * (C / 16) + w) * (kWave * 4 * (int)sizeof(TI)));
 #pragma unroll
-        for (int ks = 0; ks < KS_D; ++ks) {
-            Wf[ks] = frag(wb, wave * KS_D + ks);
-            Qf[ks] = frag(qb, wave * KS_D + ks);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = frag(pb, wave * KS_C + ks);
+        for (int ks = 0; ks < KS_D; ++ks) Wf[ks] = buf_load<typename M::frag>(rw, loff + ks * FB);
 #pragma unroll
         for (int a = 0; a < NI; ++a) {
 #pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks) Kf[a][ks] = frag(kb, (wave * NI + a) * KS_C + ks);
-            gam[a] = load4(ws.gam + ch * DK + 16 * (wave * NI + a) + 4 * lg);
+            for (int ks = 0; ks < KS_C; ++ks)
+                Kf[a][ks] = buf_load<typename M::frag>(rk, loff + (a * KS_C + ks) * FB);
+            gam[a] = buf_load<f32x4>(rg, (unsigned)(lane >> 4) * 16u + 64u * a);
         }
-#pragma unroll
-        for (int n = 0; n < NJ; ++n)
-            U[n] = *reinterpret_cast<const raw4 *>(ws.Ut + ch * (long)DV * C +
-                                                   ufrag_off(col0 + 16 * n + (lane & 15),
-                                                             16 * wave + 4 * lg));
+        U = buf_load<raw4>(ru, (unsigned)lane * 4u * sizeof(TI));
     }
 };
 
-template <typename TI, int DK, int NJ, int DEPTH>
-__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(Problem p, WsPtrs<TI> ws) {
+template <typename TI, int DK> struct OutOps {
     using M = Mma<TI>;
-    using Ops = ScanOperands<TI, DK, NJ>;
-    constexpr int KS_D = Ops::KS_D, KS_C = Ops::KS_C, NI = Ops::NI;
-    constexpr int JW = 16 * NJ;
-    constexpr int PT = 8;
-    __shared__ __attribute__((aligned(16))) TI sSt[JW][DK + PT];   // S^T (operand copy)
-    __shared__ __attribute__((aligned(16))) TI sDt[JW][C + PT];    // Delta^T
+    static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK;
+    static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);
+    typename M::frag Qf[KS_D], Pf[KS_C];
+    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int w, int lane) {
+        const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
+        const auto rq = make_rsrc(reinterpret_cast<const char *>(ws.Qt + ch * C * DK) + w * KS_D * FB);
+        const auto rp = make_rsrc(reinterpret_cast<const char *>(ws.P + ch * C * C) + w * KS_C * FB);
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) Qf[ks] = buf_load<typename M::frag>(rq, loff + ks * FB);
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = buf_load<typename M::frag>(rp, loff + ks * FB);
+    }
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+constexpr int kScan2Threads = 512;
+
+template <typename TI, int DK, int DEPTH>
+__global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws) {
+    using M = Mma<TI>;
+    using CO = ChainOps<TI, DK>;
+    using OO = OutOps<TI, DK>;
+    constexpr int KS_D = CO::KS_D, KS_C = CO::KS_C, NI = CO::NI;
+    constexpr int PT = 8;
+    __shared__ __attribute__((aligned(16))) TI sSt[2][16][DK + PT];   // S^T, double-buffered
+    __shared__ __attribute__((aligned(16))) TI sDt[2][16][C + PT];    // Delta^T, double-buffered
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l16 = lane & 15, lg = lane >> 4;
     const int H = (int)p.H, DV = (int)p.dv;
     const long T = p.T;
     const long NC = (T + C - 1) / C;
-    // Workgroups are dispatched round-robin over the 8 XCDs.  Remap so that
-    // the column slices of one head, which read the same chunk factors, run
-    // on the same XCD and share its L2.
-    const int nslice = DV / JW;
+    const int nslice = DV / 16;
     const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
     const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nwg) return;
     const long bh = logical / nslice;
     const int b = (int)(bh / H), h = (int)(bh % H);
-    const int col0 = (int)(logical % nslice) * JW;
-    TI *out = static_cast<TI *>(p.o);
-    // K-steps of P Delta that cover s <= r for this wave's rows.
-    const int nKP = (16 * (wave + 1) + M::kK - 1) / M::kK;
+    const int col0 = (int)(logical % nslice) * 16;
+    const long ch0 = bh * NC;
+    const long last = NC - 1;
+    auto chunk = [&](long c) { return ch0 + (c < 0 ? 0 : (c < last ? c : last)); };
 
-    // S rows i = 16 (wave*NI + a) + 4 lg + m, column j = col0 + 16 n + l16.
-    f32x4 S[NI][NJ];
-#pragma unroll
-    for (int a = 0; a < NI; ++a)
-#pragma unroll
-        for (int n = 0; n < NJ; ++n)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int i = 16 * (wave * NI + a) + 4 * lg + m;
-                S[a][n][m] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + 16 * n + l16] : 0.f;
-            }
-    auto write_st = [&]() {
+    if (wave < 4) {
+        // ---------------- state chain ----------------
+        const int w = wave;
+        f32x4 S[NI];
 #pragma unroll
         for (int a = 0; a < NI; ++a)
 #pragma unroll
-            for (int n = 0; n < NJ; ++n)
-                store4(&sSt[16 * n + l16][16 * (wave * NI + a) + 4 * lg], S[a][n]);
-    };
-    write_st();
-    __syncthreads();
-
-    // One chunk of the sequential pass with the factors held in `op`.  The
-    // state recurrence (Delta, then S) is the critical path; the output
-    // products are issued where they overlap its latencies.
-    auto step = [&](const Ops &op, long c) __attribute__((always_inline)) {
-        typename M::frag Sf[NJ][KS_D];
+            for (int m = 0; m < 4; ++m) {
+                const int i = 16 * (w * NI + a) + 4 * lg + m;
+                S[a][m] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + l16] : 0.f;
+            }
+        auto write_st = [&](int buf) {
 #pragma unroll
-        for (int n = 0; n < NJ; ++n)
+            for (int a = 0; a < NI; ++a) store4(&sSt[buf][l16][16 * (w * NI + a) + 4 * lg], S[a]);
+        };
+        write_st(0);
+        __syncthreads();
+        // Every step consumes its whole register set on every path: a loaded
+        // value left unused on some path makes the compiler wait for all
+        // loads in flight before it reuses any register.
+        auto step = [&](const CO &op, long c) __attribute__((always_inline)) {
+            const int cur = (int)(c & 1);
+            typename M::frag Sf[KS_D];
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) Sf[n][ks] = M::load(&sSt[16 * n + l16][0], ks * M::kK, lane);
-        // Delta(r, j) = U~ - sum_i W[r][i] S^T[j][i], two interleaved partial sums
-        f32x4 Ov[NJ];
-#pragma unroll
-        for (int n = 0; n < NJ; ++n) {
+            for (int ks = 0; ks < KS_D; ++ks) Sf[ks] = M::load(&sSt[cur][l16][0], ks * M::kK, lane);
             f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS_D; ks += 2) {
-                d0 = M::mma(op.Wf[ks], Sf[n][ks], d0);
-                if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[n][ks + 1], d1);
+                d0 = M::mma(op.Wf[ks], Sf[ks], d0);
+                if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[ks + 1], d1);
             }
-            const f32x4 Dl = to_f32x4(op.U[n]) - (d0 + d1);
-            store4(&sDt[16 * n + l16][16 * wave + 4 * lg], Dl);
-        }
-        // O'(j, r) = sum_i S^T[j][i] Qt[r][i]   (overlaps the barrier below)
+            store4(&sDt[cur][l16][16 * w + 4 * lg], to_f32x4(op.U) - (d0 + d1));
+            __syncthreads();
+            typename M::frag Df[KS_C];
 #pragma unroll
-        for (int n = 0; n < NJ; ++n) {
-            Ov[n] = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) Ov[n] = M::mma(Sf[n][ks], op.Qf[ks], Ov[n]);
-        }
-        __syncthreads();
-
-        typename M::frag Df[NJ][KS_C];
-#pragma unroll
-        for (int n = 0; n < NJ; ++n)
-#pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks) Df[n][ks] = M::load(&sDt[16 * n + l16][0], ks * M::kK, lane);
-        // S(i, j) <- e^{g_C[i]} S + sum_s Kbar^T[i][s] Delta^T[j][s]
-#pragma unroll
-        for (int n = 0; n < NJ; ++n)
+            for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(&sDt[cur][l16][0], ks * M::kK, lane);
 #pragma unroll
             for (int a = 0; a < NI; ++a) {
-                f32x4 acc = S[a][n] * op.gam[a];
+                f32x4 acc = S[a] * op.gam[a];
 #pragma unroll
-                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[n][ks], acc);
-                S[a][n] = acc;
+                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[ks], acc);
+                S[a] = acc;
             }
-        write_st();
-        // O'(j, r) += sum_s Delta^T[j][s] P[r][s], then the output rows
-        const long t0 = c * C;
-        const int r = 16 * wave + l16;
-#pragma unroll
-        for (int n = 0; n < NJ; ++n) {
-#pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks)
-                if (ks < nKP) Ov[n] = M::mma(Df[n][ks], op.Pf[ks], Ov[n]);
-            if (t0 + r < T)
-                store4(&out[((b * T + t0 + r) * H + h) * (long)DV + col0 + 16 * n + 4 * lg], Ov[n]);
+            write_st(cur ^ 1);
+            __syncthreads();
+        };
+        if constexpr (DEPTH == 3) {
+            CO A, Bq, Cq;
+            A.load(ws, chunk(0), DV, col0, w, lane);
+            Bq.load(ws, chunk(1), DV, col0, w, lane);
+            for (long c = 0; c < NC; c += 3) {
+                Cq.load(ws, chunk(c + 2), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(A, c);
+                if (c + 1 >= NC) break;
+                A.load(ws, chunk(c + 3), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Bq, c + 1);
+                if (c + 2 >= NC) break;
+                Bq.load(ws, chunk(c + 4), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Cq, c + 2);
+            }
+        } else if constexpr (DEPTH == 2) {
+            CO A, Bq;
+            A.load(ws, chunk(0), DV, col0, w, lane);
+            for (long c = 0; c < NC; c += 2) {
+                Bq.load(ws, chunk(c + 1), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
+                step(A, c);
+                if (c + 1 >= NC) break;
+                A.load(ws, chunk(c + 2), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Bq, c + 1);
+            }
+        } else {
+            CO cur;
+            for (long c = 0; c < NC; ++c) {
+                cur.load(ws, chunk(c), DV, col0, w, lane);
+                step(cur, c);
+            }
         }
+        // The output waves still finish the last chunk.
         __syncthreads();
-    };
-
-    const long ch0 = bh * NC;
-    const long last = NC - 1;
-    // Past the end the loads re-read the last chunk, so the number of loads in
-    // flight is the same on every path and the waits stay exact.
-    auto chunk = [&](long c) { return ch0 + (c < last ? c : last); };
-    if constexpr (DEPTH == 3) {
-        // Three register sets in rotation: chunk c + 2 in flight while chunk
-        // c is computed, with no register copies.
-        Ops A, Bq, Cq;
-        A.load(ws, chunk(0), DV, col0, wave, lane);
-        Bq.load(ws, chunk(1), DV, col0, wave, lane);
-        for (long c = 0; c < NC; c += 3) {
-            Cq.load(ws, chunk(c + 2), DV, col0, wave, lane);
-            step(A, c);
-            if (c + 1 >= NC) break;
-            A.load(ws, chunk(c + 3), DV, col0, wave, lane);
-            step(Bq, c + 1);
-            if (c + 2 >= NC) break;
-            Bq.load(ws, chunk(c + 4), DV, col0, wave, lane);
-            step(Cq, c + 2);
-        }
-    } else if constexpr (DEPTH == 2) {
-        Ops A, Bq;
-        A.load(ws, chunk(0), DV, col0, wave, lane);
-        for (long c = 0; c < NC; c += 2) {
-            Bq.load(ws, chunk(c + 1), DV, col0, wave, lane);
-            step(A, c);
-            if (c + 1 >= NC) break;
-            A.load(ws, chunk(c + 2), DV, col0, wave, lane);
-            step(Bq, c + 1);
-        }
-    } else {
-        Ops cur;
-        for (long c = 0; c < NC; ++c) {
-            cur.load(ws, ch0 + c, DV, col0, wave, lane);
-            step(cur, c);
-        }
-    }
-    if (p.state_out) {
+        __syncthreads();
+        if (p.state_out) {
 #pragma unroll
-        for (int a = 0; a < NI; ++a)
-#pragma unroll
-            for (int n = 0; n < NJ; ++n)
+            for (int a = 0; a < NI; ++a)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const int i = 16 * (wave * NI + a) + 4 * lg + m;
-                    p.state_out[(bh * DK + i) * DV + col0 + 16 * n + l16] = S[a][n][m];
+                    const int i = 16 * (w * NI + a) + 4 * lg + m;
+                    p.state_out[(bh * DK + i) * DV + col0 + l16] = S[a][m];
                 }
+        }
+    } else {
+        // ---------------- outputs of the previous chunk ----------------
+        const int w = wave - 4;
+        TI *out = static_cast<TI *>(p.o);
+        __syncthreads();          // S_0 in place
+        __syncthreads();          // first chunk: no output yet
+        __syncthreads();
+        // op holds the factors of chunk c; S_c and Delta_c are in LDS buffer c % 2.
+        auto step = [&](const OO &op, long c) __attribute__((always_inline)) {
+            const int buf = (int)(c & 1);
+            f32x4 Ov = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks)
+                Ov = M::mma(M::load(&sSt[buf][l16][0], ks * M::kK, lane), op.Qf[ks], Ov);
+            // P is zero above the diagonal, so all K-steps may run.
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks)
+                Ov = M::mma(M::load(&sDt[buf][l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
+            const long t = c * C + 16 * w + l16;
+            if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 4 * lg], Ov);
+            __syncthreads();
+            __syncthreads();
+        };
+        if constexpr (DEPTH == 3) {
+            OO A, Bq, Cq;
+            A.load(ws, chunk(0), w, lane);
+            Bq.load(ws, chunk(1), w, lane);
+            for (long c = 0; c < NC; c += 3) {
+                Cq.load(ws, chunk(c + 2), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(A, c);
+                if (c + 1 >= NC) break;
+                A.load(ws, chunk(c + 3), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Bq, c + 1);
+                if (c + 2 >= NC) break;
+                Bq.load(ws, chunk(c + 4), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Cq, c + 2);
+            }
+        } else if constexpr (DEPTH == 2) {
+            OO A, Bq;
+            A.load(ws, chunk(0), w, lane);
+            for (long c = 0; c < NC; c += 2) {
+                Bq.load(ws, chunk(c + 1), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(A, c);
+                if (c + 1 >= NC) break;
+                A.load(ws, chunk(c + 2), w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Bq, c + 1);
+            }
+        } else {
+            OO cur;
+            for (long c = 0; c < NC; ++c) {
+                cur.load(ws, chunk(c), w, lane);
+                step(cur, c);
+            }
+        }
     }
 }
 
@@ -1037,12 +1095,11 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
                            stream, p, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int NJ = 1;
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
-    const long nwg = p.B * p.H * (DV / (16 * NJ));
+    const long nwg = p.B * p.H * (DV / 16);
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((chunk_scan_kernel<TI, DK, NJ, DEPTH>), dim3((unsigned)grid),
-                       dim3(kScanThreads), 0, stream, p, w);
+    hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH>), dim3((unsigned)grid),
+                       dim3(kScan2Threads), 0, stream, p, w);
     return hipGetLastError();
 }
 
