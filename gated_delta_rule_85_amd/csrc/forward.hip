@@ -63,15 +63,27 @@ template <typename TI> struct WsPtrs {
     float *gam;// [nch][DK]       e^{g_C}
 };
 
+// A block of consecutive chunks processed by one prep launch and one scan
+// launch.  The workspace holds the factors of `nbmax` chunks per head; the
+// state enters from s_in (NULL = zeros) and leaves to s_out (NULL = dropped).
+struct Block {
+    long c0;             // first chunk of the block
+    int nc;              // chunks in the block
+    int nbmax;           // chunk stride of the workspace slot
+    const float *s_in;
+    float *s_out;
+};
+
 struct WsLayout {
     size_t W, Ut, Qt, Kbt, P, gam, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WsLayout ws_layout(const Problem &p) {
+// Layout of one workspace slot holding `nbmax` chunks for every head.
+WsLayout ws_layout(const Problem &p, long nbmax) {
     const size_t es = p.bf16 ? 2 : 4;
-    const size_t nch = (size_t)p.B * p.H * ((p.T + C - 1) / C);
+    const size_t nch = (size_t)p.B * p.H * nbmax;
     WsLayout L;
     size_t o = 0;
     L.W = o;   o = align256(o + nch * C * p.dk * es);
@@ -84,12 +96,34 @@ WsLayout ws_layout(const Problem &p) {
     return L;
 }
 
-template <typename TI> WsPtrs<TI> ws_ptrs(const Problem &p, void *base) {
-    WsLayout L = ws_layout(p);
+template <typename TI> WsPtrs<TI> ws_ptrs(const Problem &p, long nbmax, void *base) {
+    WsLayout L = ws_layout(p, nbmax);
     char *b = static_cast<char *>(base);
     return WsPtrs<TI>{reinterpret_cast<TI *>(b + L.W), reinterpret_cast<TI *>(b + L.Ut),
                       reinterpret_cast<TI *>(b + L.Qt), reinterpret_cast<TI *>(b + L.Kbt),
                       reinterpret_cast<TI *>(b + L.P), reinterpret_cast<float *>(b + L.gam)};
+}
+
+// Execution plan of one forward: the sequence is cut into blocks of `nb`
+// chunks.  With more than one block, two workspace slots alternate and an fp32
+// state carrier passes the state from block to block.
+struct Plan {
+    long NC, nb, nblk;
+    size_t slot, carrier, total;
+};
+
+constexpr long kBlockChunks = 64;
+
+Plan make_plan(const Problem &p) {
+    Plan q;
+    q.NC = (p.T + C - 1) / C;
+    // Long sequences in bf16 are pipelined block by block; otherwise one block.
+    q.nb = (p.bf16 && q.NC > kBlockChunks) ? kBlockChunks : q.NC;
+    q.nblk = (q.NC + q.nb - 1) / q.nb;
+    q.slot = ws_layout(p, q.nb).total;
+    q.carrier = q.nblk > 1 ? align256((size_t)p.B * p.H * p.dk * p.dv * 4) : 0;
+    q.total = (q.nblk > 1 ? 2 : 1) * q.slot + q.carrier;
+    return q;
 }
 
 // ---- small vector stores ------------------------------------------------------
@@ -204,7 +238,7 @@ __constant__ int8_t kUpperS[6] = {1, 2, 3, 2, 3, 3};
 // chunk_prep
 // ============================================================================
 template <int V, typename TI, int DK, int DV>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsPtrs<TI> ws) {
+__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsPtrs<TI> ws, Block blk) {
     using VT = VariantTraits<V>;
     using M = Mma<TI>;
     constexpr int PT = 8;                                  // pad (elements) of TI tiles
@@ -222,13 +256,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const long c = blk.c0 + blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
     const long T = p.T;
     const int H = (int)p.H;
-    const long t0 = (long)c * C;
+    const long t0 = c * C;
     const int nvalid = (int)min((long)C, T - t0);
-    const long NC = (T + C - 1) / C;
-    const long ch = ((long)b * H + h) * NC + c;
+    const long ch = ((long)b * H + h) * blk.nbmax + blockIdx.x;   // slot-local chunk-head
     const TI *q = static_cast<const TI *>(p.q);
     const TI *k = static_cast<const TI *>(p.k);
     const TI *v = static_cast<const TI *>(p.v);
@@ -485,91 +519,104 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 
 // ============================================================================
 // chunk_prep, bf16 inputs: the same factors as chunk_prep_kernel, restructured
-// for memory-level parallelism.  All global reads of the chunk (q, k, v and the
-// gates) are issued at once into LDS before any arithmetic, eight waves share
-// the work, and LDS regions are reused as the phases retire them.
+// for memory-level parallelism and occupancy.  All global reads of the chunk
+// are issued at once before any arithmetic; eight waves share the work; LDS
+// tiles are unpadded with an XOR swizzle of their 16-byte chunks and are
+// reused as the phases retire them, so that for scalar-decay variants two
+// workgroups fit on a CU and one's loads overlap the other's arithmetic.  q is
+// kept in registers rather than LDS.
 // ============================================================================
 constexpr int kPrep2Threads = 512;
 
+// Element offset in an unpadded tile with CPR 16-byte chunks per row whose
+// chunk index is XORed with the row: sixteen lanes reading one column chunk of
+// sixteen consecutive rows touch distinct banks.  EPC = elements per chunk.
+template <int CPR, int EPC> __device__ __forceinline__ int swz(int r, int col) {
+    return (r * CPR + ((col / EPC) ^ (r & (CPR - 1)))) * EPC + col % EPC;
+}
+
 template <int V, int DK, int DV>
-__global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem p,
-                                                                       WsPtrs<bf16> ws) {
+__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 1 : 2)
+void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     using VT = VariantTraits<V>;
     using M = Mma<bf16>;
     constexpr int NT = kPrep2Threads, NW = NT / kWave;
-    constexpr int PT = 8, PF = 4;
-    constexpr int KP = DK + PT, VP = DV + PT, CP = C + PT, FP = C + PF;
     constexpr int GW = VT::kChannelDecay ? DK : 1;
-    constexpr int R1 = C * KP * 2;                                         // k   -> sX
-    constexpr int R2 = C * KP * 2 > C * FP * 4 ? C * KP * 2 : C * FP * 4;  // q   -> T
-    constexpr int R3 = C * VP * 2 > C * FP * 4 ? C * VP * 2 : C * FP * 4;  // u   -> A
-    static_assert(3 * 16 * 17 * 4 <= R1, "sX fits in the k region");
-
+    constexpr int KC = DK / 8, VC = DV / 8;   // 16-byte chunks per k row / v row
+    constexpr int R1 = C * DK * 2 > C * C * 4 ? C * DK * 2 : C * C * 4;   // k   -> T
+    constexpr int R3 = C * DV * 2 > C * C * 4 ? C * DV * 2 : C * C * 4;   // u   -> A
     __shared__ __attribute__((aligned(16))) char smem1[R1];
-    __shared__ __attribute__((aligned(16))) char smem2[R2];
     __shared__ __attribute__((aligned(16))) char smem3[R3];
-    __shared__ __attribute__((aligned(16))) bf16 sAg[VT::kGates ? C : 1][KP];  // b (.) k
+    __shared__ __attribute__((aligned(16))) bf16 sAg[VT::kGates ? C * DK : 8];   // b (.) k
     __shared__ __attribute__((aligned(16))) float sG[C][GW];
     __shared__ float sBeta[C];
-    __shared__ __attribute__((aligned(16))) bf16 sAt[DK][CP];   // (a (.) e^{g})^T
-    __shared__ __attribute__((aligned(16))) bf16 sUt[DV][CP];   // U^T
-    auto sK = reinterpret_cast<bf16 (*)[KP]>(smem1);
-    auto sQ = reinterpret_cast<bf16 (*)[KP]>(smem2);
-    auto sV = reinterpret_cast<bf16 (*)[VP]>(smem3);
-    auto sX = reinterpret_cast<float (*)[16][17]>(smem1);
-    auto sT = reinterpret_cast<float (*)[FP]>(smem2);
-    auto sAm = reinterpret_cast<float (*)[FP]>(smem3);
+    __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
+    __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
+    __shared__ float sX[3][16][17];
+    bf16 *sK = reinterpret_cast<bf16 *>(smem1);    // [C][DK]
+    bf16 *sV = reinterpret_cast<bf16 *>(smem3);    // [C][DV]
+    float *sT = reinterpret_cast<float *>(smem1);  // [C][C]
+    float *sAm = reinterpret_cast<float *>(smem3); // [C][C]
+    auto kx = [](int r, int col) { return swz<KC, 8>(r, col); };
+    auto vx = [](int r, int col) { return swz<VC, 8>(r, col); };
+    auto tx = [](int r, int col) { return swz<C / 8, 8>(r, col); };   // [D][C] bf16 tiles
+    auto fx = [](int r, int col) { return swz<C / 4, 4>(r, col); };   // [C][C] fp32 tiles
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const long c = blk.c0 + blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
     const long T = p.T;
     const int H = (int)p.H;
-    const long t0 = (long)c * C;
+    const long t0 = c * C;
     const int nvalid = (int)min((long)C, T - t0);
-    const long NC = (T + C - 1) / C;
-    const long ch = ((long)b * H + h) * NC + c;
+    const long ch = ((long)b * H + h) * blk.nbmax + blockIdx.x;   // slot-local chunk-head
     const bf16 *q = static_cast<const bf16 *>(p.q);
     const bf16 *k = static_cast<const bf16 *>(p.k);
     const bf16 *v = static_cast<const bf16 *>(p.v);
     auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
+    auto zero8 = []() {
+        bf16x8 z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
+        return z;
+    };
 
     // ---- load: every global read of the chunk, issued together --------------
-    constexpr int PK = DK / 8, PV = DV / 8;
+    constexpr int NQ = (C * KC + NT - 1) / NT;
+    bf16x8 qreg[NQ];
 #pragma unroll
-    for (int idx = tid; idx < C * PK; idx += NT) {
-        const int r = idx / PK, pc = idx % PK;
-        bf16x8 kv, qv;
-        if (r < nvalid) {
+    for (int n = 0; n < NQ; ++n) {
+        const int idx = tid + n * NT;
+        const int r = idx / KC, pc = idx % KC;
+        bf16x8 kv = zero8(), qv = zero8();
+        if (idx < C * KC && r < nvalid) {
             kv = *reinterpret_cast<const bf16x8 *>(&k[tok(r) * DK + 8 * pc]);
             qv = *reinterpret_cast<const bf16x8 *>(&q[tok(r) * DK + 8 * pc]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = qv[e] = (bf16)0.f;
         }
-        *reinterpret_cast<bf16x8 *>(&sK[r][8 * pc]) = kv;
-        *reinterpret_cast<bf16x8 *>(&sQ[r][8 * pc]) = qv;
-        if constexpr (VT::kGates) {
-            bf16x8 av;
-            if (r < nvalid) {
-                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
-                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
+        qreg[n] = qv;
+        if (idx < C * KC) {
+            *reinterpret_cast<bf16x8 *>(&sK[kx(r, 8 * pc)]) = kv;
+            if constexpr (VT::kGates) {
+                bf16x8 av = zero8();
+                if (r < nvalid) {
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    av[e] = (bf16)(b0[e] * (float)kv[e]);
-                    av[e + 4] = (bf16)(b1[e] * (float)kv[e + 4]);
+                    for (int e = 0; e < 4; ++e) {
+                        av[e] = (bf16)(b0[e] * (float)kv[e]);
+                        av[e + 4] = (bf16)(b1[e] * (float)kv[e + 4]);
+                    }
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) av[e] = (bf16)0.f;
+                *reinterpret_cast<bf16x8 *>(&sAg[kx(r, 8 * pc)]) = av;
             }
-            *reinterpret_cast<bf16x8 *>(&sAg[r][8 * pc]) = av;
         }
     }
 #pragma unroll
-    for (int idx = tid; idx < C * PV; idx += NT) {
-        const int r = idx / PV, pc = idx % PV;
-        bf16x8 vv;
+    for (int idx = tid; idx < C * VC; idx += NT) {
+        const int r = idx / VC, pc = idx % VC;
+        bf16x8 vv = zero8();
         if (r < nvalid) {
             vv = *reinterpret_cast<const bf16x8 *>(&v[tok(r) * DV + 8 * pc]);
             if constexpr (VT::kGates) {
@@ -581,11 +628,8 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
                     vv[e + 4] = (bf16)(w1[e] * (float)vv[e + 4]);
                 }
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[e] = (bf16)0.f;
         }
-        *reinterpret_cast<bf16x8 *>(&sV[r][8 * pc]) = vv;
+        *reinterpret_cast<bf16x8 *>(&sV[vx(r, 8 * pc)]) = vv;
     }
     if constexpr (VT::kChannelDecay) {
 #pragma unroll
@@ -605,6 +649,18 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
             const int r = tid - (NT - C);
             sBeta[r] = r < nvalid ? p.beta[tok(r)] : 0.f;
         }
+    // q rows of this wave's Gram tiles, for phase 2 (L2 hits: read just above).
+    bf16x8 qf[2][DK / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tl = wave + u * NW;
+        const int rr = 16 * kLowerR[tl < 10 ? tl : 0] + l16;
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+            qf[u][ks] = (tl < 10 && rr < nvalid)
+                            ? *reinterpret_cast<const bf16x8 *>(&q[tok(rr) * DK + 32 * ks + 8 * lg])
+                            : zero8();
+    }
     __syncthreads();
 
     // ---- gates: decay prefix sums; KLA step size ------------------------------
@@ -635,7 +691,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
         float s2 = 0.f;
 #pragma unroll
         for (int i = 8 * part; i < DK; i += 64) {
-            const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(&sK[r][i]);
+            const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(&sK[kx(r, i)]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s2 += (float)kv[e] * (float)kv[e];
         }
@@ -648,19 +704,21 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 
     // ---- phase 1: element-wise factors ------------------------------------
     {
-        // q (.) e^{g}, row-major, 16-byte pieces
+        // q (.) e^{g}, from registers
 #pragma unroll
-        for (int idx = tid; idx < C * PK; idx += NT) {
-            const int r = idx / PK, pc = idx % PK;
-            const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(&sQ[r][8 * pc]);
-            bf16x8 o;
+        for (int n = 0; n < NQ; ++n) {
+            const int idx = tid + n * NT;
+            if (idx < C * KC) {
+                const int r = idx / KC, pc = idx % KC;
+                bf16x8 o;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float eg = 1.f;
-                if constexpr (VT::kHasDecay) eg = __expf(sG[r][VT::kChannelDecay ? 8 * pc + e : 0]);
-                o[e] = (bf16)((float)qv[e] * eg);
+                for (int e = 0; e < 8; ++e) {
+                    float eg = 1.f;
+                    if constexpr (VT::kHasDecay) eg = __expf(sG[r][VT::kChannelDecay ? 8 * pc + e : 0]);
+                    o[e] = (bf16)((float)qreg[n][e] * eg);
+                }
+                *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
             }
-            *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace
 #pragma unroll
@@ -671,9 +729,9 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = r0 + e;
-                const float kk = (float)sK[r][i];
+                const float kk = (float)sK[kx(r, i)];
                 float a;
-                if constexpr (VT::kGates) a = (float)sAg[r][i];
+                if constexpr (VT::kGates) a = (float)sAg[kx(r, i)];
                 else a = sBeta[r] * kk;
                 float eg = 1.f, egc = 1.f;
                 if constexpr (VT::kHasDecay) {
@@ -684,7 +742,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
                 at[e] = a * eg;
                 kb[e] = kk * egc;
             }
-            store8(&sAt[i][r0], at);
+            store8(&sAt[tx(i, r0)], at);
             store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
             if (idx < DK) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
         }
@@ -695,17 +753,24 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
             float u[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float vv = (float)sV[r0 + e][j];
+                const float vv = (float)sV[vx(r0 + e, j)];
                 if constexpr (VT::kGates) u[e] = vv;
                 else u[e] = sBeta[r0 + e] * vv;
             }
-            store8(&sUt[j][r0], u);
+            store8(&sUt[tx(j, r0)], u);
         }
     }
     __syncthreads();
 
-    // ---- phase 2: A and P on matrix cores (operands from LDS) -----------------
-    for (int tl = wave; tl < 10; tl += NW) {
+    // ---- phase 2: A and P on matrix cores ---------------------------------------
+    // Computed transposed, D'(s, r) = sum_i Kr[s][i] L[r][i]: a lane holds four
+    // consecutive s of one row r.  Channel-wise decay is split between the
+    // operands around g_ref = g_{C/2-1}; scalar decay multiplies the product by
+    // e^{g_r - g_s} <= 1.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tl = wave + u * NW;
+        if (tl >= 10) break;
         const int R = kLowerR[tl], S = kLowerS[tl];
         const int rs = 16 * S + l16;
         const int rr = 16 * R + l16;
@@ -713,13 +778,13 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
         float br = 0.f;
         if constexpr (VT::kScalarBeta) br = sBeta[rr];
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += M::kK) {
-            const int kb = k0 + 8 * lg;
-            const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[rs][kb]);
-            const bf16x8 qr8 = *reinterpret_cast<const bf16x8 *>(&sQ[rr][kb]);
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            const int kb = 32 * ks + 8 * lg;
+            const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rs, kb)]);
+            const bf16x8 qr8 = qf[u][ks];
             bf16x8 ar8;
-            if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[rr][kb]);
-            else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[rr][kb]);
+            if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[kx(rr, kb)]);
+            else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
             float kr[8], ar[8], qr[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -749,7 +814,7 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
             Av[m] = s2 < r ? accA[m] * f : 0.f;
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
-        *reinterpret_cast<f32x4 *>(&sAm[r][16 * S + 4 * lg]) = Av;
+        *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
         store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }
     for (int idx = tid; idx < 6 * 16 * 4; idx += NT) {
@@ -762,44 +827,47 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 
     // ---- phase 3: T = (I + A)^{-1} ------------------------------------------
     if (wave == 0) {
+        // Diagonal 16x16 blocks by forward substitution; lane = (block, column).
         const int R = lg, cc = l16;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc += sAm[16 * R + r][16 * R + j] * x[j];
+            for (int j = 0; j < r; ++j) acc += sAm[fx(16 * R + r, 16 * R + j)] * x[j];
             x[r] = r == cc ? 1.f : (r < cc ? 0.f : -acc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[16 * R + r][16 * R + cc] = x[r];
+        for (int r = 0; r < 16; ++r) sT[fx(16 * R + r, 16 * R + cc)] = x[r];
     } else {
         for (int idx = tid - kWave; idx < 6 * 256; idx += NT - kWave) {
             const int t6 = idx >> 8, e = idx & 255;
-            sT[16 * kUpperR[t6] + (e >> 4)][16 * kUpperS[t6] + (e & 15)] = 0.f;
+            sT[fx(16 * kUpperR[t6] + (e >> 4), 16 * kUpperS[t6] + (e & 15))] = 0.f;
         }
     }
     __syncthreads();
+    // Off-diagonal blocks by distance d = R - S:
+    //   T_RS = -T_RR * sum_{J=S}^{R-1} A_RJ T_JS
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;
         for (int idx = tid; idx < nb * 256; idx += NT) {
-            const int blk = idx >> 8, e = idx & 255;
-            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            const int blk2 = idx >> 8, e = idx & 255;
+            const int R = d + blk2, S = R - d, r = e >> 4, cc = e & 15;
             float acc = 0.f;
             for (int J = S; J < R; ++J)
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj)
-                    acc += sAm[16 * R + r][16 * J + jj] * sT[16 * J + jj][16 * S + cc];
-            sX[blk][r][cc] = acc;
+                    acc += sAm[fx(16 * R + r, 16 * J + jj)] * sT[fx(16 * J + jj, 16 * S + cc)];
+            sX[blk2][r][cc] = acc;
         }
         __syncthreads();
         for (int idx = tid; idx < nb * 256; idx += NT) {
-            const int blk = idx >> 8, e = idx & 255;
-            const int R = d + blk, S = R - d, r = e >> 4, cc = e & 15;
+            const int blk2 = idx >> 8, e = idx & 255;
+            const int R = d + blk2, S = R - d, r = e >> 4, cc = e & 15;
             float acc = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) acc += sT[16 * R + r][16 * R + jj] * sX[blk][jj][cc];
-            sT[16 * R + r][16 * S + cc] = -acc;
+            for (int jj = 0; jj < 16; ++jj) acc += sT[fx(16 * R + r, 16 * R + jj)] * sX[blk2][jj][cc];
+            sT[fx(16 * R + r, 16 * S + cc)] = -acc;
         }
         __syncthreads();
     }
@@ -812,28 +880,34 @@ __global__ __launch_bounds__(kPrep2Threads) void chunk_prep_bf16_kernel(Problem 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks < nK) {
-                float tmp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tmp[e] = sT[16 * R + l16][32 * ks + 8 * lg + e];
+                const int row = 16 * R + l16, col = 32 * ks + 8 * lg;
+                const f32x4 t0v = *reinterpret_cast<const f32x4 *>(&sT[fx(row, col)]);
+                const f32x4 t1v = *reinterpret_cast<const f32x4 *>(&sT[fx(row, col + 4)]);
+                const float tmp[8] = {t0v[0], t0v[1], t0v[2], t0v[3], t1v[0], t1v[1], t1v[2], t1v[3]};
                 Tf[ks] = M::from_f32x8(tmp);
             }
         }
 #pragma unroll
         for (int mi = half * (DK / 32); mi < (half + 1) * (DK / 32); ++mi) {
             f32x4 acc = zero4();
-            const bf16 *arow = &sAt[16 * mi + l16][0];
+            const int row = 16 * mi + l16;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                if (ks < nK) acc = M::mma(M::load(arow, 32 * ks, lane), Tf[ks], acc);
+                if (ks < nK)
+                    acc = M::mma(*reinterpret_cast<const M::frag *>(&sAt[tx(row, 32 * ks + 8 * lg)]),
+                                 Tf[ks], acc);
             store_frag4(ws.W + ch * C * DK, 16 * R + l16, 16 * mi + 4 * lg, DK, acc);
         }
 #pragma unroll
         for (int nj = half * (DV / 32); nj < (half + 1) * (DV / 32); ++nj) {
             f32x4 acc = zero4();
-            const bf16 *urow = &sUt[16 * nj + l16][0];
+            const int row = 16 * nj + l16;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                if (ks < nK) acc = M::mma(Tf[ks], M::load(urow, 32 * ks, lane), acc);
+                if (ks < nK)
+                    acc = M::mma(Tf[ks],
+                                 *reinterpret_cast<const M::frag *>(&sUt[tx(row, 32 * ks + 8 * lg)]),
+                                 acc);
             store4(ws.Ut + ch * DV * C + ufrag_off(16 * nj + l16, 16 * R + 4 * lg), acc);
         }
     }
@@ -897,7 +971,8 @@ template <typename TI, int DK> struct OutOps {
 constexpr int kScan2Threads = 512;
 
 template <typename TI, int DK, int DEPTH>
-__global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws) {
+__global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
+                                                                   Block blk) {
     using M = Mma<TI>;
     using CO = ChainOps<TI, DK>;
     using OO = OutOps<TI, DK>;
@@ -911,7 +986,7 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
     const int l16 = lane & 15, lg = lane >> 4;
     const int H = (int)p.H, DV = (int)p.dv;
     const long T = p.T;
-    const long NC = (T + C - 1) / C;
+    const long NC = blk.nc;                 // chunks of this block
     const int nslice = DV / 16;
     const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
@@ -920,7 +995,7 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
     const long bh = logical / nslice;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int col0 = (int)(logical % nslice) * 16;
-    const long ch0 = bh * NC;
+    const long ch0 = bh * blk.nbmax;        // slot-local chunk-heads of this head
     const long last = NC - 1;
     auto chunk = [&](long c) { return ch0 + (c < 0 ? 0 : (c < last ? c : last)); };
 
@@ -933,7 +1008,7 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int i = 16 * (w * NI + a) + 4 * lg + m;
-                S[a][m] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + l16] : 0.f;
+                S[a][m] = blk.s_in ? blk.s_in[(bh * DK + i) * DV + col0 + l16] : 0.f;
             }
         auto write_st = [&](int buf) {
 #pragma unroll
@@ -1009,13 +1084,13 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
         // The output waves still finish the last chunk.
         __syncthreads();
         __syncthreads();
-        if (p.state_out) {
+        if (blk.s_out) {
 #pragma unroll
             for (int a = 0; a < NI; ++a)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int i = 16 * (w * NI + a) + 4 * lg + m;
-                    p.state_out[(bh * DK + i) * DV + col0 + l16] = S[a][m];
+                    blk.s_out[(bh * DK + i) * DV + col0 + l16] = S[a][m];
                 }
         }
     } else {
@@ -1036,7 +1111,7 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
 #pragma unroll
             for (int ks = 0; ks < KS_C; ++ks)
                 Ov = M::mma(M::load(&sDt[buf][l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
-            const long t = c * C + 16 * w + l16;
+            const long t = (blk.c0 + c) * C + 16 * w + l16;
             if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 4 * lg], Ov);
             __syncthreads();
             __syncthreads();
@@ -1082,25 +1157,87 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
 
 // ---- dispatch -----------------------------------------------------------------
 
-template <int V, typename TI, int DK, int DV>
-hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
-    const WsPtrs<TI> w = ws_ptrs<TI>(p, ws);
-    const long NC = (p.T + C - 1) / C;
-    const dim3 pgrid((unsigned)NC, (unsigned)p.H, (unsigned)p.B);
-    if constexpr (sizeof(TI) == 2)
-        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), pgrid, dim3(kPrep2Threads), 0,
-                           stream, p, w);
-    else
-        hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>), pgrid, dim3(kPrepThreads), 0,
-                           stream, p, w);
-    hipError_t e = hipGetLastError();
+// Internal helper stream and events of the calling host thread, one set per
+// device, created on first use and kept for the life of the process.
+struct AuxStream {
+    hipStream_t s = nullptr;
+    hipEvent_t start = nullptr, prep[2] = {nullptr, nullptr}, scan[2] = {nullptr, nullptr};
+};
+constexpr int kMaxDevices = 64;
+thread_local AuxStream t_aux[kMaxDevices];
+
+hipError_t aux_stream(AuxStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    AuxStream &a = t_aux[dev];
+    if (!a.s) {
+        if ((e = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking)) != hipSuccess) return e;
+        hipEvent_t *evs[] = {&a.start, &a.prep[0], &a.prep[1], &a.scan[0], &a.scan[1]};
+        for (hipEvent_t *ev : evs)
+            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &a;
+    return hipSuccess;
+}
+
+template <int V, typename TI, int DK, int DV>
+hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, hipStream_t st) {
+    const dim3 pgrid((unsigned)blk.nc, (unsigned)p.H, (unsigned)p.B);
+    if constexpr (sizeof(TI) == 2)
+        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), pgrid, dim3(kPrep2Threads), 0, st,
+                           p, w, blk);
+    else
+        hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>), pgrid, dim3(kPrepThreads), 0, st,
+                           p, w, blk);
+    return hipGetLastError();
+}
+
+template <typename TI, int DK, int DV>
+hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, hipStream_t st) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
     const long nwg = p.B * p.H * (DV / 16);
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
     hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH>), dim3((unsigned)grid),
-                       dim3(kScan2Threads), 0, stream, p, w);
+                       dim3(kScan2Threads), 0, st, p, w, blk);
     return hipGetLastError();
+}
+
+template <int V, typename TI, int DK, int DV>
+hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
+    const Plan q = make_plan(p);
+    char *base = static_cast<char *>(ws);
+    if (q.nblk == 1) {
+        const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
+        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out};
+        hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, stream);
+        if (e != hipSuccess) return e;
+        return launch_scan<TI, DK, DV>(p, w, blk, stream);
+    }
+    // Pipelined: the prep of block i + 1 runs on the helper stream while the
+    // scan of block i runs on the caller's stream; two workspace slots
+    // alternate, and events order each slot's reuse.
+    AuxStream *aux = nullptr;
+    hipError_t e = aux_stream(&aux);
+    if (e != hipSuccess) return e;
+    float *carrier = reinterpret_cast<float *>(base + 2 * q.slot);
+    if ((e = hipEventRecord(aux->start, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(aux->s, aux->start, 0)) != hipSuccess) return e;
+    for (long i = 0; i < q.nblk; ++i) {
+        const int slot = (int)(i & 1);
+        const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base + slot * q.slot);
+        const long c0 = i * q.nb;
+        const Block blk{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
+                        i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier};
+        if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
+        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, aux->s)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
+        if ((e = launch_scan<TI, DK, DV>(p, w, blk, stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->scan[slot], stream)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int V, typename TI>
@@ -1118,7 +1255,7 @@ hipError_t launch_v(const Problem &p, void *ws, hipStream_t stream) {
 
 }  // namespace
 
-size_t forward_workspace_bytes(const Problem &p) { return ws_layout(p).total; }
+size_t forward_workspace_bytes(const Problem &p) { return make_plan(p).total; }
 
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream) {
     switch (p.variant) {
