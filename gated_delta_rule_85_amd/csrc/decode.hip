@@ -22,20 +22,54 @@
 namespace gdr {
 namespace {
 
+// A length-dk vector of the token (k, q, a per-row gate) spread over the 64
+// lanes of a wave in 4-byte words, so that it arrives in one or two fully
+// coalesced loads, and read back per key row with a lane permute.  fp32:
+// word j of lane L holds element L + 64 j.  bf16: lane L holds elements 2L and
+// 2L + 1 (lanes beyond dk/2 repeat lower ones).
+template <typename X, int DK> struct RowVec {
+    static constexpr int NW = sizeof(X) == 4 ? (DK + 63) / 64 : 1;
+    uint32_t w[NW];
+
+    __device__ __forceinline__ void load(const X *row, int lane) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(row);
+        if constexpr (sizeof(X) == 4) {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) w[j] = p[(lane + 64 * j) % DK];
+        } else {
+            w[0] = p[lane % (DK / 2)];
+        }
+    }
+    // Element r0 + 8 i, for a lane-dependent r0 in [0, 8) and a compile-time i.
+    __device__ __forceinline__ float get(int r0, int i) const {
+        if constexpr (sizeof(X) == 4) {
+            const int j = i / 8;
+            return __uint_as_float((uint32_t)__shfl((int)w[j], r0 + 8 * i - 64 * j, kWave));
+        } else {
+            const uint32_t x = (uint32_t)__shfl((int)w[0], (r0 >> 1) + 4 * i, kWave);
+            return __uint_as_float((r0 & 1) ? (x & 0xffff0000u) : (x << 16));
+        }
+    }
+};
+
 // One (b, h, CW-column) tile of the step, owned by one wave.  Lanes are laid
 // out as LPR = CW / 4 lanes per row (one float4 each, so a row segment is one
-// whole 128-byte line for CW = 32) and 64 / LPR rows per pass.  Every
+// whole 128-byte line for CW = 32) and RPP = 64 / LPR consecutive rows per
+// pass: one load instruction of the workgroup's four waves covers a contiguous
+// run of rows of one head.  Lane (r0, cg) owns rows r0 + RPP i.  Every
 // reduction over the key rows (r, y, ||k||^2, k . q) is a butterfly over the
 // lanes that share a column group: no LDS, no barrier.  load() only issues
-// loads and keeps raw values, so nothing waits on them until finish().
+// loads and keeps raw words, so nothing waits on them until finish().
 template <int V, typename TI, int DK, int CW> struct DecodeTile {
     using VT = VariantTraits<V>;
     static constexpr int LPR = CW / 4;          // lanes per row
     static constexpr int RPP = kWave / LPR;     // rows per pass
     static constexpr int PASSES = DK / RPP;
+    static_assert(RPP == 8, "row vectors are permuted for eight rows per pass");
     f32x4 s[PASSES];
-    TI kraw[PASSES], qraw[PASSES], vr[4];
-    float ar[PASSES], dr[PASSES];
+    RowVec<TI, DK> kv, qv;
+    RowVec<float, DK> av, dv_;
+    TI vr[4];
     float beta, sdec;
     f32x4 wr;
 
@@ -44,19 +78,13 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
         const long bh = tile / tph;
         const int col0 = (int)(tile % tph) * CW;
         const int cg = lane % LPR, r0 = lane / LPR;
-        const TI *q = reinterpret_cast<const TI *>(p.q) + bh * DK;
-        const TI *k = reinterpret_cast<const TI *>(p.k) + bh * DK;
-#pragma unroll
-        for (int i = 0; i < PASSES; ++i) {
-            const int row = r0 + i * RPP;
-            kraw[i] = k[row];
-            qraw[i] = q[row];
-            if constexpr (VT::kGates) ar[i] = p.erase_b[bh * DK + row];
-            if constexpr (VT::kChannelDecay) dr[i] = p.alpha[bh * DK + row];
-        }
+        kv.load(static_cast<const TI *>(p.k) + bh * DK, lane);
+        qv.load(static_cast<const TI *>(p.q) + bh * DK, lane);
+        if constexpr (VT::kGates) av.load(p.erase_b + bh * DK, lane);
+        if constexpr (VT::kChannelDecay) dv_.load(p.alpha + bh * DK, lane);
         beta = VT::kScalarBeta ? p.beta[bh] : 0.f;
         sdec = (VT::kHasDecay && !VT::kChannelDecay) ? p.alpha[bh] : 1.f;
-        const TI *v = reinterpret_cast<const TI *>(p.v) + bh * (long)dv + col0 + 4 * cg;
+        const TI *v = static_cast<const TI *>(p.v) + bh * (long)dv + col0 + 4 * cg;
 #pragma unroll
         for (int c = 0; c < 4; ++c) vr[c] = v[c];
         if constexpr (VT::kGates)
@@ -81,11 +109,11 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
         float kr[PASSES];
 #pragma unroll
         for (int i = 0; i < PASSES; ++i) {
-            kr[i] = to_f32(kraw[i]);
-            const float qq = to_f32(qraw[i]);
-            if constexpr (VT::kChannelDecay) s[i] *= dr[i];
+            kr[i] = kv.get(r0, i);
+            const float qq = qv.get(r0, i);
+            if constexpr (VT::kChannelDecay) s[i] *= dv_.get(r0, i);
             else if constexpr (VT::kHasDecay) s[i] *= sdec;
-            const float a = VT::kGates ? ar[i] * kr[i] : kr[i];
+            const float a = VT::kGates ? av.get(r0, i) * kr[i] : kr[i];
             r += a * s[i];
             y += qq * s[i];
             kn += kr[i] * kr[i];
@@ -111,7 +139,7 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
         }
         if (r0 == 0) {
             const f32x4 o = y + kq * dl;
-            TI *op = reinterpret_cast<TI *>(p.o) + bh * (long)dv + col0 + 4 * cg;
+            TI *op = static_cast<TI *>(p.o) + bh * (long)dv + col0 + 4 * cg;
 #pragma unroll
             for (int c = 0; c < 4; ++c) op[c] = from_f32<TI>(o[c]);
         }
@@ -123,7 +151,8 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
 };
 
 template <int V, typename TI, int DK, int CW, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_wave_kernel(Problem p) {
+__global__ __launch_bounds__(WAVES * 64)
+void decode_wave_kernel(Problem p) {
     using Tile = DecodeTile<V, TI, DK, CW>;
     const long tile = (long)blockIdx.x * WAVES + threadIdx.x / kWave;
     if (tile >= p.B * p.H * (p.dv / CW)) return;
