@@ -66,7 +66,7 @@ def pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 28) -> str:
         rb = val * 1024 / fr if fr else float("nan")
         wb = wv * 1024 / wr if wr else float("nan")
         lines.append(f"{_short(name)} | {fn[(name, counter)]} | {val:.1f} | {wv:.1f} | "
-                     f"{rb:.4g} | {wb:.4g} | {rb + wb:.4g}")
+                     f"{rb:.0f} | {wb:.0f} | {rb + wb:.0f}")
     return "\n".join(lines)
 
 
