@@ -550,6 +550,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ __attribute__((aligned(16))) bf16 sAg[VT::kGates ? C * DK : 8];   // b (.) k
     __shared__ __attribute__((aligned(16))) float sG[C][GW];
     __shared__ float sBeta[C];
+    constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
+    __shared__ float sEg[kRowDecay ? C : 1], sEgc[kRowDecay ? C : 1];   // e^{g_r}, e^{g_C - g_r}
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[3][16][17];
@@ -681,6 +683,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 if (lane >= off) g += y;
             }
             sG[lane][0] = g;
+            const float gC = __shfl(g, C - 1, kWave);
+            sEg[lane] = __expf(g);
+            sEgc[lane] = __expf(gC - g);
         }
     }
     if constexpr (VT::kKaczmarz) {
@@ -711,10 +716,12 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             if (idx < C * KC) {
                 const int r = idx / KC, pc = idx % KC;
                 bf16x8 o;
+                float egr = 1.f;
+                if constexpr (kRowDecay) egr = sEg[r];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float eg = 1.f;
-                    if constexpr (VT::kHasDecay) eg = __expf(sG[r][VT::kChannelDecay ? 8 * pc + e : 0]);
+                    float eg = egr;
+                    if constexpr (VT::kChannelDecay) eg = __expf(sG[r][8 * pc + e]);
                     o[e] = (bf16)((float)qreg[n][e] * eg);
                 }
                 *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
@@ -734,10 +741,13 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 if constexpr (VT::kGates) a = (float)sAg[kx(r, i)];
                 else a = sBeta[r] * kk;
                 float eg = 1.f, egc = 1.f;
-                if constexpr (VT::kHasDecay) {
-                    const float g = sG[r][VT::kChannelDecay ? i : 0];
+                if constexpr (VT::kChannelDecay) {
+                    const float g = sG[r][i];
                     eg = __expf(g);
                     egc = __expf(gC - g);
+                } else if constexpr (kRowDecay) {
+                    eg = sEg[r];
+                    egc = sEgc[r];
                 }
                 at[e] = a * eg;
                 kb[e] = kk * egc;
@@ -782,6 +792,15 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             const int kb = 32 * ks + 8 * lg;
             const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rs, kb)]);
             const bf16x8 qr8 = qf[u][ks];
+            if constexpr (!VT::kChannelDecay && !VT::kGates) {
+                // a_r = beta_r k_r and the decay are scalars per row: the stored
+                // bf16 rows go to the matrix cores as they are and the scalars
+                // multiply the product.
+                const bf16x8 kq8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
+                accA = M::mma(kr8, kq8, accA);
+                accP = M::mma(kr8, qr8, accP);
+                continue;
+            }
             bf16x8 ar8;
             if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[kx(rr, kb)]);
             else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
@@ -809,9 +828,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         for (int m = 0; m < 4; ++m) {
             const int s2 = 16 * S + 4 * lg + m;
             float f = 1.f;
-            if constexpr (VT::kHasDecay && !VT::kChannelDecay)
-                f = s2 <= r ? __expf(sG[r][0] - sG[s2][0]) : 0.f;
-            Av[m] = s2 < r ? accA[m] * f : 0.f;
+            if constexpr (kRowDecay) f = s2 <= r ? __expf(sG[r][0] - sG[s2][0]) : 0.f;
+            float fa = f;
+            if constexpr (!VT::kChannelDecay && !VT::kGates) fa = f * br;
+            Av[m] = s2 < r ? accA[m] * fa : 0.f;
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
         *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
@@ -914,21 +934,23 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 }
 
 // ============================================================================
-// chunk_scan, split roles: eight waves per workgroup.  Waves 0-3 run only the
-// state recurrence (Delta = U~ - W S, then S <- Gamma S + Kbar^T Delta) and
-// load only W, Kbar^T, U~ and e^{g_C}; waves 4-7 produce the output of the
-// previous chunk, O = Qt S + P Delta, from double-buffered copies of S^T and
-// Delta^T in LDS, and load only Qt and P.  The state chain per chunk is then
-// two short matrix-core steps between two barriers, and the output work runs
-// beside it on the same SIMDs.
+// chunk_scan, split roles: eight waves per workgroup, which owns NJ 16-column
+// tiles of one head's state.  Waves 0-3 run only the state recurrence
+// (Delta = U~ - W S, then S <- Gamma S + Kbar^T Delta) and load only W,
+// Kbar^T, U~ and e^{g_C}; waves 4-7 produce the output of the previous chunk,
+// O = Qt S + P Delta, from double-buffered copies of S^T and Delta^T in LDS,
+// and load only Qt and P.  The state chain per chunk is then two short
+// matrix-core steps between two barriers, and the output work runs beside it
+// on the same SIMDs.  The chunk factors are shared by all column tiles of a
+// head, so wider slices (larger NJ) read them fewer times in all.
 // ============================================================================
-template <typename TI, int DK> struct ChainOps {
+template <typename TI, int DK, int NJ> struct ChainOps {
     using M = Mma<TI>;
     static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK, NI = DK / 64;
     static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);   // bytes per fragment tile
     typedef typename std::conditional<sizeof(TI) == 2, bf16x4, f32x4>::type raw4;
     typename M::frag Wf[KS_D], Kf[NI][KS_C];
-    raw4 U;
+    raw4 U[NJ];
     f32x4 gam[NI];
     __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0, int w,
                                          int lane) {
@@ -948,7 +970,10 @@ template <typename TI, int DK> struct ChainOps {
                 Kf[a][ks] = buf_load<typename M::frag>(rk, loff + (a * KS_C + ks) * FB);
             gam[a] = buf_load<f32x4>(rg, (unsigned)(lane >> 4) * 16u + 64u * a);
         }
-        U = buf_load<raw4>(ru, (unsigned)lane * 4u * sizeof(TI));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            U[j] = buf_load<raw4>(ru, ((unsigned)lane + (unsigned)(j * (C / 16) * kWave)) * 4u *
+                                          sizeof(TI));
     }
 };
 
@@ -970,16 +995,17 @@ template <typename TI, int DK> struct OutOps {
 
 constexpr int kScan2Threads = 512;
 
-template <typename TI, int DK, int DEPTH>
+template <typename TI, int DK, int DEPTH, int NJ>
 __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
-    using CO = ChainOps<TI, DK>;
+    using CO = ChainOps<TI, DK, NJ>;
     using OO = OutOps<TI, DK>;
     constexpr int KS_D = CO::KS_D, KS_C = CO::KS_C, NI = CO::NI;
     constexpr int PT = 8;
-    __shared__ __attribute__((aligned(16))) TI sSt[2][16][DK + PT];   // S^T, double-buffered
-    __shared__ __attribute__((aligned(16))) TI sDt[2][16][C + PT];    // Delta^T, double-buffered
+    constexpr int SW = 16 * NJ;   // value columns of the slice
+    __shared__ __attribute__((aligned(16))) TI sSt[2][SW][DK + PT];   // S^T, double-buffered
+    __shared__ __attribute__((aligned(16))) TI sDt[2][SW][C + PT];    // Delta^T, double-buffered
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -987,14 +1013,14 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
     const int H = (int)p.H, DV = (int)p.dv;
     const long T = p.T;
     const long NC = blk.nc;                 // chunks of this block
-    const int nslice = DV / 16;
+    const int nslice = DV / SW;
     const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
     const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nwg) return;
     const long bh = logical / nslice;
     const int b = (int)(bh / H), h = (int)(bh % H);
-    const int col0 = (int)(logical % nslice) * 16;
+    const int col0 = (int)(logical % nslice) * SW;
     const long ch0 = bh * blk.nbmax;        // slot-local chunk-heads of this head
     const long last = NC - 1;
     auto chunk = [&](long c) { return ch0 + (c < 0 ? 0 : (c < last ? c : last)); };
@@ -1002,17 +1028,22 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
     if (wave < 4) {
         // ---------------- state chain ----------------
         const int w = wave;
-        f32x4 S[NI];
+        f32x4 S[NJ][NI];
 #pragma unroll
-        for (int a = 0; a < NI; ++a)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int i = 16 * (w * NI + a) + 4 * lg + m;
-                S[a][m] = blk.s_in ? blk.s_in[(bh * DK + i) * DV + col0 + l16] : 0.f;
-            }
+            for (int a = 0; a < NI; ++a)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * (w * NI + a) + 4 * lg + m;
+                    S[j][a][m] = blk.s_in ? blk.s_in[(bh * DK + i) * DV + col0 + 16 * j + l16] : 0.f;
+                }
         auto write_st = [&](int buf) {
 #pragma unroll
-            for (int a = 0; a < NI; ++a) store4(&sSt[buf][l16][16 * (w * NI + a) + 4 * lg], S[a]);
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int a = 0; a < NI; ++a)
+                    store4(&sSt[buf][16 * j + l16][16 * (w * NI + a) + 4 * lg], S[j][a]);
         };
         write_st(0);
         __syncthreads();
@@ -1021,48 +1052,39 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
         // loads in flight before it reuses any register.
         auto step = [&](const CO &op, long c) __attribute__((always_inline)) {
             const int cur = (int)(c & 1);
-            typename M::frag Sf[KS_D];
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks) Sf[ks] = M::load(&sSt[cur][l16][0], ks * M::kK, lane);
-            f32x4 d0 = zero4(), d1 = zero4();
+            for (int j = 0; j < NJ; ++j) {
+                typename M::frag Sf[KS_D];
 #pragma unroll
-            for (int ks = 0; ks < KS_D; ks += 2) {
-                d0 = M::mma(op.Wf[ks], Sf[ks], d0);
-                if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[ks + 1], d1);
+                for (int ks = 0; ks < KS_D; ++ks)
+                    Sf[ks] = M::load(&sSt[cur][16 * j + l16][0], ks * M::kK, lane);
+                f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ks += 2) {
+                    d0 = M::mma(op.Wf[ks], Sf[ks], d0);
+                    if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[ks + 1], d1);
+                }
+                store4(&sDt[cur][16 * j + l16][16 * w + 4 * lg], to_f32x4(op.U[j]) - (d0 + d1));
             }
-            store4(&sDt[cur][l16][16 * w + 4 * lg], to_f32x4(op.U) - (d0 + d1));
             __syncthreads();
-            typename M::frag Df[KS_C];
 #pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(&sDt[cur][l16][0], ks * M::kK, lane);
+            for (int j = 0; j < NJ; ++j) {
+                typename M::frag Df[KS_C];
 #pragma unroll
-            for (int a = 0; a < NI; ++a) {
-                f32x4 acc = S[a] * op.gam[a];
+                for (int ks = 0; ks < KS_C; ++ks)
+                    Df[ks] = M::load(&sDt[cur][16 * j + l16][0], ks * M::kK, lane);
 #pragma unroll
-                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[ks], acc);
-                S[a] = acc;
+                for (int a = 0; a < NI; ++a) {
+                    f32x4 acc = S[j][a] * op.gam[a];
+#pragma unroll
+                    for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[ks], acc);
+                    S[j][a] = acc;
+                }
             }
             write_st(cur ^ 1);
             __syncthreads();
         };
-        if constexpr (DEPTH == 3) {
-            CO A, Bq, Cq;
-            A.load(ws, chunk(0), DV, col0, w, lane);
-            Bq.load(ws, chunk(1), DV, col0, w, lane);
-            for (long c = 0; c < NC; c += 3) {
-                Cq.load(ws, chunk(c + 2), DV, col0, w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(A, c);
-                if (c + 1 >= NC) break;
-                A.load(ws, chunk(c + 3), DV, col0, w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(Bq, c + 1);
-                if (c + 2 >= NC) break;
-                Bq.load(ws, chunk(c + 4), DV, col0, w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(Cq, c + 2);
-            }
-        } else if constexpr (DEPTH == 2) {
+        if constexpr (DEPTH == 2) {
             CO A, Bq;
             A.load(ws, chunk(0), DV, col0, w, lane);
             for (long c = 0; c < NC; c += 2) {
@@ -1086,12 +1108,14 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
         __syncthreads();
         if (blk.s_out) {
 #pragma unroll
-            for (int a = 0; a < NI; ++a)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int i = 16 * (w * NI + a) + 4 * lg + m;
-                    blk.s_out[(bh * DK + i) * DV + col0 + l16] = S[a][m];
-                }
+                for (int a = 0; a < NI; ++a)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i = 16 * (w * NI + a) + 4 * lg + m;
+                        blk.s_out[(bh * DK + i) * DV + col0 + 16 * j + l16] = S[j][a][m];
+                    }
         }
     } else {
         // ---------------- outputs of the previous chunk ----------------
@@ -1103,37 +1127,23 @@ __global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, W
         // op holds the factors of chunk c; S_c and Delta_c are in LDS buffer c % 2.
         auto step = [&](const OO &op, long c) __attribute__((always_inline)) {
             const int buf = (int)(c & 1);
-            f32x4 Ov = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS_D; ++ks)
-                Ov = M::mma(M::load(&sSt[buf][l16][0], ks * M::kK, lane), op.Qf[ks], Ov);
-            // P is zero above the diagonal, so all K-steps may run.
-#pragma unroll
-            for (int ks = 0; ks < KS_C; ++ks)
-                Ov = M::mma(M::load(&sDt[buf][l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
             const long t = (blk.c0 + c) * C + 16 * w + l16;
-            if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 4 * lg], Ov);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                f32x4 Ov = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_D; ++ks)
+                    Ov = M::mma(M::load(&sSt[buf][16 * j + l16][0], ks * M::kK, lane), op.Qf[ks], Ov);
+                // P is zero above the diagonal, so all K-steps may run.
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks)
+                    Ov = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
+                if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 16 * j + 4 * lg], Ov);
+            }
             __syncthreads();
             __syncthreads();
         };
-        if constexpr (DEPTH == 3) {
-            OO A, Bq, Cq;
-            A.load(ws, chunk(0), w, lane);
-            Bq.load(ws, chunk(1), w, lane);
-            for (long c = 0; c < NC; c += 3) {
-                Cq.load(ws, chunk(c + 2), w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(A, c);
-                if (c + 1 >= NC) break;
-                A.load(ws, chunk(c + 3), w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(Bq, c + 1);
-                if (c + 2 >= NC) break;
-                Bq.load(ws, chunk(c + 4), w, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                step(Cq, c + 2);
-            }
-        } else if constexpr (DEPTH == 2) {
+        if constexpr (DEPTH == 2) {
             OO A, Bq;
             A.load(ws, chunk(0), w, lane);
             for (long c = 0; c < NC; c += 2) {
@@ -1197,9 +1207,13 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
 template <typename TI, int DK, int DV>
 hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, hipStream_t st) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
-    const long nwg = p.B * p.H * (DV / 16);
+    // One 16-column tile per workgroup: wider slices read the shared factors
+    // fewer times in all but lengthen each chunk's chain, and measured slower
+    // on the long-context workload.
+    constexpr int NJ = 1;
+    const long nwg = p.B * p.H * (DV / (16 * NJ));
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ>), dim3((unsigned)grid),
                        dim3(kScan2Threads), 0, st, p, w, blk);
     return hipGetLastError();
 }
