@@ -13,6 +13,11 @@ dominant kernel (decode: HBM-bound) timed with HIP events on the launch stream,
 and the CPU oracle timed on a bounded sample of the same work.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+    python bench.py --long-context [--steps 20] [--warmup 3]
+
+The second form measures the long-context shapes instead (131,072-token
+prefill, single-sequence decode from position 32,768, Kaczmarz LA against Gated
+DeltaNet) and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -124,6 +129,115 @@ def cpu_baseline(wl, T_sample, decode_steps_sample, threads):
                 decode_tokens_per_s=Bd * decode_steps_sample / t_dec)
 
 
+def long_context(args):
+    """The pages' efficiency comparison at kernel level: prefill latency of a
+    131,072-token context and single-sequence decode throughput from the state
+    at position 32,768, for the Kaczmarz layer and its Gated DeltaNet
+    counterpart (same shapes; only the step size differs).  Prints one JSON
+    line."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import WORKLOADS, make_decode_inputs, make_workload
+
+    L = binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    res = {}
+    for wid in (6, 7):
+        wl = WORKLOADS[wid]
+        B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+        log(f"{wl.name}: generating the {T}-token prefill")
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in make_workload(wl).items()}
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        fa = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"],
+                               None, None, d["eps"], None, s_T)
+        binding.check(binding.gdr_check_args(fa, 0))
+        nws = binding.gdr_forward_workspace_size(fa)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            binding.check(L.gdr_forward_chunked(ctypes.byref(fa), ws.data_ptr(), nws, sh))
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(args.steps):
+            L.gdr_forward_chunked(ctypes.byref(fa), ws.data_ptr(), nws, sh)
+        e1.record()
+        torch.cuda.synchronize()
+        pre_s = e0.elapsed_time(e1) / 1e3 / args.steps
+        del d, o, ws
+
+        pos, Bd, Sd = wl.decode["position"], wl.decode["B"], wl.decode["steps"]
+        log(f"{wl.name}: prefill of {pos} tokens, then {Sd} decode steps at batch {Bd}")
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in make_workload(wl, T=pos).items()}
+        _, s_pos = binding.forward(wl.variant, d["q"], d["k"], d["v"], alpha=d["alpha"],
+                                   beta=d["beta"], eps=d["eps"])
+        del d
+        state = s_pos.expand(Bd, H, dk, dv).contiguous()
+        dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+              for k, v in make_decode_inputs(wl).items()}
+        o_dec = torch.empty((Sd, Bd, 1, H, dv), dtype=torch.bfloat16, device=dev)
+        dargs = [binding.make_args(wl.variant, dd["q"][i], dd["k"][i], dd["v"][i], o_dec[i],
+                                   dd["alpha"][i], dd["beta"][i], None, None, dd["eps"],
+                                   state, state) for i in range(Sd)]
+        for a in dargs:
+            binding.check(binding.gdr_check_args(a, 1))
+        refs = [ctypes.byref(a) for a in dargs]
+
+        def block(handle):
+            for r in refs:
+                rc = L.gdr_decode_step(r, handle)
+                if rc:
+                    binding.check(rc)
+
+        block(sh)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            block(torch.cuda.current_stream().cuda_stream)
+        for _ in range(args.warmup):
+            graph.replay()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_s = e0.elapsed_time(e1) / 1e3 / (args.steps * Sd)
+        fl = forward_flops_per_head_token(dk, dv) * B * T * H
+        fb = forward_bytes(B, T, H, dk, dv)
+        res[wl.variant] = dict(
+            workload=wl.name,
+            prefill=dict(T=T, ms=pre_s * 1e3, tokens_per_s=B * T / pre_s,
+                         tflops=fl / pre_s / 1e12, mfma_frac=fl / pre_s / PEAK_BF16,
+                         hbm_frac=fb / pre_s / PEAK_HBM),
+            decode=dict(position=pos, batch=Bd, steps=Sd, us_per_step=dec_s * 1e6,
+                        tokens_per_s=Bd / dec_s,
+                        hbm_frac=decode_bytes(Bd, H, dk, dv) / dec_s / PEAK_HBM))
+        del state, dd, o_dec, graph
+        torch.cuda.empty_cache()
+    k, g = res["kla"], res["gated_deltanet"]
+    out = {
+        "metric": "131K-token prefill latency and decode throughput at position 32K, "
+                  "Kaczmarz LA vs Gated DeltaNet (one layer, kernel level)",
+        "value": k["prefill"]["ms"], "unit": "ms (Kaczmarz LA prefill, 131072 tokens)",
+        "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "B=1 H=16 d_k=d_v=128 bf16 layer; prefill T=131072; "
+                               "decode at batch 1 from the state after 32768 tokens"},
+        "kla": k, "gated_deltanet": g,
+        "ratios": {"prefill_latency_kla_over_gdn": k["prefill"]["ms"] / g["prefill"]["ms"],
+                   "decode_throughput_kla_over_gdn":
+                       k["decode"]["tokens_per_s"] / g["decode"]["tokens_per_s"]},
+        "git": git_sha(),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,12 +250,18 @@ def main():
                     help="launch the decode steps one by one instead of replaying a HIP graph")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--cpu-decode-steps", type=int, default=192)
+    ap.add_argument("--long-context", action="store_true",
+                    help="measure the long-context shapes (131K prefill, decode at 32K) instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs every (b, h) head on one "
               "device and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.long_context:
+        long_context(args)
+        return
 
     import torch
 

@@ -60,6 +60,17 @@ WORKLOADS = {
                 65536, 128, 128, "bf16", 85005, alpha_scale=0.1, eps=1e-6,
                 unnormalised_keys=True,
                 decode=dict(B=64, steps=1024, seed=85105)),
+    # Long-context efficiency shapes: prefill of a 131,072-token context, and
+    # single-sequence decode from the state after a 32,768-token prefill, for
+    # the Kaczmarz layer and its Gated DeltaNet counterpart (same shapes and
+    # gates; only the step size differs).
+    6: Workload("kla_bf16_B1_H16_T131072_d128_decode_at_32768", "kla", 1, 16,
+                131072, 128, 128, "bf16", 85006, alpha_scale=0.1, eps=1e-6,
+                unnormalised_keys=True,
+                decode=dict(B=1, steps=256, seed=85106, position=32768)),
+    7: Workload("gated_deltanet_bf16_B1_H16_T131072_d128_decode_at_32768", "gated_deltanet",
+                1, 16, 131072, 128, 128, "bf16", 85007, alpha_scale=0.1,
+                decode=dict(B=1, steps=256, seed=85107, position=32768)),
 }
 
 
@@ -76,8 +87,16 @@ def _normal(rng, shape):
 
 
 def _l2norm_last(x):
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x / np.maximum(n, 1e-30)).astype(np.float32)
+    # Row by row in float64, in slices that stay in cache (same values as one
+    # whole-array pass).
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty(flat.shape, dtype=np.float32)
+    step = 1 << 14
+    for i in range(0, flat.shape[0], step):
+        blk = flat[i:i + step]
+        n = np.sqrt(np.sum(blk.astype(np.float64) ** 2, axis=-1, keepdims=True))
+        out[i:i + step] = blk / np.maximum(n, 1e-30)
+    return out.reshape(x.shape)
 
 
 def _store(x, dtype):

@@ -1,6 +1,8 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration
-the benchmark times: the whole layer runs on the GPU and the oracle recomputes
-sampled heads (every token of their sequence and their final state)."""
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the whole layer runs on the GPU and the oracle recomputes
+sampled heads (every token of their sequence and their final state).
+Workloads 6 and 7 are the long-context shapes (131,072-token prefill; decode
+from the state at position 32,768)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,7 @@ def _sample_heads(B, H):
     return sorted(heads)
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5, 6, 7])
 def test_workload_forward_sampled_heads(wid):
     wl = WORKLOADS[wid]
     announce(f"workload {wid}: {wl.name}")
@@ -41,18 +43,21 @@ def test_workload_forward_sampled_heads(wid):
         assert e_o < tol and e_s < tol
 
 
-def test_workload5_decode_from_prefill_state():
-    """Decode at batch 64 from the prefill's final state, broadcast over the
-    batch; both sides start from the same fp32 state tensor."""
-    wl = WORKLOADS[5]
+@pytest.mark.parametrize("wid", [5, 6, 7])
+def test_workload_decode_from_prefill_state(wid):
+    """Decode from the state a prefill leaves at the workload's decode
+    position, broadcast over the decode batch; both sides start from the same
+    fp32 state tensor."""
+    wl = WORKLOADS[wid]
     steps = 4
-    announce("workload 5 decode: prefill state -> 4 decode steps at batch 64")
-    inp = make_workload(wl)
+    pos = wl.decode.get("position", wl.T)
+    Bd = wl.decode["B"]
+    announce(f"workload {wid} decode: prefill of {pos} tokens -> {steps} decode steps at batch {Bd}")
+    inp = make_workload(wl, T=pos)
     d = to_dev(inp)
     _, s_T = binding.forward(wl.variant, d["q"], d["k"], d["v"], alpha=d["alpha"],
                              beta=d["beta"], eps=d["eps"])
     del d, inp
-    Bd = wl.decode["B"]
     state = s_T.expand(Bd, *s_T.shape[1:]).contiguous()
     state0 = state.cpu().numpy().astype(np.float64)
     dec = make_decode_inputs(wl, steps=steps)
@@ -63,7 +68,7 @@ def test_workload5_decode_from_prefill_state():
                                         alpha=dd["alpha"][st], beta=dd["beta"][st],
                                         eps=dd["eps"]))
     torch.cuda.synchronize()
-    heads = [(0, 0), (13, 5), (63, 15)]
+    heads = sorted({(0, 0), (Bd // 5, 5), (Bd - 1, wl.H - 1)})
     ref_state = state0
     for st in range(steps):
         o_ref, ref_state = oracle.forward(wl.variant, dec["q"][st], dec["k"][st], dec["v"][st],
