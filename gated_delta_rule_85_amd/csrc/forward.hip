@@ -226,13 +226,17 @@ template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc
     }
 }
 
-// The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix, spread so
-// that four waves get 3, 3, 2, 2 of them.
-__constant__ int8_t kLowerR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kLowerS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-// The six strictly upper 16x16 tiles.
-__constant__ int8_t kUpperR[6] = {0, 0, 0, 1, 1, 2};
-__constant__ int8_t kUpperS[6] = {1, 2, 3, 2, 3, 3};
+// The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix in row
+// order, and the six strictly upper ones, as arithmetic on the tile number
+// (no table: a table read is a memory load, and its wait would also wait for
+// every load issued before it).
+__device__ __forceinline__ int lower_r(int t) { return (t >= 1) + (t >= 3) + (t >= 6); }
+__device__ __forceinline__ int lower_s(int t) {
+    const int r = lower_r(t);
+    return t - r * (r + 1) / 2;
+}
+__device__ __forceinline__ int upper_r(int t) { return (t >= 3) + (t >= 5); }
+__device__ __forceinline__ int upper_s(int t) { return t + 1 - 2 * (t >= 3) - (t >= 5); }
 
 // ============================================================================
 // chunk_prep
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     // the operands around the mid-chunk reference g_ref = g_{C/2-1}; scalar
     // decay is applied to the product as e^{g_r - g_s} <= 1.
     for (int tl = wave; tl < 10; tl += kPrepThreads / kWave) {
-        const int R = kLowerR[tl], S = kLowerS[tl];
+        const int R = lower_r(tl), S = lower_s(tl);
         const int rs = 16 * S + l16;   // row supplying the K_R operand
         const int rr = 16 * R + l16;   // row supplying the A_L / Q_L operands
         f32x4 accA = zero4(), accP = zero4();
@@ -426,8 +430,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     for (int idx = tid; idx < 6 * 16 * 4; idx += kPrepThreads) {
         // zero the strictly upper tiles of P (4 values per thread-step)
         const int t6 = idx / 64, e = idx % 64;
-        const int r = 16 * kUpperR[t6] + e / 4;
-        const int s = 16 * kUpperS[t6] + 4 * (e % 4);
+        const int r = 16 * upper_r(t6) + e / 4;
+        const int s = 16 * upper_s(t6) + 4 * (e % 4);
         store_frag4(ws.P + ch * C * C, r, s, C, zero4());
     }
     __syncthreads();
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     } else {
         for (int idx = tid - kWave; idx < 6 * 256; idx += kPrepThreads - kWave) {
             const int t6 = idx >> 8, e = idx & 255;
-            sT[16 * kUpperR[t6] + (e >> 4)][16 * kUpperS[t6] + (e & 15)] = 0.f;
+            sT[16 * upper_r(t6) + (e >> 4)][16 * upper_s(t6) + (e & 15)] = 0.f;
         }
     }
     __syncthreads();
@@ -528,6 +532,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 // ============================================================================
 constexpr int kPrep2Threads = 512;
 
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
+    return z;
+}
+
 // Element offset in an unpadded tile with CPR 16-byte chunks per row whose
 // chunk index is XORed with the row: sixteen lanes reading one column chunk of
 // sixteen consecutive rows touch distinct banks.  EPC = elements per chunk.
@@ -535,14 +546,76 @@ template <int CPR, int EPC> __device__ __forceinline__ int swz(int r, int col) {
     return (r * CPR + ((col / EPC) ^ (r & (CPR - 1)))) * EPC + col % EPC;
 }
 
+// Raw global inputs of one chunk-head, held in registers from the issue of
+// their loads (during the previous chunk-head's arithmetic) to their use.  The
+// loads are unconditional (rows past T read the last valid row) so that the
+// compiler's waits for them stay exact; staging masks those rows.
+template <int V, int DK, int DV> struct PrepRaw {
+    using VT = VariantTraits<V>;
+    static constexpr int NT = kPrep2Threads;
+    static constexpr int KC = DK / 8, VC = DV / 8;            // 16-byte chunks per row
+    static constexpr int NQ = C * KC / NT;                     // q / k chunks per thread
+    static constexpr int NV = C * VC / NT;                     // v chunks per thread
+    static constexpr int NA = VT::kChannelDecay ? C * DK / 4 / NT : 1;
+    static_assert(C * KC % NT == 0 && C * VC % NT == 0 && C * DK / 4 % NT == 0, "whole passes");
+    bf16x8 k[NQ], q[NQ], v[NV];
+    f32x4 eb[VT::kGates ? 2 * NQ : 1], ww[VT::kGates ? 2 * NV : 1];   // erase / write gates
+    f32x4 al[NA];                                              // channel-wise alpha
+    float a1, be;                                              // scalar alpha, beta / eta
+
+    __device__ __forceinline__ void issue(const Problem &p, long c, int h, int b, int tid) {
+        const long T = p.T, t0 = c * C;
+        const int H = (int)p.H;
+        const int last = (int)min((long)C, T - t0) - 1;
+        auto tok = [&](int r) -> long { return ((long)b * T + t0 + (r < last ? r : last)) * H + h; };
+        const bf16 *qp = static_cast<const bf16 *>(p.q);
+        const bf16 *kp = static_cast<const bf16 *>(p.k);
+        const bf16 *vp = static_cast<const bf16 *>(p.v);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int idx = tid + n * NT;
+            const int r = idx / KC, pc = idx % KC;
+            k[n] = *reinterpret_cast<const bf16x8 *>(&kp[tok(r) * DK + 8 * pc]);
+            q[n] = *reinterpret_cast<const bf16x8 *>(&qp[tok(r) * DK + 8 * pc]);
+            if constexpr (VT::kGates) {
+                eb[2 * n] = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
+                eb[2 * n + 1] = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int idx = tid + n * NT;
+            const int r = idx / VC, pc = idx % VC;
+            v[n] = *reinterpret_cast<const bf16x8 *>(&vp[tok(r) * DV + 8 * pc]);
+            if constexpr (VT::kGates) {
+                ww[2 * n] = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc]);
+                ww[2 * n + 1] = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc + 4]);
+            }
+        }
+        if constexpr (VT::kChannelDecay) {
+#pragma unroll
+            for (int n = 0; n < NA; ++n) {
+                const int idx = tid + n * NT;
+                const int r = idx / (DK / 4), i4 = 4 * (idx % (DK / 4));
+                al[n] = *reinterpret_cast<const f32x4 *>(&p.alpha[tok(r) * DK + i4]);
+            }
+        } else if constexpr (VT::kHasDecay) {
+            a1 = p.alpha[tok(tid & (kWave - 1))];
+        }
+        if constexpr (VT::kScalarBeta) be = p.beta[tok(tid & (C - 1))];
+    }
+};
+
 template <int V, int DK, int DV>
-__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 1 : 2)
+__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
 void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     using VT = VariantTraits<V>;
     using M = Mma<bf16>;
+    using Raw = PrepRaw<V, DK, DV>;
     constexpr int NT = kPrep2Threads, NW = NT / kWave;
     constexpr int GW = VT::kChannelDecay ? DK : 1;
     constexpr int KC = DK / 8, VC = DV / 8;   // 16-byte chunks per k row / v row
+    constexpr int NQ = Raw::NQ, NV = Raw::NV;
     constexpr int R1 = C * DK * 2 > C * C * 4 ? C * DK * 2 : C * C * 4;   // k   -> T
     constexpr int R3 = C * DV * 2 > C * C * 4 ? C * DV * 2 : C * C * 4;   // u   -> A
     __shared__ __attribute__((aligned(16))) char smem1[R1];
@@ -564,105 +637,103 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     auto tx = [](int r, int col) { return swz<C / 8, 8>(r, col); };   // [D][C] bf16 tiles
     auto fx = [](int r, int col) { return swz<C / 4, 4>(r, col); };   // [C][C] fp32 tiles
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, lg = lane >> 4;
-    const long c = blk.c0 + blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const long T = p.T;
     const int H = (int)p.H;
-    const long t0 = c * C;
-    const int nvalid = (int)min((long)C, T - t0);
-    const long ch = ((long)b * H + h) * blk.nbmax + blockIdx.x;   // slot-local chunk-head
     const bf16 *q = static_cast<const bf16 *>(p.q);
-    const bf16 *k = static_cast<const bf16 *>(p.k);
-    const bf16 *v = static_cast<const bf16 *>(p.v);
-    auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
-    auto zero8 = []() {
-        bf16x8 z;
+    // Work items are the block's chunk-heads, chunk fastest; a workgroup takes
+    // every gridDim.x-th item and loads the next one's inputs while it
+    // computes the current one.
+    const long nitems = (long)blk.nc * p.H * p.B;
+    long item = blockIdx.x;
+    if (item >= nitems) return;
+    auto chunk_of = [&](long it) { return blk.c0 + it % blk.nc; };
+    auto bh_of = [&](long it) { return it / blk.nc; };
+    Raw raw;
+    raw.issue(p, chunk_of(item), (int)(bh_of(item) % H), (int)(bh_of(item) / H), (int)threadIdx.x);
+    // q rows of this wave's Gram tiles, for phase 2 (L2 hits); rows past T
+    // read the last valid row, whose products only reach rows never stored.
+    bf16x8 qf[2][DK / 32];
+    auto load_qf = [&](long it, int l16, int lg) {
+        const long bh = bh_of(it);
+        const long t0 = chunk_of(it) * C;
+        const int last = (int)min((long)C, T - t0) - 1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
-        return z;
+        for (int u = 0; u < 2; ++u) {
+            const int tl = wave + u * NW;
+            const int rr = min(16 * lower_r(tl < 10 ? tl : 0) + l16, last);
+            const long row = ((bh / H) * T + t0 + rr) * H + bh % H;
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                qf[u][ks] = *reinterpret_cast<const bf16x8 *>(&q[row * DK + 32 * ks + 8 * lg]);
+        }
     };
 
-    // ---- load: every global read of the chunk, issued together --------------
-    constexpr int NQ = (C * KC + NT - 1) / NT;
-    bf16x8 qreg[NQ];
+    for (; item < nitems; item += gridDim.x) {
+    // The thread index is re-derived opaquely each item, so that the many
+    // per-thread LDS and workspace offsets are recomputed where they are used
+    // instead of being hoisted out of the loop and held in registers.
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const long bh = bh_of(item);
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const long c = chunk_of(item);
+    const long t0 = c * C;
+    const int nvalid = (int)min((long)C, T - t0);
+    const long ch = bh * blk.nbmax + (c - blk.c0);   // slot-local chunk-head
+    auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
+
+    __syncthreads();   // the previous item is done with every LDS tile
+    // ---- stage: the raw inputs into LDS -------------------------------------
+    // Rows past T were loaded from the last valid row; they stage as zero
+    // (k, v, b (.) k, beta) and one (alpha).
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         const int idx = tid + n * NT;
         const int r = idx / KC, pc = idx % KC;
-        bf16x8 kv = zero8(), qv = zero8();
-        if (idx < C * KC && r < nvalid) {
-            kv = *reinterpret_cast<const bf16x8 *>(&k[tok(r) * DK + 8 * pc]);
-            qv = *reinterpret_cast<const bf16x8 *>(&q[tok(r) * DK + 8 * pc]);
-        }
-        qreg[n] = qv;
-        if (idx < C * KC) {
-            *reinterpret_cast<bf16x8 *>(&sK[kx(r, 8 * pc)]) = kv;
-            if constexpr (VT::kGates) {
-                bf16x8 av = zero8();
-                if (r < nvalid) {
-                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
-                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
+        const bf16x8 kv = r < nvalid ? raw.k[n] : zero_bf16x8();
+        *reinterpret_cast<bf16x8 *>(&sK[kx(r, 8 * pc)]) = kv;
+        if constexpr (VT::kGates) {
+            bf16x8 av;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        av[e] = (bf16)(b0[e] * (float)kv[e]);
-                        av[e + 4] = (bf16)(b1[e] * (float)kv[e + 4]);
-                    }
-                }
-                *reinterpret_cast<bf16x8 *>(&sAg[kx(r, 8 * pc)]) = av;
+            for (int e = 0; e < 4; ++e) {
+                av[e] = (bf16)(raw.eb[2 * n][e] * (float)kv[e]);
+                av[e + 4] = (bf16)(raw.eb[2 * n + 1][e] * (float)kv[e + 4]);
             }
+            *reinterpret_cast<bf16x8 *>(&sAg[kx(r, 8 * pc)]) = av;
         }
     }
 #pragma unroll
-    for (int idx = tid; idx < C * VC; idx += NT) {
+    for (int n = 0; n < NV; ++n) {
+        const int idx = tid + n * NT;
         const int r = idx / VC, pc = idx % VC;
-        bf16x8 vv = zero8();
-        if (r < nvalid) {
-            vv = *reinterpret_cast<const bf16x8 *>(&v[tok(r) * DV + 8 * pc]);
-            if constexpr (VT::kGates) {
-                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc]);
-                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc + 4]);
+        bf16x8 vv = r < nvalid ? raw.v[n] : zero_bf16x8();
+        if constexpr (VT::kGates) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vv[e] = (bf16)(w0[e] * (float)vv[e]);
-                    vv[e + 4] = (bf16)(w1[e] * (float)vv[e + 4]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                vv[e] = (bf16)(raw.ww[2 * n][e] * (float)vv[e]);
+                vv[e + 4] = (bf16)(raw.ww[2 * n + 1][e] * (float)vv[e + 4]);
             }
         }
         *reinterpret_cast<bf16x8 *>(&sV[vx(r, 8 * pc)]) = vv;
     }
     if constexpr (VT::kChannelDecay) {
 #pragma unroll
-        for (int idx = tid; idx < C * DK / 4; idx += NT) {
+        for (int n = 0; n < Raw::NA; ++n) {
+            const int idx = tid + n * NT;
             const int r = idx / (DK / 4), i4 = 4 * (idx % (DK / 4));
-            f32x4 a = f32x4{1.f, 1.f, 1.f, 1.f};
-            if (r < nvalid) a = *reinterpret_cast<const f32x4 *>(&p.alpha[tok(r) * DK + i4]);
-            *reinterpret_cast<f32x4 *>(&sG[r][i4]) = a;
+            *reinterpret_cast<f32x4 *>(&sG[r][i4]) = r < nvalid ? raw.al[n] : f32x4{1.f, 1.f, 1.f, 1.f};
         }
     } else if constexpr (VT::kHasDecay) {
-        if (wave == 0) sG[lane][0] = lane < nvalid ? p.alpha[tok(lane)] : 1.f;
+        if (wave == 0) sG[lane][0] = lane < nvalid ? raw.a1 : 1.f;
     } else {
         if (tid < C) sG[tid][0] = 0.f;
     }
     if constexpr (VT::kScalarBeta)
-        if (tid >= NT - C) {
-            const int r = tid - (NT - C);
-            sBeta[r] = r < nvalid ? p.beta[tok(r)] : 0.f;
-        }
-    // q rows of this wave's Gram tiles, for phase 2 (L2 hits: read just above).
-    bf16x8 qf[2][DK / 32];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tl = wave + u * NW;
-        const int rr = 16 * kLowerR[tl < 10 ? tl : 0] + l16;
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks)
-            qf[u][ks] = (tl < 10 && rr < nvalid)
-                            ? *reinterpret_cast<const bf16x8 *>(&q[tok(rr) * DK + 32 * ks + 8 * lg])
-                            : zero8();
-    }
+        if (tid < C) sBeta[tid] = tid < nvalid ? raw.be : 0.f;
+    load_qf(item, l16, lg);
     __syncthreads();
 
     // ---- gates: decay prefix sums; KLA step size ------------------------------
@@ -722,14 +793,17 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 for (int e = 0; e < 8; ++e) {
                     float eg = egr;
                     if constexpr (VT::kChannelDecay) eg = __expf(sG[r][8 * pc + e]);
-                    o[e] = (bf16)((float)qreg[n][e] * eg);
+                    o[e] = (bf16)((float)raw.q[n][e] * eg);
                 }
                 *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
             }
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace
 #pragma unroll
-        for (int idx = tid; idx < DK * (C / 8); idx += NT) {
+        for (int n = 0; n < (DK * (C / 8) + NT - 1) / NT; ++n) {
+            // Unrolled, so that the waits for loads in flight stay exact.
+            const int idx = tid + n * NT;
+            if (idx >= DK * (C / 8)) break;
             const int i = idx % DK, r0 = 8 * (idx / DK);
             const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
             float at[8], kb[8];
@@ -758,7 +832,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         }
         // U^T into LDS
 #pragma unroll
-        for (int idx = tid; idx < DV * (C / 8); idx += NT) {
+        for (int n = 0; n < (DV * (C / 8) + NT - 1) / NT; ++n) {
+            // Unrolled, so that the waits for loads in flight stay exact.
+            const int idx = tid + n * NT;
+            if (idx >= DV * (C / 8)) break;
             const int j = idx % DV, r0 = 8 * (idx / DV);
             float u[8];
 #pragma unroll
@@ -769,6 +846,13 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             }
             store8(&sUt[tx(j, r0)], u);
         }
+    }
+    // Every raw register is consumed: the next item's loads go out now and
+    // arrive during phases 2-4 (the last item reloads itself, from L2, so that
+    // the issue is unconditional and the compiler's waits stay exact).
+    {
+        const long next = item + gridDim.x < nitems ? item + gridDim.x : item;
+        raw.issue(p, chunk_of(next), (int)(bh_of(next) % H), (int)(bh_of(next) / H), tid);
     }
     __syncthreads();
 
@@ -781,7 +865,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     for (int u = 0; u < 2; ++u) {
         const int tl = wave + u * NW;
         if (tl >= 10) break;
-        const int R = kLowerR[tl], S = kLowerS[tl];
+        const int R = lower_r(tl), S = lower_s(tl);
         const int rs = 16 * S + l16;
         const int rr = 16 * R + l16;
         f32x4 accA = zero4(), accP = zero4();
@@ -837,10 +921,11 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
         store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }
-    for (int idx = tid; idx < 6 * 16 * 4; idx += NT) {
+    if (tid < 6 * 16 * 4) {
+        const int idx = tid;
         const int t6 = idx / 64, e = idx % 64;
-        const int r = 16 * kUpperR[t6] + e / 4;
-        const int s2 = 16 * kUpperS[t6] + 4 * (e % 4);
+        const int r = 16 * upper_r(t6) + e / 4;
+        const int s2 = 16 * upper_s(t6) + 4 * (e % 4);
         store_frag4(ws.P + ch * C * C, r, s2, C, zero4());
     }
     __syncthreads();
@@ -860,34 +945,56 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[fx(16 * R + r, 16 * R + cc)] = x[r];
     } else {
-        for (int idx = tid - kWave; idx < 6 * 256; idx += NT - kWave) {
+#pragma unroll
+        for (int n = 0; n < (6 * 256 + NT - kWave - 1) / (NT - kWave); ++n) {
+            const int idx = tid - kWave + n * (NT - kWave);
+            if (idx >= 6 * 256) break;
             const int t6 = idx >> 8, e = idx & 255;
-            sT[fx(16 * kUpperR[t6] + (e >> 4), 16 * kUpperS[t6] + (e & 15))] = 0.f;
+            sT[fx(16 * upper_r(t6) + (e >> 4), 16 * upper_s(t6) + (e & 15))] = 0.f;
         }
     }
     __syncthreads();
-    // Off-diagonal blocks by distance d = R - S:
-    //   T_RS = -T_RR * sum_{J=S}^{R-1} A_RJ T_JS
+    // Off-diagonal blocks by distance d = R - S, one wave per block on fp32
+    // matrix cores (16x16x4, full fp32 products):
+    //   X = sum_{J=S}^{R-1} A_RJ T_JS,   T_RS = -T_RR X.
+    // A lane feeds row l16 / K-element lg of the left factor and K-element lg /
+    // column l16 of the right one, and receives rows 4 lg .. 4 lg + 3 of column
+    // l16; X goes through LDS to become a right-hand operand.
+    using MF = Mma<float>;
+#pragma unroll
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;
-        for (int idx = tid; idx < nb * 256; idx += NT) {
-            const int blk2 = idx >> 8, e = idx & 255;
-            const int R = d + blk2, S = R - d, r = e >> 4, cc = e & 15;
-            float acc = 0.f;
-            for (int J = S; J < R; ++J)
+        const int R = d + wave, S = wave;
+        if (wave < nb) {
+            // All operands of the block are read before the first product.
+            float a[4 * 3], t[4 * 3];
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj)
-                    acc += sAm[fx(16 * R + r, 16 * J + jj)] * sT[fx(16 * J + jj, 16 * S + cc)];
-            sX[blk2][r][cc] = acc;
+            for (int j = 0; j < d; ++j)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int J = S + j;
+                    a[4 * j + s4] = sAm[fx(16 * R + l16, 16 * J + 4 * s4 + lg)];
+                    t[4 * j + s4] = sT[fx(16 * J + 4 * s4 + lg, 16 * S + l16)];
+                }
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int j = 0; j < 4 * d; ++j) acc = MF::mma(a[j], t[j], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sX[wave][4 * lg + i][l16] = acc[i];
         }
         __syncthreads();
-        for (int idx = tid; idx < nb * 256; idx += NT) {
-            const int blk2 = idx >> 8, e = idx & 255;
-            const int R = d + blk2, S = R - d, r = e >> 4, cc = e & 15;
-            float acc = 0.f;
+        if (wave < nb) {
+            float a[4], x[4];
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) acc += sT[fx(16 * R + r, 16 * R + jj)] * sX[blk2][jj][cc];
-            sT[fx(16 * R + r, 16 * S + cc)] = -acc;
+            for (int s4 = 0; s4 < 4; ++s4) {
+                a[s4] = sT[fx(16 * R + l16, 16 * R + 4 * s4 + lg)];
+                x[s4] = sX[wave][4 * s4 + lg][l16];
+            }
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) acc = MF::mma(a[s4], x[s4], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[fx(16 * R + 4 * lg + i, 16 * S + l16)] = -acc[i];
         }
         __syncthreads();
     }
@@ -931,6 +1038,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             store4(ws.Ut + ch * DV * C + ufrag_off(16 * nj + l16, 16 * R + 4 * lg), acc);
         }
     }
+    }   // items
 }
 
 // ============================================================================
@@ -996,7 +1104,7 @@ template <typename TI, int DK> struct OutOps {
 constexpr int kScan2Threads = 512;
 
 template <typename TI, int DK, int DEPTH, int NJ>
-__global__ __launch_bounds__(kScan2Threads) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
+__global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
     using CO = ChainOps<TI, DK, NJ>;
@@ -1192,15 +1300,52 @@ hipError_t aux_stream(AuxStream **out) {
     return hipSuccess;
 }
 
+// Workgroups of the bf16 prep kernel that the device holds at once (resident
+// slots) and its compute units, queried once per device and kernel instance.
+template <int V, int DK, int DV> hipError_t prep_slots(long *slots_out, long *cus_out) {
+    static long slots[kMaxDevices] = {}, ncu[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (slots[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&chunk_prep_bf16_kernel<V, DK, DV>),
+            kPrep2Threads, 0);
+        if (e != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        ncu[dev] = cus > 0 ? cus : 1;
+        slots[dev] = (long)(per_cu > 0 ? per_cu : 1) * ncu[dev];
+    }
+    *slots_out = slots[dev];
+    *cus_out = ncu[dev];
+    return hipSuccess;
+}
+
 template <int V, typename TI, int DK, int DV>
-hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, hipStream_t st) {
-    const dim3 pgrid((unsigned)blk.nc, (unsigned)p.H, (unsigned)p.B);
-    if constexpr (sizeof(TI) == 2)
-        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), pgrid, dim3(kPrep2Threads), 0, st,
-                           p, w, blk);
-    else
+hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool concurrent,
+                       hipStream_t st) {
+    if constexpr (sizeof(TI) == 2) {
+        // Persistent workgroups, each looping over chunk-heads with the next
+        // one's inputs in flight.  Alone, the grid fills every resident slot;
+        // beside a concurrent scan, one workgroup per compute unit, so that a
+        // scan workgroup still fits on every unit.
+        long slots = 0, cus = 0;
+        hipError_t e = prep_slots<V, DK, DV>(&slots, &cus);
+        if (e != hipSuccess) return e;
+        const long items = (long)blk.nc * p.H * p.B;
+        const long want = concurrent ? cus : slots;
+        const long grid = items < want ? items : want;
+        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), dim3((unsigned)grid),
+                           dim3(kPrep2Threads), 0, st, p, w, blk);
+    } else {
+        const dim3 pgrid((unsigned)blk.nc, (unsigned)p.H, (unsigned)p.B);
         hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>), pgrid, dim3(kPrepThreads), 0, st,
                            p, w, blk);
+    }
     return hipGetLastError();
 }
 
@@ -1225,7 +1370,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
         const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out};
-        hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, stream);
+        hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
     }
@@ -1245,7 +1390,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         const Block blk{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier};
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, aux->s)) != hipSuccess) return e;
+        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, true, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
         if ((e = launch_scan<TI, DK, DV>(p, w, blk, stream)) != hipSuccess) return e;
