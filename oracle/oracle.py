@@ -9,9 +9,13 @@ function per variant) with ctypes and runs independent heads (b, h) on a
 thread pool.  Inputs are the exact stored values (bf16 or fp32) upcast to
 float64; results come back as float64 numpy arrays.
 
+``frontend`` holds the optional input transforms (q/k L2 normalisation, gate
+activations from pre-activations) in plain numpy float64.
+
 Parity status: every variant is pinned by the tests in ``tests/test_oracle_*``
 (exact rational brute force on short sequences, the Kaczmarz projection and
-line-search properties, variant reductions, closed forms); none is unpinned.
+line-search properties, variant reductions, closed forms), and the front-end by
+closed forms and library routines; none is unpinned.
 """
 from __future__ import annotations
 
@@ -102,18 +106,67 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
+# Front-end options (input transforms applied before the recurrence).
+QK_L2NORM = 1      # q and k divided by their L2 norm over the key dimension
+RAW_GATES = 2      # gate tensors hold pre-activations
+L2NORM_EPS = 1e-6  # added to the sum of squares before the square root
+
+
+def softplus(x):
+    """log(1 + e^x), evaluated without overflow: max(x, 0) + log1p(e^-|x|)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), evaluated without overflow on either side."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def l2normalize(x):
+    """x / sqrt(sum_i x_i^2 + L2NORM_EPS) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+
+
+def frontend(variant: str, q, k, alpha=None, beta=None, erase_b=None, write_w=None,
+             flags: int = 0, decay_scale: float = 0.0):
+    """The input transforms in float64, in this order, each on its own tensor:
+    with QK_L2NORM, q and k become l2normalize(q), l2normalize(k); with
+    RAW_GATES, alpha becomes exp(-decay_scale * softplus(alpha)) and beta
+    (eta for KLA), erase_b and write_w become sigmoid of themselves.  The
+    recurrence then runs on the results exactly as on stored gates."""
+    q, k = _f64(q), _f64(k)
+    alpha, beta, erase_b, write_w = _f64(alpha), _f64(beta), _f64(erase_b), _f64(write_w)
+    if flags & QK_L2NORM:
+        q, k = l2normalize(q), l2normalize(k)
+    if flags & RAW_GATES:
+        if alpha is not None:
+            alpha = np.exp(-decay_scale * softplus(alpha))
+        beta = None if beta is None else sigmoid(beta)
+        erase_b = None if erase_b is None else sigmoid(erase_b)
+        write_w = None if write_w is None else sigmoid(write_w)
+    return q, k, alpha, beta, erase_b, write_w
+
+
 def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
             write_w=None, eps: float = 0.0, state_in=None, heads=None,
-            threads: int | None = None, lib=None):
+            threads: int | None = None, lib=None, flags: int = 0, decay_scale: float = 0.0):
     """Run the sequential recurrence for ``variant``.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv]; gates as documented in
-    ``gdr_oracle.c``.  ``heads`` optionally restricts the work to a list of
+    ``gdr_oracle.c``.  ``flags`` / ``decay_scale`` select the input transforms
+    of ``frontend``.  ``heads`` optionally restricts the work to a list of
     (b, h) pairs; outputs of other heads are left as NaN.  Returns
     ``(o [B,T,H,dv], state_out [B,H,dk,dv])`` in float64.
     """
     if variant not in _ENTRY:
         raise ValueError(f"unknown variant {variant!r}")
+    if flags:
+        q, k, alpha, beta, erase_b, write_w = frontend(variant, q, k, alpha, beta, erase_b,
+                                                       write_w, flags, decay_scale)
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
