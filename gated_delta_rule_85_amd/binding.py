@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libgdr.so")
 
 VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "gdn2": 3, "kla": 4}
 GDR_F32, GDR_BF16 = 0, 1
+GDR_FLAG_QK_L2NORM, GDR_FLAG_RAW_GATES = 1, 2
 STATUS = {0: "GDR_OK", 1: "GDR_ERR_INVALID_ARGUMENT", 2: "GDR_ERR_UNSUPPORTED",
           3: "GDR_ERR_WORKSPACE", 4: "GDR_ERR_HIP"}
 
@@ -30,10 +31,10 @@ class GdrArgs(ctypes.Structure):
         ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
         ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
-        ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("q", _vp), ("k", _vp), ("v", _vp),
         ("alpha", _vp), ("beta", _vp), ("erase_b", _vp), ("write_w", _vp),
-        ("eps", ctypes.c_float), ("reserved_f", ctypes.c_float),
+        ("eps", ctypes.c_float), ("decay_scale", ctypes.c_float),
         ("state_in", _vp), ("state_out", _vp), ("o", _vp),
     ]
 
@@ -116,8 +117,9 @@ def _ptr(t):
 
 def make_args(variant: str, q, k, v, o, alpha=None, beta=None, erase_b=None,
               write_w=None, eps: float = 0.0, state_in=None, state_out=None,
-              chunk: int = 0) -> GdrArgs:
-    """Fill GdrArgs from contiguous tensors q, k [B,T,H,dk], v, o [B,T,H,dv]."""
+              chunk: int = 0, flags: int = 0, decay_scale: float = 0.0) -> GdrArgs:
+    """Fill GdrArgs from contiguous tensors q, k [B,T,H,dk], v, o [B,T,H,dv].
+    ``flags`` (GDR_FLAG_*) and ``decay_scale`` select the on-load transforms."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("alpha", alpha),
@@ -133,9 +135,9 @@ def make_args(variant: str, q, k, v, o, alpha=None, beta=None, erase_b=None,
         raise ValueError(f"unsupported dtype {q.dtype}")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    return GdrArgs(VARIANTS[variant], dt, B, T, H, dk, dv, chunk, 0,
+    return GdrArgs(VARIANTS[variant], dt, B, T, H, dk, dv, chunk, int(flags),
                    _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                   _ptr(erase_b), _ptr(write_w), float(eps), 0.0,
+                   _ptr(erase_b), _ptr(write_w), float(eps), float(decay_scale),
                    _ptr(state_in), _ptr(state_out), _ptr(o))
 
 
@@ -148,7 +150,8 @@ def _stream_handle(stream):
 
 def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
             write_w=None, eps: float = 0.0, state_in=None, output_state: bool = True,
-            o=None, state_out=None, workspace=None, stream=None):
+            o=None, state_out=None, workspace=None, stream=None, flags: int = 0,
+            decay_scale: float = 0.0):
     """Chunked forward on device tensors.  Returns (o, state_out or None)."""
     import torch
 
@@ -159,7 +162,7 @@ def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
     if output_state and state_out is None:
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
-                  state_in, state_out)
+                  state_in, state_out, flags=flags, decay_scale=decay_scale)
     check(gdr_check_args(a, 0))
     need = gdr_forward_workspace_size(a)
     if workspace is None or workspace.numel() < need:
@@ -184,7 +187,8 @@ def workspace_bytes(variant: str, q, k, v) -> int:
 
 
 def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=None,
-                write_w=None, eps: float = 0.0, o=None, state_out=None, stream=None):
+                write_w=None, eps: float = 0.0, o=None, state_out=None, stream=None,
+                flags: int = 0, decay_scale: float = 0.0):
     """One decode step: q, k [B,1,H,dk], v [B,1,H,dv]; updates ``state`` in
     place unless ``state_out`` is given.  Returns o [B,1,H,dv]."""
     import torch
@@ -194,6 +198,7 @@ def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=Non
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
-                  state, state if state_out is None else state_out)
+                  state, state if state_out is None else state_out, flags=flags,
+                  decay_scale=decay_scale)
     check(gdr_decode_step(a, _stream_handle(stream)))
     return o

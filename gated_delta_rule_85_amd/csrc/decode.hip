@@ -40,6 +40,12 @@ template <typename X, int DK> struct RowVec {
             w[0] = p[lane % (DK / 2)];
         }
     }
+    // Replace every element this lane holds by f(element) (fp32 vectors).
+    template <typename F> __device__ __forceinline__ void map(F f) {
+        static_assert(sizeof(X) == 4, "fp32 row vectors only");
+#pragma unroll
+        for (int j = 0; j < NW; ++j) w[j] = __float_as_uint(f(__uint_as_float(w[j])));
+    }
     // Element r0 + 8 i, for a lane-dependent r0 in [0, 8) and a compile-time i.
     __device__ __forceinline__ float get(int r0, int i) const {
         if constexpr (sizeof(X) == 4) {
@@ -60,7 +66,7 @@ template <typename X, int DK> struct RowVec {
 // reduction over the key rows (r, y, ||k||^2, k . q) is a butterfly over the
 // lanes that share a column group: no LDS, no barrier.  load() only issues
 // loads and keeps raw words, so nothing waits on them until finish().
-template <int V, typename TI, int DK, int CW> struct DecodeTile {
+template <int V, typename TI, int DK, int CW, bool NORM> struct DecodeTile {
     using VT = VariantTraits<V>;
     static constexpr int LPR = CW / 4;          // lanes per row
     static constexpr int RPP = kWave / LPR;     // rows per pass
@@ -100,24 +106,44 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
         const long bh = tile / tph;
         const int col0 = (int)(tile % tph) * CW;
         const int cg = lane % LPR, r0 = lane / LPR;
+        // On-load transforms: gates from pre-activations now; the q/k
+        // normalisation, a per-token scalar each, after the reductions below.
+        const bool rawg = p.flags & kRawGates;
+        const float ds = p.decay_scale;
         f32x4 u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) u[c] = to_f32(vr[c]);
-        if constexpr (VT::kGates) u *= wr;
+        if constexpr (VT::kGates) {
+            if (rawg)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) wr[c] = sigmoid_f(wr[c]);
+            u *= wr;
+        }
+        float bet = beta, sd = sdec;
+        if (rawg) {
+            if constexpr (VT::kScalarBeta) bet = sigmoid_f(beta);
+            if constexpr (VT::kHasDecay && !VT::kChannelDecay) sd = __expf(-ds * softplus_f(sdec));
+        }
+        if (rawg) {
+            // per-row gates: each lane activates the words it holds
+            if constexpr (VT::kChannelDecay) dv_.map([&](float x) { return __expf(-ds * softplus_f(x)); });
+            if constexpr (VT::kGates) av.map([](float x) { return sigmoid_f(x); });
+        }
         f32x4 r = zero4(), y = zero4();
-        float kn = 0.f, kq = 0.f;
+        float kn = 0.f, kq = 0.f, qn = 0.f;
         float kr[PASSES];
 #pragma unroll
         for (int i = 0; i < PASSES; ++i) {
             kr[i] = kv.get(r0, i);
             const float qq = qv.get(r0, i);
             if constexpr (VT::kChannelDecay) s[i] *= dv_.get(r0, i);
-            else if constexpr (VT::kHasDecay) s[i] *= sdec;
+            else if constexpr (VT::kHasDecay) s[i] *= sd;
             const float a = VT::kGates ? av.get(r0, i) * kr[i] : kr[i];
             r += a * s[i];
             y += qq * s[i];
             kn += kr[i] * kr[i];
             kq += kr[i] * qq;
+            if constexpr (NORM) qn += qq * qq;
         }
 #pragma unroll
         for (int off = LPR; off < kWave; off <<= 1) {
@@ -128,13 +154,25 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
             }
             kn += __shfl_xor(kn, off, kWave);
             kq += __shfl_xor(kq, off, kWave);
+            if constexpr (NORM) qn += __shfl_xor(qn, off, kWave);
+        }
+        // k^ = rk k and q^ = rq q: every use of k and q above is linear in
+        // each, so the scalars apply to the sums.
+        float rk = 1.f;
+        if constexpr (NORM) {
+            rk = rsqrtf(kn + kL2NormEps);
+            const float rq = rsqrtf(qn + kL2NormEps);
+            r *= rk;
+            y *= rq;
+            kq *= rk * rq;
+            kn *= rk * rk;
         }
         f32x4 dl;
         if constexpr (VT::kGates) {
             dl = u - r;
         } else {
-            float bt = beta;
-            if constexpr (VT::kKaczmarz) bt = beta / (kn + p.eps);
+            float bt = bet;
+            if constexpr (VT::kKaczmarz) bt = bet / (kn + p.eps);
             dl = bt * (u - r);
         }
         if (r0 == 0) {
@@ -146,14 +184,15 @@ template <int V, typename TI, int DK, int CW> struct DecodeTile {
         float *Sout = p.state_out + bh * DK * (long)dv + col0 + 4 * cg;
 #pragma unroll
         for (int i = 0; i < PASSES; ++i)
-            *reinterpret_cast<f32x4 *>(Sout + (long)(r0 + i * RPP) * dv) = s[i] + kr[i] * dl;
+            *reinterpret_cast<f32x4 *>(Sout + (long)(r0 + i * RPP) * dv) = s[i] + (kr[i] * rk) * dl;
     }
 };
 
-template <int V, typename TI, int DK, int CW, int WAVES>
+// NORM: q and k are L2-normalised on load (the kQkL2Norm flag).
+template <int V, typename TI, int DK, int CW, int WAVES, bool NORM>
 __global__ __launch_bounds__(WAVES * 64)
 void decode_wave_kernel(Problem p) {
-    using Tile = DecodeTile<V, TI, DK, CW>;
+    using Tile = DecodeTile<V, TI, DK, CW, NORM>;
     const long tile = (long)blockIdx.x * WAVES + threadIdx.x / kWave;
     if (tile >= p.B * p.H * (p.dv / CW)) return;
     Tile t;
@@ -167,8 +206,12 @@ hipError_t launch_dk(const Problem &p, hipStream_t stream) {
     constexpr int CW = 32, WAVES = 4;
     const long tiles = p.B * p.H * (p.dv / CW);
     dim3 grid((unsigned)((tiles + WAVES - 1) / WAVES));
-    hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES>), grid, dim3(WAVES * kWave), 0,
-                       stream, p);
+    if (p.flags & kQkL2Norm)
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, true>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, false>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
     return hipGetLastError();
 }
 

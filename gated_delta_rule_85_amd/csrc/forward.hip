@@ -257,8 +257,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     __shared__ __attribute__((aligned(16))) float sAm[C][C + PF]; // A (strictly lower)
     __shared__ __attribute__((aligned(16))) float sT[C][C + PF];  // T = (I + A)^{-1}
     __shared__ float sX[3][16][17];
+    __shared__ float sRk[C], sRq[C];   // 1/|k_r|, 1/|q_r| with the q/k normalisation, else 1
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool l2 = p.flags & kQkL2Norm, rawg = p.flags & kRawGates;
+    const float ds = p.decay_scale;
     const int l16 = lane & 15, lg = lane >> 4;
     const long c = blk.c0 + blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
@@ -272,18 +275,40 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     const TI *v = static_cast<const TI *>(p.v);
     auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
 
-    // ---- phase 0: decay prefix sums and per-token write strength ------------
+    // ---- phase 0: row norms, decay prefix sums, per-token write strength -----
+    // One wave per row: |k_r|^2 and |q_r|^2 over the key channels.
+    for (int r = wave; r < C; r += kPrepThreads / kWave) {
+        float sk = 0.f, sq = 0.f;
+        if (r < nvalid)
+            for (int i = lane; i < DK; i += kWave) {
+                const float x = to_f32(k[tok(r) * DK + i]), y = to_f32(q[tok(r) * DK + i]);
+                sk += x * x;
+                sq += y * y;
+            }
+        sk = wave_sum(sk);
+        sq = wave_sum(sq);
+        if (lane == 0) {
+            const float rk = l2 ? rsqrtf(sk + kL2NormEps) : 1.f;
+            sRk[r] = rk;
+            sRq[r] = l2 ? rsqrtf(sq + kL2NormEps) : 1.f;
+            // beta_r = eta_r / (|k_r|^2 + eps) for KLA, |k_r| of the key in use.
+            if constexpr (VT::kKaczmarz) {
+                const float eta = r < nvalid ? p.beta[tok(r)] : 0.f;
+                sBeta[r] = r < nvalid ? (rawg ? sigmoid_f(eta) : eta) / (sk * rk * rk + p.eps) : 0.f;
+            }
+        }
+    }
     if constexpr (VT::kChannelDecay) {
         if (tid < DK) {
             float g = 0.f;
             for (int r = 0; r < C; ++r) {
-                if (r < nvalid) g += logf(p.alpha[tok(r) * DK + tid]);
+                if (r < nvalid) g += log_decay(p.alpha[tok(r) * DK + tid], rawg, ds);
                 sG[r][tid] = g;
             }
         }
     } else if constexpr (VT::kHasDecay) {
         if (wave == 0) {
-            float g = lane < nvalid ? logf(p.alpha[tok(lane)]) : 0.f;
+            float g = lane < nvalid ? log_decay(p.alpha[tok(lane)], rawg, ds) : 0.f;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 float y = __shfl_up(g, off, kWave);
@@ -294,21 +319,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     } else {
         if (tid < C) sG[tid][0] = 0.f;
     }
-    if constexpr (VT::kScalarBeta) {
-        if constexpr (VT::kKaczmarz) {
-            // beta_r = eta_r / (||k_r||^2 + eps), from the stored keys.
-            for (int r = wave; r < C; r += kPrepThreads / kWave) {
-                float s = 0.f;
-                if (r < nvalid)
-                    for (int i = lane; i < DK; i += kWave) {
-                        float x = to_f32(k[tok(r) * DK + i]);
-                        s += x * x;
-                    }
-                s = wave_sum(s);
-                if (lane == 0) sBeta[r] = r < nvalid ? p.beta[tok(r)] / (s + p.eps) : 0.f;
-            }
-        } else {
-            if (tid < C) sBeta[tid] = tid < nvalid ? p.beta[tok(tid)] : 0.f;
+    if constexpr (VT::kScalarBeta && !VT::kKaczmarz) {
+        if (tid < C) {
+            const float bt = tid < nvalid ? p.beta[tok(tid)] : 0.f;
+            sBeta[tid] = tid < nvalid ? (rawg ? sigmoid_f(bt) : bt) : 0.f;
         }
     }
     __syncthreads();
@@ -328,10 +342,14 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
                 const int r = r0 + e;
                 float kk = 0.f, qq = 0.f, a = 0.f;
                 if (r < nvalid) {
-                    kk = to_f32(k[tok(r) * DK + i]);
-                    qq = to_f32(q[tok(r) * DK + i]);
-                    if constexpr (VT::kGates) a = p.erase_b[tok(r) * DK + i] * kk;
-                    else a = sBeta[r] * kk;
+                    kk = to_f32(k[tok(r) * DK + i]) * sRk[r];
+                    qq = to_f32(q[tok(r) * DK + i]) * sRq[r];
+                    if constexpr (VT::kGates) {
+                        const float bg = p.erase_b[tok(r) * DK + i];
+                        a = (rawg ? sigmoid_f(bg) : bg) * kk;
+                    } else {
+                        a = sBeta[r] * kk;
+                    }
                 }
                 float eg = 1.f, egc = 1.f;
                 if constexpr (VT::kHasDecay) {
@@ -355,8 +373,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
                 float uu = 0.f;
                 if (r < nvalid) {
                     const float vv = to_f32(v[tok(r) * DV + j]);
-                    if constexpr (VT::kGates) uu = p.write_w[tok(r) * DV + j] * vv;
-                    else uu = sBeta[r] * vv;
+                    if constexpr (VT::kGates) {
+                        const float wg = p.write_w[tok(r) * DV + j];
+                        uu = (rawg ? sigmoid_f(wg) : wg) * vv;
+                    } else {
+                        uu = sBeta[r] * vv;
+                    }
                 }
                 u[e] = uu;
             }
@@ -392,13 +414,20 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
 #pragma unroll
                 for (int e = 0; e < NL; ++e) ar[e] = qr[e] = 0.f;
             }
+            const float rks = sRk[rs], rkr = sRk[rr], rqr = sRq[rr];
 #pragma unroll
             for (int e = 0; e < NL; ++e) {
+                kr[e] *= rks;
+                ar[e] *= rkr;
+                qr[e] *= rqr;
                 float a;
-                if constexpr (VT::kGates)
-                    a = rr < nvalid ? p.erase_b[tok(rr) * DK + kb + e] * ar[e] : 0.f;
-                else
+                if constexpr (VT::kGates) {
+                    float bg = rr < nvalid ? p.erase_b[tok(rr) * DK + kb + e] : 0.f;
+                    if (rawg) bg = sigmoid_f(bg);
+                    a = rr < nvalid ? bg * ar[e] : 0.f;
+                } else {
                     a = br * ar[e];
+                }
                 if constexpr (VT::kChannelDecay) {
                     const float gref = sG[C / 2 - 1][kb + e];
                     const float fl = __expf(sG[rr][kb + e] - gref);
@@ -625,6 +654,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ float sBeta[C];
     constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
     __shared__ float sEg[kRowDecay ? C : 1], sEgc[kRowDecay ? C : 1];   // e^{g_r}, e^{g_C - g_r}
+    __shared__ float sRq[C];   // 1 / |q_r| with the q/k normalisation
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[3][16][17];
@@ -644,25 +674,27 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // Work items are the block's chunk-heads, chunk fastest; a workgroup takes
     // every gridDim.x-th item and loads the next one's inputs while it
     // computes the current one.
-    const long nitems = (long)blk.nc * p.H * p.B;
-    long item = blockIdx.x;
+    // Item indices fit in 32 bits (the host keeps B * H * 64 below 2^31), so
+    // their split into (chunk, head, batch row) is 32-bit scalar arithmetic.
+    const unsigned nc = (unsigned)blk.nc, nitems = nc * (unsigned)(p.H * p.B);
+    unsigned item = blockIdx.x;
     if (item >= nitems) return;
-    auto chunk_of = [&](long it) { return blk.c0 + it % blk.nc; };
-    auto bh_of = [&](long it) { return it / blk.nc; };
+    auto chunk_of = [&](unsigned it) { return blk.c0 + (long)(it % nc); };
+    auto head_of = [&](unsigned it) { return (int)((it / nc) % (unsigned)H); };
+    auto row_of = [&](unsigned it) { return (int)((it / nc) / (unsigned)H); };
     Raw raw;
-    raw.issue(p, chunk_of(item), (int)(bh_of(item) % H), (int)(bh_of(item) / H), (int)threadIdx.x);
+    raw.issue(p, chunk_of(item), head_of(item), row_of(item), (int)threadIdx.x);
     // q rows of this wave's Gram tiles, for phase 2 (L2 hits); rows past T
     // read the last valid row, whose products only reach rows never stored.
     bf16x8 qf[2][DK / 32];
-    auto load_qf = [&](long it, int l16, int lg) {
-        const long bh = bh_of(it);
-        const long t0 = chunk_of(it) * C;
+    auto load_qf = [&](long c, int h, int b, int l16, int lg) {
+        const long t0 = c * C;
         const int last = (int)min((long)C, T - t0) - 1;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tl = wave + u * NW;
             const int rr = min(16 * lower_r(tl < 10 ? tl : 0) + l16, last);
-            const long row = ((bh / H) * T + t0 + rr) * H + bh % H;
+            const long row = ((long)b * T + t0 + rr) * H + h;
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
                 qf[u][ks] = *reinterpret_cast<const bf16x8 *>(&q[row * DK + 32 * ks + 8 * lg]);
@@ -677,30 +709,59 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int l16 = lane & 15, lg = lane >> 4;
-    const long bh = bh_of(item);
-    const int h = (int)(bh % H), b = (int)(bh / H);
+    const int h = head_of(item), b = row_of(item);
     const long c = chunk_of(item);
     const long t0 = c * C;
     const int nvalid = (int)min((long)C, T - t0);
-    const long ch = bh * blk.nbmax + (c - blk.c0);   // slot-local chunk-head
+    const long ch = ((long)b * H + h) * blk.nbmax + (c - blk.c0);   // slot-local chunk-head
     auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
 
     __syncthreads();   // the previous item is done with every LDS tile
     // ---- stage: the raw inputs into LDS -------------------------------------
     // Rows past T were loaded from the last valid row; they stage as zero
-    // (k, v, b (.) k, beta) and one (alpha).
+    // (k, v, b (.) k, beta) and as no decay.  The on-load transforms happen
+    // here: q and k rows are normalised in registers (a row's chunks sit in
+    // KC consecutive lanes), gates are activated, and the decay is staged as
+    // its log.
+    const bool l2 = p.flags & kQkL2Norm, rawg = p.flags & kRawGates;
+    const float ds = p.decay_scale;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         const int idx = tid + n * NT;
         const int r = idx / KC, pc = idx % KC;
-        const bf16x8 kv = r < nvalid ? raw.k[n] : zero_bf16x8();
+        bf16x8 kv = r < nvalid ? raw.k[n] : zero_bf16x8();
+        if (l2) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sk += (float)kv[e] * (float)kv[e];
+                sq += (float)raw.q[n][e] * (float)raw.q[n][e];
+            }
+#pragma unroll
+            for (int off = 1; off < KC; off <<= 1) {
+                sk += __shfl_xor(sk, off, kWave);
+                sq += __shfl_xor(sq, off, kWave);
+            }
+            const float rk = rsqrtf(sk + kL2NormEps), rq = rsqrtf(sq + kL2NormEps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kv[e] = (bf16)((float)kv[e] * rk);
+                raw.q[n][e] = (bf16)((float)raw.q[n][e] * rq);
+            }
+            if (pc == 0) sRq[r] = rq;
+        }
         *reinterpret_cast<bf16x8 *>(&sK[kx(r, 8 * pc)]) = kv;
         if constexpr (VT::kGates) {
             bf16x8 av;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                av[e] = (bf16)(raw.eb[2 * n][e] * (float)kv[e]);
-                av[e + 4] = (bf16)(raw.eb[2 * n + 1][e] * (float)kv[e + 4]);
+                float b0 = raw.eb[2 * n][e], b1 = raw.eb[2 * n + 1][e];
+                if (rawg) {
+                    b0 = sigmoid_f(b0);
+                    b1 = sigmoid_f(b1);
+                }
+                av[e] = (bf16)(b0 * (float)kv[e]);
+                av[e + 4] = (bf16)(b1 * (float)kv[e + 4]);
             }
             *reinterpret_cast<bf16x8 *>(&sAg[kx(r, 8 * pc)]) = av;
         }
@@ -713,8 +774,13 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         if constexpr (VT::kGates) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vv[e] = (bf16)(raw.ww[2 * n][e] * (float)vv[e]);
-                vv[e + 4] = (bf16)(raw.ww[2 * n + 1][e] * (float)vv[e + 4]);
+                float w0 = raw.ww[2 * n][e], w1 = raw.ww[2 * n + 1][e];
+                if (rawg) {
+                    w0 = sigmoid_f(w0);
+                    w1 = sigmoid_f(w1);
+                }
+                vv[e] = (bf16)(w0 * (float)vv[e]);
+                vv[e + 4] = (bf16)(w1 * (float)vv[e + 4]);
             }
         }
         *reinterpret_cast<bf16x8 *>(&sV[vx(r, 8 * pc)]) = vv;
@@ -724,30 +790,33 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         for (int n = 0; n < Raw::NA; ++n) {
             const int idx = tid + n * NT;
             const int r = idx / (DK / 4), i4 = 4 * (idx % (DK / 4));
-            *reinterpret_cast<f32x4 *>(&sG[r][i4]) = r < nvalid ? raw.al[n] : f32x4{1.f, 1.f, 1.f, 1.f};
+            f32x4 lg4 = zero4();
+            if (r < nvalid)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lg4[e] = log_decay(raw.al[n][e], rawg, ds);
+            *reinterpret_cast<f32x4 *>(&sG[r][i4]) = lg4;
         }
     } else if constexpr (VT::kHasDecay) {
-        if (wave == 0) sG[lane][0] = lane < nvalid ? raw.a1 : 1.f;
+        if (wave == 0) sG[lane][0] = lane < nvalid ? log_decay(raw.a1, rawg, ds) : 0.f;
     } else {
         if (tid < C) sG[tid][0] = 0.f;
     }
     if constexpr (VT::kScalarBeta)
-        if (tid < C) sBeta[tid] = tid < nvalid ? raw.be : 0.f;
-    load_qf(item, l16, lg);
+        if (tid < C) sBeta[tid] = tid < nvalid ? (rawg ? sigmoid_f(raw.be) : raw.be) : 0.f;
     __syncthreads();
 
-    // ---- gates: decay prefix sums; KLA step size ------------------------------
+    // ---- gates: decay prefix sums (of the staged logs); KLA step size --------
     if constexpr (VT::kChannelDecay) {
         if (tid < DK) {
             float g = 0.f;
             for (int r = 0; r < C; ++r) {
-                g += logf(sG[r][tid]);
+                g += sG[r][tid];
                 sG[r][tid] = g;
             }
         }
     } else if constexpr (VT::kHasDecay) {
         if (wave == 0) {
-            float g = logf(sG[lane][0]);
+            float g = sG[lane][0];
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const float y = __shfl_up(g, off, kWave);
@@ -779,6 +848,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __syncthreads();
 
     // ---- phase 1: element-wise factors ------------------------------------
+    load_qf(c, h, b, l16, lg);   // for phase 2
     {
         // q (.) e^{g}, from registers
 #pragma unroll
@@ -851,8 +921,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // arrive during phases 2-4 (the last item reloads itself, from L2, so that
     // the issue is unconditional and the compiler's waits stay exact).
     {
-        const long next = item + gridDim.x < nitems ? item + gridDim.x : item;
-        raw.issue(p, chunk_of(next), (int)(bh_of(next) % H), (int)(bh_of(next) / H), tid);
+        const unsigned next = item + gridDim.x < nitems ? item + gridDim.x : item;
+        raw.issue(p, chunk_of(next), head_of(next), row_of(next), tid);
     }
     __syncthreads();
 
@@ -918,6 +988,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             Av[m] = s2 < r ? accA[m] * fa : 0.f;
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
+        if (l2) Pv *= sRq[r];   // P used the q rows as stored
         *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
         store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }

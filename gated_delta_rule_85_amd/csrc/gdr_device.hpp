@@ -24,6 +24,20 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Gate activations of pre-activations (kRawGates).  softplus(x) = log(1 + e^x)
+// evaluated as max(x, 0) + log1p(e^-|x|), without overflow; sigmoid(x) =
+// 1 / (1 + e^-x), which saturates cleanly at 0 and 1.
+__device__ __forceinline__ float softplus_f(float x) {
+    return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+// log of the decay gate: log(alpha) for a stored alpha, -s softplus(x) for a
+// pre-activation x (computed in the log domain, so strong decay cannot
+// underflow to a zero whose log is -inf).
+__device__ __forceinline__ float log_decay(float x, bool raw, float s) {
+    return raw ? -s * softplus_f(x) : logf(x);
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -28,8 +28,16 @@ gdr_status check(const gdr_args *a, int for_decode) {
         return fail(GDR_ERR_INVALID_ARGUMENT, "unknown variant %d", a->variant);
     if (a->dtype != GDR_F32 && a->dtype != GDR_BF16)
         return fail(GDR_ERR_INVALID_ARGUMENT, "unknown dtype %d", a->dtype);
-    if (a->reserved != 0 || a->reserved_f != 0.f)
-        return fail(GDR_ERR_INVALID_ARGUMENT, "reserved fields must be zero");
+    if (a->flags & ~(GDR_FLAG_QK_L2NORM | GDR_FLAG_RAW_GATES))
+        return fail(GDR_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", (unsigned)a->flags);
+    if ((a->flags & GDR_FLAG_RAW_GATES) && a->variant != GDR_DELTANET) {
+        if (!(a->decay_scale > 0.f && a->decay_scale <= 3.402823466e+38f))
+            return fail(GDR_ERR_INVALID_ARGUMENT,
+                        "decay_scale must be finite and > 0 with GDR_FLAG_RAW_GATES");
+    } else if (a->decay_scale != 0.f) {
+        return fail(GDR_ERR_INVALID_ARGUMENT,
+                    "decay_scale is only used with GDR_FLAG_RAW_GATES and a decaying variant");
+    }
     if (a->B < 1 || a->T < 1 || a->H < 1)
         return fail(GDR_ERR_INVALID_ARGUMENT, "B, T, H must be >= 1 (got %lld, %lld, %lld)",
                     (long long)a->B, (long long)a->T, (long long)a->H);
@@ -38,10 +46,10 @@ gdr_status check(const gdr_args *a, int for_decode) {
     if ((a->dk != 64 && a->dk != 128) || (a->dv != 64 && a->dv != 128))
         return fail(GDR_ERR_UNSUPPORTED, "dk and dv must each be 64 or 128 (got %lld, %lld)",
                     (long long)a->dk, (long long)a->dv);
-    if (a->B > 65535 || a->H > 65535 || a->B * a->H > (int64_t(1) << 26) ||
+    if (a->B > 65535 || a->H > 65535 || a->B * a->H > (int64_t(1) << 24) ||
         a->T > (int64_t(1) << 31))
         return fail(GDR_ERR_UNSUPPORTED, "B, H or T beyond the supported range "
-                    "(B, H <= 65535, B*H <= 2^26, T <= 2^31)");
+                    "(B, H <= 65535, B*H <= 2^24, T <= 2^31)");
     if (for_decode) {
         if (a->T != 1) return fail(GDR_ERR_INVALID_ARGUMENT, "decode needs T == 1 (got %lld)",
                                    (long long)a->T);
@@ -92,6 +100,8 @@ gdr::Problem to_problem(const gdr_args *a) {
     p.q = a->q; p.k = a->k; p.v = a->v;
     p.alpha = a->alpha; p.beta = a->beta; p.erase_b = a->erase_b; p.write_w = a->write_w;
     p.eps = a->eps;
+    p.flags = a->flags;
+    p.decay_scale = a->decay_scale;
     p.state_in = a->state_in; p.state_out = a->state_out;
     p.o = a->o;
     return p;

@@ -19,6 +19,10 @@ template <int V> struct VariantTraits {
     static constexpr bool kGates = V == kGDN2;          // erase b [dk], write w [dv]
 };
 
+// Input transforms applied on load (the values of the C ABI's gdr_flag).
+constexpr int kQkL2Norm = 1, kRawGates = 2;
+constexpr float kL2NormEps = 1e-6f;   // added to sum_i x_i^2 before the square root
+
 // Everything a kernel needs about one call; pointers are device memory.
 struct Problem {
     int variant;
@@ -28,6 +32,8 @@ struct Problem {
     const void *q, *k, *v;
     const float *alpha, *beta, *erase_b, *write_w;
     float eps;
+    int flags;           // kQkL2Norm | kRawGates
+    float decay_scale;   // s in exp(-s softplus(alpha)) with kRawGates
     const float *state_in;
     float *state_out;
     void *o;

@@ -147,6 +147,33 @@ def make_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0,
     return out
 
 
+def make_raw_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0, state_scale=0.1):
+    """Draw pre-activation inputs for the on-load transforms: q, k, v ~ N(0,1)
+    (q and k not normalised), and every gate tensor ~ N(0,1) as a
+    pre-activation (alpha per (b,t,h) or per key channel by variant).  Same
+    dict layout as ``make_inputs``; the state_in is N(0,1) * state_scale."""
+    if variant not in VARIANTS:
+        raise ValueError(variant)
+    rng = np.random.default_rng(seed)
+    out = dict(q=_store(_normal(rng, (B, T, H, dk)), dtype),
+               k=_store(_normal(rng, (B, T, H, dk)), dtype),
+               v=_store(_normal(rng, (B, T, H, dv)), dtype),
+               alpha=None, beta=None, erase_b=None, write_w=None,
+               eps=1e-6 if variant == "kla" else 0.0, state_in=None)
+    if variant in ("gated_deltanet", "kla"):
+        out["alpha"] = torch.from_numpy(_normal(rng, (B, T, H)))
+    elif variant in ("kda", "gdn2"):
+        out["alpha"] = torch.from_numpy(_normal(rng, (B, T, H, dk)))
+    if variant != "gdn2":
+        out["beta"] = torch.from_numpy(_normal(rng, (B, T, H)))
+    else:
+        out["erase_b"] = torch.from_numpy(_normal(rng, (B, T, H, dk)))
+        out["write_w"] = torch.from_numpy(_normal(rng, (B, T, H, dv)))
+    if state_scale:
+        out["state_in"] = torch.from_numpy((_normal(rng, (B, H, dk, dv)) * state_scale))
+    return out
+
+
 def make_workload(wl: Workload, T=None, B=None, H=None):
     """Inputs of a named workload, optionally cut to a shorter sequence or
     fewer batch rows / heads (the draw keeps the workload's seed)."""

@@ -101,20 +101,38 @@ typedef enum {
     GDR_BF16 = 1 /* q, k, v, o in bfloat16; products on bf16 matrix cores, fp32 accumulation */
 } gdr_dtype;
 
+/* Input transforms the kernels apply as they load the inputs (gdr_args.flags),
+ * so that a caller holding raw projections needs no separate pass over them.
+ * The recurrence then runs on the transformed values exactly as on stored ones;
+ * stored bf16 inputs are transformed in fp32 from their stored values.  ("Kaczmarz
+ * Linear Attention", ablations: key normalisation and the gating are what keep
+ * the delta rule stable; the transforms below are the usual parameterisation of
+ * the gates and keys of this family.) */
+typedef enum {
+    /* q <- q / sqrt(sum_i q_i^2 + 1e-6) and the same for k, over the dk
+     * channels of each (b, t, h). */
+    GDR_FLAG_QK_L2NORM = 1,
+    /* alpha <- exp(-decay_scale * softplus(alpha)), softplus(x) = log(1 + e^x),
+     * elementwise (scalar or per channel); beta (eta for KLA), erase_b and
+     * write_w <- sigmoid(x) = 1 / (1 + e^-x). */
+    GDR_FLAG_RAW_GATES = 2
+} gdr_flag;
+
 typedef struct gdr_args {
     int32_t variant;   /* gdr_variant */
     int32_t dtype;     /* gdr_dtype */
     int64_t B, T, H;   /* batch rows, tokens, heads; all >= 1 */
     int64_t dk, dv;    /* key and value head sizes: 64 or 128 each */
     int32_t chunk;     /* chunk length of the prefill; 0 = default (64); decode ignores it */
-    int32_t reserved;  /* must be 0 */
+    int32_t flags;     /* bitwise OR of gdr_flag; 0 = inputs used as stored */
     const void *q, *k, *v;
     const float *alpha;
     const float *beta;
     const float *erase_b;
     const float *write_w;
     float eps;         /* KLA stabiliser added to ||k||^2; ignored otherwise */
-    float reserved_f;  /* must be 0 */
+    float decay_scale; /* with GDR_FLAG_RAW_GATES and a decaying variant: the scale s
+                          of exp(-s * softplus(alpha)), finite and > 0; else 0 */
     const float *state_in; /* NULL = zero initial state */
     float *state_out;      /* NULL = final state not written; may equal state_in */
     void *o;               /* required */

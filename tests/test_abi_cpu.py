@@ -69,7 +69,9 @@ def test_valid_arguments_pass(L, variant):
     (dict(H=-1), 1), (dict(dk=96), 2), (dict(dv=32), 2), (dict(chunk=32), 2),
     (dict(q=None), 1), (dict(o=None), 1), (dict(alpha=None), 1), (dict(beta=None), 1),
     (dict(erase_b=0xa000), 1), (dict(q=0x1004), 1), (dict(state_in=0x100c), 1),
-    (dict(o=0x1000), 1), (dict(reserved=1), 1), (dict(reserved_f=1.0), 1),
+    (dict(o=0x1000), 1), (dict(flags=4), 1), (dict(flags=-1), 1), (dict(decay_scale=1.0), 1),
+    (dict(flags=2, decay_scale=0.0), 1), (dict(flags=2, decay_scale=-1.0), 1),
+    (dict(flags=2, decay_scale=float("inf")), 1), (dict(flags=2, decay_scale=float("nan")), 1),
 ])
 def test_invalid_arguments_rejected(L, over, status):
     a = _args(**over)
@@ -77,6 +79,23 @@ def test_invalid_arguments_rejected(L, over, status):
     assert binding.gdr_last_error_detail() != ""
     # The entry point rejects the same call before touching the GPU.
     assert binding.gdr_forward_chunked(a, 0x10000, 1 << 30, 0) == status
+
+
+@pytest.mark.parametrize("variant", list(binding.VARIANTS))
+def test_input_transform_flags(L, variant):
+    """q/k normalisation needs nothing else; activated gates need a positive,
+    finite decay scale exactly when the variant decays."""
+    assert binding.gdr_check_args(_args(variant, flags=binding.GDR_FLAG_QK_L2NORM), 0) == 0
+    raw = binding.GDR_FLAG_RAW_GATES | binding.GDR_FLAG_QK_L2NORM
+    if variant == "deltanet":
+        assert binding.gdr_check_args(_args(variant, flags=raw), 0) == 0
+        assert binding.gdr_check_args(_args(variant, flags=raw, decay_scale=0.5), 0) == 1
+    else:
+        assert binding.gdr_check_args(_args(variant, flags=raw, decay_scale=0.5), 0) == 0
+        assert binding.gdr_check_args(_args(variant, flags=raw), 0) == 1
+    a = _args(variant, flags=raw, decay_scale=0.0 if variant == "deltanet" else 0.5, T=1,
+              state_in=0xa000)
+    assert binding.gdr_check_args(a, 1) == 0
 
 
 def test_variant_specific_pointers(L):
