@@ -121,7 +121,8 @@ typedef enum {
 typedef struct gdr_args {
     int32_t variant;   /* gdr_variant */
     int32_t dtype;     /* gdr_dtype */
-    int64_t B, T, H;   /* batch rows, tokens, heads; all >= 1 */
+    int64_t B, T, H;   /* batch rows, tokens, heads; all >= 1; B, H <= 65535, B * H <= 2^24
+                          and T <= 2^31, else GDR_ERR_UNSUPPORTED */
     int64_t dk, dv;    /* key and value head sizes: 64 or 128 each */
     int32_t chunk;     /* chunk length of the prefill; 0 = default (64); decode ignores it */
     int32_t flags;     /* bitwise OR of gdr_flag; 0 = inputs used as stored */

@@ -67,6 +67,7 @@ def test_valid_arguments_pass(L, variant):
 @pytest.mark.parametrize("over,status", [
     (dict(variant=7), 1), (dict(dtype=5), 1), (dict(B=0), 1), (dict(T=0), 1),
     (dict(H=-1), 1), (dict(dk=96), 2), (dict(dv=32), 2), (dict(chunk=32), 2),
+    (dict(B=65536), 2), (dict(B=4097, H=4096), 2), (dict(T=(1 << 31) + 1), 2),
     (dict(q=None), 1), (dict(o=None), 1), (dict(alpha=None), 1), (dict(beta=None), 1),
     (dict(erase_b=0xa000), 1), (dict(q=0x1004), 1), (dict(state_in=0x100c), 1),
     (dict(o=0x1000), 1), (dict(flags=4), 1), (dict(flags=-1), 1), (dict(decay_scale=1.0), 1),
