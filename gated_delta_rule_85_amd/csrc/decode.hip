@@ -66,7 +66,8 @@ template <typename X, int DK> struct RowVec {
 // reduction over the key rows (r, y, ||k||^2, k . q) is a butterfly over the
 // lanes that share a column group: no LDS, no barrier.  load() only issues
 // loads and keeps raw words, so nothing waits on them until finish().
-template <int V, typename TI, int DK, int CW, bool NORM> struct DecodeTile {
+template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
+    static constexpr bool NORM = FL & kQkL2Norm, RAWG = FL & kRawGates;
     using VT = VariantTraits<V>;
     static constexpr int LPR = CW / 4;          // lanes per row
     static constexpr int RPP = kWave / LPR;     // rows per pass
@@ -108,23 +109,23 @@ template <int V, typename TI, int DK, int CW, bool NORM> struct DecodeTile {
         const int cg = lane % LPR, r0 = lane / LPR;
         // On-load transforms: gates from pre-activations now; the q/k
         // normalisation, a per-token scalar each, after the reductions below.
-        const bool rawg = p.flags & kRawGates;
+        constexpr bool rawg = RAWG;
         const float ds = p.decay_scale;
         f32x4 u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) u[c] = to_f32(vr[c]);
         if constexpr (VT::kGates) {
-            if (rawg)
+            if constexpr (rawg)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) wr[c] = sigmoid_f(wr[c]);
             u *= wr;
         }
         float bet = beta, sd = sdec;
-        if (rawg) {
+        if constexpr (rawg) {
             if constexpr (VT::kScalarBeta) bet = sigmoid_f(beta);
             if constexpr (VT::kHasDecay && !VT::kChannelDecay) sd = __expf(-ds * softplus_f(sdec));
         }
-        if (rawg) {
+        if constexpr (rawg) {
             // per-row gates: each lane activates the words it holds
             if constexpr (VT::kChannelDecay) dv_.map([&](float x) { return __expf(-ds * softplus_f(x)); });
             if constexpr (VT::kGates) av.map([](float x) { return sigmoid_f(x); });
@@ -188,11 +189,11 @@ template <int V, typename TI, int DK, int CW, bool NORM> struct DecodeTile {
     }
 };
 
-// NORM: q and k are L2-normalised on load (the kQkL2Norm flag).
-template <int V, typename TI, int DK, int CW, int WAVES, bool NORM>
+// FL: the on-load transforms (kQkL2Norm | kRawGates), one instance each.
+template <int V, typename TI, int DK, int CW, int WAVES, int FL>
 __global__ __launch_bounds__(WAVES * 64)
 void decode_wave_kernel(Problem p) {
-    using Tile = DecodeTile<V, TI, DK, CW, NORM>;
+    using Tile = DecodeTile<V, TI, DK, CW, FL>;
     const long tile = (long)blockIdx.x * WAVES + threadIdx.x / kWave;
     if (tile >= p.B * p.H * (p.dv / CW)) return;
     Tile t;
@@ -206,12 +207,24 @@ hipError_t launch_dk(const Problem &p, hipStream_t stream) {
     constexpr int CW = 32, WAVES = 4;
     const long tiles = p.B * p.H * (p.dv / CW);
     dim3 grid((unsigned)((tiles + WAVES - 1) / WAVES));
-    if (p.flags & kQkL2Norm)
-        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, true>), grid,
+    switch (p.flags & (kQkL2Norm | kRawGates)) {
+    case 0:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, 0>), grid, dim3(WAVES * kWave),
+                           0, stream, p);
+        break;
+    case kQkL2Norm:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kQkL2Norm>), grid,
                            dim3(WAVES * kWave), 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, false>), grid,
+        break;
+    case kRawGates:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kRawGates>), grid,
                            dim3(WAVES * kWave), 0, stream, p);
+        break;
+    default:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kQkL2Norm | kRawGates>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
+        break;
+    }
     return hipGetLastError();
 }
 
