@@ -1,0 +1,124 @@
+"""Pins of the gradient oracle (oracle/backward.py): its forward agrees with
+the independent C oracle, and its gradients agree with central finite
+differences of the C oracle, for every input of every variant; planted
+mistakes in its recurrence are rejected."""
+import numpy as np
+import pytest
+
+from oracle import backward, oracle
+
+VARIANTS = oracle.VARIANTS
+
+
+def _problem(variant, seed, B=1, T=7, H=2, dk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    d = dict(q=rng.normal(size=(B, T, H, dk)), k=rng.normal(size=(B, T, H, dk)) * 0.5,
+             v=rng.normal(size=(B, T, H, dv)), alpha=None, beta=None, erase_b=None,
+             write_w=None, eps=0.0, state_in=rng.normal(size=(B, H, dk, dv)))
+    if variant in ("gated_deltanet", "kla"):
+        d["alpha"] = rng.uniform(0.6, 1.0, size=(B, T, H))
+    elif variant in ("kda", "gdn2"):
+        d["alpha"] = rng.uniform(0.6, 1.0, size=(B, T, H, dk))
+    if variant != "gdn2":
+        d["beta"] = rng.uniform(0.1, 0.9, size=(B, T, H))
+    else:
+        d["erase_b"] = rng.uniform(0.1, 0.9, size=(B, T, H, dk))
+        d["write_w"] = rng.uniform(0.1, 0.9, size=(B, T, H, dv))
+    if variant == "kla":
+        d["eps"] = 0.3
+    up = dict(d_o=rng.normal(size=(B, T, H, dv)), d_state_out=rng.normal(size=(B, H, dk, dv)))
+    return d, up
+
+
+def _loss(variant, d, up):
+    o, s = oracle.forward(variant, d["q"], d["k"], d["v"], alpha=d["alpha"], beta=d["beta"],
+                          erase_b=d["erase_b"], write_w=d["write_w"], eps=d["eps"],
+                          state_in=d["state_in"], threads=1)
+    return float(np.sum(o * up["d_o"]) + np.sum(s * up["d_state_out"]))
+
+
+def _fd_grad(variant, d, up, name, h=1e-6):
+    x = d[name]
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        old = x[idx]
+        x[idx] = old + h
+        lp = _loss(variant, d, up)
+        x[idx] = old - h
+        lm = _loss(variant, d, up)
+        x[idx] = old
+        g[idx] = (lp - lm) / (2 * h)
+    return g
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_forward_agrees_with_c_oracle(variant):
+    d, _ = _problem(variant, 5)
+    o1, s1 = backward.forward(variant, **{k: d[k] for k in d})
+    o2, s2 = oracle.forward(variant, **{k: d[k] for k in d})
+    assert _rel(o1, o2) < 1e-13 and _rel(s1, s2) < 1e-13
+
+
+def _check_against_fd(mod, variant, seed=11):
+    d, up = _problem(variant, seed)
+    g = mod.backward(variant, **{k: d[k] for k in d}, **up)
+    worst = 0.0
+    for name in ("q", "k", "v", "alpha", "beta", "erase_b", "write_w", "state_in"):
+        if d[name] is None:
+            assert g[name] is None
+            continue
+        fd = _fd_grad(variant, d, up, name)
+        worst = max(worst, _rel(g[name], fd))
+    return worst
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_gradients_match_finite_differences(variant):
+    assert _check_against_fd(backward, variant) < 1e-7
+
+
+def test_zero_initial_state_and_missing_upstream():
+    d, up = _problem("kda", 3)
+    d0 = dict(d, state_in=None)
+    g = backward.backward("kda", **d0, d_o=up["d_o"])
+    z = dict(d, state_in=np.zeros_like(d["state_in"]))
+    fd = _fd_grad("kda", z, dict(up, d_state_out=np.zeros_like(up["d_state_out"])), "state_in")
+    assert _rel(g["state_in"], fd) < 1e-7
+
+
+def test_sampled_heads_only():
+    d, up = _problem("gdn2", 4, B=2, H=3)
+    full = backward.backward("gdn2", **d, **up)
+    part = backward.backward("gdn2", **d, **up, heads=[(1, 2)])
+    assert np.allclose(part["k"][1, :, 2], full["k"][1, :, 2], rtol=0, atol=1e-14)
+    assert np.isnan(part["k"][0, :, 0]).all() and np.isnan(part["state_in"][0, 1]).all()
+
+
+# planted mistakes in a copy of the module's source
+MISTAKES = [
+    ("erase_sign", "S = S - beta * torch.outer(k, k @ S) + beta * torch.outer(k, v)\n    return S, S.T @ q\n\n\ndef _step_gated",
+     "S = S + beta * torch.outer(k, k @ S) + beta * torch.outer(k, v)\n    return S, S.T @ q\n\n\ndef _step_gated", "deltanet"),
+    ("decay_on_value_axis", "S = alpha[:, None] * S                    # decay on the key rows",
+     "S = alpha[None, :S.shape[1]] * S", "kda"),
+    ("erase_gate_dropped", "r = (erase_b * k) @ S", "r = k @ S", "gdn2"),
+    ("write_gate_dropped", "torch.outer(k, write_w * v)", "torch.outer(k, v)", "gdn2"),
+    ("kla_eps_dropped", "beta = eta / (k @ k + eps)", "beta = eta / (k @ k)", "kla"),
+    ("kla_residual_before_decay", "S = alpha * S\n    e = v - S.T @ k", "e = v - S.T @ k\n    S = alpha * S", "kla"),
+    ("decay_dropped", "S = alpha * S\n    S = S - beta", "S = S - beta", "gated_deltanet"),
+    ("readout_of_old_state", "    S = S - torch.outer(k, r) + torch.outer(k, write_w * v)\n    return S, S.T @ q",
+     "    S2 = S - torch.outer(k, r) + torch.outer(k, write_w * v)\n    return S2, S.T @ q", "gdn2"),
+]
+
+
+@pytest.mark.parametrize("name,old,new,variant", MISTAKES, ids=[m[0] for m in MISTAKES])
+def test_planted_mistake_is_caught(name, old, new, variant):
+    import types
+    src = open(backward.__file__).read()
+    assert old in src, name
+    mod = types.ModuleType("mutant")
+    exec(compile(src.replace(old, new, 1), "mutant", "exec"), mod.__dict__)
+    assert _check_against_fd(mod, variant) > 1e-4, name
