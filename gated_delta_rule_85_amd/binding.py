@@ -39,6 +39,15 @@ class GdrArgs(ctypes.Structure):
     ]
 
 
+class GdrGrads(ctypes.Structure):
+    """Mirror of ``struct gdr_grads``."""
+    _fields_ = [
+        ("d_o", _vp), ("d_state_out", _vp),
+        ("d_q", _vp), ("d_k", _vp), ("d_v", _vp), ("d_alpha", _vp), ("d_beta", _vp),
+        ("d_erase_b", _vp), ("d_write_w", _vp), ("d_state_in", _vp),
+    ]
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -68,6 +77,11 @@ def lib(path: str | None = None):
     L.gdr_forward_chunked.restype = ctypes.c_int
     L.gdr_decode_step.argtypes = [A, _vp]
     L.gdr_decode_step.restype = ctypes.c_int
+    G = ctypes.POINTER(GdrGrads)
+    L.gdr_backward_workspace_size.argtypes = [A]
+    L.gdr_backward_workspace_size.restype = ctypes.c_size_t
+    L.gdr_backward_chunked.argtypes = [A, G, _vp, ctypes.c_size_t, _vp]
+    L.gdr_backward_chunked.restype = ctypes.c_int
     L.gdr_status_string.argtypes = [ctypes.c_int]
     L.gdr_status_string.restype = ctypes.c_char_p
     L.gdr_last_error_detail.argtypes = []
@@ -94,6 +108,16 @@ def gdr_forward_chunked(args: GdrArgs, workspace: int, ws_bytes: int, stream: in
 
 def gdr_decode_step(args: GdrArgs, stream: int) -> int:
     return lib().gdr_decode_step(ctypes.byref(args), stream or None)
+
+
+def gdr_backward_workspace_size(args: GdrArgs) -> int:
+    return lib().gdr_backward_workspace_size(ctypes.byref(args))
+
+
+def gdr_backward_chunked(args: GdrArgs, grads: GdrGrads, workspace: int, ws_bytes: int,
+                         stream: int) -> int:
+    return lib().gdr_backward_chunked(ctypes.byref(args), ctypes.byref(grads),
+                                      workspace or None, ws_bytes, stream or None)
 
 
 def gdr_status_string(status: int) -> str:
@@ -202,3 +226,42 @@ def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=Non
                   decay_scale=decay_scale)
     check(gdr_decode_step(a, _stream_handle(stream)))
     return o
+
+
+def backward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None, write_w=None,
+             eps: float = 0.0, state_in=None, d_o=None, d_state_out=None,
+             want_state_grad: bool = True, workspace=None, stream=None):
+    """Gradient of the chunked forward on device tensors.  ``d_o`` [B,T,H,dv] (in
+    q's dtype) and ``d_state_out`` [B,H,dk,dv] float32 are the upstream gradients
+    (None = zero).  Returns a dict of float32 gradients keyed q, k, v, alpha, beta,
+    erase_b, write_w, state_in (None where the variant takes no such input)."""
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("d_o", d_o), ("d_state_out", d_state_out)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = q.device
+    f32 = torch.float32
+    out = {
+        "q": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+        "k": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+        "v": torch.empty((B, T, H, dv), dtype=f32, device=dev),
+        "alpha": None if alpha is None else torch.empty(alpha.shape, dtype=f32, device=dev),
+        "beta": None if beta is None else torch.empty(beta.shape, dtype=f32, device=dev),
+        "erase_b": None if erase_b is None else torch.empty(erase_b.shape, dtype=f32, device=dev),
+        "write_w": None if write_w is None else torch.empty(write_w.shape, dtype=f32, device=dev),
+        "state_in": (torch.empty((B, H, dk, dv), dtype=f32, device=dev)
+                     if want_state_grad else None),
+    }
+    a = make_args(variant, q, k, v, None, alpha, beta, erase_b, write_w, eps, state_in, None)
+    g = GdrGrads(_ptr(d_o), _ptr(d_state_out), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
+                 _ptr(out["alpha"]), _ptr(out["beta"]), _ptr(out["erase_b"]),
+                 _ptr(out["write_w"]), _ptr(out["state_in"]))
+    need = gdr_backward_workspace_size(a)   # 0 for invalid args: the call below reports why
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    check(gdr_backward_chunked(a, g, workspace.data_ptr(), workspace.numel(),
+                               _stream_handle(stream)))
+    return out

@@ -48,7 +48,7 @@
 namespace gdr {
 namespace {
 
-constexpr int C = 64;              // chunk length
+constexpr int C = kChunk;          // chunk length
 constexpr int kPrepThreads = 256;
 constexpr int kXcds = 8;           // accelerator complex dies per MI355X
 
@@ -72,6 +72,7 @@ struct Block {
     int nbmax;           // chunk stride of the workspace slot
     const float *s_in;
     float *s_out;
+    float *s_chunks;     // states-only scans: the state entering each chunk, [B*H][nbmax][dk][dv]
 };
 
 struct WsLayout {
@@ -167,17 +168,6 @@ __device__ __forceinline__ void load_lane(const bf16 *src, float *x) {
 __device__ __forceinline__ void load_lane(const float *src, float *x) { x[0] = *src; }
 
 
-// ---- fragment-major workspace layout ------------------------------------------
-// Each rows x K operand factor is stored as 16-row tiles by K-steps of the
-// matrix-core instruction, and inside a tile in MFMA lane order, so that one
-// wave's fragment load of a tile is one contiguous 1 KB (bf16) read: whole
-// cache lines, no half-used lines.
-template <typename TI> __device__ __forceinline__ long frag_off(int r, int k, int K) {
-    using M = Mma<TI>;
-    const int tile = (r >> 4) * (K / M::kK) + k / M::kK;
-    const int ln = (r & 15) + 16 * ((k % M::kK) / M::kPerLane);
-    return ((long)tile * kWave + ln) * M::kPerLane + (k % M::kPerLane);
-}
 // Four (bf16: one 8-byte store) or eight (one 16-byte store) consecutive k.
 __device__ __forceinline__ void store_frag4(bf16 *base, int r, int k, int K, f32x4 x) {
     store4(base + frag_off<bf16>(r, k, K), x);
@@ -193,14 +183,6 @@ __device__ __forceinline__ void store_frag8(float *base, int r, int k, int K, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) base[frag_off<float>(r, k + e, K)] = x[e];
 }
-// U~^T is consumed in accumulator layout: for value tile j/16 and row tile
-// r/16, lane (j % 16) + 16 ((r % 16) / 4) holds rows r .. r+3 of column j.
-__device__ __forceinline__ long ufrag_off(int j, int r) {
-    return ((long)((j >> 4) * (C / 16) + (r >> 4)) * kWave + (j & 15) + 16 * ((r & 15) >> 2)) * 4 +
-           (r & 3);
-}
-
-
 // ---- buffer loads ------------------------------------------------------------
 // The scan addresses each chunk's factors through a buffer descriptor built in
 // scalar registers from the chunk's block address, plus a per-lane offset that
@@ -1174,7 +1156,9 @@ template <typename TI, int DK> struct OutOps {
 
 constexpr int kScan2Threads = 512;
 
-template <typename TI, int DK, int DEPTH, int NJ>
+// STATES: instead of the outputs, record the state entering every chunk (fp32)
+// in blk.s_chunks; the output waves then only keep the barrier count.
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES>
 __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
@@ -1231,6 +1215,17 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         // loads in flight before it reuses any register.
         auto step = [&](const CO &op, long c) __attribute__((always_inline)) {
             const int cur = (int)(c & 1);
+            if constexpr (STATES) {
+                float *sc = blk.s_chunks + (ch0 + c) * (long)DK * DV;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int a = 0; a < NI; ++a)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            sc[(long)(16 * (w * NI + a) + 4 * lg + m) * DV + col0 + 16 * j + l16] =
+                                S[j][a][m];
+            }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 typename M::frag Sf[KS_D];
@@ -1296,6 +1291,9 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                         blk.s_out[(bh * DK + i) * DV + col0 + 16 * j + l16] = S[j][a][m];
                     }
         }
+    } else if constexpr (STATES) {
+        // the chain's barriers: one after S_0, two per chunk, two at the end
+        for (long i = 0; i < 2 * NC + 3; ++i) __syncthreads();
     } else {
         // ---------------- outputs of the previous chunk ----------------
         const int w = wave - 4;
@@ -1429,8 +1427,12 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     constexpr int NJ = 1;
     const long nwg = p.B * p.H * (DV / (16 * NJ));
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ>), dim3((unsigned)grid),
-                       dim3(kScan2Threads), 0, st, p, w, blk);
+    if (blk.s_chunks)
+        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true>), dim3((unsigned)grid),
+                           dim3(kScan2Threads), 0, st, p, w, blk);
+    else
+        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false>), dim3((unsigned)grid),
+                           dim3(kScan2Threads), 0, st, p, w, blk);
     return hipGetLastError();
 }
 
@@ -1440,7 +1442,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     char *base = static_cast<char *>(ws);
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
-        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out};
+        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
@@ -1459,7 +1461,8 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base + slot * q.slot);
         const long c0 = i * q.nb;
         const Block blk{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
-                        i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier};
+                        i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
+                        nullptr};
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, true, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
@@ -1468,6 +1471,33 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         if ((e = hipEventRecord(aux->scan[slot], stream)) != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Factors of every chunk in one workspace slot and the state entering each
+// chunk, for the gradient (no outputs).
+template <int V, typename TI, int DK, int DV>
+hipError_t states_shape(const Problem &p, void *ws, float *s_chunks, ForwardStates *out,
+                        hipStream_t stream) {
+    const long NC = (p.T + C - 1) / C;
+    const WsPtrs<TI> w = ws_ptrs<TI>(p, NC, ws);
+    *out = ForwardStates{w.W, w.Ut, w.Qt, w.Kbt, w.P, w.gam, NC};
+    const Block blk{0, (int)NC, (int)NC, p.state_in, nullptr, s_chunks};
+    hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
+    if (e != hipSuccess) return e;
+    return launch_scan<TI, DK, DV>(p, w, blk, stream);
+}
+
+template <int V, typename TI>
+hipError_t states_t(const Problem &p, void *ws, float *sc, ForwardStates *out, hipStream_t st) {
+    if (p.dk == 128 && p.dv == 128) return states_shape<V, TI, 128, 128>(p, ws, sc, out, st);
+    if (p.dk == 128 && p.dv == 64) return states_shape<V, TI, 128, 64>(p, ws, sc, out, st);
+    if (p.dk == 64 && p.dv == 128) return states_shape<V, TI, 64, 128>(p, ws, sc, out, st);
+    return states_shape<V, TI, 64, 64>(p, ws, sc, out, st);
+}
+
+template <int V>
+hipError_t states_v(const Problem &p, void *ws, float *sc, ForwardStates *out, hipStream_t st) {
+    return p.bf16 ? states_t<V, bf16>(p, ws, sc, out, st) : states_t<V, float>(p, ws, sc, out, st);
 }
 
 template <int V, typename TI>
@@ -1486,6 +1516,20 @@ hipError_t launch_v(const Problem &p, void *ws, hipStream_t stream) {
 }  // namespace
 
 size_t forward_workspace_bytes(const Problem &p) { return make_plan(p).total; }
+
+size_t forward_states_bytes(const Problem &p) { return ws_layout(p, (p.T + C - 1) / C).total; }
+
+hipError_t launch_forward_states(const Problem &p, void *workspace, float *s_chunks,
+                                 ForwardStates *out, hipStream_t stream) {
+    switch (p.variant) {
+    case kDeltaNet: return states_v<kDeltaNet>(p, workspace, s_chunks, out, stream);
+    case kGatedDeltaNet: return states_v<kGatedDeltaNet>(p, workspace, s_chunks, out, stream);
+    case kKDA: return states_v<kKDA>(p, workspace, s_chunks, out, stream);
+    case kGDN2: return states_v<kGDN2>(p, workspace, s_chunks, out, stream);
+    case kKLA: return states_v<kKLA>(p, workspace, s_chunks, out, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream) {
     switch (p.variant) {

@@ -92,4 +92,25 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+constexpr int kChunk = 64;   // chunk length of the prefill
+
+// ---- fragment-major workspace layout ------------------------------------------
+// Each rows x K operand factor is stored as 16-row tiles by K-steps of the
+// matrix-core instruction, and inside a tile in MFMA lane order, so that one
+// wave's fragment load of a tile is one contiguous 1 KB (bf16) read: whole
+// cache lines, no half-used lines.
+template <typename TI> __device__ __forceinline__ long frag_off(int r, int k, int K) {
+    using M = Mma<TI>;
+    const int tile = (r >> 4) * (K / M::kK) + k / M::kK;
+    const int ln = (r & 15) + 16 * ((k % M::kK) / M::kPerLane);
+    return ((long)tile * kWave + ln) * M::kPerLane + (k % M::kPerLane);
+}
+// U~^T is consumed in accumulator layout: for value tile j/16 and row tile
+// r/16, lane (j % 16) + 16 ((r % 16) / 4) holds rows r .. r+3 of column j.
+__device__ __forceinline__ long ufrag_off(int j, int r) {
+    return ((long)((j >> 4) * (kChunk / 16) + (r >> 4)) * kWave + (j & 15) + 16 * ((r & 15) >> 2)) * 4 +
+           (r & 3);
+}
+
+
 }  // namespace gdr

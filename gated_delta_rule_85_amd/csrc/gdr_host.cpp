@@ -22,7 +22,9 @@ gdr_status fail(gdr_status s, const char *fmt, ...) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-gdr_status check(const gdr_args *a, int for_decode) {
+// mode: 0 chunked forward, 1 decode step, 2 gradient of the chunked forward.
+gdr_status check(const gdr_args *a, int mode) {
+    const int for_decode = mode == 1;
     if (!a) return fail(GDR_ERR_INVALID_ARGUMENT, "args is NULL");
     if (a->variant < GDR_DELTANET || a->variant > GDR_KLA)
         return fail(GDR_ERR_INVALID_ARGUMENT, "unknown variant %d", a->variant);
@@ -59,8 +61,16 @@ gdr_status check(const gdr_args *a, int for_decode) {
         if (a->chunk != 0 && a->chunk != 64)
             return fail(GDR_ERR_UNSUPPORTED, "chunk must be 0 or 64 (got %d)", a->chunk);
     }
-    if (!a->q || !a->k || !a->v || !a->o)
+    if (mode == 2) {
+        if (a->flags != 0)
+            return fail(GDR_ERR_UNSUPPORTED, "the gradient takes stored inputs (flags must be 0)");
+        if (a->B * a->H * ((a->T + 63) / 64) > (int64_t(1) << 31) - 1)
+            return fail(GDR_ERR_UNSUPPORTED, "B * H * ceil(T / 64) must be below 2^31");
+        if (!a->q || !a->k || !a->v)
+            return fail(GDR_ERR_INVALID_ARGUMENT, "q, k and v are required");
+    } else if (!a->q || !a->k || !a->v || !a->o) {
         return fail(GDR_ERR_INVALID_ARGUMENT, "q, k, v and o are required");
+    }
 
     const int v = a->variant;
     const bool needs_alpha = v != GDR_DELTANET;
@@ -86,8 +96,49 @@ gdr_status check(const gdr_args *a, int for_decode) {
     for (int i = 0; i < 10; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GDR_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
-    if (a->o == a->q || a->o == a->k || a->o == a->v)
+    if (mode != 2 && (a->o == a->q || a->o == a->k || a->o == a->v))
         return fail(GDR_ERR_INVALID_ARGUMENT, "o must not alias an input");
+    return GDR_OK;
+}
+
+// The gradient outputs: present exactly for the inputs the variant takes,
+// aligned, and distinct from every input and from each other.
+gdr_status check_grads(const gdr_args *a, const gdr_grads *g) {
+    if (!g) return fail(GDR_ERR_INVALID_ARGUMENT, "grads is NULL");
+    const int v = a->variant;
+    struct Out { float *p; bool need; const char *name; };
+    const Out outs[] = {{g->d_q, true, "d_q"},
+                        {g->d_k, true, "d_k"},
+                        {g->d_v, true, "d_v"},
+                        {g->d_alpha, v != GDR_DELTANET, "d_alpha"},
+                        {g->d_beta, v != GDR_GDN2, "d_beta"},
+                        {g->d_erase_b, v == GDR_GDN2, "d_erase_b"},
+                        {g->d_write_w, v == GDR_GDN2, "d_write_w"}};
+    for (const Out &o : outs)
+        if (o.need != (o.p != nullptr))
+            return fail(GDR_ERR_INVALID_ARGUMENT, o.need ? "%s is required for this variant"
+                                                         : "%s must be NULL for this variant",
+                        o.name);
+    const void *ins[] = {a->q, a->k, a->v, a->alpha, a->beta, a->erase_b, a->write_w,
+                         a->state_in, g->d_o, g->d_state_out};
+    const void *outp[] = {g->d_q, g->d_k, g->d_v, g->d_alpha, g->d_beta, g->d_erase_b,
+                          g->d_write_w, g->d_state_in};
+    const char *onames[] = {"d_q", "d_k", "d_v", "d_alpha", "d_beta", "d_erase_b",
+                            "d_write_w", "d_state_in"};
+    for (int i = 0; i < 8; ++i) {
+        if (!outp[i]) continue;
+        if (!aligned16(outp[i]))
+            return fail(GDR_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", onames[i]);
+        for (const void *in : ins)
+            if (in && in == outp[i])
+                return fail(GDR_ERR_INVALID_ARGUMENT, "%s must not alias an input", onames[i]);
+        for (int j = 0; j < i; ++j)
+            if (outp[j] == outp[i])
+                return fail(GDR_ERR_INVALID_ARGUMENT, "%s and %s are the same buffer",
+                            onames[j], onames[i]);
+    }
+    if ((g->d_o && !aligned16(g->d_o)) || (g->d_state_out && !aligned16(g->d_state_out)))
+        return fail(GDR_ERR_INVALID_ARGUMENT, "d_o and d_state_out must be 16-byte aligned");
     return GDR_OK;
 }
 
@@ -140,6 +191,32 @@ gdr_status gdr_decode_step(const gdr_args *a, void *hip_stream) {
     gdr_status s = check(a, 1);
     if (s != GDR_OK) return s;
     hipError_t e = gdr::launch_decode(to_problem(a), reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+size_t gdr_backward_workspace_size(const gdr_args *a) {
+    if (check(a, 2) != GDR_OK) return 0;
+    return gdr::backward_workspace_bytes(to_problem(a));
+}
+
+gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *workspace,
+                                size_t ws_bytes, void *hip_stream) {
+    gdr_status s = check(a, 2);
+    if (s != GDR_OK) return s;
+    if ((s = check_grads(a, g)) != GDR_OK) return s;
+    gdr::Problem p = to_problem(a);
+    p.o = nullptr;
+    p.state_out = nullptr;
+    const size_t need = gdr::backward_workspace_bytes(p);
+    if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    const gdr::Grads gr{g->d_o, g->d_state_out, g->d_q, g->d_k, g->d_v, g->d_alpha,
+                        g->d_beta, g->d_erase_b, g->d_write_w, g->d_state_in};
+    hipError_t e = gdr::launch_backward(p, gr, workspace, reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GDR_OK;
 }

@@ -46,4 +46,26 @@ hipError_t launch_decode(const Problem &p, hipStream_t stream);
 size_t forward_workspace_bytes(const Problem &p);
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream);
 
+// The chunked forward's per-chunk factors for every chunk (in the input dtype,
+// fragment-major per chunk-head; chunk-head index = (b * H + h) * nbmax + c)
+// and the fp32 state entering each chunk ([B*H][nbmax][dk][dv] in s_chunks),
+// as the gradient needs them.  No outputs are written.
+struct ForwardStates {
+    const void *W, *Ut, *Qt, *Kbt, *P;
+    const float *gam;
+    long nbmax;
+};
+size_t forward_states_bytes(const Problem &p);
+hipError_t launch_forward_states(const Problem &p, void *workspace, float *s_chunks,
+                                 ForwardStates *out, hipStream_t stream);
+
+// Gradient of the chunked forward: upstream gradients in, input gradients out.
+struct Grads {
+    const void *d_o;            // [B,T,H,dv] input dtype, or NULL
+    const float *d_state_out;   // [B,H,dk,dv] or NULL
+    float *d_q, *d_k, *d_v, *d_alpha, *d_beta, *d_erase_b, *d_write_w, *d_state_in;
+};
+size_t backward_workspace_bytes(const Problem &p);
+hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, hipStream_t stream);
+
 }  // namespace gdr

@@ -174,6 +174,16 @@ def make_raw_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0, state_scale=
     return out
 
 
+def make_upstream_grads(B, T, H, dk, dv, dtype="bf16", seed=0):
+    """Upstream gradients of the forward's two outputs for a gradient check:
+    d_o ~ N(0,1) [B,T,H,dv] stored in ``dtype`` and d_state_out ~ N(0,1)
+    [B,H,dk,dv] float32, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    d_o = _store(_normal(rng, (B, T, H, dv)), dtype)
+    d_s = torch.from_numpy(_normal(rng, (B, H, dk, dv)))
+    return dict(d_o=d_o, d_state_out=d_s)
+
+
 def make_workload(wl: Workload, T=None, B=None, H=None):
     """Inputs of a named workload, optionally cut to a shorter sequence or
     fewer batch rows / heads (the draw keeps the workload's seed)."""

@@ -164,6 +164,48 @@ gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_byt
  * for an in-place update). */
 gdr_status gdr_decode_step(const gdr_args *a, void *hip_stream);
 
+/* ---- gradient of the chunked forward ----------------------------------------
+ *
+ * Given upstream gradients dO = dL/do and dS_T = dL/dS_T of a loss L, the
+ * gradient of L with respect to every input of gdr_forward_chunked.  It is the
+ * chain rule through the chunk form the prefill computes (the WY / UT
+ * representation of "Gated DeltaNet-2", technical core, and the chunk-wise
+ * algorithm of "Kaczmarz Linear Attention", Implementation section): a reverse
+ * pass over the chunks carries dL/dS backwards, and every chunk then
+ * back-propagates through its triangular solve and Gram products
+ * independently.  The forward's per-chunk factors and states are recomputed;
+ * nothing from an earlier forward call is needed.
+ */
+typedef struct gdr_grads {
+    const void *d_o;          /* [B, T, H, dv] in the args' dtype; NULL = zero */
+    const float *d_state_out; /* [B, H, dk, dv]; NULL = zero */
+    /* Outputs, float32, dense row-major, shaped like the inputs they belong
+     * to.  Each is required exactly when the variant takes that input. */
+    float *d_q, *d_k;         /* [B, T, H, dk] */
+    float *d_v;               /* [B, T, H, dv] */
+    float *d_alpha;           /* shaped like alpha: gradient w.r.t. the linear decay */
+    float *d_beta;            /* shaped like beta (w.r.t. eta for KLA) */
+    float *d_erase_b;         /* GDN2 [B, T, H, dk] */
+    float *d_write_w;         /* GDN2 [B, T, H, dv] */
+    float *d_state_in;        /* [B, H, dk, dv]; NULL = not written.  Written also
+                                 when state_in is NULL (zero initial state). */
+} gdr_grads;
+
+/* Bytes of device workspace gdr_backward_chunked needs for `a` (0 if `a` is
+ * not valid for it).  It grows linearly with B * H * T: the per-chunk factors,
+ * the fp32 state entering every chunk and its gradient, plus a fixed scratch
+ * area for the per-chunk gradient workers. */
+size_t gdr_backward_workspace_size(const gdr_args *a);
+
+/* Gradient of gdr_forward_chunked's outputs o and state_out with respect to
+ * q, k, v, the gates and state_in.  `a` describes the forward call (o and
+ * state_out are ignored and may be NULL); a->flags must be 0 (input transforms
+ * are not differentiated: GDR_ERR_UNSUPPORTED).  Outputs must not overlap the
+ * inputs or each other.  `workspace` must be 256-byte aligned and hold at
+ * least gdr_backward_workspace_size(a) bytes. */
+gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *workspace,
+                                size_t ws_bytes, void *hip_stream);
+
 /* Static description of a status code. */
 const char *gdr_status_string(int status);
 

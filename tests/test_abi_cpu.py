@@ -133,3 +133,56 @@ def test_status_strings(L):
     for code, name in binding.STATUS.items():
         assert binding.gdr_status_string(code) == name
     assert "unknown" in binding.gdr_status_string(99)
+
+
+def _grads(variant="gated_deltanet", **over):
+    g = binding.GdrGrads(0x11000, 0x12000, 0x13000, 0x14000, 0x15000,
+                         0x16000 if variant != "deltanet" else None,
+                         0x17000 if variant != "gdn2" else None,
+                         0x18000 if variant == "gdn2" else None,
+                         0x19000 if variant == "gdn2" else None, 0x1a000)
+    for key, val in over.items():
+        setattr(g, key, val)
+    return g
+
+
+def test_grads_struct_layout():
+    assert ctypes.sizeof(binding.GdrGrads) == 10 * 8
+    assert binding.GdrGrads.d_q.offset == 16
+    assert binding.GdrGrads.d_state_in.offset == 72
+
+
+@pytest.mark.parametrize("variant", list(binding.VARIANTS))
+def test_backward_validation(L, variant):
+    """The gradient takes the forward's arguments without o; its outputs are
+    required exactly for the inputs the variant has; every rejection happens
+    on the host."""
+    a = _args(variant, o=None, state_out=None)
+    n = binding.gdr_backward_workspace_size(a)
+    assert n > binding.gdr_forward_workspace_size(_args(variant))
+    bad_args = [dict(flags=binding.GDR_FLAG_QK_L2NORM), dict(q=None), dict(dk=96)]
+    for over in bad_args:
+        b = _args(variant, o=None, **over)
+        assert binding.gdr_backward_workspace_size(b) == 0
+        assert binding.gdr_backward_chunked(b, _grads(variant), 0x100000, n, 0) in (1, 2)
+    assert binding.gdr_backward_chunked(_args(variant, o=None, flags=1), _grads(variant),
+                                        0x100000, n, 0) == 2
+    missing = "d_alpha" if variant != "deltanet" else "d_k"
+    assert binding.gdr_backward_chunked(a, _grads(variant, **{missing: None}), 0x100000, n, 0) == 1
+    extra = "d_erase_b" if variant != "gdn2" else "d_beta"
+    assert binding.gdr_backward_chunked(a, _grads(variant, **{extra: 0x1b000}), 0x100000, n, 0) == 1
+    assert binding.gdr_backward_chunked(a, _grads(variant, d_q=0x1000), 0x100000, n, 0) == 1  # = q
+    assert binding.gdr_backward_chunked(a, _grads(variant, d_k=0x13000), 0x100000, n, 0) == 1
+    assert binding.gdr_backward_chunked(a, _grads(variant, d_v=0x15004), 0x100000, n, 0) == 1
+    assert binding.gdr_backward_chunked(a, _grads(variant), None, n, 0) == 3
+    assert binding.gdr_backward_chunked(a, _grads(variant), 0x100080, n, 0) == 3
+    assert binding.gdr_backward_chunked(a, _grads(variant), 0x100000, n - 1, 0) == 3
+
+
+def test_backward_workspace_grows_with_length(L):
+    a1 = _args("kda", o=None, T=64 * 10)
+    a2 = _args("kda", o=None, T=64 * 20)
+    n1, n2 = binding.gdr_backward_workspace_size(a1), binding.gdr_backward_workspace_size(a2)
+    # per chunk-head: bf16 factors, e^{g_C}, two fp32 states and dDelta [C, dv]
+    per = 2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 2 * 4 * 128 * 64 + 4 * 64 * 64
+    assert abs((n2 - n1) - 2 * 3 * 10 * per) <= 8 * 256
