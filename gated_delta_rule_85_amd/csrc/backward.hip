@@ -65,8 +65,8 @@ constexpr int kRevThreads = 256;
 
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(kRevThreads) void reverse_scan_kernel(Problem p, ForwardStates f,
-                                                                   Grads g, float *dS_chunks,
-                                                                   float *dDelta) {
+                                                                   Grads g, TI *dS_chunks,
+                                                                   TI *dDelta) {
     constexpr int NS = DV / 16;
     __shared__ float sdS[DK][17], sdO[C][17], sdD[C][17];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kRevThreads) void reverse_scan_kernel(Problem p, Fo
         }
         for (int idx = tid; idx < DK * 16; idx += kRevThreads) {
             const int i = idx / 16, j = idx % 16;
-            dS_chunks[(ch * DK + i) * DV + col0 + j] = sdS[i][j];
+            dS_chunks[(ch * DK + i) * DV + col0 + j] = from_f32<TI>(sdS[i][j]);
         }
         __syncthreads();
         {   // dDelta = Kbar dS' + P^T dO: one 16-row tile per wave
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kRevThreads) void reverse_scan_kernel(Problem p, Fo
             for (int i = 0; i < 4; ++i) {
                 const int r = m0 + 4 * lg + i;
                 sdD[r][l16] = acc[i];
-                dDelta[(ch * C + r) * DV + col0 + l16] = acc[i];
+                dDelta[(ch * C + r) * DV + col0 + l16] = from_f32<TI>(acc[i]);
             }
         }
         __syncthreads();
@@ -153,454 +153,531 @@ __global__ __launch_bounds__(kRevThreads) void reverse_scan_kernel(Problem p, Fo
 // ============================================================================
 // per-chunk gradient
 // ============================================================================
-constexpr int kGradThreads = 256;
+// Persistent workgroups of eight waves, each looping over chunk-heads.  The
+// 64 x 64 matrices (T, A then Y, dP, dT then dA) live in LDS; the chunk's
+// C x dk operands and intermediate gradients live in a per-workgroup fp32
+// slot in global memory (rows contiguous, so every operand fetch is a 16-byte
+// load per lane or a 64-byte row segment per 16 lanes).  Input gradients are
+// written from the matrix-core accumulators.
+constexpr int kGradThreads = 512;
+constexpr int kGradWaves = kGradThreads / kWave;
+constexpr int kGradSlots = 512;   // at most two workgroups per compute unit
+constexpr int CP = C + 2;         // LDS row pitch of the C x C matrices
 
-// fp32 intermediates of one chunk-head, row-major, in one workgroup's slot.
-template <int DK, int DV> struct GradSlot {
-    enum { Xq, Xa, Xk, Qg, Ag, Kb, Wm, dQt, dKb, dWm, dAg, dXq, dXa, dXk, G, NCK };   // C x DK
-    enum { Uu, Dl, dUu, NCV };                                                            // C x DV
-    enum { Am, Pm, Tm, Dm, dTm, dPm, dAm, Ym, NCC };                                      // C x C
-    static constexpr long kCK = (long)C * DK, kCV = (long)C * DV, kCC = (long)C * C;
-    // vectors: per-row beta, per-row |k|^2, dgam (DK), row/column decay sums (2 C)
-    static constexpr long kVec = 4 * C + DK;
-    static constexpr long kFloats = NCK * kCK + NCV * kCV + NCC * kCC + kVec;
+template <int DK> struct GradSlot {
+    enum { Xq, Xa, Xk, Ag, G, dQt, dKb, dWm, dAg, dG, NCK };   // C x DK each
+    enum { Am, Pm, NCC };                                    // C x C each
+    static constexpr long kCK = (long)C * DK, kCC = (long)C * C;
+    static constexpr long kFloats = NCK * kCK + NCC * kCC;
     float *base;
     __device__ float *ck(int which) const { return base + which * kCK; }
-    __device__ float *cv(int which) const { return base + NCK * kCK + which * kCV; }
-    __device__ float *cc(int which) const { return base + NCK * kCK + NCV * kCV + which * kCC; }
-    __device__ float *vec() const { return base + NCK * kCK + NCV * kCV + NCC * kCC; }
+    __device__ float *cc(int which) const { return base + NCK * kCK + which * kCC; }
 };
 
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 ld4(const bf16 *p) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// acc += X Y^T over K for two row-major, K-contiguous operands: x4(k) and
+// y4(k) return this lane's row (m0 + l16 of X, n0 + l16 of Y) at columns
+// k .. k+3.  Within each block of 16, lane group lg takes K indices 4 lg ..
+// 4 lg + 3 across the four steps: the same permutation of K on both sides,
+// so the sum is unchanged and each operand is one 4-wide load.
+template <int K, typename FX, typename FY>
+__device__ __forceinline__ f32x4 mm_rr(FX x4, FY y4, int lg, f32x4 acc) {
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const f32x4 a = x4(k0 + 4 * lg), b = y4(k0 + 4 * lg);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// acc += A B over k in [k_begin, k_end) (multiples of 16): a(k) is this
+// lane's A element at row m0 + l16, b(k) its B element at column n0 + l16.
+template <typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm_kr(FA a, FB b, int k_begin, int k_end, int lg, f32x4 acc) {
+    for (int k0 = k_begin; k0 < k_end; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            av[s] = a(k0 + 4 * s + lg);
+            bv[s] = b(k0 + 4 * s + lg);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Sum over the 16 lanes that share lg (the columns of one accumulator row).
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// Lower-triangular 16 x 16 block t of a 4 x 4 block grid, t = 0 .. 9.
+__device__ __forceinline__ int tri_r(int t) { return (t >= 1) + (t >= 3) + (t >= 6); }
+__device__ __forceinline__ int tri_s(int t) { const int r = tri_r(t); return t - r * (r + 1) / 2; }
+
 template <int V, typename TI, int DK, int DV>
-__global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(Problem p, Grads g,
-                                                                 const float *S_chunks,
-                                                                 const float *dS_chunks,
-                                                                 const float *dDelta,
-                                                                 float *scratch) {
+__global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
+    Problem p, Grads g, const TI *S_chunks, const TI *D_chunks, const TI *dS_chunks,
+    const TI *dD_chunks, float *scratch) {
     using VT = VariantTraits<V>;
-    using Slot = GradSlot<DK, DV>;
-    constexpr int NT = kGradThreads;
+    using Slot = GradSlot<DK>;
+    constexpr int NT = kGradThreads, NW = kGradWaves;
     constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, lg = lane >> 4;
+    constexpr int NKB = DK / 16, NVB = DV / 16;
+    __shared__ float sB[4][C][CP];   // 0: T; 1: A, then Y; 2: dP; 3: dT, then dA
+    __shared__ float sG[C], sbeta[C], sn[C], ssa[C], ssu[C], sdg[C], svrow[C], svcol[C], scoef[C];
+    __shared__ float sdgam[DK], sdgc[DK];
+    float(*sT)[CP] = sB[0];
+    float(*sA)[CP] = sB[1];
+    float(*sY)[CP] = sB[1];
+    float(*sdP)[CP] = sB[2];
+    float(*sdT)[CP] = sB[3];
+    float(*sdA)[CP] = sB[3];
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int H = (int)p.H;
     const long T = p.T, NC = (p.T + C - 1) / C;
     const long nitems = NC * p.H * p.B;
     const Slot sl{scratch + (long)blockIdx.x * Slot::kFloats};
     const TI *q = static_cast<const TI *>(p.q), *k = static_cast<const TI *>(p.k);
     const TI *v = static_cast<const TI *>(p.v), *dO = static_cast<const TI *>(g.d_o);
+    const bool hdo = dO != nullptr;
     float *Xq = sl.ck(Slot::Xq), *Xa = sl.ck(Slot::Xa), *Xk = sl.ck(Slot::Xk);
-    float *Qg = sl.ck(Slot::Qg), *Ag = sl.ck(Slot::Ag), *Kb = sl.ck(Slot::Kb), *Wm = sl.ck(Slot::Wm);
-    float *dQt = sl.ck(Slot::dQt), *dKb = sl.ck(Slot::dKb), *dWm = sl.ck(Slot::dWm);
-    float *dAg = sl.ck(Slot::dAg), *dXq = sl.ck(Slot::dXq), *dXa = sl.ck(Slot::dXa);
-    float *dXk = sl.ck(Slot::dXk), *Gd = sl.ck(Slot::G);
-    float *Uu = sl.cv(Slot::Uu), *Dl = sl.cv(Slot::Dl), *dUu = sl.cv(Slot::dUu);
-    float *Am = sl.cc(Slot::Am), *Pm = sl.cc(Slot::Pm), *Tm = sl.cc(Slot::Tm), *Dm = sl.cc(Slot::Dm);
-    float *dTm = sl.cc(Slot::dTm), *dPm = sl.cc(Slot::dPm), *dAm = sl.cc(Slot::dAm), *Ym = sl.cc(Slot::Ym);
-    float *vbeta = sl.vec(), *vkn = vbeta + C, *vdgam = vkn + C, *vrow = vdgam + DK, *vcol = vrow + C;
-    constexpr int GW = VT::kChannelDecay ? DK : 1;   // columns of g in use
-    __shared__ float sA[C][C + 1], sT[C][C + 1];
+    float *Ag = sl.ck(Slot::Ag), *Gd = sl.ck(Slot::G), *dQt = sl.ck(Slot::dQt);
+    float *dKb = sl.ck(Slot::dKb), *dWm = sl.ck(Slot::dWm), *dAg = sl.ck(Slot::dAg);
+    float *dGd = sl.ck(Slot::dG), *Am = sl.cc(Slot::Am), *Pm = sl.cc(Slot::Pm);
 
     for (long item = blockIdx.x; item < nitems; item += gridDim.x) {
+        // An opaque thread index per item keeps the compiler from hoisting
+        // per-lane addresses out of the item loop (they would stay live
+        // across it and spill).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
         const long c = item % NC, bh = item / NC;
         const int b = (int)(bh / H), h = (int)(bh % H);
         const long t0 = c * C;
         const int nvalid = (int)min((long)C, T - t0);
         const long ch = bh * NC + c;
-        const float *S = S_chunks + ch * DK * DV;
-        const float *dSp = dS_chunks + ch * DK * DV;
-        const float *dD = dDelta + ch * C * DV;
+        const TI *S = S_chunks + ch * DK * DV, *Dl = D_chunks + ch * C * DV;
+        const TI *dSp = dS_chunks + ch * DK * DV, *dD = dD_chunks + ch * C * DV;
         auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
+        auto rowc = [&](int r) { return r < nvalid ? r : nvalid - 1; };   // clamped, in bounds
 
-        __syncthreads();   // the previous item is done with the slot
-        // ---- E0: decay prefix sums, step sizes ------------------------------
-        for (int i = tid; i < GW; i += NT) {
-            float gg = 0.f;
-            for (int r = 0; r < C; ++r) {
-                if (VT::kHasDecay && r < nvalid)
-                    gg += logf(VT::kChannelDecay ? p.alpha[tok(r) * DK + i] : p.alpha[tok(r)]);
-                Gd[r * DK + i] = gg;
+        __syncthreads();   // the previous item is done with LDS and the slot
+        // ---- A: decay prefix sums, step sizes, element-wise operands -------------
+        if constexpr (kRowDecay) {
+            if (wave == 0) {
+                float x = lane < nvalid ? logf(p.alpha[tok(lane)]) : 0.f;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const float y = __shfl_up(x, off, kWave);
+                    if (lane >= off) x += y;
+                }
+                sG[lane] = x;
             }
         }
-        for (int r = wave; r < C; r += NT / kWave) {
-            float s2 = 0.f;
-            if (r < nvalid)
+        if constexpr (VT::kChannelDecay) {
+            if (tid < DK) {
+                float gg = 0.f;
+                for (int r = 0; r < C; ++r) {
+                    if (r < nvalid) gg += logf(p.alpha[tok(r) * DK + tid]);
+                    Gd[r * DK + tid] = gg;
+                }
+            }
+        }
+        if (tid < C) ssa[tid] = ssu[tid] = sdg[tid] = 0.f;
+        if (tid < DK) sdgc[tid] = 0.f;
+        if constexpr (VT::kKaczmarz) {
+            for (int r = wave; r < C; r += NW) {
+                float s2 = 0.f;
                 for (int i = lane; i < DK; i += kWave) {
-                    const float x = f32(k[tok(r) * DK + i]);
+                    const float x = f32(k[tok(rowc(r)) * DK + i]);
                     s2 += x * x;
                 }
-            s2 = wave_sum(s2);
-            if (lane == 0) {
-                vkn[r] = s2;
-                float bt = 0.f;
-                if constexpr (VT::kScalarBeta) {
-                    bt = r < nvalid ? p.beta[tok(r)] : 0.f;
-                    if constexpr (VT::kKaczmarz) bt = bt / (s2 + p.eps);
+                s2 = wave_sum(s2);
+                if (lane == 0) {
+                    const float n = s2 + p.eps;
+                    sn[r] = n;
+                    sbeta[r] = r < nvalid ? p.beta[tok(r)] / n : 0.f;
                 }
-                vbeta[r] = bt;
             }
+        } else if constexpr (VT::kScalarBeta) {
+            if (tid < C) sbeta[tid] = tid < nvalid ? p.beta[tok(tid)] : 0.f;
         }
         __syncthreads();
-        // ---- E0b: element-wise operands ---------------------------------------
         for (int idx = tid; idx < C * DK; idx += NT) {
             const int r = idx / DK, i = idx % DK;
-            const int gi = VT::kChannelDecay ? i : 0;
             const bool ok = r < nvalid;
-            const float qq = ok ? f32(q[tok(r) * DK + i]) : 0.f;
-            const float kk = ok ? f32(k[tok(r) * DK + i]) : 0.f;
+            const long o = tok(rowc(r)) * DK + i;
+            const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
             float aa;
-            if constexpr (VT::kGates) aa = ok ? p.erase_b[tok(r) * DK + i] * kk : 0.f;
-            else aa = vbeta[r] * kk;
-            const float gr = Gd[r * DK + gi], gC = Gd[(C - 1) * DK + gi], gm = Gd[(C / 2 - 1) * DK + gi];
+            if constexpr (VT::kGates) aa = ok ? p.erase_b[o] * kk : 0.f;
+            else aa = sbeta[r] * kk;
+            float gr = 0.f;
             if constexpr (VT::kChannelDecay) {
-                Xq[idx] = qq * __expf(gr - gm);
-                Xa[idx] = aa * __expf(gr - gm);
-                Xk[idx] = kk * __expf(gm - gr);
+                gr = Gd[idx];
+                const float e = __expf(gr - Gd[(C / 2 - 1) * DK + i]);
+                Xq[idx] = qq * e;
+                Xa[idx] = aa * e;
+                Xk[idx] = kk / e;
             } else {
+                if constexpr (kRowDecay) gr = sG[r];
                 Xq[idx] = qq;
                 Xa[idx] = aa;
                 Xk[idx] = kk;
             }
-            const float eg = __expf(gr);
-            Qg[idx] = qq * eg;
-            Ag[idx] = aa * eg;
-            Kb[idx] = kk * __expf(gC - gr);
+            Ag[idx] = aa * __expf(gr);
         }
-        for (int idx = tid; idx < C * DV; idx += NT) {
-            const int r = idx / DV, j = idx % DV;
-            const bool ok = r < nvalid;
-            const float vv = ok ? f32(v[tok(r) * DV + j]) : 0.f;
-            if constexpr (VT::kGates) Uu[idx] = ok ? p.write_w[tok(r) * DV + j] * vv : 0.f;
-            else Uu[idx] = vbeta[r] * vv;
-        }
-        if constexpr (kRowDecay)
-            for (int idx = tid; idx < C * C; idx += NT) {
-                const int r = idx / C, s = idx % C;
-                Dm[idx] = s <= r ? __expf(Gd[r * DK] - Gd[s * DK]) : 0.f;
-            }
         __syncthreads();
-        // ---- E1: A and P ------------------------------------------------------
-        for (int t = wave; t < 32; t += NT / kWave) {
-            const bool isP = t >= 16;
-            const int tt = t & 15, m0 = 16 * (tt / 4), n0 = 16 * (tt % 4);
+        // ---- B: the Gram products A (and P for a scalar decay) ---------------------
+        for (int t = wave; t < (kRowDecay ? 20 : 10); t += NW) {
+            const bool isP = t >= 10;
+            const int R = tri_r(t % 10), Sb = tri_s(t % 10);
             const float *X = isP ? Xq : Xa;
-            f32x4 acc = mm_tile<DK>([&](int m, int kk) { return X[m * DK + kk]; },
-                                    [&](int kk, int n) { return Xk[n * DK + kk]; }, m0, n0, l16, lg,
-                                    zero4());
+            const f32x4 acc = mm_rr<DK>([&](int kk) { return ld4(X + (16 * R + l16) * DK + kk); },
+                                        [&](int kk) { return ld4(Xk + (16 * Sb + l16) * DK + kk); },
+                                        lg, zero4());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = m0 + 4 * lg + i, s = n0 + l16;
-                float val = acc[i];
-                if constexpr (kRowDecay) val *= Dm[r * C + s];
-                val = isP ? (s <= r ? val : 0.f) : (s < r ? val : 0.f);
-                (isP ? Pm : Am)[r * C + s] = val;
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * R + 4 * lg + m, s = 16 * Sb + l16;
+                float val = acc[m];
+                if constexpr (kRowDecay) val *= s <= r ? __expf(sG[r] - sG[s]) : 0.f;
+                if (isP) {
+                    Pm[r * C + s] = s <= r ? val : 0.f;
+                } else {
+                    val = s < r ? val : 0.f;
+                    sA[r][s] = val;
+                    if constexpr (kRowDecay) Am[r * C + s] = val;
+                }
             }
         }
         __syncthreads();
-        // ---- E2: T = (I + A)^{-1} by forward substitution in LDS, one column
-        // per thread: T[r][c] = [r == c] - sum_{c <= s < r} A[r][s] T[s][c].
-        for (int idx = tid; idx < C * C; idx += NT) sA[idx / C][idx % C] = Am[idx];
-        __syncthreads();
+        // ---- C: T = (I + A)^{-1}: diagonal blocks by substitution, then the
+        // off-diagonal blocks by distance, T_ij = -T_ii sum_{j<=m<i} A_im T_mj.
         if (tid < C) {
-            const int cc = tid;
-            for (int r = 0; r < C; ++r) {
+            const int o = 16 * (tid >> 4), cc = tid & 15;
+            for (int r = 0; r < 16; ++r) {
                 float acc = r == cc ? 1.f : 0.f;
-                for (int s = cc; s < r; ++s) acc -= sA[r][s] * sT[s][cc];
-                sT[r][cc] = acc;
+                for (int s = cc; s < r; ++s) acc -= sA[o + r][o + s] * sT[o + s][o + cc];
+                sT[o + r][o + cc] = r < cc ? 0.f : acc;
             }
         }
         __syncthreads();
-        for (int idx = tid; idx < C * C; idx += NT) Tm[idx] = sT[idx / C][idx % C];
-        __syncthreads();
-        // ---- E3: W = T At, U~ = T u, then Delta = U~ - W S ----------------------
-        for (int t = wave; t < 4 * (DK / 16) + 4 * (DV / 16); t += NT / kWave) {
-            const bool isU = t >= 4 * (DK / 16);
-            const int tt = isU ? t - 4 * (DK / 16) : t;
-            const int ncol = isU ? DV / 16 : DK / 16;
-            const int m0 = 16 * (tt / ncol), n0 = 16 * (tt % ncol);
-            const float *Bsrc = isU ? Uu : Ag;
-            const int ld = isU ? DV : DK;
-            f32x4 acc = mm_tile<C>([&](int m, int s) { return Tm[m * C + s]; },
-                                   [&](int s, int n) { return Bsrc[s * ld + n]; }, m0, n0, l16, lg,
-                                   zero4());
-            float *dst = isU ? Dl : Wm;
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int I = wave + d, J = wave;
+                float(*sX)[17] = reinterpret_cast<float(*)[17]>(&sdP[0][0] + wave * 16 * 17);
+                f32x4 x = mm_kr([&](int m) { return sA[16 * I + l16][m]; },
+                                [&](int m) { return sT[m][16 * J + l16]; }, 16 * J, 16 * I, lg, zero4());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(m0 + 4 * lg + i) * ld + n0 + l16] = acc[i];
-        }
-        __syncthreads();
-        for (int t = wave; t < 4 * (DV / 16); t += NT / kWave) {
-            const int m0 = 16 * (t / (DV / 16)), n0 = 16 * (t % (DV / 16));
-            f32x4 acc = mm_tile<DK>([&](int m, int i) { return Wm[m * DK + i]; },
-                                    [&](int i, int n) { return S[i * DV + n]; }, m0, n0, l16, lg,
-                                    zero4());
+                for (int m = 0; m < 4; ++m) sX[4 * lg + m][l16] = x[m];
+                __builtin_amdgcn_wave_barrier();   // LDS is in order within a wave
+                const f32x4 t = mm_kr([&](int m) { return sT[16 * I + l16][16 * I + m]; },
+                                      [&](int m) { return sX[m][l16]; }, 0, 16, lg, zero4());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Dl[(m0 + 4 * lg + i) * DV + n0 + l16] -= acc[i];
+                for (int m = 0; m < 4; ++m) sT[16 * I + 4 * lg + m][16 * J + l16] = -t[m];
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        // ---- E4: contractions over the value channels ------------------------
-        auto dOf = [&](int r, int j) -> float {
-            return (dO && r < nvalid) ? f32(dO[tok(r) * DV + j]) : 0.f;
+        // ---- D: contractions over the value channels ---------------------------------
+        //   dQt = dO S^T, dW = -dDelta S^T, dKbar = Delta dS'^T   (C x DK)
+        //   dP = lower(dO Delta^T), dT_u = dDelta u^T              (C x C, lower blocks)
+        auto ldo = [&](int r, int j) -> f32x4 {
+            if (!hdo) return zero4();
+            const f32x4 x = ld4(dO + tok(rowc(r)) * DV + j);
+            return r < nvalid ? x : zero4();
         };
-        {
-            constexpr int NCK = 4 * (DK / 16);   // tiles of a C x DK result
-            for (int t = wave; t < 3 * NCK + 32; t += NT / kWave) {
-                if (t < 3 * NCK) {
-                    const int which = t / NCK, tt = t % NCK;
-                    const int m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-                    f32x4 acc;
-                    if (which == 0)        // dQt = dO S^T
-                        acc = mm_tile<DV>(dOf, [&](int j, int i) { return S[i * DV + j]; }, m0, n0,
-                                          l16, lg, zero4());
-                    else if (which == 1)   // dKbar = Delta dS'^T
-                        acc = mm_tile<DV>([&](int r, int j) { return Dl[r * DV + j]; },
-                                          [&](int j, int i) { return dSp[i * DV + j]; }, m0, n0, l16,
-                                          lg, zero4());
-                    else                   // dW = -dDelta S^T
-                        acc = mm_tile<DV>([&](int r, int j) { return -dD[r * DV + j]; },
-                                          [&](int j, int i) { return S[i * DV + j]; }, m0, n0, l16,
-                                          lg, zero4());
-                    float *dst = which == 0 ? dQt : which == 1 ? dKb : dWm;
+        auto ldu = [&](int r, int j) -> f32x4 {
+            const long o = tok(rowc(r)) * DV + j;
+            const f32x4 x = ld4(v + o);
+            if constexpr (VT::kGates) return r < nvalid ? x * ld4(p.write_w + o) : zero4();
+            else return x * sbeta[r];
+        };
+        for (int t = wave; t < 2 * NKB + 10; t += NW) {
+            if (t < 2 * NKB) {
+                const int N = t >> 1, R0 = 2 * (t & 1);
+                f32x4 aq[2] = {zero4(), zero4()}, aw[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
+                const int si = 16 * N + l16;
+#pragma unroll 1
+                for (int j0 = 0; j0 < DV; j0 += 16) {
+                    const int j = j0 + 4 * lg;
+                    const f32x4 bs = ld4(S + si * DV + j), bd = ld4(dSp + si * DV + j);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[(m0 + 4 * lg + i) * DK + n0 + l16] = acc[i];
-                } else {
-                    const int tt = t - 3 * NCK;
-                    const bool isT = tt >= 16;
-                    const int t16 = tt & 15, m0 = 16 * (t16 / 4), n0 = 16 * (t16 % 4);
-                    f32x4 acc;
-                    if (!isT)   // dP = lower(dO Delta^T)
-                        acc = mm_tile<DV>(dOf, [&](int j, int s) { return Dl[s * DV + j]; }, m0, n0,
-                                          l16, lg, zero4());
-                    else        // dT (first part) = dDelta u^T
-                        acc = mm_tile<DV>([&](int r, int j) { return dD[r * DV + j]; },
-                                          [&](int j, int s) { return Uu[s * DV + j]; }, m0, n0, l16,
-                                          lg, zero4());
+                    for (int u = 0; u < 2; ++u) {
+                        const int r = 16 * (R0 + u) + l16;
+                        const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j), xl = ld4(Dl + r * DV + j);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = m0 + 4 * lg + i, s = n0 + l16;
-                        if (isT) dTm[r * C + s] = acc[i];
-                        else dPm[r * C + s] = s <= r ? acc[i] : 0.f;
-                    }
-                }
-            }
-        }
-        for (int i = tid; i < DK; i += NT) {   // d e^{g_C}: sum_j S dS'
-            float acc = 0.f;
-            for (int j = 0; j < DV; ++j) acc += S[i * DV + j] * dSp[i * DV + j];
-            vdgam[i] = acc;
-        }
-        __syncthreads();
-        // ---- E5: dT += dW At^T; dAt = T^T dW; du = T^T dDelta ---------------
-        {
-            constexpr int NCK = 4 * (DK / 16), NCV = 4 * (DV / 16);
-            for (int t = wave; t < 16 + NCK + NCV; t += NT / kWave) {
-                if (t < 16) {
-                    const int m0 = 16 * (t / 4), n0 = 16 * (t % 4);
-                    f32x4 acc = mm_tile<DK>([&](int r, int i) { return dWm[r * DK + i]; },
-                                            [&](int i, int s) { return Ag[s * DK + i]; }, m0, n0,
-                                            l16, lg, zero4());
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dTm[(m0 + 4 * lg + i) * C + n0 + l16] += acc[i];
-                } else if (t < 16 + NCK) {
-                    const int tt = t - 16, m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-                    f32x4 acc = mm_tile<C>([&](int r, int s) { return Tm[s * C + r]; },
-                                           [&](int s, int i) { return dWm[s * DK + i]; }, m0, n0, l16,
-                                           lg, zero4());
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dAg[(m0 + 4 * lg + i) * DK + n0 + l16] = acc[i];
-                } else {
-                    const int tt = t - 16 - NCK, m0 = 16 * (tt / (DV / 16)), n0 = 16 * (tt % (DV / 16));
-                    f32x4 acc = mm_tile<C>([&](int r, int s) { return Tm[s * C + r]; },
-                                           [&](int s, int j) { return dD[s * DV + j]; }, m0, n0, l16,
-                                           lg, zero4());
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dUu[(m0 + 4 * lg + i) * DV + n0 + l16] = acc[i];
-                }
-            }
-        }
-        __syncthreads();
-        // ---- E6: dA = -strict_lower(T^T (dT T^T)) ------------------------------
-        for (int t = wave; t < 16; t += NT / kWave) {
-            const int m0 = 16 * (t / 4), n0 = 16 * (t % 4);
-            f32x4 acc = mm_tile<C>([&](int r, int s) { return dTm[r * C + s]; },
-                                   [&](int s, int n) { return Tm[n * C + s]; }, m0, n0, l16, lg, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ym[(m0 + 4 * lg + i) * C + n0 + l16] = acc[i];
-        }
-        __syncthreads();
-        for (int t = wave; t < 16; t += NT / kWave) {
-            const int m0 = 16 * (t / 4), n0 = 16 * (t % 4);
-            f32x4 acc = mm_tile<C>([&](int r, int s) { return Tm[s * C + r]; },
-                                   [&](int s, int n) { return Ym[s * C + n]; }, m0, n0, l16, lg, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = m0 + 4 * lg + i, s = n0 + l16;
-                dAm[r * C + s] = s < r ? -acc[i] : 0.f;
-            }
-        }
-        __syncthreads();
-        // ---- E7: the Gram products' backward ------------------------------------
-        if constexpr (kRowDecay) {
-            // G = (X Y^T) (.) D with D = e^{g_r - g_s}: dg_r += sum_s dG G, dg_s -= sum_r dG G;
-            // then the operands see dG (.) D.
-            for (int r = tid; r < C; r += NT) {
-                float rs = 0.f, cs = 0.f;
-                for (int s = 0; s < C; ++s) {
-                    rs += dAm[r * C + s] * Am[r * C + s] + dPm[r * C + s] * Pm[r * C + s];
-                    cs += dAm[s * C + r] * Am[s * C + r] + dPm[s * C + r] * Pm[s * C + r];
-                }
-                vrow[r] = rs;
-                vcol[r] = cs;
-            }
-            __syncthreads();
-            for (int idx = tid; idx < C * C; idx += NT) {
-                dAm[idx] *= Dm[idx];
-                dPm[idx] *= Dm[idx];
-            }
-            __syncthreads();
-        }
-        {
-            constexpr int NCK = 4 * (DK / 16);
-            for (int t = wave; t < 3 * NCK; t += NT / kWave) {
-                const int which = t / NCK, tt = t % NCK;
-                const int m0 = 16 * (tt / (DK / 16)), n0 = 16 * (tt % (DK / 16));
-                f32x4 acc;
-                if (which == 0)        // dXa = dA Xk
-                    acc = mm_tile<C>([&](int r, int s) { return dAm[r * C + s]; },
-                                     [&](int s, int i) { return Xk[s * DK + i]; }, m0, n0, l16, lg, zero4());
-                else if (which == 1)   // dXq = dP Xk
-                    acc = mm_tile<C>([&](int r, int s) { return dPm[r * C + s]; },
-                                     [&](int s, int i) { return Xk[s * DK + i]; }, m0, n0, l16, lg, zero4());
-                else {                 // dXk = dA^T Xa + dP^T Xq
-                    acc = mm_tile<C>([&](int s, int r) { return dAm[r * C + s]; },
-                                     [&](int r, int i) { return Xa[r * DK + i]; }, m0, n0, l16, lg, zero4());
-                    acc = mm_tile<C>([&](int s, int r) { return dPm[r * C + s]; },
-                                     [&](int r, int i) { return Xq[r * DK + i]; }, m0, n0, l16, lg, acc);
-                }
-                float *dst = which == 0 ? dXa : which == 1 ? dXq : dXk;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(m0 + 4 * lg + i) * DK + n0 + l16] = acc[i];
-            }
-        }
-        __syncthreads();
-        // ---- E8: element-wise chain rule ----------------------------------------
-        // dg (per channel, or summed over channels for a scalar decay) goes into
-        // Xq's slot, the gradient with respect to a into Xa's, k into Xk's.
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            const int gi = VT::kChannelDecay ? i : 0;
-            const float gr = Gd[r * DK + gi], gC = Gd[(C - 1) * DK + gi], gm = Gd[(C / 2 - 1) * DK + gi];
-            float dq = dXq[idx], da = dXa[idx], dk = dXk[idx], dg = 0.f;
-            if constexpr (VT::kChannelDecay) {
-                dg = Xa[idx] * da + Xq[idx] * dq - Xk[idx] * dk;
-                dq *= __expf(gr - gm);
-                da *= __expf(gr - gm);
-                dk *= __expf(gm - gr);
-            }
-            const float eg = __expf(gr);
-            dq += dQt[idx] * eg;
-            da += dAg[idx] * eg;
-            dk += dKb[idx] * __expf(gC - gr);
-            dg += dQt[idx] * Qg[idx] + dAg[idx] * Ag[idx] - dKb[idx] * Kb[idx];
-            Xq[idx] = dg;
-            Xa[idx] = da;
-            Xk[idx] = dk;
-            dQt[idx] = dq;
-        }
-        __syncthreads();
-        // dg of g_C (row C-1): sum over rows of dKbar (.) Kbar, and d e^{g_C} e^{g_C}
-        for (int i = tid; i < DK; i += NT) {
-            const int gi = VT::kChannelDecay ? i : 0;
-            float acc = vdgam[i] * __expf(Gd[(C - 1) * DK + gi]);
-            for (int r = 0; r < C; ++r) acc += dKb[r * DK + i] * Kb[r * DK + i];
-            vdgam[i] = acc;
-        }
-        __syncthreads();
-        // ---- E9: outputs -------------------------------------------------------------
-        // per row: the step-size gradient needs sum_i da k and sum_j du v
-        for (int r = wave; r < C; r += NT / kWave) {
-            float sa = 0.f, su = 0.f;
-            if (r < nvalid) {
-                for (int i = lane; i < DK; i += kWave) sa += Xa[r * DK + i] * f32(k[tok(r) * DK + i]);
-                for (int j = lane; j < DV; j += kWave) su += dUu[r * DV + j] * f32(v[tok(r) * DV + j]);
-            }
-            sa = wave_sum(sa);
-            su = wave_sum(su);
-            if (lane == 0 && VT::kScalarBeta) {
-                const float dbeta = sa + su;
-                if (r < nvalid) {
-                    if constexpr (VT::kKaczmarz) {
-                        // beta = eta / n, n = |k|^2 + eps: d eta = dbeta / n, and dk gets
-                        // -2 beta dbeta k / n (added below through vkn)
-                        const float n = vkn[r] + p.eps;
-                        g.d_beta[tok(r)] = dbeta / n;
-                        vkn[r] = -2.f * vbeta[r] * dbeta / n;
-                    } else {
-                        g.d_beta[tok(r)] = dbeta;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            if (r >= nvalid) continue;
-            const long o = tok(r) * DK + i;
-            const float kk = f32(k[o]);
-            float dk = Xk[idx];
-            const float da = Xa[idx];
-            if constexpr (VT::kGates) {
-                const float bg = p.erase_b[o];
-                dk += bg * da;
-                g.d_erase_b[o] = da * kk;
-            } else {
-                dk += vbeta[r] * da;
-                if constexpr (VT::kKaczmarz) dk += vkn[r] * kk;
-            }
-            g.d_q[o] = dQt[idx];
-            g.d_k[o] = dk;
-        }
-        for (int idx = tid; idx < C * DV; idx += NT) {
-            const int r = idx / DV, j = idx % DV;
-            if (r >= nvalid) continue;
-            const long o = tok(r) * DV + j;
-            const float du = dUu[idx];
-            if constexpr (VT::kGates) {
-                g.d_v[o] = p.write_w[o] * du;
-                g.d_write_w[o] = du * f32(v[o]);
-            } else {
-                g.d_v[o] = vbeta[r] * du;
-            }
-        }
-        // decay: dl_t = sum_{r >= t} dg_r (g restarts each chunk; row C-1 also
-        // carries g_C's gradient), d alpha = dl / alpha
-        if constexpr (VT::kHasDecay) {
-            if constexpr (VT::kChannelDecay) {
-                for (int i = tid; i < DK; i += NT) {
-                    float acc = vdgam[i];
-                    for (int r = C - 1; r >= 0; --r) {
-                        acc += Xq[r * DK + i];
-                        if (r < nvalid) {
-                            const long o = tok(r) * DK + i;
-                            g.d_alpha[o] = acc / p.alpha[o];
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            aq[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], bs[s4], aq[u], 0, 0, 0);
+                            aw[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], bs[s4], aw[u], 0, 0, 0);
+                            ak[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xl[s4], bd[s4], ak[u], 0, 0, 0);
                         }
                     }
                 }
-            } else {
-                // channel sums of the per-channel terms, plus the decay matrix's
-                if (tid < C) {
-                    float s = vrow[tid] - vcol[tid];
-                    for (int i = 0; i < DK; ++i) s += Xq[tid * DK + i];
-                    dAg[tid] = s;   // dAg is free now: per-row dg
-                }
-                __syncthreads();
-                if (tid == 0) {
-                    float acc = 0.f;
-                    for (int i = 0; i < DK; ++i) acc += vdgam[i];
-                    for (int r = C - 1; r >= 0; --r) {
-                        acc += dAg[r];
-                        if (r < nvalid) g.d_alpha[tok(r)] = acc / p.alpha[tok(r)];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int o = (16 * (R0 + u) + 4 * lg + m) * DK + 16 * N + l16;
+                        dQt[o] = aq[u][m];
+                        dWm[o] = -aw[u][m];
+                        dKb[o] = ak[u][m];
                     }
+            } else {
+                const int R = tri_r(t - 2 * NKB), Sb = tri_s(t - 2 * NKB);
+                f32x4 ap = zero4(), at = zero4();
+                const int r = 16 * R + l16, s = 16 * Sb + l16;
+#pragma unroll 2
+                for (int j0 = 0; j0 < DV; j0 += 16) {
+                    const int j = j0 + 4 * lg;
+                    const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j);
+                    const f32x4 yl = ld4(Dl + s * DV + j), yu = ldu(s, j);
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        ap = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], yl[s4], ap, 0, 0, 0);
+                        at = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], yu[s4], at, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int rr = 16 * R + 4 * lg + m, ss = 16 * Sb + l16;
+                    sdP[rr][ss] = ss <= rr ? ap[m] : 0.f;
+                    sdT[rr][ss] = at[m];
+                }
+            }
+        }
+        // dL/d e^{g_C} per key channel: sum_j S dS'
+        for (int idx = tid; idx < DK * 4; idx += NT) {
+            const int i = idx >> 2, qd = idx & 3;
+            float acc = 0.f;
+#pragma unroll
+            for (int j = qd * (DV / 4); j < (qd + 1) * (DV / 4); j += 4) {
+                const f32x4 a = ld4(S + i * DV + j), bq = ld4(dSp + i * DV + j);
+                acc += a[0] * bq[0] + a[1] * bq[1] + a[2] * bq[2] + a[3] * bq[3];
+            }
+            acc += __shfl_xor(acc, 1, kWave);
+            acc += __shfl_xor(acc, 2, kWave);
+            if (qd == 0) sdgam[i] = acc;
+        }
+        __syncthreads();
+        // ---- E: dT += dW At^T (strictly lower); dAt = T^T dW; du = T^T dDelta -----
+        for (int t = wave; t < 10 + 4 * NKB + 4 * NVB; t += NW) {
+            if (t < 10) {
+                const int R = tri_r(t), Sb = tri_s(t);
+                f32x4 acc;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m] = sdT[16 * R + 4 * lg + m][16 * Sb + l16];
+                acc = mm_rr<DK>([&](int kk) { return ld4(dWm + (16 * R + l16) * DK + kk); },
+                                [&](int kk) { return ld4(Ag + (16 * Sb + l16) * DK + kk); }, lg, acc);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int r = 16 * R + 4 * lg + m, s = 16 * Sb + l16;
+                    sdT[r][s] = s < r ? acc[m] : 0.f;
+                }
+            } else if (t < 10 + 4 * NKB) {
+                const int tt = t - 10, R = tt / NKB, N = tt % NKB;
+                const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
+                                        [&](int m) { return dWm[m * DK + 16 * N + l16]; }, 16 * R, C, lg,
+                                        zero4());
+#pragma unroll
+                for (int m = 0; m < 4; ++m) dAg[(16 * R + 4 * lg + m) * DK + 16 * N + l16] = acc[m];
+            } else {
+                const int tt = t - 10 - 4 * NKB, R = tt / NVB, N = tt % NVB;
+                const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
+                                        [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, 16 * R, C,
+                                        lg, zero4());
+                const int j = 16 * N + l16;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int r = 16 * R + 4 * lg + m;
+                    const long o = tok(rowc(r)) * DV + j;
+                    const float vv = f32(v[o]), du = acc[m];
+                    if constexpr (VT::kGates) {
+                        if (r < nvalid) {
+                            g.d_v[o] = p.write_w[o] * du;
+                            g.d_write_w[o] = du * vv;
+                        }
+                    } else {
+                        if (r < nvalid) g.d_v[o] = sbeta[r] * du;
+                        const float su = row16_sum(r < nvalid ? du * vv : 0.f);
+                        if (l16 == 0) atomicAdd(&ssu[r], su);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // ---- F: dA = -strict_lower(T^T (dT T^T)) ------------------------------------
+        for (int t = wave; t < 10; t += NW) {
+            const int R = tri_r(t), Nb = tri_s(t);
+            const f32x4 acc = mm_kr([&](int m) { return sdT[16 * R + l16][m]; },
+                                    [&](int m) { return sT[16 * Nb + l16][m]; }, 0, 16 * (Nb + 1), lg,
+                                    zero4());
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sY[16 * R + 4 * lg + m][16 * Nb + l16] = acc[m];
+        }
+        __syncthreads();
+        for (int t = wave; t < 10; t += NW) {
+            const int R = tri_r(t), Nb = tri_s(t);
+            const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
+                                    [&](int m) { return sY[m][16 * Nb + l16]; }, 16 * R, C, lg, zero4());
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * R + 4 * lg + m, n = 16 * Nb + l16;
+                sdA[r][n] = n < r ? -acc[m] : 0.f;
+            }
+        }
+        __syncthreads();
+        // ---- G: a scalar decay inside the Gram products: G = (X Y^T) (.) D with
+        // D = e^{g_r - g_s} gives dg_r += sum_s dG G and dg_s -= sum_r dG G, and
+        // the operands then see dG (.) D.
+        if constexpr (kRowDecay) {
+            for (int r = wave; r < C; r += NW) {
+                const float x = sdA[r][lane] * Am[r * C + lane] + sdP[r][lane] * Pm[r * C + lane];
+                const float y = sdA[lane][r] * Am[lane * C + r] + sdP[lane][r] * Pm[lane * C + r];
+                const float xs = wave_sum(lane <= r ? x : 0.f), ys = wave_sum(lane >= r ? y : 0.f);
+                if (lane == 0) {
+                    svrow[r] = xs;
+                    svcol[r] = ys;
+                }
+            }
+            __syncthreads();
+            for (int idx = tid; idx < C * C; idx += NT) {
+                const int r = idx / C, s = idx % C;
+                const float d = s <= r ? __expf(sG[r] - sG[s]) : 0.f;
+                sdA[r][s] *= d;
+                sdP[r][s] *= d;
+            }
+            __syncthreads();
+        }
+        // ---- H: Gram backward, element-wise chain rule, outputs --------------------------
+        //   dXa = dA Xk, dXq = dP Xk, dXk = dA^T Xa + dP^T Xq
+        for (int t = wave; t < 4 * NKB; t += NW) {
+            const int R = t / NKB, N = t % NKB, col = 16 * N + l16;
+            const f32x4 xa = mm_kr([&](int m) { return sdA[16 * R + l16][m]; },
+                                   [&](int m) { return Xk[m * DK + col]; }, 0, 16 * (R + 1), lg, zero4());
+            const f32x4 xq = mm_kr([&](int m) { return sdP[16 * R + l16][m]; },
+                                   [&](int m) { return Xk[m * DK + col]; }, 0, 16 * (R + 1), lg, zero4());
+            f32x4 xk = mm_kr([&](int m) { return sdA[m][16 * R + l16]; },
+                             [&](int m) { return Xa[m * DK + col]; }, 16 * R, C, lg, zero4());
+            xk = mm_kr([&](int m) { return sdP[m][16 * R + l16]; },
+                       [&](int m) { return Xq[m * DK + col]; }, 16 * R, C, lg, xk);
+            float e_col = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * R + 4 * lg + m, idx = r * DK + col;
+                const long o = tok(rowc(r)) * DK + col;
+                const bool ok = r < nvalid;
+                const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
+                float dq = xq[m], da = xa[m], dk = xk[m], dg = 0.f;
+                float gr = 0.f, gC = 0.f;
+                if constexpr (VT::kChannelDecay) {
+                    gr = Gd[idx];
+                    gC = Gd[(C - 1) * DK + col];
+                    const float e = __expf(gr - Gd[(C / 2 - 1) * DK + col]);
+                    dg = Xa[idx] * da + Xq[idx] * dq - Xk[idx] * dk;
+                    dq *= e;
+                    da *= e;
+                    dk /= e;
+                } else if constexpr (kRowDecay) {
+                    gr = sG[r];
+                    gC = sG[C - 1];
+                }
+                const float eg = __expf(gr), ekc = __expf(gC - gr);
+                const float dqt = dQt[idx], dag = dAg[idx], dkb = dKb[idx];
+                dq += dqt * eg;
+                da += dag * eg;
+                dk += dkb * ekc;
+                const float kb = kk * ekc;
+                dg += dqt * qq * eg + dag * Ag[idx] - dkb * kb;
+                e_col += dkb * kb;
+                float sa = 0.f;
+                if (ok) {
+                    g.d_q[o] = dq;
+                    if constexpr (VT::kGates) {
+                        g.d_k[o] = dk + p.erase_b[o] * da;
+                        g.d_erase_b[o] = da * kk;
+                    } else if constexpr (VT::kKaczmarz) {
+                        dQt[idx] = dk + sbeta[r] * da;   // completed once d eta is known
+                        sa = da * kk;
+                    } else {
+                        g.d_k[o] = dk + sbeta[r] * da;
+                        sa = da * kk;
+                    }
+                }
+                if constexpr (VT::kScalarBeta) {
+                    sa = row16_sum(sa);
+                    if (l16 == 0) atomicAdd(&ssa[r], sa);
+                }
+                if constexpr (VT::kChannelDecay) dGd[idx] = dg;
+                if constexpr (kRowDecay) {
+                    dg = row16_sum(dg);
+                    if (l16 == 0) atomicAdd(&sdg[r], dg);
+                }
+            }
+            if constexpr (VT::kChannelDecay) atomicAdd(&sdgc[col], e_col);
+            if constexpr (kRowDecay) {
+                e_col = wave_sum(e_col);
+                if (lane == 0) atomicAdd(&sdgc[0], e_col);
+            }
+        }
+        __syncthreads();
+        // ---- I: step sizes, decay (reverse cumulative sum of dg within the chunk) ----
+        if constexpr (VT::kScalarBeta) {
+            if (tid < nvalid) {
+                const float db = ssa[tid] + ssu[tid];
+                if constexpr (VT::kKaczmarz) {
+                    // beta = eta / n with n = |k|^2 + eps
+                    g.d_beta[tok(tid)] = db / sn[tid];
+                    scoef[tid] = -2.f * sbeta[tid] * db / sn[tid];
+                } else {
+                    g.d_beta[tok(tid)] = db;
+                }
+            }
+        }
+        if constexpr (VT::kChannelDecay) {
+            if (tid < DK) {
+                const int i = tid;
+                float acc = sdgam[i] * __expf(Gd[(C - 1) * DK + i]) + sdgc[i];
+                for (int r = C - 1; r >= 0; --r) {
+                    acc += dGd[r * DK + i];
+                    if (r < nvalid) {
+                        const long o = tok(r) * DK + i;
+                        g.d_alpha[o] = acc / p.alpha[o];
+                    }
+                }
+            }
+        } else if constexpr (kRowDecay) {
+            if (wave == NW - 1) {
+                float gsum = 0.f;
+                for (int i = lane; i < DK; i += kWave) gsum += sdgam[i];
+                const float dgC = wave_sum(gsum) * __expf(sG[C - 1]) + sdgc[0];
+                // suffix sums over the rows: x_t + x_{t+1} + ... + x_{C-1}
+                float x = sdg[lane] + svrow[lane] - svcol[lane];
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const float y = __shfl_down(x, off, kWave);
+                    if (lane + off < kWave) x += y;
+                }
+                if (lane < nvalid) g.d_alpha[tok(lane)] = (x + dgC) / p.alpha[tok(lane)];
+            }
+        }
+        if constexpr (VT::kKaczmarz) {
+            __syncthreads();
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, i = idx % DK;
+                if (r < nvalid) {
+                    const long o = tok(r) * DK + i;
+                    g.d_k[o] = dQt[idx] + scoef[r] * f32(k[o]);
                 }
             }
         }
@@ -610,28 +687,40 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(Problem p, Gra
 template <int V, typename TI, int DK, int DV>
 hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_t st) {
     char *base = static_cast<char *>(ws);
-    const long NC = (p.T + C - 1) / C, nheads = p.B * p.H;
+    const long NC = (p.T + C - 1) / C, nch = p.B * p.H * NC;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     size_t off = al(forward_states_bytes(p));
-    float *S_chunks = reinterpret_cast<float *>(base + off);
-    off += al((size_t)nheads * NC * DK * DV * 4);
-    float *dS_chunks = reinterpret_cast<float *>(base + off);
-    off += al((size_t)nheads * NC * DK * DV * 4);
-    float *dDelta = reinterpret_cast<float *>(base + off);
-    off += al((size_t)nheads * NC * C * DV * 4);
+    TI *S_chunks = reinterpret_cast<TI *>(base + off);
+    off += al((size_t)nch * DK * DV * sizeof(TI));
+    TI *D_chunks = reinterpret_cast<TI *>(base + off);
+    off += al((size_t)nch * C * DV * sizeof(TI));
+    TI *dS_chunks = reinterpret_cast<TI *>(base + off);
+    off += al((size_t)nch * DK * DV * sizeof(TI));
+    TI *dD_chunks = reinterpret_cast<TI *>(base + off);
+    off += al((size_t)nch * C * DV * sizeof(TI));
     float *scratch = reinterpret_cast<float *>(base + off);
 
     ForwardStates f;
-    hipError_t e = launch_forward_states(p, ws, S_chunks, &f, st);
+    hipError_t e = launch_forward_states(p, ws, S_chunks, D_chunks, &f, st);
     if (e != hipSuccess) return e;
-    const long nwg = nheads * (DV / 16);
+    const long nwg = p.B * p.H * (DV / 16);
     hipLaunchKernelGGL((reverse_scan_kernel<TI, DK, DV>), dim3((unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds))),
-                       dim3(kRevThreads), 0, st, p, f, g, dS_chunks, dDelta);
+                       dim3(kRevThreads), 0, st, p, f, g, dS_chunks, dD_chunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long items = NC * nheads;
-    const long slots = 256;
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+             &per_cu, reinterpret_cast<const void *>(chunk_grad_kernel<V, TI, DK, DV>), kGradThreads,
+             0)) != hipSuccess)
+        return e;
+    long slots = (long)cus * (per_cu > 0 ? per_cu : 1);
+    if (slots > kGradSlots) slots = kGradSlots;
+    const long items = NC * p.B * p.H;
     hipLaunchKernelGGL((chunk_grad_kernel<V, TI, DK, DV>), dim3((unsigned)(items < slots ? items : slots)),
-                       dim3(kGradThreads), 0, st, p, g, S_chunks, dS_chunks, dDelta, scratch);
+                       dim3(kGradThreads), 0, st, p, g, S_chunks, D_chunks, dS_chunks, dD_chunks,
+                       scratch);
     return hipGetLastError();
 }
 
@@ -651,11 +740,12 @@ hipError_t backward_v(const Problem &p, const Grads &g, void *ws, hipStream_t st
 }  // namespace
 
 size_t backward_workspace_bytes(const Problem &p) {
-    const long NC = (p.T + C - 1) / C, nheads = p.B * p.H;
+    const long NC = (p.T + C - 1) / C, nch = p.B * p.H * NC;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    const size_t slot = (size_t)(15 * C * p.dk + 3 * C * p.dv + 8 * C * C + 4 * C + p.dk) * 4;
-    return al(forward_states_bytes(p)) + 2 * al((size_t)nheads * NC * p.dk * p.dv * 4) +
-           al((size_t)nheads * NC * C * p.dv * 4) + 256 * slot;
+    const size_t es = p.bf16 ? 2 : 4;
+    const size_t slot = (size_t)(10 * C * p.dk + 2 * C * C) * 4;
+    return al(forward_states_bytes(p)) + 2 * al((size_t)nch * p.dk * p.dv * es) +
+           2 * al((size_t)nch * C * p.dv * es) + kGradSlots * slot;
 }
 
 hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, hipStream_t stream) {

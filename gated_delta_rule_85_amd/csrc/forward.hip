@@ -72,7 +72,8 @@ struct Block {
     int nbmax;           // chunk stride of the workspace slot
     const float *s_in;
     float *s_out;
-    float *s_chunks;     // states-only scans: the state entering each chunk, [B*H][nbmax][dk][dv]
+    void *s_chunks;      // states-only scans: the state entering each chunk, [B*H][nbmax][dk][dv]
+    void *d_chunks;      //   and each chunk's Delta, [B*H][nbmax][C][dv], both in the input dtype
 };
 
 struct WsLayout {
@@ -1215,17 +1216,6 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         // loads in flight before it reuses any register.
         auto step = [&](const CO &op, long c) __attribute__((always_inline)) {
             const int cur = (int)(c & 1);
-            if constexpr (STATES) {
-                float *sc = blk.s_chunks + (ch0 + c) * (long)DK * DV;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int a = 0; a < NI; ++a)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            sc[(long)(16 * (w * NI + a) + 4 * lg + m) * DV + col0 + 16 * j + l16] =
-                                S[j][a][m];
-            }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 typename M::frag Sf[KS_D];
@@ -1292,8 +1282,22 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                     }
         }
     } else if constexpr (STATES) {
-        // the chain's barriers: one after S_0, two per chunk, two at the end
-        for (long i = 0; i < 2 * NC + 3; ++i) __syncthreads();
+        // Copy S_c and Delta_c of chunk c from LDS to the workspace, in the
+        // window where the output waves would compute O_c; same barriers.
+        const int tt = tid - 4 * kWave;
+        TI *sg = static_cast<TI *>(blk.s_chunks), *dg = static_cast<TI *>(blk.d_chunks);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        for (long c = 0; c < NC; ++c) {
+            const int buf = (int)(c & 1);
+            TI *so = sg + (ch0 + c) * (long)DK * DV + col0;
+            TI *dd = dg + (ch0 + c) * (long)C * DV + col0;
+            for (int e = tt; e < SW * DK; e += 4 * kWave) so[(e / SW) * DV + e % SW] = sSt[buf][e % SW][e / SW];
+            for (int e = tt; e < SW * C; e += 4 * kWave) dd[(e / SW) * DV + e % SW] = sDt[buf][e % SW][e / SW];
+            __syncthreads();
+            __syncthreads();
+        }
     } else {
         // ---------------- outputs of the previous chunk ----------------
         const int w = wave - 4;
@@ -1442,7 +1446,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     char *base = static_cast<char *>(ws);
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
-        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr};
+        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr, nullptr};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
@@ -1462,7 +1466,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         const long c0 = i * q.nb;
         const Block blk{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
-                        nullptr};
+                        nullptr, nullptr};
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, true, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
@@ -1476,28 +1480,31 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
 // Factors of every chunk in one workspace slot and the state entering each
 // chunk, for the gradient (no outputs).
 template <int V, typename TI, int DK, int DV>
-hipError_t states_shape(const Problem &p, void *ws, float *s_chunks, ForwardStates *out,
-                        hipStream_t stream) {
+hipError_t states_shape(const Problem &p, void *ws, void *s_chunks, void *d_chunks,
+                        ForwardStates *out, hipStream_t stream) {
     const long NC = (p.T + C - 1) / C;
     const WsPtrs<TI> w = ws_ptrs<TI>(p, NC, ws);
     *out = ForwardStates{w.W, w.Ut, w.Qt, w.Kbt, w.P, w.gam, NC};
-    const Block blk{0, (int)NC, (int)NC, p.state_in, nullptr, s_chunks};
+    const Block blk{0, (int)NC, (int)NC, p.state_in, nullptr, s_chunks, d_chunks};
     hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
     if (e != hipSuccess) return e;
     return launch_scan<TI, DK, DV>(p, w, blk, stream);
 }
 
 template <int V, typename TI>
-hipError_t states_t(const Problem &p, void *ws, float *sc, ForwardStates *out, hipStream_t st) {
-    if (p.dk == 128 && p.dv == 128) return states_shape<V, TI, 128, 128>(p, ws, sc, out, st);
-    if (p.dk == 128 && p.dv == 64) return states_shape<V, TI, 128, 64>(p, ws, sc, out, st);
-    if (p.dk == 64 && p.dv == 128) return states_shape<V, TI, 64, 128>(p, ws, sc, out, st);
-    return states_shape<V, TI, 64, 64>(p, ws, sc, out, st);
+hipError_t states_t(const Problem &p, void *ws, void *sc, void *dc, ForwardStates *out,
+                    hipStream_t st) {
+    if (p.dk == 128 && p.dv == 128) return states_shape<V, TI, 128, 128>(p, ws, sc, dc, out, st);
+    if (p.dk == 128 && p.dv == 64) return states_shape<V, TI, 128, 64>(p, ws, sc, dc, out, st);
+    if (p.dk == 64 && p.dv == 128) return states_shape<V, TI, 64, 128>(p, ws, sc, dc, out, st);
+    return states_shape<V, TI, 64, 64>(p, ws, sc, dc, out, st);
 }
 
 template <int V>
-hipError_t states_v(const Problem &p, void *ws, float *sc, ForwardStates *out, hipStream_t st) {
-    return p.bf16 ? states_t<V, bf16>(p, ws, sc, out, st) : states_t<V, float>(p, ws, sc, out, st);
+hipError_t states_v(const Problem &p, void *ws, void *sc, void *dc, ForwardStates *out,
+                    hipStream_t st) {
+    return p.bf16 ? states_t<V, bf16>(p, ws, sc, dc, out, st)
+                  : states_t<V, float>(p, ws, sc, dc, out, st);
 }
 
 template <int V, typename TI>
@@ -1519,14 +1526,15 @@ size_t forward_workspace_bytes(const Problem &p) { return make_plan(p).total; }
 
 size_t forward_states_bytes(const Problem &p) { return ws_layout(p, (p.T + C - 1) / C).total; }
 
-hipError_t launch_forward_states(const Problem &p, void *workspace, float *s_chunks,
-                                 ForwardStates *out, hipStream_t stream) {
+hipError_t launch_forward_states(const Problem &p, void *workspace, void *s_chunks,
+                                 void *d_chunks, ForwardStates *out, hipStream_t stream) {
     switch (p.variant) {
-    case kDeltaNet: return states_v<kDeltaNet>(p, workspace, s_chunks, out, stream);
-    case kGatedDeltaNet: return states_v<kGatedDeltaNet>(p, workspace, s_chunks, out, stream);
-    case kKDA: return states_v<kKDA>(p, workspace, s_chunks, out, stream);
-    case kGDN2: return states_v<kGDN2>(p, workspace, s_chunks, out, stream);
-    case kKLA: return states_v<kKLA>(p, workspace, s_chunks, out, stream);
+    case kDeltaNet: return states_v<kDeltaNet>(p, workspace, s_chunks, d_chunks, out, stream);
+    case kGatedDeltaNet:
+        return states_v<kGatedDeltaNet>(p, workspace, s_chunks, d_chunks, out, stream);
+    case kKDA: return states_v<kKDA>(p, workspace, s_chunks, d_chunks, out, stream);
+    case kGDN2: return states_v<kGDN2>(p, workspace, s_chunks, d_chunks, out, stream);
+    case kKLA: return states_v<kKLA>(p, workspace, s_chunks, d_chunks, out, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -47,17 +47,18 @@ size_t forward_workspace_bytes(const Problem &p);
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream);
 
 // The chunked forward's per-chunk factors for every chunk (in the input dtype,
-// fragment-major per chunk-head; chunk-head index = (b * H + h) * nbmax + c)
-// and the fp32 state entering each chunk ([B*H][nbmax][dk][dv] in s_chunks),
-// as the gradient needs them.  No outputs are written.
+// fragment-major per chunk-head; chunk-head index = (b * H + h) * nbmax + c),
+// the state entering each chunk ([B*H][nbmax][dk][dv] in s_chunks) and each
+// chunk's Delta = U~ - W S ([B*H][nbmax][C][dv] in d_chunks), both in the
+// input dtype, as the gradient needs them.  No outputs are written.
 struct ForwardStates {
     const void *W, *Ut, *Qt, *Kbt, *P;
     const float *gam;
     long nbmax;
 };
 size_t forward_states_bytes(const Problem &p);
-hipError_t launch_forward_states(const Problem &p, void *workspace, float *s_chunks,
-                                 ForwardStates *out, hipStream_t stream);
+hipError_t launch_forward_states(const Problem &p, void *workspace, void *s_chunks,
+                                 void *d_chunks, ForwardStates *out, hipStream_t stream);
 
 // Gradient of the chunked forward: upstream gradients in, input gradients out.
 struct Grads {

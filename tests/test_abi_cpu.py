@@ -183,6 +183,7 @@ def test_backward_workspace_grows_with_length(L):
     a1 = _args("kda", o=None, T=64 * 10)
     a2 = _args("kda", o=None, T=64 * 20)
     n1, n2 = binding.gdr_backward_workspace_size(a1), binding.gdr_backward_workspace_size(a2)
-    # per chunk-head: bf16 factors, e^{g_C}, two fp32 states and dDelta [C, dv]
-    per = 2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 2 * 4 * 128 * 64 + 4 * 64 * 64
+    # per chunk-head: bf16 factors, e^{g_C}, the state and its gradient [dk, dv]
+    # and Delta and its gradient [C, dv], all four in bf16
+    per = 2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 2 * 2 * 128 * 64 + 2 * 2 * 64 * 64
     assert abs((n2 - n1) - 2 * 3 * 10 * per) <= 8 * 256
