@@ -20,13 +20,17 @@
 // "Kaczmarz Linear Attention", Implementation: only B = Diag(beta) changes per
 // variant).  The derivation and the kernels are our own.
 //
-// Three launches after the forward's own factors and per-chunk states
+// Launches after the forward's own factors and per-chunk states and Deltas
 // (launch_forward_states):
-//   reverse_scan_kernel   one workgroup per (16 value columns, h, b): the
+//   bw_prep_kernel        per chunk-head, parallel: P^T dO, Qt^T dO and the
+//                         transposed factors the reverse chain reads.
+//   reverse_chain_kernel  one workgroup per (16 value columns, h, b): the
 //                         sequential pass; records dS' and dDelta per chunk.
 //   chunk_grad_kernel     persistent workgroups over chunk-heads: the rest, in
-//                         fp32 on the matrix cores (16x16x4) with the chunk's
-//                         intermediates in a per-workgroup global scratch slot.
+//                         fp32 on the matrix cores (16x16x4), with the chunk's
+//                         64 x 64 matrices in LDS.
+#include <type_traits>
+
 #include "gdr_device.hpp"
 
 namespace gdr {
@@ -37,117 +41,289 @@ constexpr int kXcds = 8;
 
 template <typename T> __device__ __forceinline__ float f32(T x) { return to_f32(x); }
 
-// acc += A B over one 16x16 tile at (m0, n0) on fp32 matrix cores; A(m, k) and
-// B(k, n) return operand elements.  A lane supplies row l16 / K-element lg of
-// A and K-element lg / column l16 of B, and holds rows 4 lg .. 4 lg + 3 of
-// column l16 of the result.  All operand reads of four K-steps go out first.
-template <int K, typename FA, typename FB>
-__device__ __forceinline__ f32x4 mm_tile(FA A, FB B, int m0, int n0, int l16, int lg, f32x4 acc) {
-    static_assert(K % 16 == 0, "K in steps of 16");
-#pragma unroll 2
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        float a[4], b[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            a[s] = A(m0 + l16, k0 + 4 * s + lg);
-            b[s] = B(k0 + 4 * s + lg, n0 + l16);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-    }
-    return acc;
+// ============================================================================
+// reverse pass over the chunks
+// ============================================================================
+// With dS' the gradient of the state leaving chunk c, the chunk's Delta and
+// its incoming state receive
+//     dDelta = X1 + Kbar dS',                       X1 = P^T dO,
+//     dS     = Diag(e^{g_C}) dS' + X2 - W^T dDelta,  X2 = Qt^T dO.
+// X1 and X2 do not depend on the chain: bw_prep computes them for every chunk
+// in parallel, and rewrites Kbar and W^T fragment-major with their
+// contraction index contiguous.  The sequential chain then has the shape of
+// the forward's state chain (two matrix-core steps between two barriers per
+// chunk), and copy waves move dS' and dDelta of each chunk from LDS to the
+// workspace beside it.
+
+// Chain operands of every chunk-head, in the input dtype.
+struct RevFactors {
+    void *Kb;   // [nch] C x DK   Kbar, fragment-major (rows r, contraction over i)
+    void *Wt;   // [nch] DK x C   W^T, fragment-major (rows i, contraction over r)
+    void *X1;   // [nch] C x DV   P^T dO, accumulator layout
+    void *X2;   // [nch] DK x DV  Qt^T dO, accumulator layout
+};
+
+// (row, k) of the element at offset `off` of a rows x K fragment-major matrix
+// (the inverse of frag_off).
+template <typename TI> __device__ __forceinline__ void frag_pos(int off, int K, int &r, int &k) {
+    using M = Mma<TI>;
+    const int e = off % M::kPerLane, q = off / M::kPerLane;
+    const int ln = q % kWave, tile = q / kWave, kt = K / M::kK;
+    r = (tile / kt) * 16 + (ln & 15);
+    k = (tile % kt) * M::kK + (ln >> 4) * M::kPerLane + e;
 }
 
-// ============================================================================
-// reverse scan
-// ============================================================================
-constexpr int kRevThreads = 256;
+// Offset of element (row i, value column j) of a rows x DV matrix kept in
+// accumulator layout: 16 x 16 tiles, value tile major; in a tile, lane
+// (j % 16) + 16 ((i % 16) / 4) holds rows i .. i+3 of column j.
+__device__ __forceinline__ long afrag_off(int j, int i, int rows) {
+    return ((long)((j >> 4) * (rows / 16) + (i >> 4)) * kWave + (j & 15) + 16 * ((i & 15) >> 2)) * 4 +
+           (i & 3);
+}
+
+template <typename TI> __device__ __forceinline__ void copy16(TI *dst, const TI *src, int n, int tid,
+                                                              int nt) {
+    constexpr int V = 16 / sizeof(TI);
+    for (int o = tid * V; o < n; o += nt * V)
+        *reinterpret_cast<f32x4 *>(dst + o) = *reinterpret_cast<const f32x4 *>(src + o);
+}
+
+constexpr int kBpThreads = 256;
 
 template <typename TI, int DK, int DV>
-__global__ __launch_bounds__(kRevThreads) void reverse_scan_kernel(Problem p, ForwardStates f,
-                                                                   Grads g, TI *dS_chunks,
-                                                                   TI *dDelta) {
-    constexpr int NS = DV / 16;
-    __shared__ float sdS[DK][17], sdO[C][17], sdD[C][17];
+__global__ __launch_bounds__(kBpThreads) void bw_prep_kernel(Problem p, ForwardStates f, Grads g,
+                                                            RevFactors rf) {
+    using M = Mma<TI>;
+    constexpr int NL = M::kPerLane;
+    __shared__ __attribute__((aligned(16))) TI sm[C * C + C * DK + C * DV];
+    TI *sP = sm, *sQ = sm + C * C, *sdO = sm + C * C + C * DK;   // first stage
+    TI *sK = sm, *sW = sm + C * DK;                              // second stage
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const int H = (int)p.H;
-    const long T = p.T, NC = f.nbmax;
-    const long nwg = p.B * p.H * NS;
+    const long T = p.T, NC = f.nbmax, nch = NC * p.B * p.H;
+    const TI *dO = static_cast<const TI *>(g.d_o);
+    for (long ch = blockIdx.x; ch < nch; ch += gridDim.x) {
+        const long c = ch % NC, bh = ch / NC;
+        const int b = (int)(bh / H), h = (int)(bh % H);
+        const long t0 = c * C;
+        const int nvalid = (int)min((long)C, T - t0);
+        __syncthreads();
+        copy16(sP, static_cast<const TI *>(f.P) + ch * C * C, C * C, tid, kBpThreads);
+        copy16(sQ, static_cast<const TI *>(f.Qt) + ch * C * DK, C * DK, tid, kBpThreads);
+        for (int o = 4 * tid; o < C * DV; o += 4 * kBpThreads) {
+            const int r = o / DV, j = o % DV;
+            f32x4 x = zero4();
+            if (dO && r < nvalid) x = load4(dO + (((long)b * T + t0 + r) * H + h) * DV + j);
+            store4(sdO + o, x);
+        }
+        __syncthreads();
+        // X1 = P^T dO and X2 = Qt^T dO on fp32 matrix cores
+        constexpr int NX1 = (C / 16) * (DV / 16), NX = NX1 + (DK / 16) * (DV / 16);
+        for (int t = wave; t < NX; t += kBpThreads / kWave) {
+            const bool x1 = t < NX1;
+            const int tt = x1 ? t : t - NX1;
+            const int Rb = tt / (DV / 16), Jb = tt % (DV / 16);
+            const int row = 16 * Rb + l16, col = 16 * Jb + l16;
+            f32x4 acc = zero4();
+            for (int s0 = 0; s0 < C; s0 += 16) {
+                float av[4], bv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int s = s0 + 4 * u + lg;
+                    av[u] = to_f32(x1 ? sP[frag_off<TI>(s, row, C)] : sQ[frag_off<TI>(s, row, DK)]);
+                    bv[u] = to_f32(sdO[s * DV + col]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc, 0, 0, 0);
+            }
+            TI *dst = static_cast<TI *>(x1 ? rf.X1 : rf.X2) + ch * (x1 ? C : DK) * DV;
+            store4(dst + afrag_off(col, 16 * Rb + 4 * lg, x1 ? C : DK), acc);
+        }
+        __syncthreads();
+        copy16(sK, static_cast<const TI *>(f.Kbt) + ch * DK * C, DK * C, tid, kBpThreads);
+        copy16(sW, static_cast<const TI *>(f.W) + ch * C * DK, C * DK, tid, kBpThreads);
+        __syncthreads();
+        TI *kb = static_cast<TI *>(rf.Kb) + ch * C * DK, *wt = static_cast<TI *>(rf.Wt) + ch * DK * C;
+        for (int qo = tid * NL; qo < C * DK; qo += kBpThreads * NL) {
+            int r, i, i2, r2;
+            frag_pos<TI>(qo, DK, r, i);    // Kbar element (r, i .. i+NL-1) = Kbar^T (i.., r)
+            frag_pos<TI>(qo, C, i2, r2);   // W^T element (i2, r2 .. r2+NL-1) = W (r2.., i2)
+            TI xk[NL], xw[NL];
+#pragma unroll
+            for (int e = 0; e < NL; ++e) {
+                xk[e] = sK[frag_off<TI>(i + e, r, C)];
+                xw[e] = sW[frag_off<TI>(r2 + e, i2, DK)];
+            }
+#pragma unroll
+            for (int e = 0; e < NL; ++e) {
+                kb[qo + e] = xk[e];
+                wt[qo + e] = xw[e];
+            }
+        }
+    }
+}
+
+// One chunk's chain operands, loaded through buffer descriptors (per-lane
+// offsets fixed, per-chunk address arithmetic scalar).
+template <typename TI, int DK> struct RevOps {
+    using M = Mma<TI>;
+    static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK, NI = DK / 64;
+    static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);   // bytes per fragment tile
+    typedef typename std::conditional<sizeof(TI) == 2, bf16x4, f32x4>::type raw4;
+    typename M::frag Kf[KS_D], Wf[NI][KS_C];
+    raw4 X1, X2[NI];
+    f32x4 gam[NI];
+    __device__ __forceinline__ void load(const RevFactors &rf, const float *gm, long ch, int DV,
+                                         int col0, int w, int lane) {
+        const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
+        const auto rk = make_rsrc(static_cast<const char *>(rf.Kb) + (ch * C * DK) * (long)sizeof(TI) +
+                                  w * KS_D * FB);
+        const auto rw = make_rsrc(static_cast<const char *>(rf.Wt) + (ch * DK * C) * (long)sizeof(TI) +
+                                  w * NI * KS_C * FB);
+        const auto rg = make_rsrc(gm + ch * DK + 16 * NI * w);
+        const auto r1 = make_rsrc(static_cast<const char *>(rf.X1) +
+                                  (ch * C * DV + (long)((col0 / 16) * (C / 16) + w) * kWave * 4) *
+                                      (long)sizeof(TI));
+        const auto r2 = make_rsrc(static_cast<const char *>(rf.X2) +
+                                  (ch * DK * DV + (long)((col0 / 16) * (DK / 16) + w * NI) * kWave * 4) *
+                                      (long)sizeof(TI));
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) Kf[ks] = buf_load<typename M::frag>(rk, loff + ks * FB);
+#pragma unroll
+        for (int a = 0; a < NI; ++a) {
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks)
+                Wf[a][ks] = buf_load<typename M::frag>(rw, loff + (a * KS_C + ks) * FB);
+            gam[a] = buf_load<f32x4>(rg, (unsigned)(lane >> 4) * 16u + 64u * a);
+            X2[a] = buf_load<raw4>(r2, ((unsigned)lane + (unsigned)a * kWave) * 4u * sizeof(TI));
+        }
+        X1 = buf_load<raw4>(r1, (unsigned)lane * 4u * sizeof(TI));
+    }
+};
+
+constexpr int kRevThreads = 512;
+
+// One workgroup per (16 value columns, h, b): waves 0-3 carry dS (fp32, in
+// matrix-core accumulators) backwards over the chunks; waves 4-7 copy each
+// chunk's dS' and dDelta from LDS to the workspace.
+template <typename TI, int DK, int DEPTH>
+__global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p, const float *gm,
+                                                                      RevFactors rf, Grads g,
+                                                                      TI *dS_chunks, TI *dD_chunks,
+                                                                      long NC) {
+    using M = Mma<TI>;
+    using RO = RevOps<TI, DK>;
+    constexpr int KS_D = RO::KS_D, KS_C = RO::KS_C, NI = RO::NI;
+    constexpr int PT = 8;
+    __shared__ __attribute__((aligned(16))) TI sSt[2][16][DK + PT];   // dS'^T, double-buffered
+    __shared__ __attribute__((aligned(16))) TI sDt[2][16][C + PT];    // dDelta^T, double-buffered
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int H = (int)p.H, DV = (int)p.dv;
+    const int nslice = DV / 16;
+    const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
     const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nwg) return;
-    const long bh = logical / NS;
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const int col0 = (int)(logical % NS) * 16;
-    const TI *W = static_cast<const TI *>(f.W), *Qt = static_cast<const TI *>(f.Qt);
-    const TI *Kbt = static_cast<const TI *>(f.Kbt), *P = static_cast<const TI *>(f.P);
-    const TI *dO = static_cast<const TI *>(g.d_o);
+    const long bh = logical / nslice;
+    const int col0 = (int)(logical % nslice) * 16;
+    const long ch0 = bh * NC;
+    // the n-th chunk of the reverse pass, clamped for prefetches past the end
+    auto chunk = [&](long n) { return ch0 + NC - 1 - (n < NC ? n : NC - 1); };
 
-    for (int idx = tid; idx < DK * 16; idx += kRevThreads) {
-        const int i = idx / 16, j = idx % 16;
-        sdS[i][j] = g.d_state_out ? g.d_state_out[(bh * DK + i) * DV + col0 + j] : 0.f;
-    }
-    __syncthreads();
-    for (long c = NC - 1; c >= 0; --c) {
-        const long ch = bh * NC + c;
-        // dO of this chunk's rows (zero past T and without upstream); record
-        // the gradient with respect to the state leaving the chunk.
-        for (int idx = tid; idx < C * 16; idx += kRevThreads) {
-            const int r = idx / 16, j = idx % 16;
-            const long t = c * C + r;
-            sdO[r][j] = (dO && t < T) ? f32(dO[((b * T + t) * H + h) * DV + col0 + j]) : 0.f;
-        }
-        for (int idx = tid; idx < DK * 16; idx += kRevThreads) {
-            const int i = idx / 16, j = idx % 16;
-            dS_chunks[(ch * DK + i) * DV + col0 + j] = from_f32<TI>(sdS[i][j]);
-        }
-        __syncthreads();
-        {   // dDelta = Kbar dS' + P^T dO: one 16-row tile per wave
-            const int m0 = 16 * wave;
-            f32x4 acc = zero4();
-            acc = mm_tile<DK>([&](int r, int i) { return f32(Kbt[ch * DK * C + frag_off<TI>(i, r, C)]); },
-                              [&](int i, int n) { return sdS[i][n]; }, m0, 0, l16, lg, acc);
-            acc = mm_tile<C>([&](int r, int s) { return f32(P[ch * C * C + frag_off<TI>(s, r, C)]); },
-                             [&](int s, int n) { return sdO[s][n]; }, m0, 0, l16, lg, acc);
+    if (wave < 4) {
+        const int w = wave;
+        f32x4 S[NI];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = m0 + 4 * lg + i;
-                sdD[r][l16] = acc[i];
-                dDelta[(ch * C + r) * DV + col0 + l16] = from_f32<TI>(acc[i]);
+        for (int a = 0; a < NI; ++a)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = 16 * (w * NI + a) + 4 * lg + m;
+                S[a][m] = g.d_state_out ? g.d_state_out[(bh * DK + i) * DV + col0 + l16] : 0.f;
+            }
+        auto write_st = [&](int buf) {
+#pragma unroll
+            for (int a = 0; a < NI; ++a) store4(&sSt[buf][l16][16 * (w * NI + a) + 4 * lg], S[a]);
+        };
+        write_st(0);
+        __syncthreads();
+        auto step = [&](const RO &op, long n) __attribute__((always_inline)) {
+            const int cur = (int)(n & 1);
+            typename M::frag Sf[KS_D];
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ++ks) Sf[ks] = M::load(&sSt[cur][l16][0], ks * M::kK, lane);
+            f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS_D; ks += 2) {
+                d0 = M::mma(op.Kf[ks], Sf[ks], d0);
+                if (ks + 1 < KS_D) d1 = M::mma(op.Kf[ks + 1], Sf[ks + 1], d1);
+            }
+            store4(&sDt[cur][l16][16 * w + 4 * lg], to_f32x4(op.X1) + (d0 + d1));
+            __syncthreads();
+            typename M::frag Df[KS_C];
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(&sDt[cur][l16][0], ks * M::kK, lane);
+#pragma unroll
+            for (int a = 0; a < NI; ++a) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Wf[a][ks], Df[ks], acc);
+                S[a] = S[a] * op.gam[a] + to_f32x4(op.X2[a]) - acc;
+            }
+            write_st(cur ^ 1);
+            __syncthreads();
+        };
+        if constexpr (DEPTH == 2) {
+            RO A, Bq;
+            A.load(rf, gm, chunk(0), DV, col0, w, lane);
+            for (long n = 0; n < NC; n += 2) {
+                Bq.load(rf, gm, chunk(n + 1), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
+                step(A, n);
+                if (n + 1 >= NC) break;
+                A.load(rf, gm, chunk(n + 2), DV, col0, w, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                step(Bq, n + 1);
+            }
+        } else {
+            RO cur;
+            for (long n = 0; n < NC; ++n) {
+                cur.load(rf, gm, chunk(n), DV, col0, w, lane);
+                step(cur, n);
             }
         }
+        // the copy waves still move the last chunk
         __syncthreads();
-        // dS = Diag(e^{g_C}) dS' + Qt^T dO - W^T dDelta
-        constexpr int NU = DK / 64;
-        f32x4 nd[NU];
+        __syncthreads();
+        if (g.d_state_in) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int m0 = 16 * (wave + 4 * u);
-            f32x4 aq = zero4(), aw = zero4();
-            aq = mm_tile<C>([&](int i, int s) { return f32(Qt[ch * C * DK + frag_off<TI>(s, i, DK)]); },
-                            [&](int s, int n) { return sdO[s][n]; }, m0, 0, l16, lg, aq);
-            aw = mm_tile<C>([&](int i, int r) { return f32(W[ch * C * DK + frag_off<TI>(r, i, DK)]); },
-                            [&](int r, int n) { return sdD[r][n]; }, m0, 0, l16, lg, aw);
+            for (int a = 0; a < NI; ++a)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = m0 + 4 * lg + i;
-                nd[u][i] = f.gam[ch * DK + row] * sdS[row][l16] + aq[i] - aw[i];
-            }
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * (w * NI + a) + 4 * lg + m;
+                    g.d_state_in[(bh * DK + i) * DV + col0 + l16] = S[a][m];
+                }
         }
+    } else {
+        // Copy dS' and dDelta of the n-th chunk in the window where the chain
+        // computes the next one; the same barriers as the chain.
+        const int tt = tid - 4 * kWave;
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < NU; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sdS[16 * (wave + 4 * u) + 4 * lg + i][l16] = nd[u][i];
         __syncthreads();
+        __syncthreads();
+        for (long n = 0; n < NC; ++n) {
+            const int buf = (int)(n & 1);
+            const long ch = ch0 + NC - 1 - n;
+            TI *so = dS_chunks + ch * DK * DV + col0, *dd = dD_chunks + ch * C * DV + col0;
+            for (int e = tt; e < 16 * DK; e += 4 * kWave) so[(e >> 4) * DV + (e & 15)] = sSt[buf][e & 15][e >> 4];
+            for (int e = tt; e < 16 * C; e += 4 * kWave) dd[(e >> 4) * DV + (e & 15)] = sDt[buf][e & 15][e >> 4];
+            __syncthreads();
+            __syncthreads();
+        }
     }
-    if (g.d_state_in)
-        for (int idx = tid; idx < DK * 16; idx += kRevThreads) {
-            const int i = idx / 16, j = idx % 16;
-            g.d_state_in[(bh * DK + i) * DV + col0 + j] = sdS[i][j];
-        }
 }
 
 // ============================================================================
@@ -698,14 +874,29 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_
     off += al((size_t)nch * DK * DV * sizeof(TI));
     TI *dD_chunks = reinterpret_cast<TI *>(base + off);
     off += al((size_t)nch * C * DV * sizeof(TI));
+    RevFactors rf;
+    rf.Kb = base + off;
+    off += al((size_t)nch * C * DK * sizeof(TI));
+    rf.Wt = base + off;
+    off += al((size_t)nch * DK * C * sizeof(TI));
+    rf.X1 = base + off;
+    off += al((size_t)nch * C * DV * sizeof(TI));
+    rf.X2 = base + off;
+    off += al((size_t)nch * DK * DV * sizeof(TI));
     float *scratch = reinterpret_cast<float *>(base + off);
 
     ForwardStates f;
     hipError_t e = launch_forward_states(p, ws, S_chunks, D_chunks, &f, st);
     if (e != hipSuccess) return e;
+    const long bp_grid = nch < 16384 ? nch : 16384;
+    hipLaunchKernelGGL((bw_prep_kernel<TI, DK, DV>), dim3((unsigned)bp_grid), dim3(kBpThreads), 0, st, p,
+                       f, g, rf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const long nwg = p.B * p.H * (DV / 16);
-    hipLaunchKernelGGL((reverse_scan_kernel<TI, DK, DV>), dim3((unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds))),
-                       dim3(kRevThreads), 0, st, p, f, g, dS_chunks, dD_chunks);
+    constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
+    hipLaunchKernelGGL((reverse_chain_kernel<TI, DK, DEPTH>),
+                       dim3((unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds))), dim3(kRevThreads), 0, st,
+                       p, f.gam, rf, g, dS_chunks, dD_chunks, NC);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -744,8 +935,9 @@ size_t backward_workspace_bytes(const Problem &p) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t es = p.bf16 ? 2 : 4;
     const size_t slot = (size_t)(10 * C * p.dk + 2 * C * C) * 4;
-    return al(forward_states_bytes(p)) + 2 * al((size_t)nch * p.dk * p.dv * es) +
-           2 * al((size_t)nch * C * p.dv * es) + kGradSlots * slot;
+    return al(forward_states_bytes(p)) + 3 * al((size_t)nch * p.dk * p.dv * es) +
+           3 * al((size_t)nch * C * p.dv * es) + 2 * al((size_t)nch * C * p.dk * es) +
+           kGradSlots * slot;
 }
 
 hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, hipStream_t stream) {

@@ -140,26 +140,6 @@ __device__ __forceinline__ void store8(float *dst, const float *x) {
     *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
-__device__ __forceinline__ void store4(bf16 *dst, f32x4 x) {
-    bf16x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-    *reinterpret_cast<bf16x4 *>(dst) = v;
-}
-__device__ __forceinline__ void store4(float *dst, f32x4 x) {
-    *reinterpret_cast<f32x4 *>(dst) = x;
-}
-__device__ __forceinline__ f32x4 load4(const bf16 *src) {
-    bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ f32x4 load4(const float *src) {
-    return *reinterpret_cast<const f32x4 *>(src);
-}
-__device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ f32x4 to_f32x4(f32x4 v) { return v; }
 // kPerLane consecutive input elements as floats (8 for bf16, 1 for fp32).
 __device__ __forceinline__ void load_lane(const bf16 *src, float *x) {
     bf16x8 v = *reinterpret_cast<const bf16x8 *>(src);
@@ -184,31 +164,6 @@ __device__ __forceinline__ void store_frag8(float *base, int r, int k, int K, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) base[frag_off<float>(r, k + e, K)] = x[e];
 }
-// ---- buffer loads ------------------------------------------------------------
-// The scan addresses each chunk's factors through a buffer descriptor built in
-// scalar registers from the chunk's block address, plus a per-lane offset that
-// never changes: the per-chunk address arithmetic stays scalar, so no vector
-// register that may still be the target of a load in flight is rewritten.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff,
-                                             0x00020000);
-}
-template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    if constexpr (sizeof(T) == 16) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-        return __builtin_bit_cast(T, v);
-    } else if constexpr (sizeof(T) == 8) {
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-        return __builtin_bit_cast(T, v);
-    } else {
-        static_assert(sizeof(T) == 4, "4, 8 or 16 bytes");
-        unsigned v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-        return __builtin_bit_cast(T, v);
-    }
-}
-
 // The ten lower-triangular 16x16 tiles (R >= S) of a 64x64 matrix in row
 // order, and the six strictly upper ones, as arithmetic on the tile number
 // (no table: a table read is a memory load, and its wait would also wait for

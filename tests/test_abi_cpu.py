@@ -183,7 +183,9 @@ def test_backward_workspace_grows_with_length(L):
     a1 = _args("kda", o=None, T=64 * 10)
     a2 = _args("kda", o=None, T=64 * 20)
     n1, n2 = binding.gdr_backward_workspace_size(a1), binding.gdr_backward_workspace_size(a2)
-    # per chunk-head: bf16 factors, e^{g_C}, the state and its gradient [dk, dv]
-    # and Delta and its gradient [C, dv], all four in bf16
-    per = 2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 2 * 2 * 128 * 64 + 2 * 2 * 64 * 64
+    # per chunk-head, in bf16: the forward factors (+ e^{g_C} in fp32); the
+    # state, its gradient and Qt^T dO [dk, dv]; Delta, its gradient and P^T dO
+    # [C, dv]; Kbar and W^T [C, dk]
+    per = (2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 3 * 2 * 128 * 64 + 3 * 2 * 64 * 64
+           + 2 * 2 * 64 * 128)
     assert abs((n2 - n1) - 2 * 3 * 10 * per) <= 8 * 256
