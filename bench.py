@@ -14,10 +14,13 @@ and the CPU oracle timed on a bounded sample of the same work.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
     python bench.py --long-context [--steps 20] [--warmup 3]
+    python bench.py --backward [--steps 10] [--warmup 2]
 
 The second form measures the long-context shapes instead (131,072-token
 prefill, single-sequence decode from position 32,768, Kaczmarz LA against Gated
-DeltaNet) and prints its own JSON line.
+DeltaNet) and prints its own JSON line.  The third measures the gradient of the
+chunked forward on the same Kaczmarz prefill (upstream gradients for o and S_T
+given) and prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -238,6 +241,95 @@ def long_context(args):
     print(json.dumps(out))
 
 
+def backward_flops_per_chunk_head(dk, dv, c=C, scalar_decay=True):
+    """Algorithmic FLOPs of the per-chunk gradient step, counting only the
+    needed triangles: the three C x dk products over dv (dQt, dW, dKbar), dP
+    and dT_u over dv, the Gram products A (and P for a scalar decay), the
+    triangular solve, dT += dW At^T, T^T dW, T^T dDelta, dA = -T^T dT T^T and
+    the Gram backward (dA Xk, dP Xk, dA^T Xa, dP^T Xq)."""
+    lo_inc, lo_str = c * (c + 1) / 2, c * (c - 1) / 2
+    f = 3 * 2 * c * dv * dk                       # dQt, dW, dKbar
+    f += 2 * lo_inc * dv + 2 * lo_str * dv        # dP, dT_u
+    f += 2 * lo_str * dk + (2 * lo_inc * dk if scalar_decay else 0)   # A (, P)
+    f += c ** 3 / 3                               # solve
+    f += 2 * lo_str * dk + 2 * lo_inc * dk + 2 * lo_inc * dv   # dT, T^T dW, T^T dDelta
+    f += 2 * c ** 3 / 3                           # dT T^T, T^T (.)
+    f += 2 * (2 * lo_str * dk + 2 * lo_inc * dk)  # Gram backward
+    return f
+
+
+def backward(args):
+    """Gradient of the chunked forward on the Kaczmarz prefill (B=1, H=16,
+    T=65536, d=128, bf16): upstream gradients for o and S_T in, every input
+    gradient out (fp32).  The forward on the same inputs is timed beside it.
+    Prints one JSON line."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import WORKLOADS, make_upstream_grads, make_workload
+
+    L = binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    wl = WORKLOADS[5]
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    log(f"{wl.name}: generating inputs and upstream gradients")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_workload(wl).items()}
+    up = {k: v.to(dev) for k, v in make_upstream_grads(B, T, H, dk, dv, wl.dtype,
+                                                         seed=wl.seed + 1).items()}
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    fa = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"], None,
+                           None, d["eps"], None, s_T)
+    binding.check(binding.gdr_check_args(fa, 0))
+    nfw = binding.gdr_forward_workspace_size(fa)
+    ba = binding.make_args(wl.variant, d["q"], d["k"], d["v"], None, d["alpha"], d["beta"], None,
+                           None, d["eps"], None, None)
+    nbw = binding.gdr_backward_workspace_size(ba)
+    ws = torch.empty(max(nfw, nbw), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    gr = {n: torch.empty(shape, dtype=f32, device=dev) for n, shape in
+          (("q", (B, T, H, dk)), ("k", (B, T, H, dk)), ("v", (B, T, H, dv)), ("alpha", (B, T, H)),
+           ("beta", (B, T, H)), ("s0", (B, H, dk, dv)))}
+    ga = binding.GdrGrads(up["d_o"].data_ptr(), up["d_state_out"].data_ptr(), gr["q"].data_ptr(),
+                          gr["k"].data_ptr(), gr["v"].data_ptr(), gr["alpha"].data_ptr(),
+                          gr["beta"].data_ptr(), None, None, gr["s0"].data_ptr())
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / args.steps
+
+    log(f"timing the forward and the gradient ({args.steps} steps each)")
+    fw_s = timed(lambda: binding.check(L.gdr_forward_chunked(ctypes.byref(fa), ws.data_ptr(),
+                                                             nfw, sh)))
+    bw_s = timed(lambda: binding.check(L.gdr_backward_chunked(ctypes.byref(ba), ctypes.byref(ga),
+                                                              ws.data_ptr(), nbw, sh)))
+    finite = all(bool(torch.isfinite(t).all()) for t in gr.values())
+    nch = B * H * ((T + C - 1) // C)
+    out = {
+        "metric": "gradient throughput of the chunked forward (tokens/s, one layer)",
+        "value": B * T / bw_s, "unit": "tokens/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name.split("_decode")[0] + "; upstream gradients for o and "
+                               "S_T; gradients w.r.t. q, k, v, eta, alpha and S_0 in fp32"},
+        "backward_ms": bw_s * 1e3, "forward_ms": fw_s * 1e3,
+        "backward_over_forward": bw_s / fw_s,
+        "chunk_grad_flops": backward_flops_per_chunk_head(dk, dv) * nch,
+        "workspace_bytes": nbw, "outputs_finite": finite, "git": git_sha(),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +344,8 @@ def main():
     ap.add_argument("--cpu-decode-steps", type=int, default=192)
     ap.add_argument("--long-context", action="store_true",
                     help="measure the long-context shapes (131K prefill, decode at 32K) instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="measure the gradient of the chunked forward on the Kaczmarz prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -261,6 +355,9 @@ def main():
 
     if args.long_context:
         long_context(args)
+        return
+    if args.backward:
+        backward(args)
         return
 
     import torch

@@ -33,7 +33,8 @@
  * rule: the key-norm-normalised step size.)  Channel-wise decay acts on the key
  * rows of S.
  *
- * Two entry points compute it: a chunkwise-parallel prefill over a whole
+ * Two entry points compute it (a third, gdr_backward_chunked below, computes
+ * its gradient): a chunkwise-parallel prefill over a whole
  * sequence ("Kaczmarz Linear Attention", Implementation section: the
  * chunk-wise parallel algorithm is kept and only the per-chunk diagonal
  * coefficient matrix Diag(beta_1..beta_C) changes; "Gated DeltaNet-2", technical
