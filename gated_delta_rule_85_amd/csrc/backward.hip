@@ -389,6 +389,41 @@ __device__ __forceinline__ f32x4 mm_kr(FA a, FB b, int k_begin, int k_end, int l
     return acc;
 }
 
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// acc += X Y^T over K on bf16 matrix cores: x8(k) and y8(k) return this lane's
+// row (m0 + l16 of X, n0 + l16 of Y) at columns k .. k+7.
+template <int K, typename FX, typename FY>
+__device__ __forceinline__ f32x4 mm_rr8(FX x8, FY y8, int lg, f32x4 acc) {
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += 32)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x8(k0 + 8 * lg), y8(k0 + 8 * lg), acc, 0, 0, 0);
+    return acc;
+}
+
+// acc += A B over all k in [0, K) (K a multiple of 16), unrolled so that every
+// operand read is issued ahead of the products; operands outside a triangle
+// must read as zero.
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm_kc(FA a, FB b, int lg, f32x4 acc) {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            av[s] = a(k0 + 4 * s + lg);
+            bv[s] = b(k0 + 4 * s + lg);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Strictly upper 16 x 16 block t of a 4 x 4 block grid, t = 0 .. 5.
+__device__ __forceinline__ int up_r(int t) { return (t >= 3) + (t >= 5); }
+__device__ __forceinline__ int up_s(int t) { return t + 1 - 2 * (t >= 3) - (t >= 5); }
+
 // Sum over the 16 lanes that share lg (the columns of one accumulator row).
 __device__ __forceinline__ float row16_sum(float x) {
 #pragma unroll
@@ -409,6 +444,9 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
     constexpr int NT = kGradThreads, NW = kGradWaves;
     constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
     constexpr int NKB = DK / 16, NVB = DV / 16;
+    constexpr bool kSlotX = VT::kChannelDecay;   // split Gram operands staged in the slot
+    constexpr bool kMfma8 = sizeof(TI) == 2;     // bf16 inputs: bf16 products where exact
+    static_assert(kSlotX || VT::kScalarBeta, "variants without channel decay take a scalar beta");
     __shared__ float sB[4][C][CP];   // 0: T; 1: A, then Y; 2: dP; 3: dT, then dA
     __shared__ float sG[C], sbeta[C], sn[C], ssa[C], ssu[C], sdg[C], svrow[C], svcol[C], scoef[C];
     __shared__ float sdgam[DK], sdgc[DK];
@@ -448,6 +486,42 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         const TI *dSp = dS_chunks + ch * DK * DV, *dD = dD_chunks + ch * C * DV;
         auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
         auto rowc = [&](int r) { return r < nvalid ? r : nvalid - 1; };   // clamped, in bounds
+        // Operands of the Gram products and their backward: with a channel-wise
+        // decay the split, scaled rows staged in the slot; otherwise q, k and
+        // a = beta k read from the inputs (rows past T are zero).
+        auto in4 = [&](const TI *x, int r, int kk) -> f32x4 {
+            const f32x4 y = ld4(x + tok(rowc(r)) * DK + kk);
+            return r < nvalid ? y : zero4();
+        };
+        auto in1 = [&](const TI *x, int r, int col) -> float {
+            const float y = f32(x[tok(rowc(r)) * DK + col]);
+            return r < nvalid ? y : 0.f;
+        };
+        auto xq4 = [&](int r, int kk) -> f32x4 {
+            if constexpr (kSlotX) return ld4(Xq + r * DK + kk);
+            else return in4(q, r, kk);
+        };
+        auto xk4 = [&](int r, int kk) -> f32x4 {
+            if constexpr (kSlotX) return ld4(Xk + r * DK + kk);
+            else return in4(k, r, kk);
+        };
+        auto ag4 = [&](int r, int kk) -> f32x4 {
+            if constexpr (kSlotX) return ld4(Ag + r * DK + kk);
+            else if constexpr (kRowDecay) return in4(k, r, kk) * (sbeta[r] * __expf(sG[r]));
+            else return in4(k, r, kk) * sbeta[r];
+        };
+        auto xq1 = [&](int r, int col) -> float {
+            if constexpr (kSlotX) return Xq[r * DK + col];
+            else return in1(q, r, col);
+        };
+        auto xk1 = [&](int r, int col) -> float {
+            if constexpr (kSlotX) return Xk[r * DK + col];
+            else return in1(k, r, col);
+        };
+        auto xa1 = [&](int r, int col) -> float {
+            if constexpr (kSlotX) return Xa[r * DK + col];
+            else return in1(k, r, col) * sbeta[r];
+        };
 
         __syncthreads();   // the previous item is done with LDS and the slot
         // ---- A: decay prefix sums, step sizes, element-wise operands -------------
@@ -474,59 +548,75 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         if (tid < C) ssa[tid] = ssu[tid] = sdg[tid] = 0.f;
         if (tid < DK) sdgc[tid] = 0.f;
         if constexpr (VT::kKaczmarz) {
-            for (int r = wave; r < C; r += NW) {
-                float s2 = 0.f;
-                for (int i = lane; i < DK; i += kWave) {
-                    const float x = f32(k[tok(rowc(r)) * DK + i]);
-                    s2 += x * x;
-                }
-                s2 = wave_sum(s2);
-                if (lane == 0) {
-                    const float n = s2 + p.eps;
-                    sn[r] = n;
-                    sbeta[r] = r < nvalid ? p.beta[tok(r)] / n : 0.f;
-                }
+            // |k_r|^2: eight lanes per row, one pass of loads
+            static_assert(NT == 8 * C, "eight threads per row");
+            const int r = tid >> 3, part = tid & 7;
+            const TI *kr = k + tok(rowc(r)) * DK + part * (DK / 8);
+            float s2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < DK / 8; i += 4) {
+                const f32x4 x = ld4(kr + i);
+                s2 += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+            }
+            s2 += __shfl_xor(s2, 1, kWave);
+            s2 += __shfl_xor(s2, 2, kWave);
+            s2 += __shfl_xor(s2, 4, kWave);
+            if (part == 0) {
+                const float n = s2 + p.eps;
+                sn[r] = n;
+                sbeta[r] = r < nvalid ? p.beta[tok(r)] / n : 0.f;
             }
         } else if constexpr (VT::kScalarBeta) {
             if (tid < C) sbeta[tid] = tid < nvalid ? p.beta[tok(tid)] : 0.f;
         }
         __syncthreads();
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, i = idx % DK;
-            const bool ok = r < nvalid;
-            const long o = tok(rowc(r)) * DK + i;
-            const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
-            float aa;
-            if constexpr (VT::kGates) aa = ok ? p.erase_b[o] * kk : 0.f;
-            else aa = sbeta[r] * kk;
-            float gr = 0.f;
-            if constexpr (VT::kChannelDecay) {
-                gr = Gd[idx];
+        if constexpr (kSlotX) {
+            for (int idx = tid; idx < C * DK; idx += NT) {
+                const int r = idx / DK, i = idx % DK;
+                const bool ok = r < nvalid;
+                const long o = tok(rowc(r)) * DK + i;
+                const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
+                float aa;
+                if constexpr (VT::kGates) aa = ok ? p.erase_b[o] * kk : 0.f;
+                else aa = sbeta[r] * kk;
+                const float gr = Gd[idx];
                 const float e = __expf(gr - Gd[(C / 2 - 1) * DK + i]);
                 Xq[idx] = qq * e;
                 Xa[idx] = aa * e;
                 Xk[idx] = kk / e;
-            } else {
-                if constexpr (kRowDecay) gr = sG[r];
-                Xq[idx] = qq;
-                Xa[idx] = aa;
-                Xk[idx] = kk;
+                Ag[idx] = aa * __expf(gr);
             }
-            Ag[idx] = aa * __expf(gr);
+            __syncthreads();
         }
-        __syncthreads();
         // ---- B: the Gram products A (and P for a scalar decay) ---------------------
         for (int t = wave; t < (kRowDecay ? 20 : 10); t += NW) {
             const bool isP = t >= 10;
             const int R = tri_r(t % 10), Sb = tri_s(t % 10);
-            const float *X = isP ? Xq : Xa;
-            const f32x4 acc = mm_rr<DK>([&](int kk) { return ld4(X + (16 * R + l16) * DK + kk); },
-                                        [&](int kk) { return ld4(Xk + (16 * Sb + l16) * DK + kk); },
-                                        lg, zero4());
+            f32x4 acc;
+            if constexpr (kSlotX) {
+                const float *X = isP ? Xq : Xa;
+                acc = mm_rr<DK>([&](int kk) { return ld4(X + (16 * R + l16) * DK + kk); },
+                                [&](int kk) { return ld4(Xk + (16 * Sb + l16) * DK + kk); }, lg, zero4());
+            } else {
+                // q k^T or k k^T (rows of A scaled by beta below): exact products of the inputs
+                const TI *X = isP ? q : k;
+                const int ra = 16 * R + l16, rb = 16 * Sb + l16;
+                if constexpr (kMfma8) {
+                    const bf16x8 z8 = {};
+                    acc = mm_rr8<DK>(
+                        [&](int kk) { const bf16x8 x = ld8(X + tok(rowc(ra)) * DK + kk); return ra < nvalid ? x : z8; },
+                        [&](int kk) { const bf16x8 x = ld8(k + tok(rowc(rb)) * DK + kk); return rb < nvalid ? x : z8; },
+                        lg, zero4());
+                } else {
+                    acc = mm_rr<DK>([&](int kk) { return in4(X, ra, kk); }, [&](int kk) { return in4(k, rb, kk); },
+                                    lg, zero4());
+                }
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * R + 4 * lg + m, s = 16 * Sb + l16;
                 float val = acc[m];
+                if constexpr (!kSlotX) val *= isP ? 1.f : sbeta[r];
                 if constexpr (kRowDecay) val *= s <= r ? __expf(sG[r] - sG[s]) : 0.f;
                 if (isP) {
                     Pm[r * C + s] = s <= r ? val : 0.f;
@@ -540,6 +630,14 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         __syncthreads();
         // ---- C: T = (I + A)^{-1}: diagonal blocks by substitution, then the
         // off-diagonal blocks by distance, T_ij = -T_ii sum_{j<=m<i} A_im T_mj.
+        // The strictly upper blocks of T and of A/Y are read as zeros by the
+        // full-K products below.
+        for (int idx = tid; idx < 6 * 256; idx += NT) {
+            const int t = idx >> 8, e = idx & 255;
+            const int r = 16 * up_r(t) + (e >> 4), s = 16 * up_s(t) + (e & 15);
+            sT[r][s] = 0.f;
+            sA[r][s] = 0.f;
+        }
         if (tid < C) {
             const int o = 16 * (tid >> 4), cc = tid & 15;
             for (int r = 0; r < 16; ++r) {
@@ -579,56 +677,115 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             if constexpr (VT::kGates) return r < nvalid ? x * ld4(p.write_w + o) : zero4();
             else return x * sbeta[r];
         };
-        for (int t = wave; t < 2 * NKB + 10; t += NW) {
-            if (t < 2 * NKB) {
-                const int N = t >> 1, R0 = 2 * (t & 1);
-                f32x4 aq[2] = {zero4(), zero4()}, aw[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
-                const int si = 16 * N + l16;
-#pragma unroll 1
-                for (int j0 = 0; j0 < DV; j0 += 16) {
-                    const int j = j0 + 4 * lg;
-                    const f32x4 bs = ld4(S + si * DV + j), bd = ld4(dSp + si * DV + j);
+        auto ldo8 = [&](int r, int j) -> bf16x8 {
+            const bf16x8 z8 = {};
+            if constexpr (kMfma8) {
+                if (!hdo) return z8;
+                const bf16x8 x = ld8(reinterpret_cast<const bf16 *>(dO) + tok(rowc(r)) * DV + j);
+                return r < nvalid ? x : z8;
+            } else {
+                return z8;
+            }
+        };
+        auto tdv8 = [&](const TI *x, int r, int j) -> bf16x8 {
+            if constexpr (kMfma8) return ld8(reinterpret_cast<const bf16 *>(x) + r * DV + j);
+            else return bf16x8{};
+        };
+        for (int idx = tid; idx < 6 * 256; idx += NT) {
+            const int t = idx >> 8, e = idx & 255;
+            const int r = 16 * up_r(t) + (e >> 4), s = 16 * up_s(t) + (e & 15);
+            sdP[r][s] = 0.f;
+            sdT[r][s] = 0.f;
+        }
+        constexpr int NMAIN = kMfma8 ? 4 * NKB : 2 * NKB;   // C x DK tile groups
+        for (int t = wave; t < NMAIN + 10; t += NW) {
+            if (t < NMAIN) {
+                if constexpr (kMfma8) {
+                    // bf16 inputs: every operand here is stored in bf16, so the
+                    // bf16 products are exact and only the summation order differs
+                    // bf16 inputs: every operand here is stored in bf16, so the
+                    // bf16 products are exact and only the summation order differs
+                    const int N = t >> 2, R = t & 3;
+                    f32x4 aq = zero4(), aw = zero4(), ak = zero4();
+                    const int si = 16 * N + l16, r = 16 * R + l16;
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int r = 16 * (R0 + u) + l16;
-                        const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j), xl = ld4(Dl + r * DV + j);
-#pragma unroll
-                        for (int s4 = 0; s4 < 4; ++s4) {
-                            aq[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], bs[s4], aq[u], 0, 0, 0);
-                            aw[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], bs[s4], aw[u], 0, 0, 0);
-                            ak[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xl[s4], bd[s4], ak[u], 0, 0, 0);
-                        }
+                    for (int j0 = 0; j0 < DV; j0 += 32) {
+                        const int j = j0 + 8 * lg;
+                        const bf16x8 bs = tdv8(S, si, j), bd = tdv8(dSp, si, j);
+                        aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ldo8(r, j), bs, aq, 0, 0, 0);
+                        aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(dD, r, j), bs, aw, 0, 0, 0);
+                        ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(Dl, r, j), bd, ak, 0, 0, 0);
                     }
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const int o = (16 * (R0 + u) + 4 * lg + m) * DK + 16 * N + l16;
-                        dQt[o] = aq[u][m];
-                        dWm[o] = -aw[u][m];
-                        dKb[o] = ak[u][m];
+                        const int o = (16 * R + 4 * lg + m) * DK + 16 * N + l16;
+                        dQt[o] = aq[m];
+                        dWm[o] = -aw[m];
+                        dKb[o] = ak[m];
                     }
-            } else {
-                const int R = tri_r(t - 2 * NKB), Sb = tri_s(t - 2 * NKB);
-                f32x4 ap = zero4(), at = zero4();
-                const int r = 16 * R + l16, s = 16 * Sb + l16;
-#pragma unroll 2
-                for (int j0 = 0; j0 < DV; j0 += 16) {
-                    const int j = j0 + 4 * lg;
-                    const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j);
-                    const f32x4 yl = ld4(Dl + s * DV + j), yu = ldu(s, j);
+                } else {
+                    const int N = t >> 1, R0 = 2 * (t & 1);
+                    f32x4 aq[2] = {zero4(), zero4()}, aw[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
+                    const int si = 16 * N + l16;
+#pragma unroll 1
+                    for (int j0 = 0; j0 < DV; j0 += 16) {
+                        const int j = j0 + 4 * lg;
+                        const f32x4 bs = ld4(S + si * DV + j), bd = ld4(dSp + si * DV + j);
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        ap = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], yl[s4], ap, 0, 0, 0);
-                        at = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], yu[s4], at, 0, 0, 0);
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 16 * (R0 + u) + l16;
+                            const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j), xl = ld4(Dl + r * DV + j);
+#pragma unroll
+                            for (int s4 = 0; s4 < 4; ++s4) {
+                                aq[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], bs[s4], aq[u], 0, 0, 0);
+                                aw[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], bs[s4], aw[u], 0, 0, 0);
+                                ak[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(xl[s4], bd[s4], ak[u], 0, 0, 0);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const int o = (16 * (R0 + u) + 4 * lg + m) * DK + 16 * N + l16;
+                            dQt[o] = aq[u][m];
+                            dWm[o] = -aw[u][m];
+                            dKb[o] = ak[u][m];
+                        }
+                }
+            } else {
+                const int R = tri_r(t - NMAIN), Sb = tri_s(t - NMAIN);
+                const int r = 16 * R + l16, s = 16 * Sb + l16;
+                f32x4 ap = zero4(), at = zero4();
+                float cs = 1.f;   // column scale of dT_u
+                if constexpr (kMfma8 && !VT::kGates) {
+                    // dP = dO Delta^T and dT_u = dDelta (beta v)^T = (dDelta v^T) Diag(beta)
+#pragma unroll
+                    for (int j0 = 0; j0 < DV; j0 += 32) {
+                        const int j = j0 + 8 * lg;
+                        const bf16x8 vs = ld8(reinterpret_cast<const bf16 *>(v) + tok(rowc(s)) * DV + j);
+                        ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ldo8(r, j), tdv8(Dl, s, j), ap, 0, 0, 0);
+                        at = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(dD, r, j), vs, at, 0, 0, 0);
+                    }
+                    cs = sbeta[s];   // zero past T
+                } else {
+#pragma unroll 2
+                    for (int j0 = 0; j0 < DV; j0 += 16) {
+                        const int j = j0 + 4 * lg;
+                        const f32x4 xo = ldo(r, j), xd = ld4(dD + r * DV + j);
+                        const f32x4 yl = ld4(Dl + s * DV + j), yu = ldu(s, j);
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4) {
+                            ap = __builtin_amdgcn_mfma_f32_16x16x4f32(xo[s4], yl[s4], ap, 0, 0, 0);
+                            at = __builtin_amdgcn_mfma_f32_16x16x4f32(xd[s4], yu[s4], at, 0, 0, 0);
+                        }
                     }
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int rr = 16 * R + 4 * lg + m, ss = 16 * Sb + l16;
                     sdP[rr][ss] = ss <= rr ? ap[m] : 0.f;
-                    sdT[rr][ss] = at[m];
+                    sdT[rr][ss] = at[m] * cs;
                 }
             }
         }
@@ -654,7 +811,7 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m) acc[m] = sdT[16 * R + 4 * lg + m][16 * Sb + l16];
                 acc = mm_rr<DK>([&](int kk) { return ld4(dWm + (16 * R + l16) * DK + kk); },
-                                [&](int kk) { return ld4(Ag + (16 * Sb + l16) * DK + kk); }, lg, acc);
+                                [&](int kk) { return ag4(16 * Sb + l16, kk); }, lg, acc);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int r = 16 * R + 4 * lg + m, s = 16 * Sb + l16;
@@ -662,16 +819,15 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 }
             } else if (t < 10 + 4 * NKB) {
                 const int tt = t - 10, R = tt / NKB, N = tt % NKB;
-                const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
-                                        [&](int m) { return dWm[m * DK + 16 * N + l16]; }, 16 * R, C, lg,
-                                        zero4());
+                const f32x4 acc = mm_kc<C>([&](int m) { return sT[m][16 * R + l16]; },
+                                           [&](int m) { return dWm[m * DK + 16 * N + l16]; }, lg, zero4());
 #pragma unroll
                 for (int m = 0; m < 4; ++m) dAg[(16 * R + 4 * lg + m) * DK + 16 * N + l16] = acc[m];
             } else {
                 const int tt = t - 10 - 4 * NKB, R = tt / NVB, N = tt % NVB;
-                const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
-                                        [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, 16 * R, C,
-                                        lg, zero4());
+                const f32x4 acc = mm_kc<C>([&](int m) { return sT[m][16 * R + l16]; },
+                                           [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, lg,
+                                           zero4());
                 const int j = 16 * N + l16;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -695,17 +851,16 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         // ---- F: dA = -strict_lower(T^T (dT T^T)) ------------------------------------
         for (int t = wave; t < 10; t += NW) {
             const int R = tri_r(t), Nb = tri_s(t);
-            const f32x4 acc = mm_kr([&](int m) { return sdT[16 * R + l16][m]; },
-                                    [&](int m) { return sT[16 * Nb + l16][m]; }, 0, 16 * (Nb + 1), lg,
-                                    zero4());
+            const f32x4 acc = mm_kc<C>([&](int m) { return sdT[16 * R + l16][m]; },
+                                       [&](int m) { return sT[16 * Nb + l16][m]; }, lg, zero4());
 #pragma unroll
             for (int m = 0; m < 4; ++m) sY[16 * R + 4 * lg + m][16 * Nb + l16] = acc[m];
         }
         __syncthreads();
         for (int t = wave; t < 10; t += NW) {
             const int R = tri_r(t), Nb = tri_s(t);
-            const f32x4 acc = mm_kr([&](int m) { return sT[m][16 * R + l16]; },
-                                    [&](int m) { return sY[m][16 * Nb + l16]; }, 16 * R, C, lg, zero4());
+            const f32x4 acc = mm_kc<C>([&](int m) { return sT[m][16 * R + l16]; },
+                                       [&](int m) { return sY[m][16 * Nb + l16]; }, lg, zero4());
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 16 * R + 4 * lg + m, n = 16 * Nb + l16;
@@ -739,14 +894,15 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         //   dXa = dA Xk, dXq = dP Xk, dXk = dA^T Xa + dP^T Xq
         for (int t = wave; t < 4 * NKB; t += NW) {
             const int R = t / NKB, N = t % NKB, col = 16 * N + l16;
-            const f32x4 xa = mm_kr([&](int m) { return sdA[16 * R + l16][m]; },
-                                   [&](int m) { return Xk[m * DK + col]; }, 0, 16 * (R + 1), lg, zero4());
-            const f32x4 xq = mm_kr([&](int m) { return sdP[16 * R + l16][m]; },
-                                   [&](int m) { return Xk[m * DK + col]; }, 0, 16 * (R + 1), lg, zero4());
-            f32x4 xk = mm_kr([&](int m) { return sdA[m][16 * R + l16]; },
-                             [&](int m) { return Xa[m * DK + col]; }, 16 * R, C, lg, zero4());
-            xk = mm_kr([&](int m) { return sdP[m][16 * R + l16]; },
-                       [&](int m) { return Xq[m * DK + col]; }, 16 * R, C, lg, xk);
+            // full K: dA and dP are zero outside their lower triangles
+            const f32x4 xa = mm_kc<C>([&](int m) { return sdA[16 * R + l16][m]; },
+                                      [&](int m) { return xk1(m, col); }, lg, zero4());
+            const f32x4 xq = mm_kc<C>([&](int m) { return sdP[16 * R + l16][m]; },
+                                      [&](int m) { return xk1(m, col); }, lg, zero4());
+            f32x4 xk = mm_kc<C>([&](int m) { return sdA[m][16 * R + l16]; },
+                                [&](int m) { return xa1(m, col); }, lg, zero4());
+            xk = mm_kc<C>([&](int m) { return sdP[m][16 * R + l16]; },
+                          [&](int m) { return xq1(m, col); }, lg, xk);
             float e_col = 0.f;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -754,6 +910,9 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 const long o = tok(rowc(r)) * DK + col;
                 const bool ok = r < nvalid;
                 const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
+                float bg = 0.f;
+                if constexpr (VT::kGates) bg = ok ? p.erase_b[o] : 0.f;
+                const float aa = (VT::kGates ? bg : sbeta[r]) * kk;
                 float dq = xq[m], da = xa[m], dk = xk[m], dg = 0.f;
                 float gr = 0.f, gC = 0.f;
                 if constexpr (VT::kChannelDecay) {
@@ -774,13 +933,13 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 da += dag * eg;
                 dk += dkb * ekc;
                 const float kb = kk * ekc;
-                dg += dqt * qq * eg + dag * Ag[idx] - dkb * kb;
+                dg += (dqt * qq + dag * aa) * eg - dkb * kb;
                 e_col += dkb * kb;
                 float sa = 0.f;
                 if (ok) {
                     g.d_q[o] = dq;
                     if constexpr (VT::kGates) {
-                        g.d_k[o] = dk + p.erase_b[o] * da;
+                        g.d_k[o] = dk + bg * da;
                         g.d_erase_b[o] = da * kk;
                     } else if constexpr (VT::kKaczmarz) {
                         dQt[idx] = dk + sbeta[r] * da;   // completed once d eta is known
