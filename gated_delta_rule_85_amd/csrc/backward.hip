@@ -420,6 +420,34 @@ __device__ __forceinline__ f32x4 mm_kc(FA a, FB b, int lg, f32x4 acc) {
     return acc;
 }
 
+// acc += A B over k in [K0, K1) (compile-time multiples of 16), unrolled.
+template <int K0, int K1, typename FA, typename FB>
+__device__ __forceinline__ f32x4 mm_kt(FA a, FB b, int lg, f32x4 acc) {
+#pragma unroll
+    for (int k0 = K0; k0 < K1; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            av[s] = a(k0 + 4 * s + lg);
+            bv[s] = b(k0 + 4 * s + lg);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Calls f(std::integral_constant<int, R>) for a wave-uniform block row R in
+// 0 .. 3, so that triangular K ranges become compile-time constants.
+template <typename F> __device__ __forceinline__ void with_block(int R, F f) {
+    switch (R) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    default: f(std::integral_constant<int, 3>{}); break;
+    }
+}
+
 // Strictly upper 16 x 16 block t of a 4 x 4 block grid, t = 0 .. 5.
 __device__ __forceinline__ int up_r(int t) { return (t >= 3) + (t >= 5); }
 __device__ __forceinline__ int up_s(int t) { return t + 1 - 2 * (t >= 3) - (t >= 5); }
@@ -697,32 +725,36 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             sdP[r][s] = 0.f;
             sdT[r][s] = 0.f;
         }
-        constexpr int NMAIN = kMfma8 ? 4 * NKB : 2 * NKB;   // C x DK tile groups
+        constexpr int NMAIN = 2 * NKB;   // C x DK tile groups: 16 columns, two block rows
         for (int t = wave; t < NMAIN + 10; t += NW) {
             if (t < NMAIN) {
                 if constexpr (kMfma8) {
                     // bf16 inputs: every operand here is stored in bf16, so the
                     // bf16 products are exact and only the summation order differs
-                    // bf16 inputs: every operand here is stored in bf16, so the
-                    // bf16 products are exact and only the summation order differs
-                    const int N = t >> 2, R = t & 3;
-                    f32x4 aq = zero4(), aw = zero4(), ak = zero4();
-                    const int si = 16 * N + l16, r = 16 * R + l16;
-#pragma unroll
+                    const int N = t >> 1, R0 = 2 * (t & 1);
+                    f32x4 aq[2] = {zero4(), zero4()}, aw[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
+                    const int si = 16 * N + l16;
+#pragma unroll 1
                     for (int j0 = 0; j0 < DV; j0 += 32) {
                         const int j = j0 + 8 * lg;
                         const bf16x8 bs = tdv8(S, si, j), bd = tdv8(dSp, si, j);
-                        aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ldo8(r, j), bs, aq, 0, 0, 0);
-                        aw = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(dD, r, j), bs, aw, 0, 0, 0);
-                        ak = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(Dl, r, j), bd, ak, 0, 0, 0);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 16 * (R0 + u) + l16;
+                            aq[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ldo8(r, j), bs, aq[u], 0, 0, 0);
+                            aw[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(dD, r, j), bs, aw[u], 0, 0, 0);
+                            ak[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tdv8(Dl, r, j), bd, ak[u], 0, 0, 0);
+                        }
                     }
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int o = (16 * R + 4 * lg + m) * DK + 16 * N + l16;
-                        dQt[o] = aq[m];
-                        dWm[o] = -aw[m];
-                        dKb[o] = ak[m];
-                    }
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const int o = (16 * (R0 + u) + 4 * lg + m) * DK + 16 * N + l16;
+                            dQt[o] = aq[u][m];
+                            dWm[o] = -aw[u][m];
+                            dKb[o] = ak[u][m];
+                        }
                 } else {
                     const int N = t >> 1, R0 = 2 * (t & 1);
                     f32x4 aq[2] = {zero4(), zero4()}, aw[2] = {zero4(), zero4()}, ak[2] = {zero4(), zero4()};
@@ -818,16 +850,24 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                     sdT[r][s] = s < r ? acc[m] : 0.f;
                 }
             } else if (t < 10 + 4 * NKB) {
+                // T^T is upper triangular: s from the tile's own block row on
                 const int tt = t - 10, R = tt / NKB, N = tt % NKB;
-                const f32x4 acc = mm_kc<C>([&](int m) { return sT[m][16 * R + l16]; },
-                                           [&](int m) { return dWm[m * DK + 16 * N + l16]; }, lg, zero4());
+                f32x4 acc = zero4();
+                with_block(R, [&](auto Rc) {
+                    constexpr int RB = decltype(Rc)::value;
+                    acc = mm_kt<16 * RB, C>([&](int m) { return sT[m][16 * RB + l16]; },
+                                            [&](int m) { return dWm[m * DK + 16 * N + l16]; }, lg, acc);
+                });
 #pragma unroll
                 for (int m = 0; m < 4; ++m) dAg[(16 * R + 4 * lg + m) * DK + 16 * N + l16] = acc[m];
             } else {
                 const int tt = t - 10 - 4 * NKB, R = tt / NVB, N = tt % NVB;
-                const f32x4 acc = mm_kc<C>([&](int m) { return sT[m][16 * R + l16]; },
-                                           [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, lg,
-                                           zero4());
+                f32x4 acc = zero4();
+                with_block(R, [&](auto Rc) {
+                    constexpr int RB = decltype(Rc)::value;
+                    acc = mm_kt<16 * RB, C>([&](int m) { return sT[m][16 * RB + l16]; },
+                                            [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, lg, acc);
+                });
                 const int j = 16 * N + l16;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -894,15 +934,20 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         //   dXa = dA Xk, dXq = dP Xk, dXk = dA^T Xa + dP^T Xq
         for (int t = wave; t < 4 * NKB; t += NW) {
             const int R = t / NKB, N = t % NKB, col = 16 * N + l16;
-            // full K: dA and dP are zero outside their lower triangles
-            const f32x4 xa = mm_kc<C>([&](int m) { return sdA[16 * R + l16][m]; },
-                                      [&](int m) { return xk1(m, col); }, lg, zero4());
-            const f32x4 xq = mm_kc<C>([&](int m) { return sdP[16 * R + l16][m]; },
-                                      [&](int m) { return xk1(m, col); }, lg, zero4());
-            f32x4 xk = mm_kc<C>([&](int m) { return sdA[m][16 * R + l16]; },
-                                [&](int m) { return xa1(m, col); }, lg, zero4());
-            xk = mm_kc<C>([&](int m) { return sdP[m][16 * R + l16]; },
-                          [&](int m) { return xq1(m, col); }, lg, xk);
+            // dA and dP are lower triangular: rows of this block row take
+            // s < 16 (R + 1), columns take r >= 16 R
+            f32x4 xa = zero4(), xq = zero4(), xk = zero4();
+            with_block(R, [&](auto Rc) {
+                constexpr int RB = decltype(Rc)::value;
+                xa = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdA[16 * RB + l16][m]; },
+                                             [&](int m) { return xk1(m, col); }, lg, xa);
+                xq = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdP[16 * RB + l16][m]; },
+                                             [&](int m) { return xk1(m, col); }, lg, xq);
+                xk = mm_kt<16 * RB, C>([&](int m) { return sdA[m][16 * RB + l16]; },
+                                       [&](int m) { return xa1(m, col); }, lg, xk);
+                xk = mm_kt<16 * RB, C>([&](int m) { return sdP[m][16 * RB + l16]; },
+                                       [&](int m) { return xq1(m, col); }, lg, xk);
+            });
             float e_col = 0.f;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
