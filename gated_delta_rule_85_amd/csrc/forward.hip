@@ -1137,6 +1137,9 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
     const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (logical >= nwg) return;
+    // The scan is the sequential part: when the next block's prep shares the
+    // compute unit, its waves are issued first.
+    __builtin_amdgcn_s_setprio(3);
     const long bh = logical / nslice;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int col0 = (int)(logical % nslice) * SW;
