@@ -43,6 +43,11 @@
  *   erase_b   GDN-2: [B, T, H, dk]   write_w  GDN-2: [B, T, H, dv]
  *   state_in  [B, H, dk, dv] or NULL (zeros)
  *   state_out [B, H, dk, dv]         o        [B, T, H, dv]
+ *   delta     [B, T, H, dv] or NULL: the residual each token writes,
+ *             delta_t with S_t = S~_t + k_t delta_t^T (the error a layer passes
+ *             on in cross-layer routing: "Linear Attention Architectures",
+ *             the cross-layer routing section, where CLER passes the error and
+ *             CLVR the value target)
  *
  * Each entry point processes one head (b, h); heads are independent, so the
  * caller may run different heads on different threads.
@@ -61,6 +66,7 @@ typedef struct {
     const double *state_in;
     double *state_out;
     double *o;
+    double *delta;
 } oracle_problem;
 
 /* Offsets into the [B,T,H,d] token arrays and the [B,H,dk,dv] state. */
@@ -107,6 +113,17 @@ static void read_out(const oracle_problem *p, long b, long t, long h, const doub
     }
 }
 
+/* delta_t[j] = scale * (x[j] - y[j]) (y may be NULL for zero), if requested. */
+static void record_delta(const oracle_problem *p, long b, long t, long h, double scale,
+                         const double *x, const double *xw, const double *y)
+{
+    if (!p->delta)
+        return;
+    double *d = p->delta + tok(p, b, t, h, p->dv);
+    for (long j = 0; j < p->dv; ++j)
+        d[j] = scale * ((xw ? xw[j] : 1.0) * x[j] - (y ? y[j] : 0.0));
+}
+
 /* DeltaNet: S <- S - beta k (k^T S) + beta k v^T. */
 int oracle_deltanet_head(const oracle_problem *p, long b, long h)
 {
@@ -128,6 +145,7 @@ int oracle_deltanet_head(const oracle_problem *p, long b, long h)
                 acc += k[i] * S[i * dv + j];
             kS[j] = acc;
         }
+        record_delta(p, b, t, h, beta, v, NULL, kS);
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = S[i * dv + j] - beta * k[i] * kS[j] + beta * k[i] * v[j];
@@ -164,6 +182,7 @@ int oracle_gated_deltanet_head(const oracle_problem *p, long b, long h)
                 acc += k[i] * S[i * dv + j];
             kS[j] = acc;
         }
+        record_delta(p, b, t, h, beta, v, NULL, kS);
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = S[i * dv + j] - beta * k[i] * kS[j] + beta * k[i] * v[j];
@@ -201,6 +220,7 @@ int oracle_kda_head(const oracle_problem *p, long b, long h)
                 acc += k[i] * S[i * dv + j];
             kS[j] = acc;
         }
+        record_delta(p, b, t, h, beta, v, NULL, kS);
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = S[i * dv + j] - beta * k[i] * kS[j] + beta * k[i] * v[j];
@@ -242,6 +262,7 @@ int oracle_gdn2_head(const oracle_problem *p, long b, long h)
                 acc += eb[i] * k[i] * S[i * dv + j];
             r[j] = acc;
         }
+        record_delta(p, b, t, h, 1.0, v, ww, r);
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = S[i * dv + j] - k[i] * r[j] + k[i] * ww[j] * v[j];
@@ -282,6 +303,7 @@ int oracle_kla_head(const oracle_problem *p, long b, long h)
                 acc += S[i * dv + j] * k[i];
             e[j] = v[j] - acc;
         }
+        record_delta(p, b, t, h, beta, e, NULL, NULL);
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 S[i * dv + j] = S[i * dv + j] + beta * k[i] * e[j];

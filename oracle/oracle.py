@@ -50,7 +50,7 @@ class _Problem(ctypes.Structure):
         ("q", _dp), ("k", _dp), ("v", _dp),
         ("alpha", _dp), ("beta", _dp), ("erase_b", _dp), ("write_w", _dp),
         ("eps", ctypes.c_double),
-        ("state_in", _dp), ("state_out", _dp), ("o", _dp),
+        ("state_in", _dp), ("state_out", _dp), ("o", _dp), ("delta", _dp),
     ]
 
 
@@ -153,14 +153,20 @@ def frontend(variant: str, q, k, alpha=None, beta=None, erase_b=None, write_w=No
 
 def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
             write_w=None, eps: float = 0.0, state_in=None, heads=None,
-            threads: int | None = None, lib=None, flags: int = 0, decay_scale: float = 0.0):
+            threads: int | None = None, lib=None, flags: int = 0, decay_scale: float = 0.0,
+            v_route=None, want_delta: bool = False):
     """Run the sequential recurrence for ``variant``.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv]; gates as documented in
     ``gdr_oracle.c``.  ``flags`` / ``decay_scale`` select the input transforms
-    of ``frontend``.  ``heads`` optionally restricts the work to a list of
+    of ``frontend``.  ``v_route`` ([B, T, H, dv], optional) is a value routed in
+    from another layer: the recurrence uses v + v_route as its value
+    ("Linear Attention Architectures", cross-layer routing: CLVR passes the
+    value target on).  ``heads`` optionally restricts the work to a list of
     (b, h) pairs; outputs of other heads are left as NaN.  Returns
-    ``(o [B,T,H,dv], state_out [B,H,dk,dv])`` in float64.
+    ``(o [B,T,H,dv], state_out [B,H,dk,dv])`` in float64, and with
+    ``want_delta`` also the residual each token writes, delta [B,T,H,dv]
+    (S_t = S~_t + k_t delta_t^T).
     """
     if variant not in _ENTRY:
         raise ValueError(f"unknown variant {variant!r}")
@@ -168,16 +174,19 @@ def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
         q, k, alpha, beta, erase_b, write_w = frontend(variant, q, k, alpha, beta, erase_b,
                                                        write_w, flags, decay_scale)
     q, k, v = _f64(q), _f64(k), _f64(v)
+    if v_route is not None:
+        v = v + _f64(v_route)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     arrays = dict(alpha=_f64(alpha), beta=_f64(beta), erase_b=_f64(erase_b),
                   write_w=_f64(write_w), state_in=_f64(state_in))
     o = np.full((B, T, H, dv), np.nan)
     s_out = np.full((B, H, dk, dv), np.nan)
+    delta = np.full((B, T, H, dv), np.nan) if want_delta else None
     prob = _Problem(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
                     _ptr(arrays["alpha"]), _ptr(arrays["beta"]),
                     _ptr(arrays["erase_b"]), _ptr(arrays["write_w"]),
-                    float(eps), _ptr(arrays["state_in"]), _ptr(s_out), _ptr(o))
+                    float(eps), _ptr(arrays["state_in"]), _ptr(s_out), _ptr(o), _ptr(delta))
     lib = lib if lib is not None else load()
     fn = getattr(lib, _ENTRY[variant])
     todo = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
@@ -196,4 +205,4 @@ def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
             list(ex.map(run, todo))
     # keep the argument arrays alive until the calls are done
     del arrays
-    return o, s_out
+    return (o, s_out, delta) if want_delta else (o, s_out)
