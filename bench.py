@@ -15,12 +15,16 @@ and the CPU oracle timed on a bounded sample of the same work.
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
     python bench.py --long-context [--steps 20] [--warmup 3]
     python bench.py --backward [--steps 10] [--warmup 2]
+    python bench.py --routing [--steps 20] [--warmup 3]
 
 The second form measures the long-context shapes instead (131,072-token
 prefill, single-sequence decode from position 32,768, Kaczmarz LA against Gated
 DeltaNet) and prints its own JSON line.  The third measures the gradient of the
 chunked forward on the same Kaczmarz prefill (upstream gradients for o and S_T
-given) and prints its own JSON line.
+given) and prints its own JSON line.  The fourth measures what cross-layer
+routing costs on the same Kaczmarz layer: the prefill and the batch-64 decode
+step with a routed value added on load and the per-token written residual
+stored, against the plain calls.
 """
 from __future__ import annotations
 
@@ -330,6 +334,86 @@ def backward(args):
     print(json.dumps(out))
 
 
+def routing(args):
+    """Cost of cross-layer routing on the Kaczmarz layer: prefill (B=1, H=16,
+    T=65536) and one decode step at batch 64, each plain, with the residual
+    output, and with the routed value plus the residual output.  Prints one
+    JSON line."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import (WORKLOADS, make_decode_inputs, make_routed_value,
+                                                make_workload)
+
+    L = binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    wl = WORKLOADS[5]
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    log(f"{wl.name}: generating inputs and a routed value")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_workload(wl).items()}
+    vr = make_routed_value(B, T, H, dv, wl.dtype, seed=wl.seed + 2).to(dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    delta = torch.empty_like(o)
+    s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    pre = {}
+    for name, r, dl in (("plain", None, None), ("residual_out", None, delta),
+                        ("routed_value_and_residual_out", vr, delta)):
+        a = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"], None,
+                              None, d["eps"], None, s_T, v_route=r, delta_out=dl)
+        binding.check(binding.gdr_check_args(a, 0))
+        n = binding.gdr_forward_workspace_size(a)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        pre[name] = timed(lambda: binding.check(L.gdr_forward_chunked(ctypes.byref(a), ws.data_ptr(),
+                                                                     n, sh)), args.steps) * 1e3
+        del ws
+    del d, vr, o, delta
+    Bd = wl.decode["B"]
+    dd = {k: (v[0].to(dev) if isinstance(v, torch.Tensor) else v)
+          for k, v in make_decode_inputs(wl, steps=1).items()}
+    state = torch.zeros((Bd, H, dk, dv), dtype=torch.float32, device=dev)
+    od = torch.empty((Bd, 1, H, dv), dtype=torch.bfloat16, device=dev)
+    vrd = make_routed_value(Bd, 1, H, dv, wl.dtype, seed=wl.seed + 3).to(dev)
+    dld = torch.empty_like(od)
+    dec = {}
+    for name, r, dl in (("plain", None, None), ("residual_out", None, dld),
+                        ("routed_value_and_residual_out", vrd, dld)):
+        a = binding.make_args(wl.variant, dd["q"], dd["k"], dd["v"], od, dd["alpha"], dd["beta"],
+                              None, None, dd["eps"], state, state, v_route=r, delta_out=dl)
+        binding.check(binding.gdr_check_args(a, 1))
+        dec[name] = timed(lambda: binding.check(L.gdr_decode_step(ctypes.byref(a), sh)),
+                          args.steps * 20) * 1e6
+    out = {
+        "metric": "cost of cross-layer routing (routed value on load, per-token residual out)",
+        "value": pre["routed_value_and_residual_out"] / pre["plain"], "unit": "prefill time ratio",
+        "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Kaczmarz LA layer B=1 H=16 T=65536 d=128 bf16 prefill; decode "
+                               "step at batch 64 (inputs of one step, repeated)"},
+        "prefill_ms": pre, "decode_us": dec,
+        "bytes_added": {"prefill_routed_value": B * T * H * dv * 2,
+                        "prefill_residual_out": B * T * H * dv * 2,
+                        "decode_routed_value": Bd * H * dv * 2, "decode_residual_out": Bd * H * dv * 2},
+        "git": git_sha(),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +430,8 @@ def main():
                     help="measure the long-context shapes (131K prefill, decode at 32K) instead")
     ap.add_argument("--backward", action="store_true",
                     help="measure the gradient of the chunked forward on the Kaczmarz prefill")
+    ap.add_argument("--routing", action="store_true",
+                    help="measure the cost of the cross-layer routing input and output")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -358,6 +444,9 @@ def main():
         return
     if args.backward:
         backward(args)
+        return
+    if args.routing:
+        routing(args)
         return
 
     import torch

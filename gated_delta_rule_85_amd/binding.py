@@ -36,6 +36,7 @@ class GdrArgs(ctypes.Structure):
         ("alpha", _vp), ("beta", _vp), ("erase_b", _vp), ("write_w", _vp),
         ("eps", ctypes.c_float), ("decay_scale", ctypes.c_float),
         ("state_in", _vp), ("state_out", _vp), ("o", _vp),
+        ("v_route", _vp), ("delta_out", _vp),
     ]
 
 
@@ -141,14 +142,18 @@ def _ptr(t):
 
 def make_args(variant: str, q, k, v, o, alpha=None, beta=None, erase_b=None,
               write_w=None, eps: float = 0.0, state_in=None, state_out=None,
-              chunk: int = 0, flags: int = 0, decay_scale: float = 0.0) -> GdrArgs:
+              chunk: int = 0, flags: int = 0, decay_scale: float = 0.0,
+              v_route=None, delta_out=None) -> GdrArgs:
     """Fill GdrArgs from contiguous tensors q, k [B,T,H,dk], v, o [B,T,H,dv].
-    ``flags`` (GDR_FLAG_*) and ``decay_scale`` select the on-load transforms."""
+    ``flags`` (GDR_FLAG_*) and ``decay_scale`` select the on-load transforms;
+    ``v_route`` and ``delta_out`` ([B,T,H,dv], q's dtype) the cross-layer
+    routing input and output."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("alpha", alpha),
                     ("beta", beta), ("erase_b", erase_b), ("write_w", write_w),
-                    ("state_in", state_in), ("state_out", state_out)):
+                    ("state_in", state_in), ("state_out", state_out),
+                    ("v_route", v_route), ("delta_out", delta_out)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if q.dtype == torch.bfloat16:
@@ -162,7 +167,7 @@ def make_args(variant: str, q, k, v, o, alpha=None, beta=None, erase_b=None,
     return GdrArgs(VARIANTS[variant], dt, B, T, H, dk, dv, chunk, int(flags),
                    _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                    _ptr(erase_b), _ptr(write_w), float(eps), float(decay_scale),
-                   _ptr(state_in), _ptr(state_out), _ptr(o))
+                   _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(v_route), _ptr(delta_out))
 
 
 def _stream_handle(stream):
@@ -175,8 +180,9 @@ def _stream_handle(stream):
 def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
             write_w=None, eps: float = 0.0, state_in=None, output_state: bool = True,
             o=None, state_out=None, workspace=None, stream=None, flags: int = 0,
-            decay_scale: float = 0.0):
-    """Chunked forward on device tensors.  Returns (o, state_out or None)."""
+            decay_scale: float = 0.0, v_route=None, want_delta: bool = False):
+    """Chunked forward on device tensors.  Returns (o, state_out or None), and
+    with ``want_delta`` also the per-token written residual [B,T,H,dv]."""
     import torch
 
     B, T, H, dk = q.shape
@@ -185,15 +191,17 @@ def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     if output_state and state_out is None:
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device) if want_delta else None
     a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
-                  state_in, state_out, flags=flags, decay_scale=decay_scale)
+                  state_in, state_out, flags=flags, decay_scale=decay_scale,
+                  v_route=v_route, delta_out=delta)
     check(gdr_check_args(a, 0))
     need = gdr_forward_workspace_size(a)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     check(gdr_forward_chunked(a, workspace.data_ptr(), workspace.numel(),
                               _stream_handle(stream)))
-    return o, state_out
+    return (o, state_out, delta) if want_delta else (o, state_out)
 
 
 def workspace_bytes(variant: str, q, k, v) -> int:
@@ -206,15 +214,16 @@ def workspace_bytes(variant: str, q, k, v) -> int:
                 16 if variant != "deltanet" else None,
                 16 if variant != "gdn2" else None,
                 16 if variant == "gdn2" else None, 16 if variant == "gdn2" else None,
-                1e-6 if variant == "kla" else 0.0, 0.0, None, None, 32)
+                1e-6 if variant == "kla" else 0.0, 0.0, None, None, 32, None, None)
     return gdr_forward_workspace_size(a)
 
 
 def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=None,
                 write_w=None, eps: float = 0.0, o=None, state_out=None, stream=None,
-                flags: int = 0, decay_scale: float = 0.0):
+                flags: int = 0, decay_scale: float = 0.0, v_route=None, delta_out=None):
     """One decode step: q, k [B,1,H,dk], v [B,1,H,dv]; updates ``state`` in
-    place unless ``state_out`` is given.  Returns o [B,1,H,dv]."""
+    place unless ``state_out`` is given.  ``v_route`` / ``delta_out`` are the
+    routing input and output (optional).  Returns o [B,1,H,dv]."""
     import torch
 
     B, T, H, dk = q.shape
@@ -223,7 +232,7 @@ def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=Non
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
                   state, state if state_out is None else state_out, flags=flags,
-                  decay_scale=decay_scale)
+                  decay_scale=decay_scale, v_route=v_route, delta_out=delta_out)
     check(gdr_decode_step(a, _stream_handle(stream)))
     return o
 

@@ -317,9 +317,10 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
         for (long n = 0; n < NC; ++n) {
             const int buf = (int)(n & 1);
             const long ch = ch0 + NC - 1 - n;
-            TI *so = dS_chunks + ch * DK * DV + col0, *dd = dD_chunks + ch * C * DV + col0;
-            for (int e = tt; e < 16 * DK; e += 4 * kWave) so[(e >> 4) * DV + (e & 15)] = sSt[buf][e & 15][e >> 4];
-            for (int e = tt; e < 16 * C; e += 4 * kWave) dd[(e >> 4) * DV + (e & 15)] = sDt[buf][e & 15][e >> 4];
+            copy_transposed<TI, 16, DK + PT>(dS_chunks + ch * DK * DV + col0, DV, sSt[buf], DK, DK, tt,
+                                             4 * kWave);
+            copy_transposed<TI, 16, C + PT>(dD_chunks + ch * C * DV + col0, DV, sDt[buf], C, C, tt,
+                                            4 * kWave);
             __syncthreads();
             __syncthreads();
         }

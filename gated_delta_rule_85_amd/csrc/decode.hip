@@ -66,8 +66,12 @@ template <typename X, int DK> struct RowVec {
 // reduction over the key rows (r, y, ||k||^2, k . q) is a butterfly over the
 // lanes that share a column group: no LDS, no barrier.  load() only issues
 // loads and keeps raw words, so nothing waits on them until finish().
+// FL: kQkL2Norm | kRawGates, and kRouteIO when a routed value is added to v
+// or the written residual is stored (each pointer may still be NULL).
+constexpr int kRouteIO = 4;
+
 template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
-    static constexpr bool NORM = FL & kQkL2Norm, RAWG = FL & kRawGates;
+    static constexpr bool NORM = FL & kQkL2Norm, RAWG = FL & kRawGates, ROUTE = FL & kRouteIO;
     using VT = VariantTraits<V>;
     static constexpr int LPR = CW / 4;          // lanes per row
     static constexpr int RPP = kWave / LPR;     // rows per pass
@@ -76,7 +80,7 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
     f32x4 s[PASSES];
     RowVec<TI, DK> kv, qv;
     RowVec<float, DK> av, dv_;
-    TI vr[4];
+    TI vr[4], vx[ROUTE ? 4 : 1];   // vx: the routed value
     float beta, sdec;
     f32x4 wr;
 
@@ -94,6 +98,12 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
         const TI *v = static_cast<const TI *>(p.v) + bh * (long)dv + col0 + 4 * cg;
 #pragma unroll
         for (int c = 0; c < 4; ++c) vr[c] = v[c];
+        if constexpr (ROUTE) {
+            const TI *x = p.v_route ? static_cast<const TI *>(p.v_route) + bh * (long)dv + col0 + 4 * cg
+                                    : v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vx[c] = x[c];
+        }
         if constexpr (VT::kGates)
             wr = *reinterpret_cast<const f32x4 *>(p.write_w + bh * (long)dv + col0 + 4 * cg);
         const float *Sin = p.state_in + bh * DK * (long)dv + col0 + 4 * cg;
@@ -114,6 +124,10 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
         f32x4 u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) u[c] = to_f32(vr[c]);
+        if constexpr (ROUTE)
+            if (p.v_route)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) u[c] += to_f32(vx[c]);
         if constexpr (VT::kGates) {
             if constexpr (rawg)
 #pragma unroll
@@ -181,6 +195,12 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
             TI *op = static_cast<TI *>(p.o) + bh * (long)dv + col0 + 4 * cg;
 #pragma unroll
             for (int c = 0; c < 4; ++c) op[c] = from_f32<TI>(o[c]);
+            if constexpr (ROUTE)
+                if (p.delta_out) {
+                    TI *dp = static_cast<TI *>(p.delta_out) + bh * (long)dv + col0 + 4 * cg;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dp[c] = from_f32<TI>(dl[c]);
+                }
         }
         float *Sout = p.state_out + bh * DK * (long)dv + col0 + 4 * cg;
 #pragma unroll
@@ -207,7 +227,26 @@ hipError_t launch_dk(const Problem &p, hipStream_t stream) {
     constexpr int CW = 32, WAVES = 4;
     const long tiles = p.B * p.H * (p.dv / CW);
     dim3 grid((unsigned)((tiles + WAVES - 1) / WAVES));
-    switch (p.flags & (kQkL2Norm | kRawGates)) {
+    const int fl = (p.flags & (kQkL2Norm | kRawGates)) |
+                   ((p.v_route || p.delta_out) ? kRouteIO : 0);
+    switch (fl) {
+    case kRouteIO:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kRouteIO>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
+        break;
+    case kRouteIO | kQkL2Norm:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kRouteIO | kQkL2Norm>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
+        break;
+    case kRouteIO | kRawGates:
+        hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, kRouteIO | kRawGates>), grid,
+                           dim3(WAVES * kWave), 0, stream, p);
+        break;
+    case kRouteIO | kQkL2Norm | kRawGates:
+        hipLaunchKernelGGL(
+            (decode_wave_kernel<V, TI, DK, CW, WAVES, kRouteIO | kQkL2Norm | kRawGates>), grid,
+            dim3(WAVES * kWave), 0, stream, p);
+        break;
     case 0:
         hipLaunchKernelGGL((decode_wave_kernel<V, TI, DK, CW, WAVES, 0>), grid, dim3(WAVES * kWave),
                            0, stream, p);

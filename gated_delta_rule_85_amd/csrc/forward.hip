@@ -310,7 +310,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
                 const int r = r0 + e;
                 float uu = 0.f;
                 if (r < nvalid) {
-                    const float vv = to_f32(v[tok(r) * DV + j]);
+                    float vv = to_f32(v[tok(r) * DV + j]);
+                    if (p.v_route) vv += to_f32(static_cast<const TI *>(p.v_route)[tok(r) * DV + j]);
                     if constexpr (VT::kGates) {
                         const float wg = p.write_w[tok(r) * DV + j];
                         uu = (rawg ? sigmoid_f(wg) : wg) * vv;
@@ -517,7 +518,7 @@ template <int CPR, int EPC> __device__ __forceinline__ int swz(int r, int col) {
 // their loads (during the previous chunk-head's arithmetic) to their use.  The
 // loads are unconditional (rows past T read the last valid row) so that the
 // compiler's waits for them stay exact; staging masks those rows.
-template <int V, int DK, int DV> struct PrepRaw {
+template <int V, int DK, int DV, bool RT> struct PrepRaw {
     using VT = VariantTraits<V>;
     static constexpr int NT = kPrep2Threads;
     static constexpr int KC = DK / 8, VC = DV / 8;            // 16-byte chunks per row
@@ -525,7 +526,7 @@ template <int V, int DK, int DV> struct PrepRaw {
     static constexpr int NV = C * VC / NT;                     // v chunks per thread
     static constexpr int NA = VT::kChannelDecay ? C * DK / 4 / NT : 1;
     static_assert(C * KC % NT == 0 && C * VC % NT == 0 && C * DK / 4 % NT == 0, "whole passes");
-    bf16x8 k[NQ], q[NQ], v[NV];
+    bf16x8 k[NQ], q[NQ], v[NV], vr[RT ? NV : 1];   // vr: the routed value
     f32x4 eb[VT::kGates ? 2 * NQ : 1], ww[VT::kGates ? 2 * NV : 1];   // erase / write gates
     f32x4 al[NA];                                              // channel-wise alpha
     float a1, be;                                              // scalar alpha, beta / eta
@@ -554,6 +555,9 @@ template <int V, int DK, int DV> struct PrepRaw {
             const int idx = tid + n * NT;
             const int r = idx / VC, pc = idx % VC;
             v[n] = *reinterpret_cast<const bf16x8 *>(&vp[tok(r) * DV + 8 * pc]);
+            if constexpr (RT)
+                vr[n] = *reinterpret_cast<const bf16x8 *>(
+                    &static_cast<const bf16 *>(p.v_route)[tok(r) * DV + 8 * pc]);
             if constexpr (VT::kGates) {
                 ww[2 * n] = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc]);
                 ww[2 * n + 1] = *reinterpret_cast<const f32x4 *>(&p.write_w[tok(r) * DV + 8 * pc + 4]);
@@ -573,12 +577,13 @@ template <int V, int DK, int DV> struct PrepRaw {
     }
 };
 
-template <int V, int DK, int DV>
+// RT: a routed value is added to v as it is staged.
+template <int V, int DK, int DV, bool RT>
 __global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
 void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     using VT = VariantTraits<V>;
     using M = Mma<bf16>;
-    using Raw = PrepRaw<V, DK, DV>;
+    using Raw = PrepRaw<V, DK, DV, RT>;
     constexpr int NT = kPrep2Threads, NW = NT / kWave;
     constexpr int GW = VT::kChannelDecay ? DK : 1;
     constexpr int KC = DK / 8, VC = DV / 8;   // 16-byte chunks per k row / v row
@@ -709,6 +714,11 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         const int idx = tid + n * NT;
         const int r = idx / VC, pc = idx % VC;
         bf16x8 vv = r < nvalid ? raw.v[n] : zero_bf16x8();
+        if constexpr (RT) {
+            const bf16x8 vr = r < nvalid ? raw.vr[n] : zero_bf16x8();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = (bf16)((float)vv[e] + (float)vr[e]);
+        }
         if constexpr (VT::kGates) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1249,10 +1259,10 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         __syncthreads();
         for (long c = 0; c < NC; ++c) {
             const int buf = (int)(c & 1);
-            TI *so = sg + (ch0 + c) * (long)DK * DV + col0;
-            TI *dd = dg + (ch0 + c) * (long)C * DV + col0;
-            for (int e = tt; e < SW * DK; e += 4 * kWave) so[(e / SW) * DV + e % SW] = sSt[buf][e % SW][e / SW];
-            for (int e = tt; e < SW * C; e += 4 * kWave) dd[(e / SW) * DV + e % SW] = sDt[buf][e % SW][e / SW];
+            copy_transposed<TI, SW, DK + PT>(sg + (ch0 + c) * (long)DK * DV + col0, DV, sSt[buf], DK,
+                                             DK, tt, 4 * kWave);
+            copy_transposed<TI, SW, C + PT>(dg + (ch0 + c) * (long)C * DV + col0, DV, sDt[buf], C, C,
+                                            tt, 4 * kWave);
             __syncthreads();
             __syncthreads();
         }
@@ -1278,6 +1288,13 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                 for (int ks = 0; ks < KS_C; ++ks)
                     Ov = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
                 if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 16 * j + 4 * lg], Ov);
+            }
+            if (p.delta_out) {
+                // each token's written residual: the chunk's Delta, rows past T dropped
+                const long tc = (blk.c0 + c) * C;
+                copy_transposed<TI, SW, C + PT>(
+                    static_cast<TI *>(p.delta_out) + ((b * T + tc) * H + h) * (long)DV + col0,
+                    (long)H * DV, sDt[buf], C, T - tc, tid - 4 * kWave, 4 * kWave);
             }
             __syncthreads();
             __syncthreads();
@@ -1333,7 +1350,7 @@ hipError_t aux_stream(AuxStream **out) {
 
 // Workgroups of the bf16 prep kernel that the device holds at once (resident
 // slots) and its compute units, queried once per device and kernel instance.
-template <int V, int DK, int DV> hipError_t prep_slots(long *slots_out, long *cus_out) {
+template <int V, int DK, int DV, bool RT> hipError_t prep_slots(long *slots_out, long *cus_out) {
     static long slots[kMaxDevices] = {}, ncu[kMaxDevices] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1342,7 +1359,7 @@ template <int V, int DK, int DV> hipError_t prep_slots(long *slots_out, long *cu
     if (slots[dev] == 0) {
         int per_cu = 0, cus = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&chunk_prep_bf16_kernel<V, DK, DV>),
+            &per_cu, reinterpret_cast<const void *>(&chunk_prep_bf16_kernel<V, DK, DV, RT>),
             kPrep2Threads, 0);
         if (e != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
@@ -1365,13 +1382,19 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
         // beside a concurrent scan, one workgroup per compute unit, so that a
         // scan workgroup still fits on every unit.
         long slots = 0, cus = 0;
-        hipError_t e = prep_slots<V, DK, DV>(&slots, &cus);
+        const bool rt = p.v_route != nullptr;
+        hipError_t e = rt ? prep_slots<V, DK, DV, true>(&slots, &cus)
+                          : prep_slots<V, DK, DV, false>(&slots, &cus);
         if (e != hipSuccess) return e;
         const long items = (long)blk.nc * p.H * p.B;
         const long want = concurrent ? cus : slots;
         const long grid = items < want ? items : want;
-        hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV>), dim3((unsigned)grid),
-                           dim3(kPrep2Threads), 0, st, p, w, blk);
+        if (rt)
+            hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV, true>), dim3((unsigned)grid),
+                               dim3(kPrep2Threads), 0, st, p, w, blk);
+        else
+            hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV, false>), dim3((unsigned)grid),
+                               dim3(kPrep2Threads), 0, st, p, w, blk);
     } else {
         const dim3 pgrid((unsigned)blk.nc, (unsigned)p.H, (unsigned)p.B);
         hipLaunchKernelGGL((chunk_prep_kernel<V, TI, DK, DV>), pgrid, dim3(kPrepThreads), 0, st,

@@ -134,6 +134,34 @@ __device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
 }
 __device__ __forceinline__ f32x4 to_f32x4(f32x4 v) { return v; }
 
+// Copies an SW x n block kept transposed in LDS (src[j][r]: SW columns of n
+// rows) to rows r < n_valid of a row-major destination (element (r, j) at
+// dst[r * ld + j]), eight consecutive columns per thread and store.
+template <typename TI, int SW, int P>
+__device__ __forceinline__ void copy_transposed(TI *dst, long ld, const TI (*src)[P], int n,
+                                                long n_valid, int tt, int nt) {
+    static_assert(SW % 8 == 0, "eight columns per store");
+    for (int qd = tt; qd < n * (SW / 8); qd += nt) {
+        const int r = qd / (SW / 8), j0 = 8 * (qd % (SW / 8));
+        if (r >= n_valid) continue;
+        if constexpr (sizeof(TI) == 2) {
+            bf16x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = src[j0 + e][r];
+            *reinterpret_cast<bf16x8 *>(dst + r * ld + j0) = x;
+        } else {
+            f32x4 x0, x1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x0[e] = src[j0 + e][r];
+                x1[e] = src[j0 + 4 + e][r];
+            }
+            *reinterpret_cast<f32x4 *>(dst + r * ld + j0) = x0;
+            *reinterpret_cast<f32x4 *>(dst + r * ld + j0 + 4) = x1;
+        }
+    }
+}
+
 // ---- buffer loads ------------------------------------------------------------
 // The scan addresses each chunk's factors through a buffer descriptor built in
 // scalar registers from the chunk's block address, plus a per-lane offset that

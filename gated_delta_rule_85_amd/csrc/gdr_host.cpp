@@ -90,14 +90,27 @@ gdr_status check(const gdr_args *a, int mode) {
         return fail(GDR_ERR_INVALID_ARGUMENT, "eps must be >= 0");
 
     const void *ptrs[] = {a->q, a->k, a->v, a->o, a->alpha, a->beta, a->erase_b,
-                          a->write_w, a->state_in, a->state_out};
+                          a->write_w, a->state_in, a->state_out, a->v_route, a->delta_out};
     const char *names[] = {"q", "k", "v", "o", "alpha", "beta", "erase_b",
-                           "write_w", "state_in", "state_out"};
-    for (int i = 0; i < 10; ++i)
+                           "write_w", "state_in", "state_out", "v_route", "delta_out"};
+    for (int i = 0; i < 12; ++i)
         if (ptrs[i] && !aligned16(ptrs[i]))
             return fail(GDR_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
-    if (mode != 2 && (a->o == a->q || a->o == a->k || a->o == a->v))
+    if (mode == 2) {
+        if (a->v_route)
+            return fail(GDR_ERR_UNSUPPORTED, "the gradient takes v_route = NULL (pass v + v_route "
+                                             "as v; the gradient w.r.t. v_route equals d_v)");
+        return GDR_OK;
+    }
+    if (a->o == a->q || a->o == a->k || a->o == a->v || (a->v_route && a->o == a->v_route))
         return fail(GDR_ERR_INVALID_ARGUMENT, "o must not alias an input");
+    if (a->delta_out) {
+        const void *others[] = {a->q, a->k, a->v, a->o, a->alpha, a->beta, a->erase_b,
+                                a->write_w, a->state_in, a->state_out, a->v_route};
+        for (const void *x : others)
+            if (x == a->delta_out)
+                return fail(GDR_ERR_INVALID_ARGUMENT, "delta_out must not alias another argument");
+    }
     return GDR_OK;
 }
 
@@ -155,6 +168,8 @@ gdr::Problem to_problem(const gdr_args *a) {
     p.decay_scale = a->decay_scale;
     p.state_in = a->state_in; p.state_out = a->state_out;
     p.o = a->o;
+    p.v_route = a->v_route;
+    p.delta_out = a->delta_out;
     return p;
 }
 
@@ -208,6 +223,7 @@ gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *wor
     gdr::Problem p = to_problem(a);
     p.o = nullptr;
     p.state_out = nullptr;
+    p.delta_out = nullptr;
     const size_t need = gdr::backward_workspace_bytes(p);
     if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)

@@ -37,6 +37,8 @@ struct Problem {
     const float *state_in;
     float *state_out;
     void *o;
+    const void *v_route;   // added to v as it is loaded (NULL = none)
+    void *delta_out;       // per-token written residual delta_t (NULL = not written)
 };
 
 // Decode step (T == 1).  Returns the launch status.

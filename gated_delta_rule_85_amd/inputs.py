@@ -174,6 +174,12 @@ def make_raw_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0, state_scale=
     return out
 
 
+def make_routed_value(B, T, H, dv, dtype="bf16", seed=0, scale=1.0):
+    """A value routed in from another layer, N(0,1) * scale [B,T,H,dv] in ``dtype``."""
+    rng = np.random.default_rng(seed)
+    return _store(_normal(rng, (B, T, H, dv)) * scale, dtype)
+
+
 def make_upstream_grads(B, T, H, dk, dv, dtype="bf16", seed=0):
     """Upstream gradients of the forward's two outputs for a gradient check:
     d_o ~ N(0,1) [B,T,H,dv] stored in ``dtype`` and d_state_out ~ N(0,1)

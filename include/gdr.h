@@ -138,6 +138,17 @@ typedef struct gdr_args {
     const float *state_in; /* NULL = zero initial state */
     float *state_out;      /* NULL = final state not written; may equal state_in */
     void *o;               /* required */
+    /* Cross-layer routing ("Linear Attention Architectures: Mechanisms,
+     * Trade-offs, and Cross-Layer Routing", the cross-layer routing section: a
+     * lower layer hands a higher layer either its value target, CLVR, or its
+     * error, CLER). */
+    const void *v_route;   /* optional [B, T, H, dv] in `dtype`: a value routed in
+                              from another layer; the kernels use v + v_route as
+                              the value as they load it.  NULL = none */
+    void *delta_out;       /* optional output [B, T, H, dv] in `dtype`: the residual
+                              delta_t each token writes, S_t = S~_t + k_t delta_t^T
+                              (beta_t (v_t - S~_t^T k_t) for the beta variants).
+                              NULL = not written */
 } gdr_args;
 
 /* Validate `a` for gdr_forward_chunked (for_decode = 0) or gdr_decode_step

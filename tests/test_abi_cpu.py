@@ -38,8 +38,9 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_struct_layout_matches_header():
-    # int32 x2, int64 x5, int32 x2, pointers x7, float x2, pointers x3
-    assert ctypes.sizeof(binding.GdrArgs) == 8 + 40 + 8 + 7 * 8 + 8 + 3 * 8
+    # int32 x2, int64 x5, int32 x2, pointers x7, float x2, pointers x5
+    assert ctypes.sizeof(binding.GdrArgs) == 8 + 40 + 8 + 7 * 8 + 8 + 5 * 8
+    assert binding.GdrArgs.v_route.offset == 144 and binding.GdrArgs.delta_out.offset == 152
     assert binding.GdrArgs.q.offset == 56
     assert binding.GdrArgs.eps.offset == 112
 
@@ -53,7 +54,7 @@ def _args(name="gated_deltanet", B=2, T=100, H=3, dk=128, dv=64, dtype=binding.G
                         0x5000 if variant != "gdn2" else None,
                         0x6000 if variant == "gdn2" else None,
                         0x7000 if variant == "gdn2" else None,
-                        1e-6 if variant == "kla" else 0.0, 0.0, None, 0x8000, 0x9000)
+                        1e-6 if variant == "kla" else 0.0, 0.0, None, 0x8000, 0x9000, None, None)
     for key, val in over.items():
         setattr(a, key, val)
     return a
@@ -189,3 +190,19 @@ def test_backward_workspace_grows_with_length(L):
     per = (2 * (64 * 128 * 3 + 64 * 64 + 64 * 64) + 4 * 128 + 3 * 2 * 128 * 64 + 3 * 2 * 64 * 64
            + 2 * 2 * 64 * 128)
     assert abs((n2 - n1) - 2 * 3 * 10 * per) <= 8 * 256
+
+
+def test_routing_arguments(L):
+    """The routed value and the residual output are optional, aligned, and the
+    output aliases nothing; the gradient takes no routed value."""
+    assert binding.gdr_check_args(_args(v_route=0xa000, delta_out=0xb000), 0) == 0
+    assert binding.gdr_check_args(_args(T=1, state_in=0x8000, v_route=0xa000,
+                                        delta_out=0xb000), 1) == 0
+    assert binding.gdr_check_args(_args(v_route=0xa008), 0) == 1
+    assert binding.gdr_check_args(_args(delta_out=0xb004), 0) == 1
+    for alias in (0x1000, 0x3000, 0x9000, 0xa000):
+        assert binding.gdr_check_args(_args(v_route=0xa000, delta_out=alias), 0) == 1
+    assert binding.gdr_check_args(_args(o=0xa000, v_route=0xa000), 0) == 1
+    b = _args(o=None, state_out=None, v_route=0xa000)
+    assert binding.gdr_backward_chunked(b, _grads(), 0x100000, 1 << 40, 0) == 2
+    assert binding.gdr_backward_workspace_size(b) == 0
