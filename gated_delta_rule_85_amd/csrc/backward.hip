@@ -26,9 +26,10 @@
 //                         transposed factors the reverse chain reads.
 //   reverse_chain_kernel  one workgroup per (16 value columns, h, b): the
 //                         sequential pass; records dS' and dDelta per chunk.
-//   chunk_grad_kernel     persistent workgroups over chunk-heads: the rest, in
-//                         fp32 on the matrix cores (16x16x4), with the chunk's
-//                         64 x 64 matrices in LDS.
+//   chunk_grad_kernel     persistent workgroups over chunk-heads: the rest, on
+//                         fp32 matrix cores (16x16x4) and, where both operands
+//                         are stored in bf16, exact bf16 ones (16x16x32), with
+//                         the chunk's 64 x 64 matrices in LDS.
 #include <type_traits>
 
 #include "gdr_device.hpp"
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int H = (int)p.H, DV = (int)p.dv;
+    const int DV = (int)p.dv;
     const int nslice = DV / 16;
     const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
@@ -525,14 +526,6 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         auto in1 = [&](const TI *x, int r, int col) -> float {
             const float y = f32(x[tok(rowc(r)) * DK + col]);
             return r < nvalid ? y : 0.f;
-        };
-        auto xq4 = [&](int r, int kk) -> f32x4 {
-            if constexpr (kSlotX) return ld4(Xq + r * DK + kk);
-            else return in4(q, r, kk);
-        };
-        auto xk4 = [&](int r, int kk) -> f32x4 {
-            if constexpr (kSlotX) return ld4(Xk + r * DK + kk);
-            else return in4(k, r, kk);
         };
         auto ag4 = [&](int r, int kk) -> f32x4 {
             if constexpr (kSlotX) return ld4(Ag + r * DK + kk);

@@ -657,7 +657,6 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const long t0 = c * C;
     const int nvalid = (int)min((long)C, T - t0);
     const long ch = ((long)b * H + h) * blk.nbmax + (c - blk.c0);   // slot-local chunk-head
-    auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
 
     __syncthreads();   // the previous item is done with every LDS tile
     // ---- stage: the raw inputs into LDS -------------------------------------
