@@ -21,7 +21,7 @@
 // variant).  The derivation and the kernels are our own.
 //
 // Launches after the forward's own factors and per-chunk states and Deltas
-// (launch_forward_states):
+// (launch_states_prep, launch_states_scan):
 //   bw_prep_kernel        per chunk-head, parallel: P^T dO, Qt^T dO and the
 //                         transposed factors the reverse chain reads.
 //   reverse_chain_kernel  one workgroup per (16 value columns, h, b): the
@@ -93,7 +93,7 @@ constexpr int kBpThreads = 256;
 
 template <typename TI, int DK, int DV>
 __global__ __launch_bounds__(kBpThreads) void bw_prep_kernel(Problem p, ForwardStates f, Grads g,
-                                                            RevFactors rf) {
+                                                            RevFactors rf, long c0, int ncb) {
     using M = Mma<TI>;
     constexpr int NL = M::kPerLane;
     __shared__ __attribute__((aligned(16))) TI sm[C * C + C * DK + C * DV];
@@ -103,10 +103,11 @@ __global__ __launch_bounds__(kBpThreads) void bw_prep_kernel(Problem p, ForwardS
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const int H = (int)p.H;
-    const long T = p.T, NC = f.nbmax, nch = NC * p.B * p.H;
+    const long T = p.T, NC = f.nbmax, nitems = (long)ncb * p.B * p.H;
     const TI *dO = static_cast<const TI *>(g.d_o);
-    for (long ch = blockIdx.x; ch < nch; ch += gridDim.x) {
-        const long c = ch % NC, bh = ch / NC;
+    for (long item = blockIdx.x; item < nitems; item += gridDim.x) {
+        // chunks c0 .. c0 + ncb - 1 of every head
+        const long c = c0 + item % ncb, bh = item / ncb, ch = bh * NC + c;
         const int b = (int)(bh / H), h = (int)(bh % H);
         const long t0 = c * C;
         const int nvalid = (int)min((long)C, T - t0);
@@ -209,11 +210,12 @@ constexpr int kRevThreads = 512;
 // One workgroup per (16 value columns, h, b): waves 0-3 carry dS (fp32, in
 // matrix-core accumulators) backwards over the chunks; waves 4-7 copy each
 // chunk's dS' and dDelta from LDS to the workspace.
+// Chunks c0 + ncb - 1 down to c0; dS enters from ds_in (NULL = zeros) and
+// leaves to ds_out (NULL = dropped).
 template <typename TI, int DK, int DEPTH>
-__global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p, const float *gm,
-                                                                      RevFactors rf, Grads g,
-                                                                      TI *dS_chunks, TI *dD_chunks,
-                                                                      long NC) {
+__global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(
+    Problem p, const float *gm, RevFactors rf, TI *dS_chunks, TI *dD_chunks, long NC, long c0,
+    int ncb, const float *ds_in, float *ds_out) {
     using M = Mma<TI>;
     using RO = RevOps<TI, DK>;
     constexpr int KS_D = RO::KS_D, KS_C = RO::KS_C, NI = RO::NI;
@@ -231,9 +233,9 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
     if (logical >= nwg) return;
     const long bh = logical / nslice;
     const int col0 = (int)(logical % nslice) * 16;
-    const long ch0 = bh * NC;
+    const long ch0 = bh * NC + c0;
     // the n-th chunk of the reverse pass, clamped for prefetches past the end
-    auto chunk = [&](long n) { return ch0 + NC - 1 - (n < NC ? n : NC - 1); };
+    auto chunk = [&](long n) { return ch0 + ncb - 1 - (n < ncb ? n : ncb - 1); };
 
     if (wave < 4) {
         const int w = wave;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int i = 16 * (w * NI + a) + 4 * lg + m;
-                S[a][m] = g.d_state_out ? g.d_state_out[(bh * DK + i) * DV + col0 + l16] : 0.f;
+                S[a][m] = ds_in ? ds_in[(bh * DK + i) * DV + col0 + l16] : 0.f;
             }
         auto write_st = [&](int buf) {
 #pragma unroll
@@ -280,18 +282,18 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
         if constexpr (DEPTH == 2) {
             RO A, Bq;
             A.load(rf, gm, chunk(0), DV, col0, w, lane);
-            for (long n = 0; n < NC; n += 2) {
+            for (long n = 0; n < ncb; n += 2) {
                 Bq.load(rf, gm, chunk(n + 1), DV, col0, w, lane);
                 __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
                 step(A, n);
-                if (n + 1 >= NC) break;
+                if (n + 1 >= ncb) break;
                 A.load(rf, gm, chunk(n + 2), DV, col0, w, lane);
                 __builtin_amdgcn_sched_barrier(0);
                 step(Bq, n + 1);
             }
         } else {
             RO cur;
-            for (long n = 0; n < NC; ++n) {
+            for (long n = 0; n < ncb; ++n) {
                 cur.load(rf, gm, chunk(n), DV, col0, w, lane);
                 step(cur, n);
             }
@@ -299,13 +301,13 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
         // the copy waves still move the last chunk
         __syncthreads();
         __syncthreads();
-        if (g.d_state_in) {
+        if (ds_out) {
 #pragma unroll
             for (int a = 0; a < NI; ++a)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int i = 16 * (w * NI + a) + 4 * lg + m;
-                    g.d_state_in[(bh * DK + i) * DV + col0 + l16] = S[a][m];
+                    ds_out[(bh * DK + i) * DV + col0 + l16] = S[a][m];
                 }
         }
     } else {
@@ -315,9 +317,9 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(Problem p
         __syncthreads();
         __syncthreads();
         __syncthreads();
-        for (long n = 0; n < NC; ++n) {
+        for (long n = 0; n < ncb; ++n) {
             const int buf = (int)(n & 1);
-            const long ch = ch0 + NC - 1 - n;
+            const long ch = ch0 + ncb - 1 - n;
             copy_transposed<TI, 16, DK + PT>(dS_chunks + ch * DK * DV + col0, DV, sSt[buf], DK, DK, tt,
                                              4 * kWave);
             copy_transposed<TI, 16, C + PT>(dD_chunks + ch * C * DV + col0, DV, sDt[buf], C, C, tt,
@@ -468,7 +470,7 @@ __device__ __forceinline__ int tri_s(int t) { const int r = tri_r(t); return t -
 template <int V, typename TI, int DK, int DV>
 __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
     Problem p, Grads g, const TI *S_chunks, const TI *D_chunks, const TI *dS_chunks,
-    const TI *dD_chunks, float *scratch) {
+    const TI *dD_chunks, float *scratch, long c0, int ncb) {
     using VT = VariantTraits<V>;
     using Slot = GradSlot<DK>;
     constexpr int NT = kGradThreads, NW = kGradWaves;
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int H = (int)p.H;
     const long T = p.T, NC = (p.T + C - 1) / C;
-    const long nitems = NC * p.H * p.B;
+    const long nitems = (long)ncb * p.H * p.B;   // chunks c0 .. c0 + ncb - 1 of every head
     const Slot sl{scratch + (long)blockIdx.x * Slot::kFloats};
     const TI *q = static_cast<const TI *>(p.q), *k = static_cast<const TI *>(p.k);
     const TI *v = static_cast<const TI *>(p.v), *dO = static_cast<const TI *>(g.d_o);
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-        const long c = item % NC, bh = item / NC;
+        const long c = c0 + item % ncb, bh = item / ncb;
         const int b = (int)(bh / H), h = (int)(bh % H);
         const long t0 = c * C;
         const int nvalid = (int)min((long)C, T - t0);
@@ -1083,18 +1085,27 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_
     off += al((size_t)nch * DK * DV * sizeof(TI));
     float *scratch = reinterpret_cast<float *>(base + off);
 
-    ForwardStates f;
-    hipError_t e = launch_forward_states(p, ws, S_chunks, D_chunks, &f, st);
+    // One pass per kernel over all chunks, in order on `st`.  (Overlapping the
+    // sequential passes with the parallel ones on a second stream measured
+    // slower: the two kinds of kernel slow each other down more than they
+    // overlap.)  The kernels take a block of chunks [c0, c0 + ncb); here the
+    // block is the whole sequence.
+    const ForwardStates f = forward_states_ptrs(p, ws);
+    hipError_t e = launch_states_prep(p, ws, 0, (int)NC, false, st);
     if (e != hipSuccess) return e;
-    const long bp_grid = nch < 16384 ? nch : 16384;
-    hipLaunchKernelGGL((bw_prep_kernel<TI, DK, DV>), dim3((unsigned)bp_grid), dim3(kBpThreads), 0, st, p,
-                       f, g, rf);
+    if ((e = launch_states_scan(p, ws, 0, (int)NC, p.state_in, nullptr, S_chunks, D_chunks, st)) !=
+        hipSuccess)
+        return e;
+    const long items = NC * p.B * p.H;
+    hipLaunchKernelGGL((bw_prep_kernel<TI, DK, DV>), dim3((unsigned)(items < 16384 ? items : 16384)),
+                       dim3(kBpThreads), 0, st, p, f, g, rf, 0L, (int)NC);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long nwg = p.B * p.H * (DV / 16);
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
     hipLaunchKernelGGL((reverse_chain_kernel<TI, DK, DEPTH>),
                        dim3((unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds))), dim3(kRevThreads), 0, st,
-                       p, f.gam, rf, g, dS_chunks, dD_chunks, NC);
+                       p, f.gam, rf, dS_chunks, dD_chunks, NC, 0L, (int)NC, g.d_state_out,
+                       g.d_state_in);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -1106,10 +1117,9 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_
         return e;
     long slots = (long)cus * (per_cu > 0 ? per_cu : 1);
     if (slots > kGradSlots) slots = kGradSlots;
-    const long items = NC * p.B * p.H;
     hipLaunchKernelGGL((chunk_grad_kernel<V, TI, DK, DV>), dim3((unsigned)(items < slots ? items : slots)),
                        dim3(kGradThreads), 0, st, p, g, S_chunks, D_chunks, dS_chunks, dD_chunks,
-                       scratch);
+                       scratch, 0L, (int)NC);
     return hipGetLastError();
 }
 

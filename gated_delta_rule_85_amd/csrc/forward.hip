@@ -115,12 +115,20 @@ struct Plan {
 };
 
 constexpr long kBlockChunks = 64;
+constexpr long kPipelineChunks = 512;          // pipeline from this many chunks on
+constexpr size_t kSinglePassBytes = 1ull << 30;  // or when one pass's factors exceed this
 
 Plan make_plan(const Problem &p) {
     Plan q;
     q.NC = (p.T + C - 1) / C;
-    // Long sequences in bf16 are pipelined block by block; otherwise one block.
-    q.nb = (p.bf16 && q.NC > kBlockChunks) ? kBlockChunks : q.NC;
+    // Long bf16 sequences are pipelined in blocks of 64 chunks: the scan then
+    // reads factors the prep has just written, still in the caches.  Below
+    // that the prep and the scan run as one pass each, which measured faster:
+    // with few blocks there is little to overlap, and the two kernels slow
+    // each other down.  The single pass's workspace is capped.
+    const bool pipe = p.bf16 && q.NC > kBlockChunks &&
+                      (q.NC >= kPipelineChunks || ws_layout(p, q.NC).total > kSinglePassBytes);
+    q.nb = pipe ? kBlockChunks : q.NC;
     q.nblk = (q.NC + q.nb - 1) / q.nb;
     q.slot = ws_layout(p, q.nb).total;
     q.carrier = q.nblk > 1 ? align256((size_t)p.B * p.H * p.dk * p.dv * 4) : 0;
@@ -1457,34 +1465,43 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     return hipSuccess;
 }
 
-// Factors of every chunk in one workspace slot and the state entering each
-// chunk, for the gradient (no outputs).
-template <int V, typename TI, int DK, int DV>
-hipError_t states_shape(const Problem &p, void *ws, void *s_chunks, void *d_chunks,
-                        ForwardStates *out, hipStream_t stream) {
-    const long NC = (p.T + C - 1) / C;
-    const WsPtrs<TI> w = ws_ptrs<TI>(p, NC, ws);
-    *out = ForwardStates{w.W, w.Ut, w.Qt, w.Kbt, w.P, w.gam, NC};
-    const Block blk{0, (int)NC, (int)NC, p.state_in, nullptr, s_chunks, d_chunks};
-    hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
-    if (e != hipSuccess) return e;
-    return launch_scan<TI, DK, DV>(p, w, blk, stream);
+// ---- the gradient's states pass ----------------------------------------------
+// The workspace holds the factors of all chunks at their own positions: the
+// pointers of a block are shifted by its first chunk, so the kernels' block-
+// local chunk index lands on the global one.
+template <typename TI> WsPtrs<TI> shifted(WsPtrs<TI> w, const Problem &p, long c0) {
+    w.W += c0 * C * p.dk;
+    w.Ut += c0 * C * p.dv;
+    w.Qt += c0 * C * p.dk;
+    w.Kbt += c0 * C * p.dk;
+    w.P += c0 * C * C;
+    w.gam += c0 * p.dk;
+    return w;
 }
 
-template <int V, typename TI>
-hipError_t states_t(const Problem &p, void *ws, void *sc, void *dc, ForwardStates *out,
-                    hipStream_t st) {
-    if (p.dk == 128 && p.dv == 128) return states_shape<V, TI, 128, 128>(p, ws, sc, dc, out, st);
-    if (p.dk == 128 && p.dv == 64) return states_shape<V, TI, 128, 64>(p, ws, sc, dc, out, st);
-    if (p.dk == 64 && p.dv == 128) return states_shape<V, TI, 64, 128>(p, ws, sc, dc, out, st);
-    return states_shape<V, TI, 64, 64>(p, ws, sc, dc, out, st);
-}
+template <typename T> struct type_tag { using type = T; };
 
-template <int V>
-hipError_t states_v(const Problem &p, void *ws, void *sc, void *dc, ForwardStates *out,
-                    hipStream_t st) {
-    return p.bf16 ? states_t<V, bf16>(p, ws, sc, dc, out, st)
-                  : states_t<V, float>(p, ws, sc, dc, out, st);
+// Calls f(variant, dtype tag, DK, DV) with compile-time constants for p.
+template <typename F> hipError_t dispatch_shape(const Problem &p, F &&f) {
+    auto with_type = [&](auto v) {
+        auto with_dims = [&](auto ti) {
+            using I = std::integral_constant<int, 128>;
+            using J = std::integral_constant<int, 64>;
+            if (p.dk == 128 && p.dv == 128) return f(v, ti, I{}, I{});
+            if (p.dk == 128 && p.dv == 64) return f(v, ti, I{}, J{});
+            if (p.dk == 64 && p.dv == 128) return f(v, ti, J{}, I{});
+            return f(v, ti, J{}, J{});
+        };
+        return p.bf16 ? with_dims(type_tag<bf16>{}) : with_dims(type_tag<float>{});
+    };
+    switch (p.variant) {
+    case kDeltaNet: return with_type(std::integral_constant<int, kDeltaNet>{});
+    case kGatedDeltaNet: return with_type(std::integral_constant<int, kGatedDeltaNet>{});
+    case kKDA: return with_type(std::integral_constant<int, kKDA>{});
+    case kGDN2: return with_type(std::integral_constant<int, kGDN2>{});
+    case kKLA: return with_type(std::integral_constant<int, kKLA>{});
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int V, typename TI>
@@ -1506,17 +1523,39 @@ size_t forward_workspace_bytes(const Problem &p) { return make_plan(p).total; }
 
 size_t forward_states_bytes(const Problem &p) { return ws_layout(p, (p.T + C - 1) / C).total; }
 
-hipError_t launch_forward_states(const Problem &p, void *workspace, void *s_chunks,
-                                 void *d_chunks, ForwardStates *out, hipStream_t stream) {
-    switch (p.variant) {
-    case kDeltaNet: return states_v<kDeltaNet>(p, workspace, s_chunks, d_chunks, out, stream);
-    case kGatedDeltaNet:
-        return states_v<kGatedDeltaNet>(p, workspace, s_chunks, d_chunks, out, stream);
-    case kKDA: return states_v<kKDA>(p, workspace, s_chunks, d_chunks, out, stream);
-    case kGDN2: return states_v<kGDN2>(p, workspace, s_chunks, d_chunks, out, stream);
-    case kKLA: return states_v<kKLA>(p, workspace, s_chunks, d_chunks, out, stream);
-    default: return hipErrorInvalidValue;
-    }
+ForwardStates forward_states_ptrs(const Problem &p, void *workspace) {
+    const long NC = (p.T + C - 1) / C;
+    const WsLayout L = ws_layout(p, NC);
+    char *b = static_cast<char *>(workspace);
+    return ForwardStates{b + L.W, b + L.Ut, b + L.Qt, b + L.Kbt, b + L.P,
+                         reinterpret_cast<const float *>(b + L.gam), NC};
+}
+
+hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc, bool concurrent,
+                              hipStream_t stream) {
+    return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) {
+        using TI = typename decltype(ti)::type;
+        constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
+        const long NC = (p.T + C - 1) / C;
+        const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
+        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr};
+        return launch_prep<V, TI, DK, DV>(p, w, blk, concurrent, stream);
+    });
+}
+
+hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
+                              const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
+                              hipStream_t stream) {
+    return dispatch_shape(p, [&](auto, auto ti, auto dk, auto dv) {
+        using TI = typename decltype(ti)::type;
+        constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+        const long NC = (p.T + C - 1) / C;
+        const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
+        const Block blk{c0, nc, (int)NC, s_in, s_out,
+                        static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
+                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV};
+        return launch_scan<TI, DK, DV>(p, w, blk, stream);
+    });
 }
 
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream) {

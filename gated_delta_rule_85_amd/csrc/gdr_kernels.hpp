@@ -48,19 +48,26 @@ hipError_t launch_decode(const Problem &p, hipStream_t stream);
 size_t forward_workspace_bytes(const Problem &p);
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream);
 
-// The chunked forward's per-chunk factors for every chunk (in the input dtype,
-// fragment-major per chunk-head; chunk-head index = (b * H + h) * nbmax + c),
-// the state entering each chunk ([B*H][nbmax][dk][dv] in s_chunks) and each
-// chunk's Delta = U~ - W S ([B*H][nbmax][C][dv] in d_chunks), both in the
-// input dtype, as the gradient needs them.  No outputs are written.
+// The chunked forward's per-chunk factors (in the input dtype, fragment-major
+// per chunk-head; chunk-head index = (b * H + h) * nbmax + c) for all
+// nbmax = ceil(T / C) chunks of every head, as the gradient needs them.
 struct ForwardStates {
     const void *W, *Ut, *Qt, *Kbt, *P;
     const float *gam;
     long nbmax;
 };
 size_t forward_states_bytes(const Problem &p);
-hipError_t launch_forward_states(const Problem &p, void *workspace, void *s_chunks,
-                                 void *d_chunks, ForwardStates *out, hipStream_t stream);
+ForwardStates forward_states_ptrs(const Problem &p, void *workspace);
+// The gradient's states pass, one block of chunks [c0, c0 + nc) at a time:
+// the factors of the block (prep), then the scan over it from s_in (NULL =
+// zeros) to s_out (NULL = dropped), recording the state entering each chunk
+// ([B*H][nbmax][dk][dv] in s_chunks) and each chunk's Delta = U~ - W S
+// ([B*H][nbmax][C][dv] in d_chunks), both in the input dtype.  No outputs.
+hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc, bool concurrent,
+                              hipStream_t stream);
+hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
+                              const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
+                              hipStream_t stream);
 
 // Gradient of the chunked forward: upstream gradients in, input gradients out.
 struct Grads {

@@ -47,7 +47,7 @@
  *   - Every tensor pointer is device memory owned by the caller.  The library
  *     never allocates device memory, frees or synchronises; work is enqueued on
  *     the HIP stream passed as `hip_stream` (a hipStream_t; NULL = the null
- *     stream).  A long bf16 prefill (more than 64 chunks) is pipelined over a
+ *     stream).  A long bf16 prefill (512 chunks or more) is pipelined over a
  *     second, internal stream, ordered against `hip_stream` with events: the
  *     library creates that stream and five events once per host thread and
  *     device and keeps them for the life of the process.  The call still
@@ -164,10 +164,11 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
 /* Chunkwise-parallel forward over T tokens for every (b, h): writes o and,
  * if state_out != NULL, the final state.  state_out may alias state_in; no
  * other output may overlap an input.  `workspace` must be 256-byte aligned and
- * at least gdr_forward_workspace_size(a) bytes; it holds the per-chunk factors
- * of at most two blocks of 64 chunks plus a state carrier, so it does not grow
- * with T beyond 64 chunks.  Calls that share a workspace must be ordered on one
- * stream. */
+ * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
+ * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
+ * (at most 1 GiB; about 56 KB per chunk and head at dk = dv = 128 in bf16),
+ * else of two blocks of 64 chunks plus a state carrier, so it stops growing
+ * with T.  Calls that share a workspace must be ordered on one stream. */
 gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
                                void *hip_stream);
 

@@ -75,8 +75,8 @@ def test_forward_transforms_head_sizes(variant, dk, dv):
 
 @pytest.mark.parametrize("variant", ["kla", "gdn2"])
 def test_forward_transforms_pipelined(variant):
-    """More than 64 chunks: the blocked two-stream path, sampled heads."""
-    _check_forward(variant, "bf16", L2 | RAW, B=1, T=8292, H=4, seed=21,
+    """514 chunks: the blocked two-stream path, sampled heads."""
+    _check_forward(variant, "bf16", L2 | RAW, B=1, T=64 * 64 * 8 + 100, H=4, seed=21,
                    heads=[(0, 0), (0, 3)])
 
 

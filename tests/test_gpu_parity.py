@@ -173,11 +173,12 @@ def test_heads_and_batches_are_independent():
 
 # ------------------------------------------------- pipelined (multi-block) forward
 
+@pytest.mark.parametrize("T", [64 * 64 * 8 + 100, 64 * 64 * 2 + 100], ids=["pipelined", "one_pass"])
 @pytest.mark.parametrize("variant", ["gdn2", "kla", "deltanet"])
-def test_forward_pipelined_blocks(variant):
-    """Long bf16 sequences run as blocks of 64 chunks on two streams: three
-    blocks with a ragged last chunk, a non-zero initial state."""
-    T = 64 * 64 * 2 + 100
+def test_forward_pipelined_blocks(variant, T):
+    """Long bf16 sequences: from 512 chunks on as blocks of 64 chunks on two
+    streams (nine blocks here), below that as one pass (130 chunks); a ragged
+    last chunk and a non-zero initial state."""
     announce(f"pipelined forward {variant} T={T}")
     inp = make_inputs(variant, 1, T, 2, 128, 128, "bf16", seed=77, state_scale=0.5)
     o, s = gpu_forward(variant, to_dev(inp))
@@ -189,12 +190,13 @@ def test_forward_pipelined_blocks(variant):
 
 
 def test_forward_pipelined_split_resume():
-    """A pipelined pass split at a block boundary equals the whole pass."""
-    T = 64 * 64 * 3
+    """A pipelined pass (576 chunks) equals the same sequence split in two
+    one-pass calls, the second resuming from the first's final state."""
+    T = 64 * 64 * 9
     inp = make_inputs("gated_deltanet", 1, T, 2, 128, 128, "bf16", seed=79, state_scale=0.2)
     d = to_dev(inp)
     o_all, s_all = gpu_forward("gated_deltanet", d)
-    cut = 64 * 64 + 64 * 5
+    cut = 64 * 64 * 4 + 64 * 5
     part = lambda a, b_: {k: (v[:, a:b_].contiguous() if isinstance(v, torch.Tensor) and k != "state_in"
                               else v) for k, v in d.items()}
     o1, s1 = gpu_forward("gated_deltanet", part(0, cut))
@@ -204,9 +206,10 @@ def test_forward_pipelined_split_resume():
 
 
 def test_forward_graph_capture_replays():
-    """The two-stream pipelined forward captured into a HIP graph and replayed
-    several times, with other work in between, matches the eager result."""
-    T = 64 * 64 * 2 + 64
+    """The two-stream pipelined forward (513 chunks) captured into a HIP graph
+    and replayed several times, with other work in between, matches the eager
+    result."""
+    T = 64 * 64 * 8 + 64
     inp = make_inputs("kla", 1, T, 2, 128, 128, "bf16", seed=81, state_scale=0.3)
     d = to_dev(inp)
     o_ref, s_ref = gpu_forward("kla", d)
