@@ -46,20 +46,26 @@ def test_workload_forward_sampled_heads(wid):
 @pytest.mark.parametrize("wid", [5, 6, 7])
 def test_workload_decode_from_prefill_state(wid):
     """Decode from the state a prefill leaves at the workload's decode
-    position, broadcast over the decode batch; both sides start from the same
-    fp32 state tensor."""
+    position, broadcast over the decode batch.  Each side runs its own chain
+    (prefill, then the decode steps) from the same seeded inputs; the oracle
+    follows the sampled heads only."""
     wl = WORKLOADS[wid]
     steps = 4
     pos = wl.decode.get("position", wl.T)
     Bd = wl.decode["B"]
     announce(f"workload {wid} decode: prefill of {pos} tokens -> {steps} decode steps at batch {Bd}")
+    heads = sorted({(0, 0), (Bd // 5, 5), (Bd - 1, wl.H - 1)})
     inp = make_workload(wl, T=pos)
     d = to_dev(inp)
     _, s_T = binding.forward(wl.variant, d["q"], d["k"], d["v"], alpha=d["alpha"],
                              beta=d["beta"], eps=d["eps"])
-    del d, inp
+    del d
+    _, s_ref = oracle.forward(wl.variant, inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                              beta=inp["beta"], eps=inp["eps"],
+                              heads=sorted({(0, h) for _, h in heads}))
+    del inp
     state = s_T.expand(Bd, *s_T.shape[1:]).contiguous()
-    state0 = state.cpu().numpy().astype(np.float64)
+    ref_state = np.broadcast_to(s_ref, (Bd,) + s_ref.shape[1:]).copy()
     dec = make_decode_inputs(wl, steps=steps)
     dd = to_dev(dec)
     outs = []
@@ -68,8 +74,6 @@ def test_workload_decode_from_prefill_state(wid):
                                         alpha=dd["alpha"][st], beta=dd["beta"][st],
                                         eps=dd["eps"]))
     torch.cuda.synchronize()
-    heads = sorted({(0, 0), (Bd // 5, 5), (Bd - 1, wl.H - 1)})
-    ref_state = state0
     for st in range(steps):
         o_ref, ref_state = oracle.forward(wl.variant, dec["q"][st], dec["k"][st], dec["v"][st],
                                           alpha=dec["alpha"][st], beta=dec["beta"][st],
@@ -78,10 +82,10 @@ def test_workload_decode_from_prefill_state(wid):
         for b, h in heads:
             e = rel_err(o_gpu[b:b + 1, :, h:h + 1], o_ref[b:b + 1, :, h:h + 1], (0, 2))
             assert e < 2e-2, (st, b, h, e)
-        # continue the reference from the exact state of the sampled heads only
-        ref_state = np.where(np.isnan(ref_state), state0, ref_state)
+        # heads outside the sample are NaN in the reference; keep them finite
+        ref_state = np.nan_to_num(ref_state)
     s_gpu = state.cpu().numpy()
     for b, h in heads:
         e = rel_err(s_gpu[b:b + 1, h:h + 1], ref_state[b:b + 1, h:h + 1], (0, 1))
         announce(f"  decode head ({b},{h}): state rel_err {e:.3e}")
-        assert e < 1e-4
+        assert e < 2e-2
