@@ -16,6 +16,7 @@ and the CPU oracle timed on a bounded sample of the same work.
     python bench.py --long-context [--steps 20] [--warmup 3]
     python bench.py --backward [--steps 10] [--warmup 2]
     python bench.py --routing [--steps 20] [--warmup 3]
+    python bench.py --cold-decode [--steps 200] [--warmup 1]
 
 The second form measures the long-context shapes instead (131,072-token
 prefill, single-sequence decode from position 32,768, Kaczmarz LA against Gated
@@ -24,7 +25,9 @@ chunked forward on the same Kaczmarz prefill (upstream gradients for o and S_T
 given) and prints its own JSON line.  The fourth measures what cross-layer
 routing costs on the same Kaczmarz layer: the prefill and the batch-64 decode
 step with a routed value added on load and the per-token written residual
-stored, against the plain calls.
+stored, against the plain calls.  The fifth times single decode launches with
+the state evicted from the last-level cache before each one, beside the same
+launches warm, and measures the box's own copy bandwidth and GEMM rate.
 """
 from __future__ import annotations
 
@@ -414,6 +417,115 @@ def routing(args):
     print(json.dumps(out))
 
 
+def cold_decode(args):
+    """Decode step of the Kaczmarz layer at batch 64 with the state cold: the
+    64 MiB state fits in the 256 MiB last-level cache (MALL), so back-to-back
+    steps find it there.  Here every step is preceded by a read sweep over a
+    1 GiB buffer, which evicts the state to HBM, and each decode launch is timed
+    on its own with HIP events on the launch stream; the same per-launch timing
+    without the sweep gives the warm figure.  Also measures the box's own
+    peaks: HBM copy and read bandwidth over buffers far larger than the MALL,
+    and a large bf16 library GEMM.  Prints one JSON line."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import WORKLOADS, make_decode_inputs, make_workload
+
+    L = binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    wl = WORKLOADS[5]
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    Bd, n = wl.decode["B"], args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # The decode starts from the prefill's final state, as in the main bench.
+    log("prefill for the starting state")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_workload(wl).items()}
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    fa = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"], None,
+                           None, d["eps"], None, s_T)
+    nws = binding.gdr_forward_workspace_size(fa)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    binding.check(L.gdr_forward_chunked(ctypes.byref(fa), ws.data_ptr(), nws, sh))
+    torch.cuda.synchronize()
+    del d, o, ws
+    dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+          for k, v in make_decode_inputs(wl, steps=n).items()}
+    state = torch.empty((Bd, H, dk, dv), dtype=torch.float32, device=dev)
+    state.copy_(s_T.expand(Bd, H, dk, dv))
+    o_dec = torch.empty((n, Bd, 1, H, dv), dtype=torch.bfloat16, device=dev)
+    dargs = [binding.make_args(wl.variant, dd["q"][s], dd["k"][s], dd["v"][s], o_dec[s],
+                               dd["alpha"][s], dd["beta"][s], None, None, dd["eps"], state, state)
+             for s in range(n)]
+    for a in dargs:
+        binding.check(binding.gdr_check_args(a, 1))
+    flush = torch.ones(256 << 20, dtype=torch.float32, device=dev)   # 1 GiB
+
+    def per_launch(cold):
+        evs = [(ev(), ev()) for _ in range(n)]
+        for s in range(n):
+            if cold:
+                flush.sum()
+            evs[s][0].record(stream)
+            binding.check(L.gdr_decode_step(ctypes.byref(dargs[s]), sh))
+            evs[s][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return dict(median_us=us[n // 2], mean_us=sum(us) / n, min_us=us[0], max_us=us[-1])
+
+    for _ in range(args.warmup):
+        per_launch(True)
+    log(f"{n} decode launches each, warm and cold")
+    warm = per_launch(False)
+    cold = per_launch(True)
+    db = decode_bytes(Bd, H, dk, dv)
+    for r in (warm, cold):
+        r["GBps_algorithmic"] = db / (r["median_us"] * 1e-6) / 1e9
+        r["hbm_frac"] = db / (r["median_us"] * 1e-6) / PEAK_HBM
+
+    # Box-measured peaks.
+    def rate(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    log("measuring HBM copy / read bandwidth and a bf16 GEMM")
+    src = torch.ones(512 << 20, dtype=torch.float32, device=dev)   # 2 GiB
+    dst = torch.empty_like(src)
+    t_copy = rate(lambda: dst.copy_(src))
+    t_read = rate(lambda: src.sum())
+    del src, dst
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    bt = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    t_mm = rate(lambda: torch.mm(a, bt), reps=10)
+    peaks = dict(copy_GBps=2 * (2 << 30) / t_copy / 1e9, read_GBps=(2 << 30) / t_read / 1e9,
+                 bf16_gemm_8192_TFLOPs=2 * 8192 ** 3 / t_mm / 1e12,
+                 note="copy counts bytes read plus written over 2 GiB buffers; GEMM is "
+                      "torch.mm (hipBLASLt) at 8192^3")
+    out = {
+        "metric": "decode step with the state evicted from the last-level cache",
+        "value": cold["median_us"], "unit": "us per decode step (median, cold state)",
+        "higher_is_better": False, "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Kaczmarz LA decode step, batch 64, 16 heads, d=128, fp32 state "
+                               "from the T=65536 prefill; a 1 GiB read sweep before each cold "
+                               "launch"},
+        "warm": warm, "cold": cold, "algorithmic_bytes": db,
+        "measured_peaks": peaks, "git": git_sha(),
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -432,6 +544,9 @@ def main():
                     help="measure the gradient of the chunked forward on the Kaczmarz prefill")
     ap.add_argument("--routing", action="store_true",
                     help="measure the cost of the cross-layer routing input and output")
+    ap.add_argument("--cold-decode", action="store_true",
+                    help="time decode launches one by one with the state evicted from the "
+                         "last-level cache, and measure the box's copy / GEMM peaks")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -447,6 +562,9 @@ def main():
         return
     if args.routing:
         routing(args)
+        return
+    if args.cold_decode:
+        cold_decode(args)
         return
 
     import torch
@@ -575,11 +693,13 @@ def main():
     fb = forward_bytes(B, T, H, dk, dv)
     db = decode_bytes(Bd, H, dk, dv)
     dec_bw = db / dec_s
-    prefill = dict(tokens_per_s=B * T / fwd_s, ms=fwd_s * 1e3,
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    prefill = dict(tokens_per_s=B * T / fwd_s, ms=fwd_s * 1e3, ms_median=med(fwd_ms),
                    tflops=fl / fwd_s / 1e12, mfma_frac=fl / fwd_s / PEAK_BF16,
                    hbm_GBps=fb / fwd_s / 1e9, hbm_frac=fb / fwd_s / PEAK_HBM,
                    algorithmic_flop=fl, algorithmic_bytes=fb)
     decode = dict(tokens_per_s=Bd / dec_s, us_per_step=dec_s * 1e6,
+                  us_per_step_median=med(dec_ms) * 1e3 / Sd,
                   GBps=dec_bw / 1e9, hbm_frac=dec_bw / PEAK_HBM, algorithmic_bytes=db,
                   steps_per_bench_step=Sd, batch=Bd)
     t_dec_total = dec_s * Sd

@@ -166,7 +166,7 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
  * other output may overlap an input.  `workspace` must be 256-byte aligned and
  * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
  * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
- * (at most 1 GiB; about 56 KB per chunk and head at dk = dv = 128 in bf16),
+ * (at most 1 GiB; 72.5 KB per chunk and head at dk = dv = 128 in bf16),
  * else of two blocks of 64 chunks plus a state carrier, so it stops growing
  * with T.  Calls that share a workspace must be ordered on one stream. */
 gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
