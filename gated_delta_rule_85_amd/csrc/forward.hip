@@ -74,6 +74,13 @@ struct Block {
     float *s_out;
     void *s_chunks;      // states-only scans: the state entering each chunk, [B*H][nbmax][dk][dv]
     void *d_chunks;      //   and each chunk's Delta, [B*H][nbmax][C][dv], both in the input dtype
+    // bf16 prep beside a concurrent scan: after its first item, a workgroup
+    // takes its next one from a shared ticket counter (NULL = every
+    // gridDim.x-th item).  Every item processed draws one ticket, so a launch
+    // advances the counter by exactly its item count; ticket_base is the
+    // counter's value when the launch starts.
+    unsigned *ticket;
+    unsigned ticket_base;
 };
 
 struct WsLayout {
@@ -111,7 +118,7 @@ template <typename TI> WsPtrs<TI> ws_ptrs(const Problem &p, long nbmax, void *ba
 // state carrier passes the state from block to block.
 struct Plan {
     long NC, nb, nblk;
-    size_t slot, carrier, total;
+    size_t slot, carrier, ticket, total;
 };
 
 constexpr long kBlockChunks = 64;
@@ -132,7 +139,8 @@ Plan make_plan(const Problem &p) {
     q.nblk = (q.NC + q.nb - 1) / q.nb;
     q.slot = ws_layout(p, q.nb).total;
     q.carrier = q.nblk > 1 ? align256((size_t)p.B * p.H * p.dk * p.dv * 4) : 0;
-    q.total = (q.nblk > 1 ? 2 : 1) * q.slot + q.carrier;
+    q.ticket = q.nblk > 1 ? 256 : 0;   // the prep's ticket counter
+    q.total = (q.nblk > 1 ? 2 : 1) * q.slot + q.carrier + q.ticket;
     return q;
 }
 
@@ -630,6 +638,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const unsigned nc = (unsigned)blk.nc, nitems = nc * (unsigned)(p.H * p.B);
     unsigned item = blockIdx.x;
     if (item >= nitems) return;
+    __shared__ unsigned sNext;   // the item after the current one
     auto chunk_of = [&](unsigned it) { return blk.c0 + (long)(it % nc); };
     auto head_of = [&](unsigned it) { return (int)((it / nc) % (unsigned)H); };
     auto row_of = [&](unsigned it) { return (int)((it / nc) / (unsigned)H); };
@@ -652,7 +661,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         }
     };
 
-    for (; item < nitems; item += gridDim.x) {
+    for (;;) {
     // The thread index is re-derived opaquely each item, so that the many
     // per-thread LDS and workspace offsets are recomputed where they are used
     // instead of being hoisted out of the loop and held in registers.
@@ -667,6 +676,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const long ch = ((long)b * H + h) * blk.nbmax + (c - blk.c0);   // slot-local chunk-head
 
     __syncthreads();   // the previous item is done with every LDS tile
+    // The next item: a ticket drawn now (its latency hides behind the staging,
+    // after which it is published) or the static stride.
+    unsigned tk = 0;
+    if (blk.ticket && tid == 0) tk = atomicAdd(blk.ticket, 1u);
     // ---- stage: the raw inputs into LDS -------------------------------------
     // Rows past T were loaded from the last valid row; they stage as zero
     // (k, v, b (.) k, beta) and as no decay.  The on-load transforms happen
@@ -758,6 +771,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     }
     if constexpr (VT::kScalarBeta)
         if (tid < C) sBeta[tid] = tid < nvalid ? (rawg ? sigmoid_f(raw.be) : raw.be) : 0.f;
+    if (tid == 0) sNext = blk.ticket ? gridDim.x + (tk - blk.ticket_base) : item + gridDim.x;
     __syncthreads();
 
     // ---- gates: decay prefix sums (of the staged logs); KLA step size --------
@@ -875,8 +889,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // Every raw register is consumed: the next item's loads go out now and
     // arrive during phases 2-4 (the last item reloads itself, from L2, so that
     // the issue is unconditional and the compiler's waits stay exact).
+    const unsigned next_item = sNext;
     {
-        const unsigned next = item + gridDim.x < nitems ? item + gridDim.x : item;
+        const unsigned next = next_item < nitems ? next_item : item;
         raw.issue(p, chunk_of(next), head_of(next), row_of(next), tid);
     }
     __syncthreads();
@@ -1064,6 +1079,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             store4(ws.Ut + ch * DV * C + ufrag_off(16 * nj + l16, 16 * R + 4 * lg), acc);
         }
     }
+    item = next_item;
+    if (item >= nitems) break;
     }   // items
 }
 
@@ -1330,6 +1347,12 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
 
 // ---- dispatch -----------------------------------------------------------------
 
+// Clears the prep's ticket counter at the start of a pipelined forward (a
+// kernel rather than a memset node, so that the call can be graph-captured).
+__global__ void zero_ticket_kernel(unsigned *t) {
+    if (threadIdx.x == 0) *t = 0u;
+}
+
 // Internal helper stream and events of the calling host thread, one set per
 // device, created on first use and kept for the life of the process.
 struct AuxStream {
@@ -1434,7 +1457,8 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     char *base = static_cast<char *>(ws);
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
-        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr, nullptr};
+        const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr, nullptr,
+                        nullptr, 0u};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
@@ -1446,15 +1470,26 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     hipError_t e = aux_stream(&aux);
     if (e != hipSuccess) return e;
     float *carrier = reinterpret_cast<float *>(base + 2 * q.slot);
+    unsigned *ticket = reinterpret_cast<unsigned *>(base + 2 * q.slot + q.carrier);
+    hipLaunchKernelGGL(zero_ticket_kernel, dim3(1), dim3(64), 0, stream, ticket);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    unsigned ticket_base = 0;
     if ((e = hipEventRecord(aux->start, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(aux->s, aux->start, 0)) != hipSuccess) return e;
     for (long i = 0; i < q.nblk; ++i) {
         const int slot = (int)(i & 1);
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base + slot * q.slot);
         const long c0 = i * q.nb;
-        const Block blk{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
+        const int nc = (int)min(q.nb, q.NC - c0);
+        // Scalar-decay preps share compute units with the scan and take items
+        // from the ticket counter, so the units without a scan take more of
+        // them.  A channel-decay prep fills a unit's registers and never
+        // shares one; its static split measured faster.
+        const Block blk{c0, nc, (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
-                        nullptr, nullptr};
+                        nullptr, nullptr, VariantTraits<V>::kChannelDecay ? nullptr : ticket,
+                        ticket_base};
+        ticket_base += (unsigned)(nc * p.H * p.B);
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, true, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
@@ -1538,7 +1573,7 @@ hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc
         constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
         const long NC = (p.T + C - 1) / C;
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
-        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr};
+        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u};
         return launch_prep<V, TI, DK, DV>(p, w, blk, concurrent, stream);
     });
 }
@@ -1553,7 +1588,7 @@ hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
         const Block blk{c0, nc, (int)NC, s_in, s_out,
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
-                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV};
+                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u};
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
     });
 }
