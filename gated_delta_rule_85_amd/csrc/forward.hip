@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     constexpr int GW = VT::kChannelDecay ? DK : 1;         // width of a g row
     constexpr int NL = M::kPerLane;
 
-    __shared__ float sG[C][GW];
+    __shared__ __attribute__((aligned(16))) float sG[C][GW];
     __shared__ float sBeta[C];
     __shared__ __attribute__((aligned(16))) TI sAt[DK][C + PT];   // (a (.) e^{g})^T
     __shared__ __attribute__((aligned(16))) TI sUt[DV][C + PT];   // U^T
@@ -644,21 +644,25 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     auto row_of = [&](unsigned it) { return (int)((it / nc) / (unsigned)H); };
     Raw raw;
     raw.issue(p, chunk_of(item), head_of(item), row_of(item), (int)threadIdx.x);
-    // q rows of this wave's Gram tiles, for phase 2 (L2 hits); rows past T
-    // read the last valid row, whose products only reach rows never stored.
-    bf16x8 qf[2][DK / 32];
+    // Gram tiles of this wave: row block gR, column blocks gS0 .. gS0+gN-1.
+    // The ten lower-triangular 16x16 tiles are grouped so that a wave's tiles
+    // share their q rows: (3,0-1) (3,2-3) (2,0-1) (2,2) (1,0-1) (0,0); waves
+    // 6 and 7 have none.
+    const int gR = wave < 2 ? 3 : (wave < 4 ? 2 : (wave == 4 ? 1 : 0));
+    const int gS0 = (wave == 1 || wave == 3) ? 2 : 0;
+    const int gN = wave < 6 ? ((wave == 3 || wave == 5) ? 1 : 2) : 0;
+    // q rows of block gR, for phase 2 (L2 hits); rows past T read the last
+    // valid row, whose products only reach rows never stored.  Every wave
+    // loads them, so that the loads and their waits are unconditional.
+    bf16x8 qf[DK / 32];
     auto load_qf = [&](long c, int h, int b, int l16, int lg) {
         const long t0 = c * C;
         const int last = (int)min((long)C, T - t0) - 1;
+        const int rr = min(16 * gR + l16, last);
+        const long row = ((long)b * T + t0 + rr) * H + h;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tl = wave + u * NW;
-            const int rr = min(16 * lower_r(tl < 10 ? tl : 0) + l16, last);
-            const long row = ((long)b * T + t0 + rr) * H + h;
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                qf[u][ks] = *reinterpret_cast<const bf16x8 *>(&q[row * DK + 32 * ks + 8 * lg]);
-        }
+        for (int ks = 0; ks < DK / 32; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8 *>(&q[row * DK + 32 * ks + 8 * lg]);
     };
 
     for (;;) {
@@ -837,53 +841,74 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
             }
         }
-        // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace
-#pragma unroll
-        for (int n = 0; n < (DK * (C / 8) + NT - 1) / NT; ++n) {
-            // Unrolled, so that the waits for loads in flight stay exact.
-            const int idx = tid + n * NT;
-            if (idx >= DK * (C / 8)) break;
-            const int i = idx % DK, r0 = 8 * (idx / DK);
-            const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
-            float at[8], kb[8];
+        // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace.
+        // A thread transposes two columns of eight rows: its eight 4-byte
+        // reads are all issued before any arithmetic, so they wait once.
+        static_assert(DK / 2 * (C / 8) <= NT && DV / 2 * (C / 8) <= NT, "one pass");
+        if (tid < DK / 2 * (C / 8)) {
+            const int i0 = 2 * (tid % (DK / 2)), r0 = 8 * (tid / (DK / 2));
+            uint32_t kw[8], aw[VT::kGates ? 8 : 1];
+            float2 gw[VT::kChannelDecay ? 8 : 1];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int r = r0 + e;
-                const float kk = (float)sK[kx(r, i)];
-                float a;
-                if constexpr (VT::kGates) a = (float)sAg[kx(r, i)];
-                else a = sBeta[r] * kk;
-                float eg = 1.f, egc = 1.f;
-                if constexpr (VT::kChannelDecay) {
-                    const float g = sG[r][i];
-                    eg = __expf(g);
-                    egc = __expf(gC - g);
-                } else if constexpr (kRowDecay) {
-                    eg = sEg[r];
-                    egc = sEgc[r];
+                kw[e] = *reinterpret_cast<const uint32_t *>(&sK[kx(r0 + e, i0)]);
+                if constexpr (VT::kGates)
+                    aw[e] = *reinterpret_cast<const uint32_t *>(&sAg[kx(r0 + e, i0)]);
+                if constexpr (VT::kChannelDecay)
+                    gw[e] = *reinterpret_cast<const float2 *>(&sG[r0 + e][i0]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int i = i0 + cc;
+                const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
+                // element cc of a word holding two bf16 (little-endian)
+                auto half = [&](uint32_t w) {
+                    return __uint_as_float(cc ? (w & 0xffff0000u) : (w << 16));
+                };
+                float at[8], kb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = r0 + e;
+                    const float kk = half(kw[e]);
+                    float a;
+                    if constexpr (VT::kGates) a = half(aw[e]);
+                    else a = sBeta[r] * kk;
+                    float eg = 1.f, egc = 1.f;
+                    if constexpr (VT::kChannelDecay) {
+                        const float g = cc ? gw[e].y : gw[e].x;
+                        eg = __expf(g);
+                        egc = __expf(gC - g);
+                    } else if constexpr (kRowDecay) {
+                        eg = sEg[r];
+                        egc = sEgc[r];
+                    }
+                    at[e] = a * eg;
+                    kb[e] = kk * egc;
                 }
-                at[e] = a * eg;
-                kb[e] = kk * egc;
+                store8(&sAt[tx(i, r0)], at);
+                store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
+                if (r0 == 0) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
             }
-            store8(&sAt[tx(i, r0)], at);
-            store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
-            if (idx < DK) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
         }
-        // U^T into LDS
+        // U^T into LDS, two columns of eight rows per thread in the same way
+        if (tid < DV / 2 * (C / 8)) {
+            const int j0 = 2 * (tid % (DV / 2)), r0 = 8 * (tid / (DV / 2));
+            uint32_t vw[8];
 #pragma unroll
-        for (int n = 0; n < (DV * (C / 8) + NT - 1) / NT; ++n) {
-            // Unrolled, so that the waits for loads in flight stay exact.
-            const int idx = tid + n * NT;
-            if (idx >= DV * (C / 8)) break;
-            const int j = idx % DV, r0 = 8 * (idx / DV);
-            float u[8];
+            for (int e = 0; e < 8; ++e) vw[e] = *reinterpret_cast<const uint32_t *>(&sV[vx(r0 + e, j0)]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float vv = (float)sV[vx(r0 + e, j)];
-                if constexpr (VT::kGates) u[e] = vv;
-                else u[e] = sBeta[r0 + e] * vv;
+            for (int cc = 0; cc < 2; ++cc) {
+                float u[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float vv = __uint_as_float(cc ? (vw[e] & 0xffff0000u) : (vw[e] << 16));
+                    if constexpr (VT::kGates) u[e] = vv;
+                    else u[e] = sBeta[r0 + e] * vv;
+                }
+                store8(&sUt[tx(j0 + cc, r0)], u);
             }
-            store8(&sUt[tx(j, r0)], u);
         }
     }
     // Every raw register is consumed: the next item's loads go out now and
@@ -903,9 +928,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // e^{g_r - g_s} <= 1.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int tl = wave + u * NW;
-        if (tl >= 10) break;
-        const int R = lower_r(tl), S = lower_s(tl);
+        if (u >= gN) break;
+        const int R = gR, S = gS0 + u;
         const int rs = 16 * S + l16;
         const int rr = 16 * R + l16;
         f32x4 accA = zero4(), accP = zero4();
@@ -915,7 +939,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         for (int ks = 0; ks < DK / 32; ++ks) {
             const int kb = 32 * ks + 8 * lg;
             const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rs, kb)]);
-            const bf16x8 qr8 = qf[u][ks];
+            const bf16x8 qr8 = qf[ks];
             if constexpr (!VT::kChannelDecay && !VT::kGates) {
                 // a_r = beta_r k_r and the decay are scalars per row: the stored
                 // bf16 rows go to the matrix cores as they are and the scalars
