@@ -616,7 +616,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ float sRq[C];   // 1 / |q_r| with the q/k normalisation
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
-    __shared__ float sX[3][16][17];
+    __shared__ float sX[4][16][17];
     bf16 *sK = reinterpret_cast<bf16 *>(smem1);    // [C][DK]
     bf16 *sV = reinterpret_cast<bf16 *>(smem3);    // [C][DV]
     float *sT = reinterpret_cast<float *>(smem1);  // [C][C]
@@ -1019,50 +1019,69 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         }
     }
     __syncthreads();
-    // Off-diagonal blocks by distance d = R - S, one wave per block on fp32
-    // matrix cores (16x16x4, full fp32 products):
-    //   X = sum_{J=S}^{R-1} A_RJ T_JS,   T_RS = -T_RR X.
+    // Off-diagonal blocks by 2 x 2 block recursion on fp32 matrix cores
+    // (16x16x4, full fp32 products).  With L = [[L11, 0], [L21, L22]] unit
+    // lower triangular, L^{-1} = [[T11, 0], [-T22 L21 T11, T22]]:
+    //   16x16 level: T10 = -T11 (A10 T00), T32 = -T33 (A32 T22)   (waves 0, 1)
+    //   32x32 level: Y = [A20 A21; A30 A31] [T00 0; T10 T11]      (waves 0-3)
+    //                [T20 T21; T30 T31] = -[T22 0; T32 T33] Y
     // A lane feeds row l16 / K-element lg of the left factor and K-element lg /
     // column l16 of the right one, and receives rows 4 lg .. 4 lg + 3 of column
-    // l16; X goes through LDS to become a right-hand operand.
+    // l16; intermediate tiles go through sX to become right-hand operands.
     using MF = Mma<float>;
+    // acc += X(xr, xc) Y(yr, yc) for 16x16 blocks of two C x C fp32 LDS tiles
+    auto mm16 = [&](f32x4 acc, const float *X, int xr, int xc, const float *Y, int yr, int yc) {
+        float a[4], t[4];
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        const int nb = 4 - d;
-        const int R = d + wave, S = wave;
-        if (wave < nb) {
-            // All operands of the block are read before the first product.
-            float a[4 * 3], t[4 * 3];
-#pragma unroll
-            for (int j = 0; j < d; ++j)
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int J = S + j;
-                    a[4 * j + s4] = sAm[fx(16 * R + l16, 16 * J + 4 * s4 + lg)];
-                    t[4 * j + s4] = sT[fx(16 * J + 4 * s4 + lg, 16 * S + l16)];
-                }
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int j = 0; j < 4 * d; ++j) acc = MF::mma(a[j], t[j], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sX[wave][4 * lg + i][l16] = acc[i];
+        for (int s4 = 0; s4 < 4; ++s4) {
+            a[s4] = X[fx(16 * xr + l16, 16 * xc + 4 * s4 + lg)];
+            t[s4] = Y[fx(16 * yr + 4 * s4 + lg, 16 * yc + l16)];
         }
-        __syncthreads();
-        if (wave < nb) {
-            float a[4], x[4];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                a[s4] = sT[fx(16 * R + l16, 16 * R + 4 * s4 + lg)];
-                x[s4] = sX[wave][4 * s4 + lg][l16];
-            }
-            f32x4 acc = zero4();
+        for (int s4 = 0; s4 < 4; ++s4) acc = MF::mma(a[s4], t[s4], acc);
+        return acc;
+    };
+    // acc += T(r, r') Z for a 16x16 intermediate Z held in sX[z]
+    auto mm16x = [&](f32x4 acc, int r, int r2, int z) {
+        float a[4], t[4];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) acc = MF::mma(a[s4], x[s4], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sT[fx(16 * R + 4 * lg + i, 16 * S + l16)] = -acc[i];
+        for (int s4 = 0; s4 < 4; ++s4) {
+            a[s4] = sT[fx(16 * r + l16, 16 * r2 + 4 * s4 + lg)];
+            t[s4] = sX[z][4 * s4 + lg][l16];
         }
-        __syncthreads();
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) acc = MF::mma(a[s4], t[s4], acc);
+        return acc;
+    };
+    if (wave < 2) {
+        const int R = 1 + 2 * wave, S = R - 1;
+        const f32x4 xv = mm16(zero4(), sAm, R, S, sT, S, S);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sX[wave][4 * lg + i][l16] = xv[i];
+        // The wave reads back what it wrote: LDS keeps one wave's accesses in
+        // order; the fence keeps the compiler from reordering them.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const f32x4 tv = mm16x(zero4(), R, R, wave);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[fx(16 * R + 4 * lg + i, 16 * S + l16)] = -tv[i];
     }
+    __syncthreads();
+    if (wave < 4) {
+        const int R = 2 + (wave >> 1), S = wave & 1;
+        f32x4 yv = mm16(zero4(), sAm, R, S, sT, S, S);
+        if (S == 0) yv = mm16(yv, sAm, R, 1, sT, 1, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sX[wave][4 * lg + i][l16] = yv[i];
+    }
+    __syncthreads();
+    if (wave < 4) {
+        const int R = 2 + (wave >> 1), S = wave & 1;
+        f32x4 tv = mm16x(zero4(), R, R, wave);
+        if (R == 3) tv = mm16x(tv, 3, 2, wave - 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[fx(16 * R + 4 * lg + i, 16 * S + l16)] = -tv[i];
+    }
+    __syncthreads();
 
     // ---- phase 4: W and U~ on matrix cores --------------------------------------
     {
