@@ -78,9 +78,11 @@ struct Block {
     // takes its next one from a shared ticket counter (NULL = every
     // gridDim.x-th item).  Every item processed draws one ticket, so a launch
     // advances the counter by exactly its item count; ticket_base is the
-    // counter's value when the launch starts.
+    // counter's value when the launch starts.  ticket_clear (if not NULL) is
+    // set to zero by the launch, for the launches after it.
     unsigned *ticket;
     unsigned ticket_base;
+    unsigned *ticket_clear;
 };
 
 struct WsLayout {
@@ -637,6 +639,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // their split into (chunk, head, batch row) is 32-bit scalar arithmetic.
     const unsigned nc = (unsigned)blk.nc, nitems = nc * (unsigned)(p.H * p.B);
     unsigned item = blockIdx.x;
+    if (blk.ticket_clear && item == 0 && threadIdx.x == 0) *blk.ticket_clear = 0u;
     if (item >= nitems) return;
     __shared__ unsigned sNext;   // the item after the current one
     auto chunk_of = [&](unsigned it) { return blk.c0 + (long)(it % nc); };
@@ -1390,11 +1393,6 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
 
 // ---- dispatch -----------------------------------------------------------------
 
-// Clears the prep's ticket counter at the start of a pipelined forward (a
-// kernel rather than a memset node, so that the call can be graph-captured).
-__global__ void zero_ticket_kernel(unsigned *t) {
-    if (threadIdx.x == 0) *t = 0u;
-}
 
 // Internal helper stream and events of the calling host thread, one set per
 // device, created on first use and kept for the life of the process.
@@ -1501,7 +1499,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
         const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr, nullptr,
-                        nullptr, 0u};
+                        nullptr, 0u, nullptr};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
@@ -1513,9 +1511,9 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     hipError_t e = aux_stream(&aux);
     if (e != hipSuccess) return e;
     float *carrier = reinterpret_cast<float *>(base + 2 * q.slot);
+    // The first prep runs alone: every resident slot, a fixed stride, and it
+    // clears the ticket counter that the later ones (beside a scan) draw from.
     unsigned *ticket = reinterpret_cast<unsigned *>(base + 2 * q.slot + q.carrier);
-    hipLaunchKernelGGL(zero_ticket_kernel, dim3(1), dim3(64), 0, stream, ticket);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     unsigned ticket_base = 0;
     if ((e = hipEventRecord(aux->start, stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(aux->s, aux->start, 0)) != hipSuccess) return e;
@@ -1528,13 +1526,14 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         // from the ticket counter, so the units without a scan take more of
         // them.  A channel-decay prep fills a unit's registers and never
         // shares one; its static split measured faster.
+        const bool tickets = i > 0 && !VariantTraits<V>::kChannelDecay;
         const Block blk{c0, nc, (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
-                        nullptr, nullptr, VariantTraits<V>::kChannelDecay ? nullptr : ticket,
-                        ticket_base};
-        ticket_base += (unsigned)(nc * p.H * p.B);
+                        nullptr, nullptr, tickets ? ticket : nullptr, ticket_base,
+                        i == 0 ? ticket : nullptr};
+        if (tickets) ticket_base += (unsigned)(nc * p.H * p.B);
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, true, aux->s)) != hipSuccess) return e;
+        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, i > 0, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
         if ((e = launch_scan<TI, DK, DV>(p, w, blk, stream)) != hipSuccess) return e;
@@ -1616,7 +1615,7 @@ hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc
         constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
         const long NC = (p.T + C - 1) / C;
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
-        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u};
+        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u, nullptr};
         return launch_prep<V, TI, DK, DV>(p, w, blk, concurrent, stream);
     });
 }
@@ -1631,7 +1630,7 @@ hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
         const Block blk{c0, nc, (int)NC, s_in, s_out,
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
-                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u};
+                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr};
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
     });
 }
