@@ -83,6 +83,11 @@ struct Block {
     unsigned *ticket;
     unsigned ticket_base;
     unsigned *ticket_clear;
+    // Scan: write o with streaming (non-temporal) stores (a separate kernel
+    // instance).  A 16-column slice writes 32 of each token row's bytes; in
+    // the pipelined forward, keeping these partial lines out of the caches
+    // leaves them to the next block's factors.
+    bool nt_out;
 };
 
 struct WsLayout {
@@ -1194,7 +1199,7 @@ constexpr int kScan2Threads = 512;
 
 // STATES: instead of the outputs, record the state entering every chunk (fp32)
 // in blk.s_chunks; the output waves then only keep the barrier count.
-template <typename TI, int DK, int DEPTH, int NJ, bool STATES>
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO>
 __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
@@ -1357,7 +1362,11 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks)
                     Ov = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
-                if (t < T) store4(&out[((b * T + t) * H + h) * (long)DV + col0 + 16 * j + 4 * lg], Ov);
+                TI *dst = &out[((b * T + t) * H + h) * (long)DV + col0 + 16 * j + 4 * lg];
+                if (t < T) {
+                    if constexpr (NTO) store4_nt(dst, Ov);
+                    else store4(dst, Ov);
+                }
             }
             if (p.delta_out) {
                 // each token's written residual: the chunk's Delta, rows past T dropped
@@ -1484,10 +1493,13 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     const long nwg = p.B * p.H * (DV / (16 * NJ));
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
     if (blk.s_chunks)
-        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true, false>), dim3((unsigned)grid),
+                           dim3(kScan2Threads), 0, st, p, w, blk);
+    else if (blk.nt_out)
+        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, true>), dim3((unsigned)grid),
                            dim3(kScan2Threads), 0, st, p, w, blk);
     else
-        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, false>), dim3((unsigned)grid),
                            dim3(kScan2Threads), 0, st, p, w, blk);
     return hipGetLastError();
 }
@@ -1499,7 +1511,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     if (q.nblk == 1) {
         const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base);
         const Block blk{0, (int)q.NC, (int)q.nb, p.state_in, p.state_out, nullptr, nullptr,
-                        nullptr, 0u, nullptr};
+                        nullptr, 0u, nullptr, false};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
@@ -1530,7 +1542,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         const Block blk{c0, nc, (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
                         nullptr, nullptr, tickets ? ticket : nullptr, ticket_base,
-                        i == 0 ? ticket : nullptr};
+                        i == 0 ? ticket : nullptr, true};
         if (tickets) ticket_base += (unsigned)(nc * p.H * p.B);
         if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, i > 0, aux->s)) != hipSuccess) return e;
@@ -1615,7 +1627,8 @@ hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc
         constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
         const long NC = (p.T + C - 1) / C;
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
-        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u, nullptr};
+        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u, nullptr,
+                        false};
         return launch_prep<V, TI, DK, DV>(p, w, blk, concurrent, stream);
     });
 }
@@ -1630,7 +1643,8 @@ hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
         const Block blk{c0, nc, (int)NC, s_in, s_out,
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
-                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr};
+                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr,
+                        false};
         return launch_scan<TI, DK, DV>(p, w, blk, stream);
     });
 }
