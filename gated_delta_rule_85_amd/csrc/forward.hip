@@ -1196,6 +1196,12 @@ template <typename TI, int DK> struct OutOps {
 };
 
 constexpr int kScan2Threads = 512;
+// The output waves stage o in LDS and write it every kOutBurst chunks.  Loads
+// and stores share one wait counter, and the compiler lets a store complete
+// out of order, so a wait for the next chunk's prefetched factors also waits
+// for any o store issued after those loads; staged, only one wait in
+// kOutBurst does.
+constexpr int kOutBurst = 8;
 
 // STATES: instead of the outputs, record the state entering every chunk (fp32)
 // in blk.s_chunks; the output waves then only keep the barrier count.
@@ -1210,6 +1216,8 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
     constexpr int SW = 16 * NJ;   // value columns of the slice
     __shared__ __attribute__((aligned(16))) TI sSt[2][SW][DK + PT];   // S^T, double-buffered
     __shared__ __attribute__((aligned(16))) TI sDt[2][SW][C + PT];    // Delta^T, double-buffered
+    // o of the last kOutBurst chunks, written to HBM in one burst (see below)
+    __shared__ __attribute__((aligned(16))) TI sO[STATES ? 1 : kOutBurst][C][SW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -1348,10 +1356,30 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         __syncthreads();          // S_0 in place
         __syncthreads();          // first chunk: no output yet
         __syncthreads();
+        // Writes the staged o of chunks c - c % kOutBurst .. c: each wave its
+        // own sixteen token rows, one 16-byte piece per lane and store.
+        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+        auto flush = [&](long c) {
+            constexpr int EPP = 16 / (int)sizeof(TI);   // elements per piece
+            constexpr int PPR = SW / EPP;               // pieces per token row
+            const long first = c - c % kOutBurst;
+            const int n = (int)(c - first + 1) * 16 * PPR;
+            for (int idx = lane; idx < n; idx += kWave) {
+                const int kk = idx / (16 * PPR), rem = idx % (16 * PPR);
+                const int tl = 16 * w + rem / PPR, pc = rem % PPR;
+                const long tt = (blk.c0 + first + kk) * C + tl;
+                if (tt < T) {
+                    const u32x4v x = *reinterpret_cast<const u32x4v *>(&sO[kk][tl][pc * EPP]);
+                    u32x4v *dst = reinterpret_cast<u32x4v *>(
+                        &out[((b * T + tt) * H + h) * (long)DV + col0 + pc * EPP]);
+                    if constexpr (NTO) __builtin_nontemporal_store(x, dst);
+                    else *dst = x;
+                }
+            }
+        };
         // op holds the factors of chunk c; S_c and Delta_c are in LDS buffer c % 2.
         auto step = [&](const OO &op, long c) __attribute__((always_inline)) {
             const int buf = (int)(c & 1);
-            const long t = (blk.c0 + c) * C + 16 * w + l16;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 f32x4 Ov = zero4();
@@ -1362,12 +1390,9 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks)
                     Ov = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
-                TI *dst = &out[((b * T + t) * H + h) * (long)DV + col0 + 16 * j + 4 * lg];
-                if (t < T) {
-                    if constexpr (NTO) store4_nt(dst, Ov);
-                    else store4(dst, Ov);
-                }
+                store4(&sO[c % kOutBurst][16 * w + l16][16 * j + 4 * lg], Ov);
             }
+            if (c % kOutBurst == kOutBurst - 1 || c == NC - 1) flush(c);
             if (p.delta_out) {
                 // each token's written residual: the chunk's Delta, rows past T dropped
                 const long tc = (blk.c0 + c) * C;

@@ -122,16 +122,6 @@ __device__ __forceinline__ void store4(bf16 *dst, f32x4 x) {
 __device__ __forceinline__ void store4(float *dst, f32x4 x) {
     *reinterpret_cast<f32x4 *>(dst) = x;
 }
-// The same with the non-temporal (streaming) cache policy.
-__device__ __forceinline__ void store4_nt(bf16 *dst, f32x4 x) {
-    bf16x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4 *>(dst));
-}
-__device__ __forceinline__ void store4_nt(float *dst, f32x4 x) {
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(dst));
-}
 __device__ __forceinline__ f32x4 load4(const bf16 *src) {
     bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
