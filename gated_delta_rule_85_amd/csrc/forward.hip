@@ -829,7 +829,13 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __syncthreads();
 
     // ---- phase 1: element-wise factors ------------------------------------
+    // The workspace stores of this phase (q (.) e^g, Kbar^T, e^{g_C}) are
+    // issued after the Gram products: loads and stores share one wait
+    // counter, so a store issued between the Gram operand loads and their
+    // use would be waited for with them.
     load_qf(c, h, b, l16, lg);   // for phase 2
+    bf16x8 qo[NQ], kbo[2];
+    float gamo[2];
     {
         // q (.) e^{g}, from registers
 #pragma unroll
@@ -846,7 +852,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                     if constexpr (VT::kChannelDecay) eg = __expf(sG[r][8 * pc + e]);
                     o[e] = (bf16)((float)raw.q[n][e] * eg);
                 }
-                *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
+                qo[n] = o;
             }
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace.
@@ -895,8 +901,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                     kb[e] = kk * egc;
                 }
                 store8(&sAt[tx(i, r0)], at);
-                store_frag8(ws.Kbt + ch * DK * C, i, r0, C, kb);
-                if (r0 == 0) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kbo[cc][e] = (bf16)kb[e];
+                gamo[cc] = VT::kHasDecay ? __expf(gC) : 1.f;
             }
         }
         // U^T into LDS, two columns of eight rows per thread in the same way
@@ -1000,6 +1007,22 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         const int r = 16 * upper_r(t6) + e / 4;
         const int s2 = 16 * upper_s(t6) + 4 * (e % 4);
         store_frag4(ws.P + ch * C * C, r, s2, C, zero4());
+    }
+    // the phase-1 workspace stores
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+        const int idx = tid + n * NT;
+        if (idx < C * KC)
+            *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(idx / KC, 8 * (idx % KC), DK)) =
+                qo[n];
+    }
+    if (tid < DK / 2 * (C / 8)) {
+        const int i0 = 2 * (tid % (DK / 2)), r0 = 8 * (tid / (DK / 2));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i0 + cc, r0, C)) = kbo[cc];
+            if (r0 == 0) ws.gam[ch * DK + i0 + cc] = gamo[cc];
+        }
     }
     __syncthreads();
 
