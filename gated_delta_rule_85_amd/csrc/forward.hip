@@ -1169,7 +1169,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 // on the same SIMDs.  The chunk factors are shared by all column tiles of a
 // head, so wider slices (larger NJ) read them fewer times in all.
 // ============================================================================
-template <typename TI, int DK, int NJ> struct ChainOps {
+// SG: the decay is a scalar per chunk (every entry of e^{g_C} is equal), so
+// one 4-byte load per lane replaces the per-row vector loads.
+template <typename TI, int DK, int NJ, bool SG> struct ChainOps {
     using M = Mma<TI>;
     static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK, NI = DK / 64;
     static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);   // bytes per fragment tile
@@ -1193,7 +1195,12 @@ template <typename TI, int DK, int NJ> struct ChainOps {
 #pragma unroll
             for (int ks = 0; ks < KS_C; ++ks)
                 Kf[a][ks] = buf_load<typename M::frag>(rk, loff + (a * KS_C + ks) * FB);
-            gam[a] = buf_load<f32x4>(rg, (unsigned)(lane >> 4) * 16u + 64u * a);
+            if constexpr (!SG) gam[a] = buf_load<f32x4>(rg, (unsigned)(lane >> 4) * 16u + 64u * a);
+        }
+        if constexpr (SG) {
+            const float g = buf_load<float>(rg, 0u);
+#pragma unroll
+            for (int a = 0; a < NI; ++a) gam[a] = f32x4{g, g, g, g};
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
@@ -1228,11 +1235,11 @@ constexpr int kOutBurst = 8;
 
 // STATES: instead of the outputs, record the state entering every chunk (fp32)
 // in blk.s_chunks; the output waves then only keep the barrier count.
-template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO>
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG>
 __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
-    using CO = ChainOps<TI, DK, NJ>;
+    using CO = ChainOps<TI, DK, NJ, SG>;
     using OO = OutOps<TI, DK>;
     constexpr int KS_D = CO::KS_D, KS_C = CO::KS_C, NI = CO::NI;
     constexpr int PT = 8;
@@ -1532,7 +1539,8 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
 }
 
 template <typename TI, int DK, int DV>
-hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, hipStream_t st) {
+hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool scalar_decay,
+                       hipStream_t st) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
     // One 16-column tile per workgroup: wider slices read the shared factors
     // fewer times in all but lengthen each chunk's chain, and measured slower
@@ -1540,15 +1548,20 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     constexpr int NJ = 1;
     const long nwg = p.B * p.H * (DV / (16 * NJ));
     const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    if (blk.s_chunks)
-        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true, false>), dim3((unsigned)grid),
-                           dim3(kScan2Threads), 0, st, p, w, blk);
-    else if (blk.nt_out)
-        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, true>), dim3((unsigned)grid),
-                           dim3(kScan2Threads), 0, st, p, w, blk);
-    else
-        hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, false>), dim3((unsigned)grid),
-                           dim3(kScan2Threads), 0, st, p, w, blk);
+    auto go = [&](auto sg) {
+        constexpr bool SG = decltype(sg)::value;
+        if (blk.s_chunks)
+            hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true, false, SG>),
+                               dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
+        else if (blk.nt_out)
+            hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, true, SG>),
+                               dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
+        else
+            hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, false, SG>),
+                               dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
+    };
+    if (scalar_decay) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 
@@ -1562,7 +1575,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
                         nullptr, 0u, nullptr, false};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
-        return launch_scan<TI, DK, DV>(p, w, blk, stream);
+        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream);
     }
     // Pipelined: the prep of block i + 1 runs on the helper stream while the
     // scan of block i runs on the caller's stream; two workspace slots
@@ -1596,7 +1609,9 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, i > 0, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_scan<TI, DK, DV>(p, w, blk, stream)) != hipSuccess) return e;
+        if ((e = launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream)) !=
+            hipSuccess)
+            return e;
         if ((e = hipEventRecord(aux->scan[slot], stream)) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1684,16 +1699,16 @@ hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc
 hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
                               const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
                               hipStream_t stream) {
-    return dispatch_shape(p, [&](auto, auto ti, auto dk, auto dv) {
+    return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) {
         using TI = typename decltype(ti)::type;
-        constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+        constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
         const long NC = (p.T + C - 1) / C;
         const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
         const Block blk{c0, nc, (int)NC, s_in, s_out,
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
                         static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr,
                         false};
-        return launch_scan<TI, DK, DV>(p, w, blk, stream);
+        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream);
     });
 }
 
