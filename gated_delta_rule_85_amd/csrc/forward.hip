@@ -1538,18 +1538,42 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     return hipGetLastError();
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(long *out) {
+    static long ncu[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (ncu[dev] == 0) {
+        int cus = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return e;
+        ncu[dev] = cus > 0 ? cus : 1;
+    }
+    *out = ncu[dev];
+    return hipSuccess;
+}
+
 template <typename TI, int DK, int DV>
 hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool scalar_decay,
                        hipStream_t st) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
-    // One 16-column tile per workgroup: wider slices read the shared factors
-    // fewer times in all but lengthen each chunk's chain, and measured slower
-    // on the long-context workload.
-    constexpr int NJ = 1;
-    const long nwg = p.B * p.H * (DV / (16 * NJ));
-    const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-    auto go = [&](auto sg) {
+    // Value columns per workgroup: 16, so that every head's chain is cut into
+    // as many short, independent column slices as possible.  When 16-column
+    // slices would need more workgroups than there are compute units, 32
+    // (scalar decay, bf16: the instance that fits the register budget beside
+    // a prep workgroup) halves the factor loads per column instead; below
+    // that, the longer per-chunk chain of a wide slice costs more than it saves.
+    long cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const bool wide = sizeof(TI) == 2 && scalar_decay && DV % 32 == 0 && p.B * p.H * (DV / 16) > cus;
+    auto go = [&](auto sg, auto nj) {
         constexpr bool SG = decltype(sg)::value;
+        constexpr int NJ = decltype(nj)::value;
+        const long nwg = p.B * p.H * (DV / (16 * NJ));
+        const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
         if (blk.s_chunks)
             hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true, false, SG>),
                                dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
@@ -1560,8 +1584,11 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
             hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, false, SG>),
                                dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
     };
-    if (scalar_decay) go(std::true_type{});
-    else go(std::false_type{});
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, sizeof(TI) == 2 && DV % 32 == 0 ? 2 : 1>;
+    if (!scalar_decay) go(std::false_type{}, One{});
+    else if (wide) go(std::true_type{}, Two{});
+    else go(std::true_type{}, One{});
     return hipGetLastError();
 }
 

@@ -189,6 +189,36 @@ def test_forward_pipelined_blocks(variant, T):
     assert e_o < 2e-2 and e_s < 2e-2
 
 
+@pytest.mark.parametrize("variant", ["kla", "gated_deltanet", "deltanet"])
+def test_forward_wide_scan_slices(variant):
+    """Batch 4 x 16 heads at d = 128 gives more 16-column scan slices than the
+    chip has compute units, so a scalar-decay bf16 scan takes 32 columns per
+    workgroup; a ragged last chunk and a non-zero initial state."""
+    announce(f"wide scan slices {variant}")
+    inp = make_inputs(variant, 4, 300, 16, 128, 128, "bf16", seed=83, state_scale=0.5)
+    o, s = gpu_forward(variant, to_dev(inp))
+    o_ref, s_ref = run_oracle(variant, inp)
+    e_o = rel_err(o.float().cpu(), o_ref, (0, 2))
+    e_s = rel_err(s.cpu(), s_ref, (0, 1))
+    announce(f"  rel_err o={e_o:.3e} S={e_s:.3e}")
+    assert e_o < 2e-2 and e_s < 2e-2
+
+
+def test_forward_wide_scan_slices_pipelined():
+    """The same wide slices in the pipelined forward (B = 4, H = 16, 514
+    chunks), checked on sampled heads."""
+    T = 64 * 513 + 37
+    inp = make_inputs("kla", 4, T, 16, 128, 128, "bf16", seed=85, state_scale=0.3)
+    o, s = gpu_forward("kla", to_dev(inp))
+    heads = [(0, 0), (1, 7), (3, 15)]
+    o_ref, s_ref = run_oracle("kla", inp, heads=heads)
+    for b, h in heads:
+        e_o = rel_err(o[b:b + 1, :, h:h + 1].float().cpu(), o_ref[b:b + 1, :, h:h + 1], (0, 2))
+        e_s = rel_err(s[b:b + 1, h:h + 1].cpu(), s_ref[b:b + 1, h:h + 1], (0, 1))
+        announce(f"  head ({b}, {h}): rel_err o={e_o:.3e} S={e_s:.3e}")
+        assert e_o < 2e-2 and e_s < 2e-2
+
+
 def test_forward_pipelined_split_resume():
     """A pipelined pass (576 chunks) equals the same sequence split in two
     one-pass calls, the second resuming from the first's final state."""
