@@ -832,7 +832,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // The workspace stores of this phase (q (.) e^g, Kbar^T, e^{g_C}) are
     // issued after the Gram products: loads and stores share one wait
     // counter, so a store issued between the Gram operand loads and their
-    // use would be waited for with them.
+    // use would be waited for with them.  The instance with a routed value
+    // holds more registers and stores them at once instead (holding them
+    // there spills more than the wait costs).
+    constexpr bool kDefer = !RT;
     load_qf(c, h, b, l16, lg);   // for phase 2
     bf16x8 qo[NQ], kbo[2];
     float gamo[2];
@@ -853,6 +856,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                     o[e] = (bf16)((float)raw.q[n][e] * eg);
                 }
                 qo[n] = o;
+                if constexpr (!kDefer)
+                    *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
             }
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace.
@@ -904,6 +909,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kbo[cc][e] = (bf16)kb[e];
                 gamo[cc] = VT::kHasDecay ? __expf(gC) : 1.f;
+                if constexpr (!kDefer) {
+                    *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i, r0, C)) = kbo[cc];
+                    if (r0 == 0) ws.gam[ch * DK + i] = gamo[cc];
+                }
             }
         }
         // U^T into LDS, two columns of eight rows per thread in the same way
@@ -1009,6 +1018,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         store_frag4(ws.P + ch * C * C, r, s2, C, zero4());
     }
     // the phase-1 workspace stores
+    if constexpr (kDefer) {
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         const int idx = tid + n * NT;
@@ -1023,6 +1033,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i0 + cc, r0, C)) = kbo[cc];
             if (r0 == 0) ws.gam[ch * DK + i0 + cc] = gamo[cc];
         }
+    }
     }
     __syncthreads();
 
