@@ -928,6 +928,44 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         }
         // ---- H: Gram backward, element-wise chain rule, outputs --------------------------
         //   dXa = dA Xk, dXq = dP Xk, dXk = dA^T Xa + dP^T Xq
+        // bf16 inputs without a channel decay: the chunk's q and k are staged
+        // in LDS over the retired T and Y tiles, transposed with a 66-element
+        // pitch (a lane's column reads then fall in distinct banks), so the
+        // operand reads below are LDS reads rather than one global load per
+        // element.  Rows past T stage as zeros.
+        constexpr bool kStageQK = !kSlotX && sizeof(TI) == 2;
+        constexpr int QP = C + 2;
+        static_assert(!kStageQK || DK * QP * 2 <= C * CP * 4, "a staged tile fits a C x CP fp32 tile");
+        bf16 (*sQt)[QP] = reinterpret_cast<bf16 (*)[QP]>(&sB[0][0][0]);
+        bf16 (*sKt)[QP] = reinterpret_cast<bf16 (*)[QP]>(&sB[1][0][0]);
+        if constexpr (kStageQK) {
+            for (int idx = tid; idx < C * DK / 8; idx += NT) {
+                const int r = idx / (DK / 8), c8 = 8 * (idx % (DK / 8));
+                const bool ok = r < nvalid;
+                const long o = tok(rowc(r)) * DK + c8;
+                const bf16x8 z8 = {};
+                const bf16x8 qv = ok ? ld8(reinterpret_cast<const bf16 *>(q) + o) : z8;
+                const bf16x8 kv = ok ? ld8(reinterpret_cast<const bf16 *>(k) + o) : z8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sQt[c8 + e][r] = qv[e];
+                    sKt[c8 + e][r] = kv[e];
+                }
+            }
+            __syncthreads();
+        }
+        auto hk = [&](int m, int cc) -> float {
+            if constexpr (kStageQK) return (float)sKt[cc][m];
+            else return xk1(m, cc);
+        };
+        auto ha = [&](int m, int cc) -> float {
+            if constexpr (kStageQK) return (float)sKt[cc][m] * sbeta[m];
+            else return xa1(m, cc);
+        };
+        auto hq = [&](int m, int cc) -> float {
+            if constexpr (kStageQK) return (float)sQt[cc][m];
+            else return xq1(m, cc);
+        };
         for (int t = wave; t < 4 * NKB; t += NW) {
             const int R = t / NKB, N = t % NKB, col = 16 * N + l16;
             // dA and dP are lower triangular: rows of this block row take
@@ -936,13 +974,13 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             with_block(R, [&](auto Rc) {
                 constexpr int RB = decltype(Rc)::value;
                 xa = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdA[16 * RB + l16][m]; },
-                                             [&](int m) { return xk1(m, col); }, lg, xa);
+                                             [&](int m) { return hk(m, col); }, lg, xa);
                 xq = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdP[16 * RB + l16][m]; },
-                                             [&](int m) { return xk1(m, col); }, lg, xq);
+                                             [&](int m) { return hk(m, col); }, lg, xq);
                 xk = mm_kt<16 * RB, C>([&](int m) { return sdA[m][16 * RB + l16]; },
-                                       [&](int m) { return xa1(m, col); }, lg, xk);
+                                       [&](int m) { return ha(m, col); }, lg, xk);
                 xk = mm_kt<16 * RB, C>([&](int m) { return sdP[m][16 * RB + l16]; },
-                                       [&](int m) { return xq1(m, col); }, lg, xk);
+                                       [&](int m) { return hq(m, col); }, lg, xk);
             });
             float e_col = 0.f;
 #pragma unroll
@@ -950,7 +988,14 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 const int r = 16 * R + 4 * lg + m, idx = r * DK + col;
                 const long o = tok(rowc(r)) * DK + col;
                 const bool ok = r < nvalid;
-                const float qq = ok ? f32(q[o]) : 0.f, kk = ok ? f32(k[o]) : 0.f;
+                float qq, kk;
+                if constexpr (kStageQK) {
+                    qq = (float)sQt[col][r];
+                    kk = (float)sKt[col][r];
+                } else {
+                    qq = ok ? f32(q[o]) : 0.f;
+                    kk = ok ? f32(k[o]) : 0.f;
+                }
                 float bg = 0.f;
                 if constexpr (VT::kGates) bg = ok ? p.erase_b[o] : 0.f;
                 const float aa = (VT::kGates ? bg : sbeta[r]) * kk;
@@ -1053,7 +1098,10 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 const int r = idx / DK, i = idx % DK;
                 if (r < nvalid) {
                     const long o = tok(r) * DK + i;
-                    g.d_k[o] = dQt[idx] + scoef[r] * f32(k[o]);
+                    float kk;
+                    if constexpr (kStageQK) kk = (float)sKt[i][r];   // still staged
+                    else kk = f32(k[o]);
+                    g.d_k[o] = dQt[idx] + scoef[r] * kk;
                 }
             }
         }
