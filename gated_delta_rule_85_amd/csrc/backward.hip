@@ -832,6 +832,22 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         }
         __syncthreads();
         // ---- E: dT += dW At^T (strictly lower); dAt = T^T dW; du = T^T dDelta -----
+        // bf16: the chunk's dDelta is staged in LDS over the retired A tile,
+        // transposed with a 66-element pitch, for the du products.
+        constexpr bool kStageD = sizeof(TI) == 2;
+        constexpr int QP = C + 2;
+        static_assert(!kStageD || (DV * QP * 2 <= C * CP * 4 && DK * QP * 2 <= C * CP * 4),
+                      "a staged tile fits a C x CP fp32 tile");
+        bf16 (*sDd)[QP] = reinterpret_cast<bf16 (*)[QP]>(&sB[1][0][0]);
+        if constexpr (kStageD) {
+            for (int idx = tid; idx < C * DV / 8; idx += NT) {
+                const int r = idx / (DV / 8), c8 = 8 * (idx % (DV / 8));
+                const bf16x8 d8 = ld8(reinterpret_cast<const bf16 *>(dD) + r * DV + c8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sDd[c8 + e][r] = d8[e];
+            }
+            __syncthreads();
+        }
         for (int t = wave; t < 10 + 4 * NKB + 4 * NVB; t += NW) {
             if (t < 10) {
                 const int R = tri_r(t), Sb = tri_s(t);
@@ -862,7 +878,10 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 with_block(R, [&](auto Rc) {
                     constexpr int RB = decltype(Rc)::value;
                     acc = mm_kt<16 * RB, C>([&](int m) { return sT[m][16 * RB + l16]; },
-                                            [&](int m) { return f32(dD[m * DV + 16 * N + l16]); }, lg, acc);
+                                            [&](int m) {
+                                                if constexpr (kStageD) return (float)sDd[16 * N + l16][m];
+                                                else return f32(dD[m * DV + 16 * N + l16]);
+                                            }, lg, acc);
                 });
                 const int j = 16 * N + l16;
 #pragma unroll
@@ -934,8 +953,6 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
         // operand reads below are LDS reads rather than one global load per
         // element.  Rows past T stage as zeros.
         constexpr bool kStageQK = !kSlotX && sizeof(TI) == 2;
-        constexpr int QP = C + 2;
-        static_assert(!kStageQK || DK * QP * 2 <= C * CP * 4, "a staged tile fits a C x CP fp32 tile");
         bf16 (*sQt)[QP] = reinterpret_cast<bf16 (*)[QP]>(&sB[0][0][0]);
         bf16 (*sKt)[QP] = reinterpret_cast<bf16 (*)[QP]>(&sB[1][0][0]);
         if constexpr (kStageQK) {
