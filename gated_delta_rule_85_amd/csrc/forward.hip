@@ -1494,6 +1494,32 @@ hipError_t aux_stream(AuxStream **out) {
     return hipSuccess;
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(long *out) {
+    static long ncu[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (ncu[dev] == 0) {
+        int cus = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return e;
+        ncu[dev] = cus > 0 ? cus : 1;
+    }
+    *out = ncu[dev];
+    return hipSuccess;
+}
+
+// Whether the scan takes 32-column slices (see launch_scan), and its number of
+// workgroups.
+bool scan_wide(const Problem &p, bool scalar_decay, long cus) {
+    return p.bf16 && scalar_decay && p.dv % 32 == 0 && p.B * p.H * (p.dv / 16) > cus;
+}
+long scan_workgroups(const Problem &p, bool scalar_decay, long cus) {
+    return p.B * p.H * (p.dv / (scan_wide(p, scalar_decay, cus) ? 32 : 16));
+}
+
 // Workgroups of the bf16 prep kernel that the device holds at once (resident
 // slots) and its compute units, queried once per device and kernel instance.
 template <int V, int DK, int DV, bool RT> hipError_t prep_slots(long *slots_out, long *cus_out) {
@@ -1526,14 +1552,18 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
         // Persistent workgroups, each looping over chunk-heads with the next
         // one's inputs in flight.  Alone, the grid fills every resident slot;
         // beside a concurrent scan, one workgroup per compute unit, so that a
-        // scan workgroup still fits on every unit.
+        // scan workgroup still fits on every unit, plus a second one for each
+        // unit the scan leaves free: in whichever order the two grids are
+        // placed, every scan workgroup still finds a unit with room.
         long slots = 0, cus = 0;
         const bool rt = p.v_route != nullptr;
         hipError_t e = rt ? prep_slots<V, DK, DV, true>(&slots, &cus)
                           : prep_slots<V, DK, DV, false>(&slots, &cus);
         if (e != hipSuccess) return e;
         const long items = (long)blk.nc * p.H * p.B;
-        const long want = concurrent ? cus : slots;
+        const long free_cus = cus - scan_workgroups(p, !VariantTraits<V>::kChannelDecay, cus);
+        const long extra = free_cus > 0 ? (free_cus < slots - cus ? free_cus : slots - cus) : 0;
+        const long want = concurrent ? cus + extra : slots;
         const long grid = items < want ? items : want;
         if (rt)
             hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV, true>), dim3((unsigned)grid),
@@ -1549,22 +1579,6 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     return hipGetLastError();
 }
 
-// Compute units of the current device, queried once per device.
-hipError_t device_cus(long *out) {
-    static long ncu[kMaxDevices] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (ncu[dev] == 0) {
-        int cus = 0;
-        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-            return e;
-        ncu[dev] = cus > 0 ? cus : 1;
-    }
-    *out = ncu[dev];
-    return hipSuccess;
-}
 
 template <typename TI, int DK, int DV>
 hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool scalar_decay,
@@ -1579,7 +1593,7 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     long cus = 0;
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    const bool wide = sizeof(TI) == 2 && scalar_decay && DV % 32 == 0 && p.B * p.H * (DV / 16) > cus;
+    const bool wide = scan_wide(p, scalar_decay, cus);
     auto go = [&](auto sg, auto nj) {
         constexpr bool SG = decltype(sg)::value;
         constexpr int NJ = decltype(nj)::value;
