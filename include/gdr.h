@@ -167,8 +167,9 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
  * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
  * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
  * (at most 1 GiB; 72.5 KB per chunk and head at dk = dv = 128 in bf16),
- * else of two blocks of 64 chunks plus a state carrier, so it stops growing
- * with T.  Calls that share a workspace must be ordered on one stream. */
+ * else of two blocks of 64 chunks plus a state carrier and a work counter, so
+ * it stops growing with T.  Calls that share a workspace must be ordered on
+ * one stream. */
 gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
                                void *hip_stream);
 
