@@ -21,13 +21,14 @@
 // derivation and the kernel design are our own.
 //
 // Two kernels:
-//   chunk_prep  one workgroup per (chunk, h, b), fully parallel.  Gate prefix
-//               sums, the two 64x64 Gram products A and P on bf16 matrix cores
-//               (fp32 accumulate), the unit-lower-triangular inverse T in LDS
-//               (fp32; 16x16 diagonal blocks by substitution, off-diagonal
-//               blocks by block recursion), then W and U~ on matrix cores.
-//               It writes per-chunk factors W, U~^T, q(.)e^{g}, K-bar^T, P and
-//               e^{g_C} to the workspace.
+//   chunk_prep  fully parallel over (chunk, h, b): persistent workgroups that
+//               loop over chunk-heads (bf16; one workgroup per chunk-head for
+//               fp32).  Gate prefix sums, the two 64x64 Gram products A and P
+//               on bf16 matrix cores (fp32 accumulate), the unit-lower-
+//               triangular inverse T in LDS (fp32; 16x16 diagonal blocks by
+//               substitution, off-diagonal blocks by a 2 x 2 block recursion),
+//               then W and U~ on matrix cores.  It writes per-chunk factors W,
+//               U~^T, q(.)e^{g}, K-bar^T, P and e^{g_C} to the workspace.
 //   chunk_scan  one workgroup per (slice of 16*NJ value columns, h, b): the
 //               sequential pass over chunks.  Columns of S evolve independently
 //               given the chunk factors, so the state is split by value
@@ -35,6 +36,8 @@
 //               accumulators for the whole sequence and a bf16 copy of S^T in
 //               LDS feeds the products.  The next chunk's factors are loaded
 //               while the current one is computed.
+// A long bf16 sequence runs as blocks of 64 chunks, the prep of block i + 1
+// beside the scan of block i (see launch_shape).
 //
 // All products are written as D = A * B^T over a K-contiguous pair of
 // operands, so every fragment is one 16-byte load; operand order is chosen so
@@ -638,10 +641,12 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const int H = (int)p.H;
     const bf16 *q = static_cast<const bf16 *>(p.q);
     // Work items are the block's chunk-heads, chunk fastest; a workgroup takes
-    // every gridDim.x-th item and loads the next one's inputs while it
-    // computes the current one.
-    // Item indices fit in 32 bits (the host keeps B * H * 64 below 2^31), so
-    // their split into (chunk, head, batch row) is 32-bit scalar arithmetic.
+    // item blockIdx.x first, then every gridDim.x-th item or the next ticket
+    // (blk.ticket), and loads the next item's inputs while it computes the
+    // current one.
+    // Item indices fit in 32 bits (the host keeps B * H * ceil(T / 64) below
+    // 2^31), so their split into (chunk, head, batch row) is 32-bit scalar
+    // arithmetic.
     const unsigned nc = (unsigned)blk.nc, nitems = nc * (unsigned)(p.H * p.B);
     unsigned item = blockIdx.x;
     if (blk.ticket_clear && item == 0 && threadIdx.x == 0) *blk.ticket_clear = 0u;
