@@ -627,6 +627,12 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[4][16][17];
+    // Channel decay without gates (KDA): the Gram products' split operands,
+    // k e^{g_ref - g} (right) and beta k e^{g - g_ref}, q e^{g - g_ref} (left),
+    // formed once per item in phase 1 instead of per tile in phase 2 (this
+    // prep runs one workgroup per CU, so the 48 KB of LDS are there).
+    constexpr bool kSplit = VT::kChannelDecay && !VT::kGates;
+    __shared__ __attribute__((aligned(16))) bf16 sSplit[kSplit ? 3 : 1][kSplit ? C * DK : 8];
     bf16 *sK = reinterpret_cast<bf16 *>(smem1);    // [C][DK]
     bf16 *sV = reinterpret_cast<bf16 *>(smem3);    // [C][DV]
     float *sT = reinterpret_cast<float *>(smem1);  // [C][C]
@@ -920,6 +926,27 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 }
             }
         }
+        if constexpr (kSplit) {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+                const int idx = tid + n * NT;
+                const int r = idx / KC, pc = idx % KC;
+                const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(r, 8 * pc)]);
+                const float br = sBeta[r];
+                bf16x8 kr8, al8, ql8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float gref = sG[C / 2 - 1][8 * pc + e], g = sG[r][8 * pc + e];
+                    const float fl = __expf(g - gref);
+                    kr8[e] = (bf16)((float)k8[e] * __expf(gref - g));
+                    al8[e] = (bf16)(br * (float)k8[e] * fl);
+                    ql8[e] = (bf16)((float)raw.q[n][e] * fl);
+                }
+                *reinterpret_cast<bf16x8 *>(&sSplit[0][kx(r, 8 * pc)]) = kr8;
+                *reinterpret_cast<bf16x8 *>(&sSplit[1][kx(r, 8 * pc)]) = al8;
+                *reinterpret_cast<bf16x8 *>(&sSplit[2][kx(r, 8 * pc)]) = ql8;
+            }
+        }
         // U^T into LDS, two columns of eight rows per thread in the same way
         if (tid < DV / 2 * (C / 8)) {
             const int j0 = 2 * (tid % (DV / 2)), r0 = 8 * (tid / (DV / 2));
@@ -978,6 +1005,12 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 accP = M::mma(kr8, qr8, accP);
                 continue;
             }
+            if constexpr (kSplit) {
+                const bf16x8 kq = *reinterpret_cast<const bf16x8 *>(&sSplit[0][kx(rs, kb)]);
+                accA = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sSplit[1][kx(rr, kb)]), accA);
+                accP = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sSplit[2][kx(rr, kb)]), accP);
+                continue;
+            }
             bf16x8 ar8;
             if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[kx(rr, kb)]);
             else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
@@ -1011,7 +1044,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             Av[m] = s2 < r ? accA[m] * fa : 0.f;
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
-        if (l2) Pv *= sRq[r];   // P used the q rows as stored
+        if (l2 && !kSplit) Pv *= sRq[r];   // P used the q rows as stored (kSplit: normalised)
         *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
         store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }

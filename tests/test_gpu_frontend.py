@@ -73,7 +73,7 @@ def test_forward_transforms_head_sizes(variant, dk, dv):
     _check_forward(variant, "bf16", L2 | RAW, dk=dk, dv=dv, T=130, seed=11)
 
 
-@pytest.mark.parametrize("variant", ["kla", "gdn2"])
+@pytest.mark.parametrize("variant", ["kla", "kda", "gdn2"])
 def test_forward_transforms_pipelined(variant):
     """514 chunks: the blocked two-stream path, sampled heads."""
     _check_forward(variant, "bf16", L2 | RAW, B=1, T=64 * 64 * 8 + 100, H=4, seed=21,
