@@ -627,12 +627,17 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[4][16][17];
-    // Channel decay without gates (KDA): the Gram products' split operands,
-    // k e^{g_ref - g} (right) and beta k e^{g - g_ref}, q e^{g - g_ref} (left),
-    // formed once per item in phase 1 instead of per tile in phase 2 (this
-    // prep runs one workgroup per CU, so the 48 KB of LDS are there).
-    constexpr bool kSplit = VT::kChannelDecay && !VT::kGates;
-    __shared__ __attribute__((aligned(16))) bf16 sSplit[kSplit ? 3 : 1][kSplit ? C * DK : 8];
+    // Channel decay: the Gram products' split operands, k e^{g_ref - g}
+    // (right) and a e^{g - g_ref}, q e^{g - g_ref} (left), are formed once per
+    // item in phase 1 instead of per tile in phase 2 (this prep runs one
+    // workgroup per CU, so the LDS is there).  With gates, a = b (.) k is
+    // scaled in place in its own tile.
+    constexpr bool kSplit = VT::kChannelDecay;
+    constexpr int NS = VT::kGates ? 2 : 3;
+    __shared__ __attribute__((aligned(16))) bf16 sSplit[kSplit ? NS : 1][kSplit ? C * DK : 8];
+    bf16 *const sKr = sSplit[0];
+    bf16 *const sQl = sSplit[kSplit ? NS - 1 : 0];
+    bf16 *const sAl = VT::kGates ? sAg : sSplit[kSplit && !VT::kGates ? 1 : 0];
     bf16 *sK = reinterpret_cast<bf16 *>(smem1);    // [C][DK]
     bf16 *sV = reinterpret_cast<bf16 *>(smem3);    // [C][DV]
     float *sT = reinterpret_cast<float *>(smem1);  // [C][C]
@@ -670,9 +675,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const int gR = wave < 2 ? 3 : (wave < 4 ? 2 : (wave == 4 ? 1 : 0));
     const int gS0 = (wave == 1 || wave == 3) ? 2 : 0;
     const int gN = wave < 6 ? ((wave == 3 || wave == 5) ? 1 : 2) : 0;
-    // q rows of block gR, for phase 2 (L2 hits); rows past T read the last
-    // valid row, whose products only reach rows never stored.  Every wave
-    // loads them, so that the loads and their waits are unconditional.
+    // q rows of block gR, for phase 2 with scalar decay (L2 hits); rows past
+    // T read the last valid row, whose products only reach rows never stored.
+    // Every wave loads them, so that the loads and their waits are
+    // unconditional.
     bf16x8 qf[DK / 32];
     auto load_qf = [&](long c, int h, int b, int l16, int lg) {
         const long t0 = c * C;
@@ -847,7 +853,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // holds more registers and stores them at once instead (holding them
     // there spills more than the wait costs).
     constexpr bool kDefer = !RT;
-    load_qf(c, h, b, l16, lg);   // for phase 2
+    if constexpr (!kSplit) load_qf(c, h, b, l16, lg);   // for phase 2
     bf16x8 qo[NQ], kbo[2];
     float gamo[2];
     {
@@ -879,6 +885,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             const int i0 = 2 * (tid % (DK / 2)), r0 = 8 * (tid / (DK / 2));
             uint32_t kw[8], aw[VT::kGates ? 8 : 1];
             float2 gw[VT::kChannelDecay ? 8 : 1];
+            bf16x2 alw[VT::kGates ? 8 : 1];   // a e^{g - g_ref}, written back in place
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kw[e] = *reinterpret_cast<const uint32_t *>(&sK[kx(r0 + e, i0)]);
@@ -892,6 +899,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             for (int cc = 0; cc < 2; ++cc) {
                 const int i = i0 + cc;
                 const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
+                const float gref = sG[C / 2 - 1][VT::kChannelDecay ? i : 0];
                 // element cc of a word holding two bf16 (little-endian)
                 auto half = [&](uint32_t w) {
                     return __uint_as_float(cc ? (w & 0xffff0000u) : (w << 16));
@@ -909,6 +917,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                         const float g = cc ? gw[e].y : gw[e].x;
                         eg = __expf(g);
                         egc = __expf(gC - g);
+                        if constexpr (VT::kGates) alw[e][cc] = (bf16)(a * __expf(g - gref));
                     } else if constexpr (kRowDecay) {
                         eg = sEg[r];
                         egc = sEgc[r];
@@ -925,6 +934,11 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                     if (r0 == 0) ws.gam[ch * DK + i] = gamo[cc];
                 }
             }
+            // the same elements this thread read, so no other thread races it
+            if constexpr (VT::kGates) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) *reinterpret_cast<bf16x2 *>(&sAg[kx(r0 + e, i0)]) = alw[e];
+            }
         }
         if constexpr (kSplit) {
 #pragma unroll
@@ -932,19 +946,19 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 const int idx = tid + n * NT;
                 const int r = idx / KC, pc = idx % KC;
                 const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(r, 8 * pc)]);
-                const float br = sBeta[r];
+                const float br = VT::kScalarBeta ? sBeta[r] : 0.f;
                 bf16x8 kr8, al8, ql8;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float gref = sG[C / 2 - 1][8 * pc + e], g = sG[r][8 * pc + e];
                     const float fl = __expf(g - gref);
                     kr8[e] = (bf16)((float)k8[e] * __expf(gref - g));
-                    al8[e] = (bf16)(br * (float)k8[e] * fl);
+                    if constexpr (!VT::kGates) al8[e] = (bf16)(br * (float)k8[e] * fl);
                     ql8[e] = (bf16)((float)raw.q[n][e] * fl);
                 }
-                *reinterpret_cast<bf16x8 *>(&sSplit[0][kx(r, 8 * pc)]) = kr8;
-                *reinterpret_cast<bf16x8 *>(&sSplit[1][kx(r, 8 * pc)]) = al8;
-                *reinterpret_cast<bf16x8 *>(&sSplit[2][kx(r, 8 * pc)]) = ql8;
+                *reinterpret_cast<bf16x8 *>(&sKr[kx(r, 8 * pc)]) = kr8;
+                if constexpr (!VT::kGates) *reinterpret_cast<bf16x8 *>(&sAl[kx(r, 8 * pc)]) = al8;
+                *reinterpret_cast<bf16x8 *>(&sQl[kx(r, 8 * pc)]) = ql8;
             }
         }
         // U^T into LDS, two columns of eight rows per thread in the same way
@@ -994,43 +1008,19 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
             const int kb = 32 * ks + 8 * lg;
-            const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rs, kb)]);
-            const bf16x8 qr8 = qf[ks];
-            if constexpr (!VT::kChannelDecay && !VT::kGates) {
+            if constexpr (!kSplit) {
                 // a_r = beta_r k_r and the decay are scalars per row: the stored
                 // bf16 rows go to the matrix cores as they are and the scalars
                 // multiply the product.
+                const bf16x8 kr8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rs, kb)]);
                 const bf16x8 kq8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
                 accA = M::mma(kr8, kq8, accA);
-                accP = M::mma(kr8, qr8, accP);
-                continue;
+                accP = M::mma(kr8, qf[ks], accP);
+            } else {
+                const bf16x8 kq = *reinterpret_cast<const bf16x8 *>(&sKr[kx(rs, kb)]);
+                accA = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sAl[kx(rr, kb)]), accA);
+                accP = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sQl[kx(rr, kb)]), accP);
             }
-            if constexpr (kSplit) {
-                const bf16x8 kq = *reinterpret_cast<const bf16x8 *>(&sSplit[0][kx(rs, kb)]);
-                accA = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sSplit[1][kx(rr, kb)]), accA);
-                accP = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sSplit[2][kx(rr, kb)]), accP);
-                continue;
-            }
-            bf16x8 ar8;
-            if constexpr (VT::kGates) ar8 = *reinterpret_cast<const bf16x8 *>(&sAg[kx(rr, kb)]);
-            else ar8 = *reinterpret_cast<const bf16x8 *>(&sK[kx(rr, kb)]);
-            float kr[8], ar[8], qr[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kr[e] = (float)kr8[e];
-                qr[e] = (float)qr8[e];
-                ar[e] = VT::kGates ? (float)ar8[e] : br * (float)ar8[e];
-                if constexpr (VT::kChannelDecay) {
-                    const float gref = sG[C / 2 - 1][kb + e];
-                    const float fl = __expf(sG[rr][kb + e] - gref);
-                    kr[e] *= __expf(gref - sG[rs][kb + e]);
-                    ar[e] *= fl;
-                    qr[e] *= fl;
-                }
-            }
-            const M::frag fk = M::from_f32x8(kr);
-            accA = M::mma(fk, M::from_f32x8(ar), accA);
-            accP = M::mma(fk, M::from_f32x8(qr), accP);
         }
         const int r = rr;
         f32x4 Av, Pv;
