@@ -1447,19 +1447,30 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
             }
         };
         // op holds the factors of chunk c; S_c and Delta_c are in LDS buffer c % 2.
+        // The chain overwrites S_c's buffer in the second half of its next
+        // step and Delta_c's only in the step after, so Qt S runs beside the
+        // chain's Delta step and P Delta (and the stores) beside its state
+        // update.
         auto step = [&](const OO &op, long c) __attribute__((always_inline)) {
             const int buf = (int)(c & 1);
+            f32x4 Ov[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                f32x4 Ov = zero4();
+                Ov[j] = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KS_D; ++ks)
-                    Ov = M::mma(M::load(&sSt[buf][16 * j + l16][0], ks * M::kK, lane), op.Qf[ks], Ov);
+                    Ov[j] = M::mma(M::load(&sSt[buf][16 * j + l16][0], ks * M::kK, lane), op.Qf[ks],
+                                   Ov[j]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
                 // P is zero above the diagonal, so all K-steps may run.
 #pragma unroll
                 for (int ks = 0; ks < KS_C; ++ks)
-                    Ov = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks], Ov);
-                store4(&sO[c % kOutBurst][16 * w + l16][16 * j + 4 * lg], Ov);
+                    Ov[j] = M::mma(M::load(&sDt[buf][16 * j + l16][0], ks * M::kK, lane), op.Pf[ks],
+                                   Ov[j]);
+                store4(&sO[c % kOutBurst][16 * w + l16][16 * j + 4 * lg], Ov[j]);
             }
             if (c % kOutBurst == kOutBurst - 1 || c == NC - 1) flush(c);
             if (p.delta_out) {
@@ -1469,7 +1480,6 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                     static_cast<TI *>(p.delta_out) + ((b * T + tc) * H + h) * (long)DV + col0,
                     (long)H * DV, sDt[buf], C, T - tc, tid - 4 * kWave, 4 * kWave);
             }
-            __syncthreads();
             __syncthreads();
         };
         if constexpr (DEPTH == 2) {
