@@ -1218,17 +1218,27 @@ template <typename TI, int DK, int NJ, bool SG> struct ChainOps {
     typename M::frag Wf[KS_D], Kf[NI][KS_C];
     raw4 U[NJ];
     f32x4 gam[NI];
-    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int DV, int col0, int w,
-                                         int lane) {
+    // The factors of the Delta step (W, U~) and of the state update (Kbar^T,
+    // e^{g_C}) load separately, so that each half of a step can issue the
+    // next chunk's share.
+    __device__ __forceinline__ void load_w(const WsPtrs<TI> &ws, long ch, int DV, int col0, int w,
+                                           int lane) {
         const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
         const auto rw = make_rsrc(reinterpret_cast<const char *>(ws.W + ch * C * DK) + w * KS_D * FB);
-        const auto rk = make_rsrc(reinterpret_cast<const char *>(ws.Kbt + ch * DK * C) +
-                                  w * NI * KS_C * FB);
-        const auto rg = make_rsrc(ws.gam + ch * DK + 16 * NI * w);
         const auto ru = make_rsrc(reinterpret_cast<const char *>(ws.Ut + ch * (long)DV * C) +
                                   ((col0 / 16) * (C / 16) + w) * (kWave * 4 * (int)sizeof(TI)));
 #pragma unroll
         for (int ks = 0; ks < KS_D; ++ks) Wf[ks] = buf_load<typename M::frag>(rw, loff + ks * FB);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            U[j] = buf_load<raw4>(ru, ((unsigned)lane + (unsigned)(j * (C / 16) * kWave)) * 4u *
+                                          sizeof(TI));
+    }
+    __device__ __forceinline__ void load_k(const WsPtrs<TI> &ws, long ch, int w, int lane) {
+        const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
+        const auto rk = make_rsrc(reinterpret_cast<const char *>(ws.Kbt + ch * DK * C) +
+                                  w * NI * KS_C * FB);
+        const auto rg = make_rsrc(ws.gam + ch * DK + 16 * NI * w);
 #pragma unroll
         for (int a = 0; a < NI; ++a) {
 #pragma unroll
@@ -1241,10 +1251,6 @@ template <typename TI, int DK, int NJ, bool SG> struct ChainOps {
 #pragma unroll
             for (int a = 0; a < NI; ++a) gam[a] = f32x4{g, g, g, g};
         }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            U[j] = buf_load<raw4>(ru, ((unsigned)lane + (unsigned)(j * (C / 16) * kWave)) * 4u *
-                                          sizeof(TI));
     }
 };
 
@@ -1253,12 +1259,15 @@ template <typename TI, int DK> struct OutOps {
     static constexpr int KS_D = DK / M::kK, KS_C = C / M::kK;
     static constexpr int FB = kWave * M::kPerLane * (int)sizeof(TI);
     typename M::frag Qf[KS_D], Pf[KS_C];
-    __device__ __forceinline__ void load(const WsPtrs<TI> &ws, long ch, int w, int lane) {
+    __device__ __forceinline__ void load_q(const WsPtrs<TI> &ws, long ch, int w, int lane) {
         const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
         const auto rq = make_rsrc(reinterpret_cast<const char *>(ws.Qt + ch * C * DK) + w * KS_D * FB);
-        const auto rp = make_rsrc(reinterpret_cast<const char *>(ws.P + ch * C * C) + w * KS_C * FB);
 #pragma unroll
         for (int ks = 0; ks < KS_D; ++ks) Qf[ks] = buf_load<typename M::frag>(rq, loff + ks * FB);
+    }
+    __device__ __forceinline__ void load_p(const WsPtrs<TI> &ws, long ch, int w, int lane) {
+        const unsigned loff = (unsigned)lane * (M::kPerLane * sizeof(TI));
+        const auto rp = make_rsrc(reinterpret_cast<const char *>(ws.P + ch * C * C) + w * KS_C * FB);
 #pragma unroll
         for (int ks = 0; ks < KS_C; ++ks) Pf[ks] = buf_load<typename M::frag>(rp, loff + ks * FB);
     }
@@ -1334,7 +1343,9 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         // Every step consumes its whole register set on every path: a loaded
         // value left unused on some path makes the compiler wait for all
         // loads in flight before it reuses any register.
-        auto step = [&](const CO &op, long c) __attribute__((always_inline)) {
+        // pre_update issues the next chunk's state-update factors once this
+        // step's Delta is in LDS.
+        auto step = [&](const CO &op, long c, auto &&pre_update) __attribute__((always_inline)) {
             const int cur = (int)(c & 1);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -1350,6 +1361,7 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                 }
                 store4(&sDt[cur][16 * j + l16][16 * w + 4 * lg], to_f32x4(op.U[j]) - (d0 + d1));
             }
+            pre_update();
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -1370,21 +1382,23 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         };
         if constexpr (DEPTH == 2) {
             CO A, Bq;
-            A.load(ws, chunk(0), DV, col0, w, lane);
+            A.load_w(ws, chunk(0), DV, col0, w, lane);
+            A.load_k(ws, chunk(0), w, lane);
             for (long c = 0; c < NC; c += 2) {
-                Bq.load(ws, chunk(c + 1), DV, col0, w, lane);
+                Bq.load_w(ws, chunk(c + 1), DV, col0, w, lane);
                 __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
-                step(A, c);
+                step(A, c, [&] { Bq.load_k(ws, chunk(c + 1), w, lane); });
                 if (c + 1 >= NC) break;
-                A.load(ws, chunk(c + 2), DV, col0, w, lane);
+                A.load_w(ws, chunk(c + 2), DV, col0, w, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                step(Bq, c + 1);
+                step(Bq, c + 1, [&] { A.load_k(ws, chunk(c + 2), w, lane); });
             }
         } else {
             CO cur;
             for (long c = 0; c < NC; ++c) {
-                cur.load(ws, chunk(c), DV, col0, w, lane);
-                step(cur, c);
+                cur.load_w(ws, chunk(c), DV, col0, w, lane);
+                cur.load_k(ws, chunk(c), w, lane);
+                step(cur, c, [] {});
             }
         }
         // The output waves still finish the last chunk.
@@ -1421,6 +1435,7 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
     } else {
         // ---------------- outputs of the previous chunk ----------------
         const int w = wave - 4;
+        __builtin_amdgcn_s_setprio(2);   // the chain waves' instructions go first
         TI *out = static_cast<TI *>(p.o);
         __syncthreads();          // S_0 in place
         __syncthreads();          // first chunk: no output yet
@@ -1451,7 +1466,8 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         // step and Delta_c's only in the step after, so Qt S runs beside the
         // chain's Delta step and P Delta (and the stores) beside its state
         // update.
-        auto step = [&](const OO &op, long c) __attribute__((always_inline)) {
+        // pre_pd issues the next chunk's P once Qt S is done.
+        auto step = [&](const OO &op, long c, auto &&pre_pd) __attribute__((always_inline)) {
             const int buf = (int)(c & 1);
             f32x4 Ov[NJ];
 #pragma unroll
@@ -1462,6 +1478,7 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
                     Ov[j] = M::mma(M::load(&sSt[buf][16 * j + l16][0], ks * M::kK, lane), op.Qf[ks],
                                    Ov[j]);
             }
+            pre_pd();
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -1484,21 +1501,23 @@ __global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p
         };
         if constexpr (DEPTH == 2) {
             OO A, Bq;
-            A.load(ws, chunk(0), w, lane);
+            A.load_q(ws, chunk(0), w, lane);
+            A.load_p(ws, chunk(0), w, lane);
             for (long c = 0; c < NC; c += 2) {
-                Bq.load(ws, chunk(c + 1), w, lane);
+                Bq.load_q(ws, chunk(c + 1), w, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                step(A, c);
+                step(A, c, [&] { Bq.load_p(ws, chunk(c + 1), w, lane); });
                 if (c + 1 >= NC) break;
-                A.load(ws, chunk(c + 2), w, lane);
+                A.load_q(ws, chunk(c + 2), w, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                step(Bq, c + 1);
+                step(Bq, c + 1, [&] { A.load_p(ws, chunk(c + 2), w, lane); });
             }
         } else {
             OO cur;
             for (long c = 0; c < NC; ++c) {
-                cur.load(ws, chunk(c), w, lane);
-                step(cur, c);
+                cur.load_q(ws, chunk(c), w, lane);
+                cur.load_p(ws, chunk(c), w, lane);
+                step(cur, c, [] {});
             }
         }
     }
