@@ -846,13 +846,15 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __syncthreads();
 
     // ---- phase 1: element-wise factors ------------------------------------
-    // The workspace stores of this phase (q (.) e^g, Kbar^T, e^{g_C}) are
-    // issued after the Gram products: loads and stores share one wait
+    // KLA issues the workspace stores of this phase (q (.) e^g, Kbar^T,
+    // e^{g_C}) after the Gram products: loads and stores share one wait
     // counter, so a store issued between the Gram operand loads and their
-    // use would be waited for with them.  The instance with a routed value
-    // holds more registers and stores them at once instead (holding them
-    // there spills more than the wait costs).
-    constexpr bool kDefer = !RT;
+    // use would be waited for with them.  Elsewhere they go out at once:
+    // with a routed value, for DeltaNet and Gated DeltaNet, and for d_v < d_k,
+    // holding them spills, and a spill reload waits for every load in flight
+    // (the next item's prefetch included); with a channel decay the Gram
+    // products load nothing from global memory, so there is no wait to avoid.
+    constexpr bool kDefer = !RT && V == kKLA && DV >= DK;
     if constexpr (!kSplit) load_qf(c, h, b, l16, lg);   // for phase 2
     bf16x8 qo[NQ], kbo[2];
     float gamo[2];
@@ -1043,7 +1045,12 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         const int t6 = idx / 64, e = idx % 64;
         const int r = 16 * upper_r(t6) + e / 4;
         const int s2 = 16 * upper_s(t6) + 4 * (e % 4);
-        store_frag4(ws.P + ch * C * C, r, s2, C, zero4());
+        // The zero is made here, opaque to the compiler: hoisted out of the
+        // item loop it was spilled, and its reload (a scratch load) waited for
+        // every load in flight, the next item's prefetch included.
+        unsigned z = 0u;
+        asm volatile("" : "+v"(z));
+        *reinterpret_cast<uint2 *>(ws.P + ch * C * C + frag_off<bf16>(r, s2, C)) = make_uint2(z, z);
     }
     // the phase-1 workspace stores
     if constexpr (kDefer) {
