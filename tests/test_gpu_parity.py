@@ -72,7 +72,7 @@ def test_forward_matches_oracle(variant, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
-@pytest.mark.parametrize("variant", ["deltanet", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_forward_head_sizes(variant, dtype, dk, dv):
     announce(f"forward sizes {variant} {dtype} dk={dk} dv={dv}")
     inp = make_inputs(variant, 1, 150, 2, dk, dv, dtype, seed=300, state_scale=0.3)
