@@ -722,7 +722,56 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             sdT[r][s] = 0.f;
         }
         constexpr int NMAIN = 2 * NKB;   // C x DK tile groups: 16 columns, two block rows
-        for (int t = wave; t < NMAIN + 10; t += NW) {
+        // bf16 with two tile groups per wave (t = wave and wave + NW): both
+        // have the same two block rows, so one pass over the value channels
+        // loads those rows' dO, dDelta and Delta once for both, and the wave
+        // waits for its operands half as often.  Each accumulator sees the same
+        // products in the same order as in the per-tile loop below.
+        constexpr bool kPair = kMfma8 && NMAIN == 2 * NW;
+        int t_first = wave;
+        if constexpr (kPair) {
+            const int R0 = 2 * (wave & 1);
+            const int Nt[2] = {wave >> 1, (wave + NW) >> 1};
+            f32x4 aq[2][2], aw[2][2], ak[2][2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) aq[x][u] = aw[x][u] = ak[x][u] = zero4();
+#pragma unroll 1
+            for (int j0 = 0; j0 < DV; j0 += 32) {
+                const int j = j0 + 8 * lg;
+                bf16x8 bs[2], bd[2];
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    bs[x] = tdv8(S, 16 * Nt[x] + l16, j);
+                    bd[x] = tdv8(dSp, 16 * Nt[x] + l16, j);
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = 16 * (R0 + u) + l16;
+                    const bf16x8 xo = ldo8(r, j), xd = tdv8(dD, r, j), xl = tdv8(Dl, r, j);
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        aq[x][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xo, bs[x], aq[x][u], 0, 0, 0);
+                        aw[x][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xd, bs[x], aw[x][u], 0, 0, 0);
+                        ak[x][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bd[x], ak[x][u], 0, 0, 0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int o = (16 * (R0 + u) + 4 * lg + m) * DK + 16 * Nt[x] + l16;
+                        dQt[o] = aq[x][u][m];
+                        dWm[o] = -aw[x][u][m];
+                        dKb[o] = ak[x][u][m];
+                    }
+            t_first = NMAIN + wave;
+        }
+        for (int t = t_first; t < NMAIN + 10; t += NW) {
             if (t < NMAIN) {
                 if constexpr (kMfma8) {
                     // bf16 inputs: every operand here is stored in bf16, so the
