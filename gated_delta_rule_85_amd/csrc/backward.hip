@@ -129,16 +129,34 @@ __global__ __launch_bounds__(kBpThreads) void bw_prep_kernel(Problem p, ForwardS
             const int Rb = tt / (DV / 16), Jb = tt % (DV / 16);
             const int row = 16 * Rb + l16, col = 16 * Jb + l16;
             f32x4 acc = zero4();
-            for (int s0 = 0; s0 < C; s0 += 16) {
-                float av[4], bv[4];
+            if constexpr (sizeof(TI) == 2) {
+                // bf16 operands: their products are exact in fp32, so the bf16
+                // matrix cores give the fp32 result up to summation order, with
+                // an eighth of the matrix-core instructions.
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s = s0 + 4 * u + lg;
-                    av[u] = to_f32(x1 ? sP[frag_off<TI>(s, row, C)] : sQ[frag_off<TI>(s, row, DK)]);
-                    bv[u] = to_f32(sdO[s * DV + col]);
+                for (int s0 = 0; s0 < C; s0 += 32) {
+                    bf16x8 a8, b8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = s0 + 8 * lg + e;
+                        a8[e] = x1 ? sP[frag_off<TI>(s, row, C)] : sQ[frag_off<TI>(s, row, DK)];
+                        b8[e] = sdO[s * DV + col];
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
                 }
+            } else {
+                for (int s0 = 0; s0 < C; s0 += 16) {
+                    float av[4], bv[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc, 0, 0, 0);
+                    for (int u = 0; u < 4; ++u) {
+                        const int s = s0 + 4 * u + lg;
+                        av[u] = to_f32(x1 ? sP[frag_off<TI>(s, row, C)] : sQ[frag_off<TI>(s, row, DK)]);
+                        bv[u] = to_f32(sdO[s * DV + col]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc, 0, 0, 0);
+                }
             }
             TI *dst = static_cast<TI *>(x1 ? rf.X1 : rf.X2) + ch * (x1 ? C : DK) * DV;
             store4(dst + afrag_off(col, 16 * Rb + 4 * lg, x1 ? C : DK), acc);
