@@ -1290,8 +1290,10 @@ constexpr int kOutBurst = 8;
 
 // STATES: instead of the outputs, record the state entering every chunk (fp32)
 // in blk.s_chunks; the output waves then only keep the barrier count.
+// A scalar decay's instances keep to 128 registers, so that a prep workgroup
+// fits beside them; a channel decay's never share a unit with a prep.
 template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG>
-__global__ __launch_bounds__(kScan2Threads, 4) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
+__global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
     using CO = ChainOps<TI, DK, NJ, SG>;
@@ -1576,12 +1578,13 @@ hipError_t device_cus(long *out) {
 }
 
 // Whether the scan takes 32-column slices (see launch_scan), and its number of
-// workgroups.
-bool scan_wide(const Problem &p, bool scalar_decay, long cus) {
-    return p.bf16 && scalar_decay && p.dv % 32 == 0 && p.B * p.H * (p.dv / 16) > cus;
+// workgroups.  concurrent: a prep runs beside it.
+bool scan_wide(const Problem &p, bool scalar_decay, bool concurrent, long cus) {
+    if (!p.bf16 || p.dv % 32 != 0) return false;
+    return scalar_decay ? p.B * p.H * (p.dv / 16) > cus : concurrent;
 }
-long scan_workgroups(const Problem &p, bool scalar_decay, long cus) {
-    return p.B * p.H * (p.dv / (scan_wide(p, scalar_decay, cus) ? 32 : 16));
+long scan_workgroups(const Problem &p, bool scalar_decay, bool concurrent, long cus) {
+    return p.B * p.H * (p.dv / (scan_wide(p, scalar_decay, concurrent, cus) ? 32 : 16));
 }
 
 // Workgroups of the bf16 prep kernel that the device holds at once (resident
@@ -1625,9 +1628,15 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
                           : prep_slots<V, DK, DV, false>(&slots, &cus);
         if (e != hipSuccess) return e;
         const long items = (long)blk.nc * p.H * p.B;
-        const long free_cus = cus - scan_workgroups(p, !VariantTraits<V>::kChannelDecay, cus);
+        const long free_cus =
+            cus - scan_workgroups(p, !VariantTraits<V>::kChannelDecay, concurrent, cus);
         const long extra = free_cus > 0 ? (free_cus < slots - cus ? free_cus : slots - cus) : 0;
-        const long want = concurrent ? cus + extra : slots;
+        // A channel-decay prep (one workgroup per unit) never shares a unit
+        // with the scan: beside one it takes just the units the scan leaves
+        // free, so that no workgroup of its static split starts late.
+        long want = slots;
+        if (concurrent)
+            want = VariantTraits<V>::kChannelDecay ? (free_cus > 0 ? free_cus : cus) : cus + extra;
         const long grid = items < want ? items : want;
         if (rt)
             hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV, true>), dim3((unsigned)grid),
@@ -1646,7 +1655,7 @@ hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
 
 template <typename TI, int DK, int DV>
 hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool scalar_decay,
-                       hipStream_t st) {
+                       bool concurrent, hipStream_t st) {
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
     // Value columns per workgroup: 16, so that every head's chain is cut into
     // as many short, independent column slices as possible.  When 16-column
@@ -1654,10 +1663,13 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     // (scalar decay, bf16: the instance that fits the register budget beside
     // a prep workgroup) halves the factor loads per column instead; below
     // that, the longer per-chunk chain of a wide slice costs more than it saves.
+    // A channel-decay scan beside its prep takes 32 columns too: that prep
+    // cannot share a unit with it, and the units a wide scan frees speed the
+    // prep up more than the longer chain slows the scan.
     long cus = 0;
     hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
-    const bool wide = scan_wide(p, scalar_decay, cus);
+    const bool wide = scan_wide(p, scalar_decay, concurrent, cus);
     auto go = [&](auto sg, auto nj) {
         constexpr bool SG = decltype(sg)::value;
         constexpr int NJ = decltype(nj)::value;
@@ -1675,7 +1687,10 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     };
     using One = std::integral_constant<int, 1>;
     using Two = std::integral_constant<int, sizeof(TI) == 2 && DV % 32 == 0 ? 2 : 1>;
-    if (!scalar_decay) go(std::false_type{}, One{});
+    if (!scalar_decay) {
+        if (wide) go(std::false_type{}, Two{});
+        else go(std::false_type{}, One{});
+    }
     else if (wide) go(std::true_type{}, Two{});
     else go(std::true_type{}, One{});
     return hipGetLastError();
@@ -1691,7 +1706,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
                         nullptr, 0u, nullptr, false};
         hipError_t e = launch_prep<V, TI, DK, DV>(p, w, blk, false, stream);
         if (e != hipSuccess) return e;
-        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream);
+        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, false, stream);
     }
     // Pipelined: the prep of block i + 1 runs on the helper stream while the
     // scan of block i runs on the caller's stream; two workspace slots
@@ -1714,7 +1729,8 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         // Scalar-decay preps share compute units with the scan and take items
         // from the ticket counter, so the units without a scan take more of
         // them.  A channel-decay prep fills a unit's registers and never
-        // shares one; its static split measured faster.
+        // shares one; it runs on the units the scan leaves free, with a static
+        // split, which measured faster.
         const bool tickets = i > 0 && !VariantTraits<V>::kChannelDecay;
         const Block blk{c0, nc, (int)q.nb,
                         i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
@@ -1725,7 +1741,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, i > 0, aux->s)) != hipSuccess) return e;
         if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream)) !=
+        if ((e = launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, true, stream)) !=
             hipSuccess)
             return e;
         if ((e = hipEventRecord(aux->scan[slot], stream)) != hipSuccess) return e;
@@ -1824,7 +1840,7 @@ hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
                         static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr,
                         false};
-        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, stream);
+        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, false, stream);
     });
 }
 
