@@ -142,9 +142,12 @@ Plan make_plan(const Problem &p) {
     // reads factors the prep has just written, still in the caches.  Below
     // that the prep and the scan run as one pass each, which measured faster:
     // with few blocks there is little to overlap, and the two kernels slow
-    // each other down.  The single pass's workspace is capped.
+    // each other down.  A channel decay's heavier prep gains from the overlap
+    // from half that length.  The single pass's workspace is capped.
+    const bool channel = p.variant == kKDA || p.variant == kGDN2;
+    const long from = channel ? kPipelineChunks / 2 : kPipelineChunks;
     const bool pipe = p.bf16 && q.NC > kBlockChunks &&
-                      (q.NC >= kPipelineChunks || ws_layout(p, q.NC).total > kSinglePassBytes);
+                      (q.NC >= from || ws_layout(p, q.NC).total > kSinglePassBytes);
     q.nb = pipe ? kBlockChunks : q.NC;
     q.nblk = (q.NC + q.nb - 1) / q.nb;
     q.slot = ws_layout(p, q.nb).total;

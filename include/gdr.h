@@ -47,12 +47,13 @@
  *   - Every tensor pointer is device memory owned by the caller.  The library
  *     never allocates device memory, frees or synchronises; work is enqueued on
  *     the HIP stream passed as `hip_stream` (a hipStream_t; NULL = the null
- *     stream).  A long bf16 prefill (512 chunks or more) is pipelined over a
- *     second, internal stream, ordered against `hip_stream` with events: the
- *     library creates that stream and five events once per host thread and
- *     device and keeps them for the life of the process.  The call still
- *     behaves as one operation on `hip_stream` (later work on it waits for all
- *     of it), and it can be captured into a HIP graph.
+ *     stream).  A long bf16 prefill (512 chunks or more; 256 for KDA and
+ *     GDN-2) is pipelined over a second, internal stream, ordered against
+ *     `hip_stream` with events: the library creates that stream and five
+ *     events once per host thread and device and keeps them for the life of
+ *     the process.  The call still behaves as one operation on `hip_stream`
+ *     (later work on it waits for all of it), and it can be captured into a
+ *     HIP graph.
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
  *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
@@ -166,7 +167,8 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
  * other output may overlap an input.  `workspace` must be 256-byte aligned and
  * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
  * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
- * (at most 1 GiB; 72.5 KB per chunk and head at dk = dv = 128 in bf16),
+ * (256 for KDA and GDN-2; at most 1 GiB; 72.5 KB per chunk and head at
+ * dk = dv = 128 in bf16),
  * else of two blocks of 64 chunks plus a state carrier and a work counter, so
  * it stops growing with T.  Calls that share a workspace must be ordered on
  * one stream. */

@@ -236,6 +236,22 @@ def test_forward_channel_decay_pipelined_wide_scan(variant):
         assert e_o < 2e-2 and e_s < 2e-2
 
 
+@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+def test_forward_channel_decay_pipelined_short(variant):
+    """A channel decay is pipelined from 256 chunks on (here 301: five blocks,
+    the last one ragged), checked on sampled heads."""
+    T = 64 * 300 + 17
+    inp = make_inputs(variant, 1, T, 4, 128, 128, "bf16", seed=87, state_scale=0.3)
+    o, s = gpu_forward(variant, to_dev(inp))
+    heads = [(0, 0), (0, 3)]
+    o_ref, s_ref = run_oracle(variant, inp, heads=heads)
+    for b, h in heads:
+        e_o = rel_err(o[b:b + 1, :, h:h + 1].float().cpu(), o_ref[b:b + 1, :, h:h + 1], (0, 2))
+        e_s = rel_err(s[b:b + 1, h:h + 1].cpu(), s_ref[b:b + 1, h:h + 1], (0, 1))
+        announce(f"  {variant} head ({b}, {h}): rel_err o={e_o:.3e} S={e_s:.3e}")
+        assert e_o < 2e-2 and e_s < 2e-2
+
+
 def test_forward_pipelined_split_resume():
     """A pipelined pass (576 chunks) equals the same sequence split in two
     one-pass calls, the second resuming from the first's final state."""
