@@ -135,6 +135,8 @@ constexpr long kBlockChunks = 64;
 constexpr long kPipelineChunks = 512;          // pipeline from this many chunks on
 constexpr size_t kSinglePassBytes = 1ull << 30;  // or when one pass's factors exceed this
 
+hipError_t device_cus(long *out);   // compute units of the current device
+
 Plan make_plan(const Problem &p) {
     Plan q;
     q.NC = (p.T + C - 1) / C;
@@ -143,9 +145,16 @@ Plan make_plan(const Problem &p) {
     // that the prep and the scan run as one pass each, which measured faster:
     // with few blocks there is little to overlap, and the two kernels slow
     // each other down.  A channel decay's heavier prep gains from the overlap
-    // from half that length.  The single pass's workspace is capped.
+    // from half that length, and so does a scalar decay's when its scan
+    // (16-column slices) takes more than a quarter and at most half of the
+    // compute units: fewer leave each block's prep too little to do, more
+    // leave it too few units.  The single pass's workspace is capped.
     const bool channel = p.variant == kKDA || p.variant == kGDN2;
-    const long from = channel ? kPipelineChunks / 2 : kPipelineChunks;
+    long cus = 0;
+    const long slices = p.B * p.H * (p.dv / 16);
+    const bool half =
+        device_cus(&cus) == hipSuccess && slices > cus / 4 && slices <= cus / 2;
+    const long from = (channel || half) ? kPipelineChunks / 2 : kPipelineChunks;
     const bool pipe = p.bf16 && q.NC > kBlockChunks &&
                       (q.NC >= from || ws_layout(p, q.NC).total > kSinglePassBytes);
     q.nb = pipe ? kBlockChunks : q.NC;

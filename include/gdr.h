@@ -48,10 +48,12 @@
  *     never allocates device memory, frees or synchronises; work is enqueued on
  *     the HIP stream passed as `hip_stream` (a hipStream_t; NULL = the null
  *     stream).  A long bf16 prefill (512 chunks or more; 256 for KDA and
- *     GDN-2) is pipelined over a second, internal stream, ordered against
- *     `hip_stream` with events: the library creates that stream and five
- *     events once per host thread and device and keeps them for the life of
- *     the process.  The call still behaves as one operation on `hip_stream`
+ *     GDN-2, and for the others when B * H * dv / 16 is above a quarter and
+ *     at most half of the device's compute units) is pipelined over a
+ *     second, internal stream, ordered against `hip_stream` with events: the
+ *     library creates that stream and five events once per host thread and
+ *     device and keeps them for the life of the process.  The call still
+ *     behaves as one operation on `hip_stream`
  *     (later work on it waits for all of it), and it can be captured into a
  *     HIP graph.
  *   - Layouts are dense row-major:
@@ -167,7 +169,7 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
  * other output may overlap an input.  `workspace` must be 256-byte aligned and
  * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
  * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
- * (256 for KDA and GDN-2; at most 1 GiB; 72.5 KB per chunk and head at
+ * (256 in the cases above; at most 1 GiB; 72.5 KB per chunk and head at
  * dk = dv = 128 in bf16),
  * else of two blocks of 64 chunks plus a state carrier and a work counter, so
  * it stops growing with T.  Calls that share a workspace must be ordered on

@@ -236,14 +236,15 @@ def test_forward_channel_decay_pipelined_wide_scan(variant):
         assert e_o < 2e-2 and e_s < 2e-2
 
 
-@pytest.mark.parametrize("variant", ["kda", "gdn2"])
-def test_forward_channel_decay_pipelined_short(variant):
-    """A channel decay is pipelined from 256 chunks on (here 301: five blocks,
-    the last one ragged), checked on sampled heads."""
+@pytest.mark.parametrize("variant,H", [("kda", 4), ("gdn2", 4), ("kla", 16), ("gated_deltanet", 16)])
+def test_forward_pipelined_from_256_chunks(variant, H):
+    """Pipelined from 256 chunks on (here 301: five blocks, the last one
+    ragged): a channel decay always, a scalar decay when its scan takes half
+    the compute units (B = 1, H = 16); checked on sampled heads."""
     T = 64 * 300 + 17
-    inp = make_inputs(variant, 1, T, 4, 128, 128, "bf16", seed=87, state_scale=0.3)
+    inp = make_inputs(variant, 1, T, H, 128, 128, "bf16", seed=87, state_scale=0.3)
     o, s = gpu_forward(variant, to_dev(inp))
-    heads = [(0, 0), (0, 3)]
+    heads = [(0, 0), (0, H - 1)]
     o_ref, s_ref = run_oracle(variant, inp, heads=heads)
     for b, h in heads:
         e_o = rel_err(o[b:b + 1, :, h:h + 1].float().cpu(), o_ref[b:b + 1, :, h:h + 1], (0, 2))
