@@ -53,9 +53,8 @@
  *     second, internal stream, ordered against `hip_stream` with events: the
  *     library creates that stream and five events once per host thread and
  *     device and keeps them for the life of the process.  The call still
- *     behaves as one operation on `hip_stream`
- *     (later work on it waits for all of it), and it can be captured into a
- *     HIP graph.
+ *     behaves as one operation on `hip_stream` (later work on it waits for
+ *     all of it), and it can be captured into a HIP graph.
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
  *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
