@@ -500,6 +500,12 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
     __shared__ float sB[4][C][CP];   // 0: T; 1: A, then Y; 2: dP; 3: dT, then dA
     __shared__ float sG[C], sbeta[C], sn[C], ssa[C], ssu[C], sdg[C], svrow[C], svcol[C], scoef[C];
     __shared__ float sdgam[DK], sdgc[DK];
+    // Channel decay: the split Gram operands are scaled relative to their own
+    // 16-row block's reference m_R = (g_{16R} + g_{16R+15}) / 2; an
+    // off-diagonal tile (R, S) multiplies its right operand by the middle
+    // factor e^{m_R - m_S} <= 1, pair_of(R, S), and row 6 holds ones for the
+    // diagonal tiles.
+    __shared__ __attribute__((aligned(16))) float sMf[kSlotX ? 7 : 1][kSlotX ? DK : 4];
     float(*sT)[CP] = sB[0];
     float(*sA)[CP] = sB[1];
     float(*sY)[CP] = sB[1];
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             if (tid < DK) {
                 float gg = 0.f;
                 for (int r = 0; r < C; ++r) {
-                    if (r < nvalid) gg += logf(p.alpha[tok(r) * DK + tid]);
+                    if (r < nvalid) gg += fmaxf(logf(p.alpha[tok(r) * DK + tid]), kLogDecayFloor);
                     Gd[r * DK + tid] = gg;
                 }
             }
@@ -622,11 +628,23 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 if constexpr (VT::kGates) aa = ok ? p.erase_b[o] * kk : 0.f;
                 else aa = sbeta[r] * kk;
                 const float gr = Gd[idx];
-                const float e = __expf(gr - Gd[(C / 2 - 1) * DK + i]);
+                const int rb = 16 * (r >> 4);
+                const float mref = 0.5f * (Gd[rb * DK + i] + Gd[(rb + 15) * DK + i]);
+                const float e = __expf(gr - mref);
                 Xq[idx] = qq * e;
                 Xa[idx] = aa * e;
-                Xk[idx] = kk / e;
+                Xk[idx] = kk * __expf(mref - gr);
                 Ag[idx] = aa * __expf(gr);
+            }
+            for (int idx = tid; idx < 7 * DK; idx += NT) {
+                const int pr = idx / DK, i = idx % DK;
+                float m = 1.f;
+                if (pr < 6) {
+                    const int R = pair_r(pr), S = pair_s(pr);
+                    m = __expf(0.5f * (Gd[16 * R * DK + i] + Gd[(16 * R + 15) * DK + i]) -
+                               0.5f * (Gd[16 * S * DK + i] + Gd[(16 * S + 15) * DK + i]));
+                }
+                sMf[pr][i] = m;
             }
             __syncthreads();
         }
@@ -637,8 +655,10 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             f32x4 acc;
             if constexpr (kSlotX) {
                 const float *X = isP ? Xq : Xa;
+                const float *mrow = sMf[Sb < R ? pair_of(R, Sb) : 6];
                 acc = mm_rr<DK>([&](int kk) { return ld4(X + (16 * R + l16) * DK + kk); },
-                                [&](int kk) { return ld4(Xk + (16 * Sb + l16) * DK + kk); }, lg, zero4());
+                                [&](int kk) { return ld4(Xk + (16 * Sb + l16) * DK + kk) * ld4(mrow + kk); },
+                                lg, zero4());
             } else {
                 // q k^T or k k^T (rows of A scaled by beta below): exact products of the inputs
                 const TI *X = isP ? q : k;
@@ -1042,6 +1062,12 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             if constexpr (kStageQK) return (float)sKt[cc][m];
             else return xk1(m, cc);
         };
+        // middle factor of tile (R, S) of the split Gram operands at channel cc
+        // (1 on the diagonal and without a channel decay)
+        auto mfac = [&](int R, int S, int cc) -> float {
+            if constexpr (kSlotX) return sMf[S < R ? pair_of(R, S) : 6][cc];
+            else return 1.f;
+        };
         auto ha = [&](int m, int cc) -> float {
             if constexpr (kStageQK) return (float)sKt[cc][m] * sbeta[m];
             else return xa1(m, cc);
@@ -1058,13 +1084,15 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
             with_block(R, [&](auto Rc) {
                 constexpr int RB = decltype(Rc)::value;
                 xa = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdA[16 * RB + l16][m]; },
-                                             [&](int m) { return hk(m, col); }, lg, xa);
+                                             [&](int m) { return hk(m, col) * mfac(RB, m >> 4, col); },
+                                             lg, xa);
                 xq = mm_kt<0, 16 * (RB + 1)>([&](int m) { return sdP[16 * RB + l16][m]; },
-                                             [&](int m) { return hk(m, col); }, lg, xq);
+                                             [&](int m) { return hk(m, col) * mfac(RB, m >> 4, col); },
+                                             lg, xq);
                 xk = mm_kt<16 * RB, C>([&](int m) { return sdA[m][16 * RB + l16]; },
-                                       [&](int m) { return ha(m, col); }, lg, xk);
+                                       [&](int m) { return ha(m, col) * mfac(m >> 4, RB, col); }, lg, xk);
                 xk = mm_kt<16 * RB, C>([&](int m) { return sdP[m][16 * RB + l16]; },
-                                       [&](int m) { return hq(m, col); }, lg, xk);
+                                       [&](int m) { return hq(m, col) * mfac(m >> 4, RB, col); }, lg, xk);
             });
             float e_col = 0.f;
 #pragma unroll
@@ -1088,11 +1116,12 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 if constexpr (VT::kChannelDecay) {
                     gr = Gd[idx];
                     gC = Gd[(C - 1) * DK + col];
-                    const float e = __expf(gr - Gd[(C / 2 - 1) * DK + col]);
+                    const float mref = 0.5f * (Gd[16 * R * DK + col] + Gd[(16 * R + 15) * DK + col]);
+                    const float e = __expf(gr - mref);
                     dg = Xa[idx] * da + Xq[idx] * dq - Xk[idx] * dk;
                     dq *= e;
                     da *= e;
-                    dk /= e;
+                    dk *= __expf(mref - gr);
                 } else if constexpr (kRowDecay) {
                     gr = sG[r];
                     gC = sG[C - 1];
@@ -1156,8 +1185,10 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
                 for (int r = C - 1; r >= 0; --r) {
                     acc += dGd[r * DK + i];
                     if (r < nvalid) {
+                        // d/d alpha of the chunk form, whose log decay is
+                        // floored: taken at the applied decay max(alpha, e^F)
                         const long o = tok(r) * DK + i;
-                        g.d_alpha[o] = acc / p.alpha[o];
+                        g.d_alpha[o] = acc / fmaxf(p.alpha[o], kDecayFloor);
                     }
                 }
             }

@@ -44,6 +44,7 @@
 // that each lane's four accumulator values are four consecutive elements of
 // the destination.  The chunk factors are stored fragment-major, so the scan
 // reads each operand tile as one contiguous 1 KB block.
+#include <atomic>
 #include <type_traits>
 
 #include "gdr_device.hpp"
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
         if (tid < DK) {
             float g = 0.f;
             for (int r = 0; r < C; ++r) {
-                if (r < nvalid) g += log_decay(p.alpha[tok(r) * DK + tid], rawg, ds);
+                if (r < nvalid) g += fmaxf(log_decay(p.alpha[tok(r) * DK + tid], rawg, ds), kLogDecayFloor);
                 sG[r][tid] = g;
             }
         }
@@ -366,8 +367,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     // ---- phase 2: A and P on matrix cores -----------------------------------
     // Computed transposed, D'(s, r) = sum_i Kr[s][i] L[r][i], so a lane holds
     // four consecutive s of one row r.  Channel-wise decay is split between
-    // the operands around the mid-chunk reference g_ref = g_{C/2-1}; scalar
-    // decay is applied to the product as e^{g_r - g_s} <= 1.
+    // the operands around the reference m_R = (g_{16R} + g_{16R+15}) / 2 of the
+    // tile's row block R: the left factor e^{g_r - m_R} and the right factor
+    // e^{m_R - g_s} each stay within e^{+-7.5 F} (F the log-decay floor), and
+    // off the diagonal (s in an earlier block) the right one is at most 1.
+    // Scalar decay is applied to the product as e^{g_r - g_s} <= 1.
     for (int tl = wave; tl < 10; tl += kPrepThreads / kWave) {
         const int R = lower_r(tl), S = lower_s(tl);
         const int rs = 16 * S + l16;   // row supplying the K_R operand
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
                     a = br * ar[e];
                 }
                 if constexpr (VT::kChannelDecay) {
-                    const float gref = sG[C / 2 - 1][kb + e];
+                    const float gref = 0.5f * (sG[16 * R][kb + e] + sG[16 * R + 15][kb + e]);
                     const float fl = __expf(sG[rr][kb + e] - gref);
                     kr[e] *= __expf(gref - sG[rs][kb + e]);
                     a *= fl;
@@ -639,14 +643,20 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[4][16][17];
-    // Channel decay: the Gram products' split operands, k e^{g_ref - g}
-    // (right) and a e^{g - g_ref}, q e^{g - g_ref} (left), are formed once per
-    // item in phase 1 instead of per tile in phase 2 (this prep runs one
-    // workgroup per CU, so the LDS is there).  With gates, a = b (.) k is
-    // scaled in place in its own tile.
+    // Channel decay: the Gram products' split operands, k e^{m - g} (right)
+    // and a e^{g - m}, q e^{g - m} (left), with m = (g_{16R} + g_{16R+15}) / 2
+    // the reference of the row's own 16-row block R, are formed once per item
+    // in phase 1 instead of per tile in phase 2 (this prep runs one workgroup
+    // per CU, so the LDS is there).  With gates, a = b (.) k is scaled in
+    // place in its own tile.  A diagonal tile (R, R) multiplies them as they
+    // are.  An off-diagonal tile (R, S), S < R, needs its right operand
+    // relative to m_R instead of m_S: its k fragments are multiplied by the
+    // middle factor e^{m_R - m_S} <= 1 from sM (both left and right factors of
+    // such a tile then stay bounded, the right one by 1).
     constexpr bool kSplit = VT::kChannelDecay;
     constexpr int NS = VT::kGates ? 2 : 3;
     __shared__ __attribute__((aligned(16))) bf16 sSplit[kSplit ? NS : 1][kSplit ? C * DK : 8];
+    __shared__ __attribute__((aligned(16))) float sM[kSplit ? 6 : 1][kSplit ? DK : 4];
     bf16 *const sKr = sSplit[0];
     bf16 *const sQl = sSplit[kSplit ? NS - 1 : 0];
     bf16 *const sAl = VT::kGates ? sAg : sSplit[kSplit && !VT::kGates ? 1 : 0];
@@ -802,7 +812,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             f32x4 lg4 = zero4();
             if (r < nvalid)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lg4[e] = log_decay(raw.al[n][e], rawg, ds);
+                for (int e = 0; e < 4; ++e)
+                    lg4[e] = fmaxf(log_decay(raw.al[n][e], rawg, ds), kLogDecayFloor);
             *reinterpret_cast<f32x4 *>(&sG[r][i4]) = lg4;
         }
     } else if constexpr (VT::kHasDecay) {
@@ -913,7 +924,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             for (int cc = 0; cc < 2; ++cc) {
                 const int i = i0 + cc;
                 const float gC = sG[C - 1][VT::kChannelDecay ? i : 0];
-                const float gref = sG[C / 2 - 1][VT::kChannelDecay ? i : 0];
+                // the reference of the 16-row block holding rows r0 .. r0 + 7
+                const int ib = VT::kChannelDecay ? i : 0;
+                const float gref = 0.5f * (sG[16 * (r0 >> 4)][ib] + sG[16 * (r0 >> 4) + 15][ib]);
                 // element cc of a word holding two bf16 (little-endian)
                 auto half = [&](uint32_t w) {
                     return __uint_as_float(cc ? (w & 0xffff0000u) : (w << 16));
@@ -964,7 +977,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 bf16x8 kr8, al8, ql8;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float gref = sG[C / 2 - 1][8 * pc + e], g = sG[r][8 * pc + e];
+                    const int i = 8 * pc + e;
+                    const float gref = 0.5f * (sG[16 * (r >> 4)][i] + sG[16 * (r >> 4) + 15][i]);
+                    const float g = sG[r][i];
                     const float fl = __expf(g - gref);
                     kr8[e] = (bf16)((float)k8[e] * __expf(gref - g));
                     if constexpr (!VT::kGates) al8[e] = (bf16)(br * (float)k8[e] * fl);
@@ -973,6 +988,14 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 *reinterpret_cast<bf16x8 *>(&sKr[kx(r, 8 * pc)]) = kr8;
                 if constexpr (!VT::kGates) *reinterpret_cast<bf16x8 *>(&sAl[kx(r, 8 * pc)]) = al8;
                 *reinterpret_cast<bf16x8 *>(&sQl[kx(r, 8 * pc)]) = ql8;
+            }
+            // middle factors e^{m_R - m_S} of the six off-diagonal tiles
+            for (int idx = tid; idx < 6 * DK; idx += NT) {
+                const int pr = idx / DK, i = idx % DK;
+                const int R = pair_r(pr), S = pair_s(pr);
+                const float mR = 0.5f * (sG[16 * R][i] + sG[16 * R + 15][i]);
+                const float mS = 0.5f * (sG[16 * S][i] + sG[16 * S + 15][i]);
+                sM[pr][i] = __expf(mR - mS);
             }
         }
         // U^T into LDS, two columns of eight rows per thread in the same way
@@ -1008,8 +1031,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // ---- phase 2: A and P on matrix cores ---------------------------------------
     // Computed transposed, D'(s, r) = sum_i Kr[s][i] L[r][i]: a lane holds four
     // consecutive s of one row r.  Channel-wise decay is split between the
-    // operands around g_ref = g_{C/2-1}; scalar decay multiplies the product by
-    // e^{g_r - g_s} <= 1.
+    // operands around each 16-row block's reference (see sSplit); scalar decay
+    // multiplies the product by e^{g_r - g_s} <= 1.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (u >= gN) break;
@@ -1031,7 +1054,17 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                 accA = M::mma(kr8, kq8, accA);
                 accP = M::mma(kr8, qf[ks], accP);
             } else {
-                const bf16x8 kq = *reinterpret_cast<const bf16x8 *>(&sKr[kx(rs, kb)]);
+                bf16x8 kq = *reinterpret_cast<const bf16x8 *>(&sKr[kx(rs, kb)]);
+                if (S < R) {   // wave-uniform
+                    const float *mf = &sM[kSplit ? pair_of(R, S) : 0][kSplit ? kb : 0];
+                    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(mf);
+                    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(mf + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kq[e] = (bf16)((float)kq[e] * m0[e]);
+                        kq[e + 4] = (bf16)((float)kq[e + 4] * m1[e]);
+                    }
+                }
                 accA = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sAl[kx(rr, kb)]), accA);
                 accP = M::mma(kq, *reinterpret_cast<const bf16x8 *>(&sQl[kx(rr, kb)]), accP);
             }
@@ -1572,20 +1605,24 @@ hipError_t aux_stream(AuxStream **out) {
     return hipSuccess;
 }
 
-// Compute units of the current device, queried once per device.
+// Compute units of the current device, queried once per device.  Threads
+// that race on the first query each store the same value; the atomics make
+// that well defined.
 hipError_t device_cus(long *out) {
-    static long ncu[kMaxDevices] = {};
+    static std::atomic<long> ncu[kMaxDevices] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (ncu[dev] == 0) {
+    long n = ncu[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         int cus = 0;
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
             return e;
-        ncu[dev] = cus > 0 ? cus : 1;
+        n = cus > 0 ? cus : 1;
+        ncu[dev].store(n, std::memory_order_relaxed);
     }
-    *out = ncu[dev];
+    *out = n;
     return hipSuccess;
 }
 
@@ -1601,13 +1638,16 @@ long scan_workgroups(const Problem &p, bool scalar_decay, bool concurrent, long 
 
 // Workgroups of the bf16 prep kernel that the device holds at once (resident
 // slots) and its compute units, queried once per device and kernel instance.
+// The unit count is stored before the slot count (release) and read after it
+// (acquire), so a thread that sees the slots also sees the units.
 template <int V, int DK, int DV, bool RT> hipError_t prep_slots(long *slots_out, long *cus_out) {
-    static long slots[kMaxDevices] = {}, ncu[kMaxDevices] = {};
+    static std::atomic<long> slots[kMaxDevices] = {}, ncu[kMaxDevices] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (slots[dev] == 0) {
+    long sl = slots[dev].load(std::memory_order_acquire), nc = 0;
+    if (sl == 0) {
         int per_cu = 0, cus = 0;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void *>(&chunk_prep_bf16_kernel<V, DK, DV, RT>),
@@ -1616,11 +1656,15 @@ template <int V, int DK, int DV, bool RT> hipError_t prep_slots(long *slots_out,
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
             hipSuccess)
             return e;
-        ncu[dev] = cus > 0 ? cus : 1;
-        slots[dev] = (long)(per_cu > 0 ? per_cu : 1) * ncu[dev];
+        nc = cus > 0 ? cus : 1;
+        sl = (long)(per_cu > 0 ? per_cu : 1) * nc;
+        ncu[dev].store(nc, std::memory_order_relaxed);
+        slots[dev].store(sl, std::memory_order_release);
+    } else {
+        nc = ncu[dev].load(std::memory_order_relaxed);
     }
-    *slots_out = slots[dev];
-    *cus_out = ncu[dev];
+    *slots_out = sl;
+    *cus_out = nc;
     return hipSuccess;
 }
 

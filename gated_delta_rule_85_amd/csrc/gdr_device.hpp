@@ -39,6 +39,25 @@ __device__ __forceinline__ float log_decay(float x, bool raw, float s) {
     return raw ? -s * softplus_f(x) : logf(x);
 }
 
+// Floor of a per-channel log decay inside the chunk form.  The chunk form
+// splits a channel-wise decay e^{g_r - g_s} between the two operands of its
+// Gram products around one reference per 16-row block, the midpoint of that
+// block's log-decay range; with every token's log decay at least -F, each
+// factor stays within e^{+-7.5 F} (15 decays per block), inside the fp32 and
+// bf16 range for F = 10.  A decay below e^{-10} ~ 4.5e-5 is applied as
+// e^{-10}: the part of a channel's state it lets through is then at most
+// 4.5e-5 of that state instead of less.  Decays at or above e^{-10} are exact.
+// The decode step applies every decay as given.
+constexpr float kLogDecayFloor = -10.f;
+// e^{kLogDecayFloor}: the smallest decay the chunk form applies.
+constexpr float kDecayFloor = 4.53999297624848515e-5f;
+// Middle factors of the off-diagonal 16x16 tiles of a 64-row chunk: pair p of
+// the six strictly lower tile positions (R, S) = (1,0) (2,0) (2,1) (3,0) (3,1)
+// (3,2), p = R (R - 1) / 2 + S.
+__device__ __forceinline__ int pair_r(int p) { return 1 + (p >= 1) + (p >= 3); }
+__device__ __forceinline__ int pair_s(int p) { const int r = pair_r(p); return p - r * (r - 1) / 2; }
+__device__ __forceinline__ int pair_of(int R, int S) { return R * (R - 1) / 2 + S; }
+
 // Sum over the 64 lanes of a wave; every lane gets the result.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -174,6 +174,29 @@ def make_raw_inputs(variant, B, T, H, dk, dv, dtype="bf16", seed=0, state_scale=
     return out
 
 
+def with_strong_channel_decay(inp, frac=1 / 3, lo=1e-3, hi=0.05, seed=0, log=False):
+    """Replace the per-channel decay of ``frac`` of the key channels of every
+    head by values drawn uniformly from [lo, hi] (one draw per (b, t, h, i);
+    with ``log``, uniformly in log(alpha) between log(lo) and log(hi)).
+    The channels are drawn per (b, h).  Returns a new dict; the other tensors
+    are shared.  Strong channel-wise decay is what sets the Kimi and Gated
+    DeltaNet-2 variants apart from a scalar forget gate."""
+    alpha = inp["alpha"]
+    if alpha is None or alpha.dim() != 4:
+        raise ValueError("needs a per-channel decay [B, T, H, dk]")
+    rng = np.random.default_rng(seed)
+    B, T, H, dk = alpha.shape
+    pick = rng.random((B, 1, H, dk)) < frac
+    if log:
+        strong = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(B, T, H, dk)))
+    else:
+        strong = rng.uniform(lo, hi, size=(B, T, H, dk))
+    a = np.where(pick, strong, alpha.numpy().astype(np.float64)).astype(np.float32)
+    out = dict(inp)
+    out["alpha"] = torch.from_numpy(a)
+    return out
+
+
 def make_routed_value(B, T, H, dv, dtype="bf16", seed=0, scale=1.0):
     """A value routed in from another layer, N(0,1) * scale [B,T,H,dv] in ``dtype``."""
     rng = np.random.default_rng(seed)

@@ -58,7 +58,16 @@
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
  *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
- *                DELTANET: must be NULL.  Linear decay in (0, 1].
+ *                DELTANET: must be NULL.  Linear decay in (0, 1].  A scalar
+ *                decay is applied exactly everywhere.  A channel-wise decay
+ *                (KDA, GDN2) below e^-10 (about 4.5e-5; with
+ *                GDR_FLAG_RAW_GATES, decay_scale * softplus(x) above 10) is
+ *                applied as e^-10 by the chunked forward and its gradient: the
+ *                chunk form splits the decay between two matrix-core operands,
+ *                and this floor keeps both factors inside the float range.  At
+ *                most 4.5e-5 of that channel's state then passes the token
+ *                where less should; decays at or above e^-10 are exact.  The
+ *                decode step applies every decay as given.
  *       beta     DELTANET, GATED_DELTANET, KDA: beta [B, T, H];
  *                KLA: eta [B, T, H];  GDN2: must be NULL.
  *       erase_b  GDN2: [B, T, H, dk], else NULL.
@@ -70,8 +79,13 @@
  *     nothing.  Gate values are device data and are not checked: NaN or Inf
  *     propagate.  Launch failures return GDR_ERR_HIP; faults inside a kernel
  *     surface at the caller's next synchronisation.
- *   - The functions keep no state between calls and may be called from several
- *     threads; a thread-local message explains the last failure.
+ *   - The functions may be called from several host threads at once.  Calls
+ *     keep no data of their own between them; the library keeps, per device,
+ *     its compute-unit count and the resident-workgroup counts of its kernels
+ *     (queried once; the workspace size of a call depends on the current
+ *     device's unit count), and per host thread and device the internal stream
+ *     and events above.  None of these is ever released.  A thread-local
+ *     message explains the last failure.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -200,7 +214,11 @@ typedef struct gdr_grads {
      * to.  Each is required exactly when the variant takes that input. */
     float *d_q, *d_k;         /* [B, T, H, dk] */
     float *d_v;               /* [B, T, H, dv] */
-    float *d_alpha;           /* shaped like alpha: gradient w.r.t. the linear decay */
+    float *d_alpha;           /* shaped like alpha: gradient w.r.t. the linear decay,
+                                 formed as (dL/d log alpha) / alpha, so its
+                                 absolute error grows like 1/alpha for small
+                                 decays; for a channel-wise decay below e^-10
+                                 it is taken at e^-10 (see alpha above) */
     float *d_beta;            /* shaped like beta (w.r.t. eta for KLA) */
     float *d_erase_b;         /* GDN2 [B, T, H, dk] */
     float *d_write_w;         /* GDN2 [B, T, H, dv] */
