@@ -76,6 +76,8 @@ def lib(path: str | None = None):
     L.gdr_forward_workspace_size.restype = ctypes.c_size_t
     L.gdr_forward_chunked.argtypes = [A, _vp, ctypes.c_size_t, _vp]
     L.gdr_forward_chunked.restype = ctypes.c_int
+    L.gdr_forward_chunked_noalloc.argtypes = [A, _vp]
+    L.gdr_forward_chunked_noalloc.restype = ctypes.c_int
     L.gdr_decode_step.argtypes = [A, _vp]
     L.gdr_decode_step.restype = ctypes.c_int
     G = ctypes.POINTER(GdrGrads)
@@ -105,6 +107,14 @@ def gdr_forward_workspace_size(args: GdrArgs) -> int:
 def gdr_forward_chunked(args: GdrArgs, workspace: int, ws_bytes: int, stream: int) -> int:
     return lib().gdr_forward_chunked(ctypes.byref(args), workspace or None, ws_bytes,
                                      stream or None)
+
+
+# GDR_NOALLOC_WORKSPACE_MAX of gdr.h: the static workspace of the allocation-free forward
+NOALLOC_WORKSPACE_MAX = 256 << 20
+
+
+def gdr_forward_chunked_noalloc(args: GdrArgs, stream: int) -> int:
+    return lib().gdr_forward_chunked_noalloc(ctypes.byref(args), stream or None)
 
 
 def gdr_decode_step(args: GdrArgs, stream: int) -> int:
@@ -202,6 +212,20 @@ def forward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
     check(gdr_forward_chunked(a, workspace.data_ptr(), workspace.numel(),
                               _stream_handle(stream)))
     return (o, state_out, delta) if want_delta else (o, state_out)
+
+
+def forward_noalloc(variant: str, q, k, v, alpha=None, beta=None, erase_b=None,
+                    write_w=None, eps: float = 0.0, state_in=None, o=None, state_out=None,
+                    stream=None, flags: int = 0, decay_scale: float = 0.0, v_route=None,
+                    delta_out=None):
+    """gdr_forward_chunked_noalloc on device tensors: the outputs (o, and
+    state_out if given) must be passed in, so that nothing is allocated.
+    Returns (o, state_out)."""
+    a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps,
+                  state_in, state_out, flags=flags, decay_scale=decay_scale,
+                  v_route=v_route, delta_out=delta_out)
+    check(gdr_forward_chunked_noalloc(a, _stream_handle(stream)))
+    return o, state_out
 
 
 def workspace_bytes(variant: str, q, k, v) -> int:

@@ -5,10 +5,40 @@
 #include <stdarg.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "gdr.h"
 #include "gdr_kernels.hpp"
 
+// Workspace of gdr_forward_chunked_noalloc: one array per device, placed by
+// the code object's loader, never allocated by a call.  Host code must not
+// pass this name to a kernel or a copy (on the host it is a stand-in, not a
+// device address); it uses the address hipGetSymbolAddress returns for the
+// current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_WORKSPACE_MAX];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch[kMaxScratchDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first call made with that device current and kept.  Threads that race on the
+// first lookup store the same address.
+hipError_t noalloc_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return hipSuccess;
+}
 
 thread_local char g_detail[512];
 
@@ -198,6 +228,25 @@ gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_byt
             return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
     }
     hipError_t e = gdr::launch_forward(p, workspace, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status gdr_forward_chunked_noalloc(const gdr_args *a, void *hip_stream) {
+    gdr_status s = check(a, 0);
+    if (s != GDR_OK) return s;
+    gdr::Problem p = to_problem(a);
+    const size_t need = gdr::forward_workspace_bytes(p);
+    if (need > GDR_NOALLOC_WORKSPACE_MAX)
+        return fail(GDR_ERR_WORKSPACE,
+                    "this call needs %zu bytes of workspace; the static workspace of "
+                    "gdr_forward_chunked_noalloc holds %zu (use gdr_forward_chunked)",
+                    need, (size_t)GDR_NOALLOC_WORKSPACE_MAX);
+    void *ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(GDR_ERR_HIP, "static workspace lookup failed: %s", hipGetErrorString(e));
+    e = gdr::launch_forward(p, ws, reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GDR_OK;
 }

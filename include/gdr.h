@@ -190,6 +190,21 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
 gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_bytes,
                                void *hip_stream);
 
+/* gdr_forward_chunked for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, the same kernels and results, with the
+ * workspace taken from a static device array of GDR_NOALLOC_WORKSPACE_MAX bytes
+ * that the library holds on every device it runs on until the process ends.
+ * The call allocates and frees nothing; its first call with a device current
+ * looks up that device's array, and like gdr_forward_chunked a pipelined call
+ * creates the internal stream and events on a thread's first such call.
+ * Returns GDR_ERR_WORKSPACE, enqueuing nothing, when
+ * gdr_forward_workspace_size(a) exceeds GDR_NOALLOC_WORKSPACE_MAX.  All calls
+ * on one device share its array: calls that may overlap on a device (other
+ * streams, other threads) race and must be ordered by the caller. */
+#define GDR_NOALLOC_WORKSPACE_MAX ((size_t)256 << 20)
+gdr_status gdr_forward_chunked_noalloc(const gdr_args *a, void *hip_stream);
+
 /* One recurrent decode step (requires T == 1) for every (b, h): reads
  * state_in (required), writes o and state_out (required; may equal state_in
  * for an in-place update). */

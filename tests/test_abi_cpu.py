@@ -79,8 +79,15 @@ def test_invalid_arguments_rejected(L, over, status):
     a = _args(**over)
     assert binding.gdr_check_args(a, 0) == status
     assert binding.gdr_last_error_detail() != ""
-    # The entry point rejects the same call before touching the GPU.
+    # The entry points reject the same call before touching the GPU.
     assert binding.gdr_forward_chunked(a, 0x10000, 1 << 30, 0) == status
+    assert binding.gdr_forward_chunked_noalloc(a, 0) == status
+
+
+def test_noalloc_workspace_limit_matches_header():
+    m = re.search(r"#define GDR_NOALLOC_WORKSPACE_MAX \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_WORKSPACE_MAX
 
 
 @pytest.mark.parametrize("variant", list(binding.VARIANTS))

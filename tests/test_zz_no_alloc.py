@@ -1,0 +1,71 @@
+"""The allocation-free chunked forward (gdr_forward_chunked_noalloc) against
+gdr_forward_chunked, through the C ABI, on two calls in a row: the Kaczmarz
+long-context prefill that the benchmark times (B=1, H=16, T=65536, bf16,
+pipelined through the static workspace), then smaller calls in one pass, bf16
+and fp32, scalar and channel decay.  Both entry points run the same kernels on
+the same plan, so their outputs must be bit-identical (a stricter bar than the
+oracle tolerance, which the other parity tests hold the shared kernels to).
+A call whose workspace exceeds the static array is rejected before any work."""
+import pytest
+import torch
+
+from gated_delta_rule_85_amd import binding
+from gated_delta_rule_85_amd.inputs import make_inputs
+from tests.gpu_common import announce, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.lib()
+
+
+def _both(variant, d):
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    o_ref, s_ref = binding.forward(variant, d["q"], d["k"], d["v"], alpha=d["alpha"],
+                                   beta=d["beta"], erase_b=d["erase_b"], write_w=d["write_w"],
+                                   eps=d["eps"], state_in=d["state_in"])
+    o = torch.full((B, T, H, dv), float("nan"), dtype=d["q"].dtype, device=d["q"].device)
+    s = torch.full((B, H, dk, dv), float("nan"), dtype=torch.float32, device=d["q"].device)
+    binding.forward_noalloc(variant, d["q"], d["k"], d["v"], alpha=d["alpha"], beta=d["beta"],
+                            erase_b=d["erase_b"], write_w=d["write_w"], eps=d["eps"],
+                            state_in=d["state_in"], o=o, state_out=s)
+    torch.cuda.synchronize()
+    return o, s, o_ref, s_ref
+
+
+CASES = [  # (variant, B, T, H, dtype): each pair of consecutive cases is a larger then a smaller call
+    ("kla", 1, 65536, 16, "bf16"),
+    ("kla", 2, 205, 3, "bf16"),
+    ("kda", 1, 256 * 64 + 37, 4, "bf16"),
+    ("gdn2", 2, 150, 2, "fp32"),
+]
+
+
+def test_noalloc_matches_forward_on_consecutive_calls():
+    for variant, B, T, H, dtype in CASES:
+        announce(f"noalloc {variant} B={B} T={T} H={H} {dtype}")
+        inp = make_inputs(variant, B, T, H, 128, 128, dtype, seed=1234 + T,
+                          alpha_scale=0.05 if variant in ("kda", "gdn2") else 0.1,
+                          state_scale=0.2)
+        o, s, o_ref, s_ref = _both(variant, to_dev(inp))
+        assert torch.equal(o, o_ref), f"o differs for {variant} T={T}"
+        assert torch.equal(s, s_ref), f"state differs for {variant} T={T}"
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array():
+    """Gated DeltaNet-2 at B=2, H=16, T=8192 (128 chunks, one pass) needs ~300 MB."""
+    inp = make_inputs("gdn2", 2, 8192, 16, 128, 128, "bf16", seed=5)
+    d = to_dev(inp)
+    need = binding.workspace_bytes("gdn2", d["q"], d["k"], d["v"])
+    assert need > binding.NOALLOC_WORKSPACE_MAX
+    o = torch.zeros(2, 8192, 16, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(binding.GdrError) as err:
+        binding.forward_noalloc("gdn2", d["q"], d["k"], d["v"], alpha=d["alpha"],
+                                erase_b=d["erase_b"], write_w=d["write_w"], o=o)
+    assert err.value.status == 3 and "static workspace" in str(err.value)
+    torch.cuda.synchronize()
+    assert not o.any()   # nothing was enqueued
