@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, dense bf16 matrix cores
+PEAK_FP32_MATRIX = 157.3e12  # FLOP/s, fp32 matrix cores
 C = 64                     # chunk length
 
 
@@ -64,6 +65,17 @@ def forward_bytes(B, T, H, dk, dv, in_bytes=2, channel_decay=False):
     gates read once, S_0 absent (zeros), S_T written."""
     tok = B * T * H
     gates = 4 * (dk if channel_decay else 1) + 4  # alpha + eta
+    return tok * (in_bytes * (2 * dk + 2 * dv) + gates) + B * H * dk * dv * 4
+
+
+def forward_bytes_variant(variant, B, T, H, dk, dv, in_bytes):
+    """Algorithmic HBM bytes of one forward of any variant: q, k, v read and o
+    written once, each gate tensor the variant takes read once (alpha per
+    token or per key channel, beta/eta per token, GDN-2's erase gate per key
+    and write gate per value channel), S_0 absent, S_T written."""
+    tok = B * T * H
+    gates = {"deltanet": 4, "gated_deltanet": 8, "kla": 8, "kda": 4 * dk + 4,
+             "gdn2": 4 * dk + 4 * dk + 4 * dv}[variant]
     return tok * (in_bytes * (2 * dk + 2 * dv) + gates) + B * H * dk * dv * 4
 
 
@@ -526,12 +538,64 @@ def cold_decode(args):
     print(json.dumps(out))
 
 
+def other_workloads(L, dev, sh, steps, warmup):
+    """The forward of workloads 1-4 (DeltaNet fp32, Gated DeltaNet, KDA,
+    Gated DeltaNet-2), each timed with HIP events on the launch stream over
+    `steps` back-to-back calls after `warmup` untimed ones."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import WORKLOADS, make_workload
+
+    res = {}
+    for wid in (1, 2, 3, 4):
+        wl = WORKLOADS[wid]
+        B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in make_workload(wl).items()}
+        o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
+        s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        a = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"],
+                              d["erase_b"], d["write_w"], d["eps"], None, s_T)
+        binding.check(binding.gdr_check_args(a, 0))
+        n = binding.gdr_forward_workspace_size(a)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        ref = ctypes.byref(a)
+        for _ in range(warmup):
+            binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / steps
+        in_bytes = 2 if wl.dtype == "bf16" else 4
+        fl = forward_flops_per_head_token(dk, dv) * B * T * H
+        fb = forward_bytes_variant(wl.variant, B, T, H, dk, dv, in_bytes)
+        peak_mm = PEAK_BF16 if wl.dtype == "bf16" else PEAK_FP32_MATRIX
+        res[wl.name] = dict(variant=wl.variant, dtype=wl.dtype, B=B, T=T, H=H, dk=dk, dv=dv,
+                            ms=t * 1e3, tokens_per_s=B * T / t, tflops=fl / t / 1e12,
+                            mfma_frac=fl / t / peak_mm,
+                            mfma_peak_TFLOPs=peak_mm / 1e12, hbm_GBps=fb / t / 1e9,
+                            hbm_frac=fb / t / PEAK_HBM, algorithmic_flop=fl,
+                            algorithmic_bytes=fb)
+        log(f"{wl.name}: {t * 1e6:.1f} us")
+        del d, o, s_T, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cold-state decode and the forward of workloads 1-4 "
+                         "(profiler runs of the main step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--no-graph", action="store_true",
@@ -676,6 +740,44 @@ def main():
         log("copy calibration: 268435456 bytes read and written")
         del src, dst
 
+    # ---- after the timed region: the decode with its state in HBM ----------
+    # Back to back, the 64 MiB batch state stays in the 256 MiB last-level
+    # cache (MALL) between steps, so the timed figure above is a cache-resident
+    # one.  Here each launch follows a 1 GiB read sweep that evicts the state,
+    # and is timed on its own on the launch stream; the box's device-copy rate
+    # over 2 GiB buffers is measured beside it.
+    n_cold = 0 if args.no_extras else 64
+    if n_cold:
+        log("cold-state decode launches and the box's copy rate")
+        flush = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+        pairs = [(ev(), ev()) for _ in range(n_cold)]
+        for s_ in range(n_cold):
+            flush.sum()
+            pairs[s_][0].record(stream)
+            binding.check(dec_fn(dargs_ref[s_], sh))
+            pairs[s_][1].record(stream)
+        torch.cuda.synchronize()
+        cold_us = sorted(a_.elapsed_time(b_) * 1e3 for a_, b_ in pairs)
+        del flush
+        src = torch.ones(512 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = ev(), ev()
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_Bps = 2 * src.numel() * 4 / (c0.elapsed_time(c1) / 1e3 / 10)
+        del src, dst
+        torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_extras:
+        log("forward of workloads 1-4")
+        others = other_workloads(L, dev, sh, steps=20, warmup=3)
+
     fwd_ms = [t["f0"].elapsed_time(t["f1"]) for t in timers]
     dec_ms = [t["f1"].elapsed_time(t["d1"]) for t in timers]
     fwd_s = sum(fwd_ms) / len(fwd_ms) / 1e3
@@ -698,16 +800,32 @@ def main():
                    tflops=fl / fwd_s / 1e12, mfma_frac=fl / fwd_s / PEAK_BF16,
                    hbm_GBps=fb / fwd_s / 1e9, hbm_frac=fb / fwd_s / PEAK_HBM,
                    algorithmic_flop=fl, algorithmic_bytes=fb)
+    cold_state = None
+    if n_cold:
+        cold_med = cold_us[n_cold // 2] * 1e-6
+        cold_state = dict(
+            note=f"{n_cold} single launches, each after a 1 GiB read sweep that evicts the "
+                 "state to HBM; median launch",
+            us_per_step=cold_med * 1e6, min_us=cold_us[0], max_us=cold_us[-1],
+            GBps=db / cold_med / 1e9, hbm_frac=db / cold_med / PEAK_HBM,
+            box_copy_GBps=copy_Bps / 1e9, frac_of_box_copy=db / cold_med / copy_Bps,
+            box_copy_note="torch device copy of 2 GiB, bytes read plus written")
     decode = dict(tokens_per_s=Bd / dec_s, us_per_step=dec_s * 1e6,
                   us_per_step_median=med(dec_ms) * 1e3 / Sd,
                   GBps=dec_bw / 1e9, hbm_frac=dec_bw / PEAK_HBM, algorithmic_bytes=db,
-                  steps_per_bench_step=Sd, batch=Bd)
+                  steps_per_bench_step=Sd, batch=Bd,
+                  state_residency="last-level cache (MALL): the 64 MiB state stays in the "
+                                  "256 MiB MALL between back-to-back steps",
+                  cold_state=cold_state)
     t_dec_total = dec_s * Sd
     dominant = "decode" if t_dec_total >= fwd_s else "prefill"
     if dominant == "decode":
         roofline = dict(kernel="decode_wave_kernel<KLA,bf16,128,32,4>", bound="hbm",
                         achieved=dec_bw / 1e9, peak=PEAK_HBM / 1e9, unit="GB/s",
                         frac=dec_bw / PEAK_HBM,
+                        state_residency="MALL (warm, as timed); with the state in HBM see "
+                                        "decode.cold_state",
+                        frac_state_in_hbm=cold_state["hbm_frac"] if cold_state else None,
                         traffic=measured_traffic("decode_wave_kernel",
                                                  "gated_delta_rule_85_amd/csrc/decode.hip"),
                         traffic_unit="bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
@@ -751,6 +869,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "decode": decode,
+        "forward_other_workloads": others,
         "git": git_sha(),
     }
     print(json.dumps(out))

@@ -3,6 +3,13 @@
     python -m gated_delta_rule_85_amd.rocpd_summary trace RUN_results.db
         per-kernel dispatch count and duration (from --kernel-trace --stats)
 
+    python -m gated_delta_rule_85_amd.rocpd_summary mfma RUN_results.db [SIMDS] [XCDS]
+        per-kernel matrix-core counters from one --pmc run of SQ_VALU_MFMA_BUSY_CYCLES,
+        SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F32 and GRBM_GUI_ACTIVE:
+        matrix-core FLOPs (MOPS x 512), and utilisation = busy cycles summed over
+        the SIMDs / (active cycles of one XCD x SIMDS); GRBM_GUI_ACTIVE arrives
+        summed over the XCDS accelerator dies (default 1024 SIMDs, 8 XCDs)
+
     python -m gated_delta_rule_85_amd.rocpd_summary pmc FETCH.db WRITE.db [COPY_BYTES]
         mean FETCH_SIZE / WRITE_SIZE per dispatch (KiB) from two --pmc runs,
         and bytes per dispatch after calibration against the plain device copy
@@ -70,9 +77,39 @@ def pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 28) -> str:
     return "\n".join(lines)
 
 
+def mfma(db: str, simds: int = 1024, xcds: int = 8) -> str:
+    con = sqlite3.connect(db)
+    agg = collections.defaultdict(list)
+    dur = collections.defaultdict(dict)
+    for name, counter, value, d, did in con.execute(
+            "select kernel_name, counter_name, value, duration, dispatch_id "
+            "from counters_collection"):
+        agg[(name, counter)].append(value)
+        dur[name][did] = d
+    out = ["| kernel | dispatches | avg us | GRBM_GUI_ACTIVE / XCD | MFMA busy cycles | "
+           "bf16 GFLOP | fp32 GFLOP | matrix TFLOP/s | MFMA util % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    mean = lambda n, c: sum(agg[(n, c)]) / len(agg[(n, c)]) if agg.get((n, c)) else 0.0
+    names = sorted({n for n, _ in agg}, key=lambda n: -mean(n, "SQ_VALU_MFMA_BUSY_CYCLES"))
+    for n in names:
+        busy = mean(n, "SQ_VALU_MFMA_BUSY_CYCLES")
+        if busy == 0:
+            continue
+        act = mean(n, "GRBM_GUI_ACTIVE") / xcds
+        fb = mean(n, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        ff = mean(n, "SQ_INSTS_VALU_MFMA_MOPS_F32") * 512
+        us = sum(dur[n].values()) / len(dur[n]) / 1e3
+        out.append(f"| `{_short(n)}` | {len(dur[n])} | {us:.1f} | {act:.0f} | {busy:.0f} | "
+                   f"{fb / 1e9:.3f} | {ff / 1e9:.3f} | {(fb + ff) / (us * 1e-6) / 1e12:.1f} | "
+                   f"{100 * busy / (act * simds):.2f} |")
+    return "\n".join(out)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "trace":
         print(trace(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "mfma":
+        print(mfma(argv[1], *(int(x) for x in argv[2:4])))
     elif len(argv) >= 3 and argv[0] == "pmc":
         print(pmc(argv[1], argv[2], int(argv[3]) if len(argv) > 3 else 1 << 28))
     else:
