@@ -14,7 +14,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdr.so")
+# GDR_LIB selects another build of the library (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("GDR_LIB") or os.path.join(PKG, "libgdr.so")
 
 VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "gdn2": 3, "kla": 4}
 GDR_F32, GDR_BF16 = 0, 1

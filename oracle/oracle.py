@@ -74,10 +74,16 @@ def load(path: str | None = None):
         else:
             if _lib is not None:
                 return _lib
-            if (not os.path.exists(_LIB)
-                    or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
-                build()
-            lib = ctypes.CDLL(_LIB)
+            # GDR_ORACLE_LIB selects another build of the oracle (the tests'
+            # sanitizer build); otherwise the default one, rebuilt when stale.
+            other = os.environ.get("GDR_ORACLE_LIB")
+            if other:
+                lib = ctypes.CDLL(other)
+            else:
+                if (not os.path.exists(_LIB)
+                        or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                    build()
+                lib = ctypes.CDLL(_LIB)
         for name in _ENTRY.values():
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.POINTER(_Problem), ctypes.c_long, ctypes.c_long]
