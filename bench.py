@@ -333,6 +333,13 @@ def backward(args):
                                                              nfw, sh)))
     bw_s = timed(lambda: binding.check(L.gdr_backward_chunked(ctypes.byref(ba), ctypes.byref(ga),
                                                               ws.data_ptr(), nbw, sh)))
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 268435456 bytes read and written")
+        del src, dst
     finite = all(bool(torch.isfinite(t).all()) for t in gr.values())
     nch = B * H * ((T + C - 1) // C)
     out = {

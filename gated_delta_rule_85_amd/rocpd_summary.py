@@ -13,8 +13,9 @@
     python -m gated_delta_rule_85_amd.rocpd_summary pmc FETCH.db WRITE.db [COPY_BYTES]
         mean FETCH_SIZE / WRITE_SIZE per dispatch (KiB) from two --pmc runs,
         and bytes per dispatch after calibration against the plain device copy
-        of COPY_BYTES bytes found in the same runs (its counters divided by its
-        known size give the factor that turns a counter into bytes)
+        of COPY_BYTES bytes found in the same runs (the largest copy dispatch;
+        its counters divided by its known size give the factor that turns a
+        counter into bytes)
 """
 from __future__ import annotations
 
@@ -52,15 +53,24 @@ def _pmc(db: str):
     return {k: sum(v) / len(v) for k, v in agg.items()}, {k: len(v) for k, v in agg.items()}
 
 
+def _max_copy(db: str, counter: str):
+    """The counter of the largest plain device copy in the run: the calibration
+    copy (other, smaller copies may run too)."""
+    con = sqlite3.connect(db)
+    vals = [v for (v,) in con.execute(
+        "select value from counters_collection where counter_name = ? and kernel_name like "
+        "'%copyBuffer%'", (counter,))]
+    return max(vals) if vals else None
+
+
 def pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 28) -> str:
     f, fn = _pmc(fetch_db)
     w, _ = _pmc(write_db)
-    copy = [k for k in f if "copyBuffer" in k[0]]
     fr = wr = None
-    if copy:
-        name = copy[0][0]
-        fr = f[(name, "FETCH_SIZE")] * 1024 / copy_bytes
-        wr = w.get((name, "WRITE_SIZE"), 0) * 1024 / copy_bytes
+    cf, cw = _max_copy(fetch_db, "FETCH_SIZE"), _max_copy(write_db, "WRITE_SIZE")
+    if cf and cw:
+        fr = cf * 1024 / copy_bytes
+        wr = cw * 1024 / copy_bytes
     lines = [f"calibration (plain device copy of {copy_bytes} bytes): "
              f"FETCH_SIZE reads {fr:.4f} x bytes, WRITE_SIZE reads {wr:.4f} x bytes"
              if fr else "calibration: no copy kernel found"]

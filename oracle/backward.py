@@ -166,3 +166,68 @@ def backward(variant, q, k, v, alpha=None, beta=None, erase_b=None, write_w=None
                 x[~sel[:, None, :].repeat(x.shape[1], axis=1)] = np.nan
         out[n] = x
     return out
+
+
+def backward_head_checkpointed(variant, q, k, v, alpha=None, beta=None, erase_b=None,
+                               write_w=None, eps=0.0, state_in=None, d_o=None, d_state_out=None,
+                               every=64):
+    """The same gradient as ``backward`` for one head, in bounded memory: one
+    head's inputs q, k [T, dk], v [T, dv], gates [T] or [T, d], state_in
+    [dk, dv] (None = zeros), upstream d_o [T, dv] and d_state_out [dk, dv].
+
+    The recurrence runs forward once without a graph, keeping the state at
+    every ``every``-th token.  Then, for each segment of ``every`` tokens from
+    the last to the first, it runs the segment again from its stored state
+    with autograd and takes the gradient of
+        sum(o_seg * d_o_seg) + sum(S_end * G_end),
+    where G_end is dL/dS at the segment's end (d_state_out for the last
+    segment, else what the later segment returned for its start state).  This
+    is the chain rule through the token-by-token recurrence, cut at the stored
+    states; no chunk form is involved.  Returns a dict of float64 numpy
+    arrays shaped like the inputs (None where the variant has no such input),
+    with "state_in" always present."""
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)   # one head of small products: threads only add overhead
+    try:
+        return _backward_head_checkpointed(variant, q, k, v, alpha, beta, erase_b, write_w, eps,
+                                           state_in, d_o, d_state_out, every)
+    finally:
+        torch.set_num_threads(prev)
+
+
+def _backward_head_checkpointed(variant, q, k, v, alpha, beta, erase_b, write_w, eps, state_in,
+                                d_o, d_state_out, every):
+    T, dk = np.shape(q)[0], np.shape(q)[1]
+    dv = np.shape(v)[1]
+    raw = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, erase_b=erase_b, write_w=write_w)
+    ins = {n: _t64(x) for n, x in raw.items()}
+    S = _t64(state_in) if state_in is not None else torch.zeros(dk, dv, dtype=torch.float64)
+    d_o = None if d_o is None else _t64(d_o)
+    G = (_t64(d_state_out) if d_state_out is not None
+         else torch.zeros(dk, dv, dtype=torch.float64))
+    starts = list(range(0, T, every))
+    saved = []
+    with torch.no_grad():
+        for t0 in starts:
+            saved.append(S.clone())
+            sl = {n: (None if x is None else x[t0:t0 + every]) for n, x in ins.items()}
+            _, S = _head_forward(variant, sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"],
+                                 sl["erase_b"], sl["write_w"], float(eps), S)
+    out = {n: (None if x is None else np.zeros(tuple(x.shape))) for n, x in ins.items()}
+    for t0, S0 in zip(reversed(starts), reversed(saved)):
+        leaf = {n: (None if x is None else x[t0:t0 + every].clone().requires_grad_(True))
+                for n, x in ins.items()}
+        S0 = S0.clone().requires_grad_(True)
+        o, S_end = _head_forward(variant, leaf["q"], leaf["k"], leaf["v"], leaf["alpha"],
+                                 leaf["beta"], leaf["erase_b"], leaf["write_w"], float(eps), S0)
+        loss = torch.sum(S_end * G)
+        if d_o is not None:
+            loss = loss + torch.sum(o * d_o[t0:t0 + every])
+        names = [n for n, x in leaf.items() if x is not None]
+        grads = torch.autograd.grad(loss, [leaf[n] for n in names] + [S0], allow_unused=True)
+        for n, gr in zip(names, grads[:-1]):
+            if gr is not None:
+                out[n][t0:t0 + every] = gr.numpy()
+        G = grads[-1].detach()
+    out["state_in"] = G.numpy()
+    return out

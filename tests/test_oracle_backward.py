@@ -5,6 +5,7 @@ mistakes in its recurrence are rejected."""
 import numpy as np
 import pytest
 
+from gated_delta_rule_85_amd.inputs import make_inputs, make_upstream_grads
 from oracle import backward, oracle
 
 VARIANTS = oracle.VARIANTS
@@ -122,3 +123,30 @@ def test_planted_mistake_is_caught(name, old, new, variant):
     mod = types.ModuleType("mutant")
     exec(compile(src.replace(old, new, 1), "mutant", "exec"), mod.__dict__)
     assert _check_against_fd(mod, variant) > 1e-4, name
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_checkpointed_gradient_equals_plain(variant):
+    """The chunk-checkpointed gradient oracle (used at long lengths) returns
+    the plain gradient oracle's values: same recurrence, same order of
+    operations, only cut into segments at stored states."""
+    inp = make_inputs(variant, 1, 150, 2, 16, 8, "fp32", seed=4, state_scale=0.3,
+                      alpha_scale=0.05)
+    up = make_upstream_grads(1, 150, 2, 16, 8, "fp32", seed=5)
+    ref = backward.backward(variant, inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                      beta=inp["beta"], erase_b=inp["erase_b"], write_w=inp["write_w"],
+                      eps=inp["eps"], state_in=inp["state_in"], d_o=up["d_o"],
+                      d_state_out=up["d_state_out"])
+    h = 1
+    g = lambda x: None if x is None else x.numpy()[0, :, h]
+    ck = backward.backward_head_checkpointed(variant, g(inp["q"]), g(inp["k"]), g(inp["v"]),
+                                       g(inp["alpha"]), g(inp["beta"]), g(inp["erase_b"]),
+                                       g(inp["write_w"]), inp["eps"],
+                                       inp["state_in"].numpy()[0, h], up["d_o"].numpy()[0, :, h],
+                                       up["d_state_out"].numpy()[0, h], every=32)
+    for n, x in ck.items():
+        if x is None:
+            assert ref[n] is None
+            continue
+        r = ref[n][0, h] if n == "state_in" else ref[n][0, :, h]
+        assert np.max(np.abs(x - r)) <= 1e-12 * max(1.0, np.max(np.abs(r))), n
