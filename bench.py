@@ -436,6 +436,44 @@ def routing(args):
     print(json.dumps(out))
 
 
+def state_rmw_reference(dev, stream, n_floats, n_cold, flush):
+    """The plainest pass over memory of the decode state's size: torch's
+    in-place multiply of an fp32 tensor of n_floats elements (read once,
+    written once), back to back (warm: the tensor stays in the last-level
+    cache) and as single launches after a read sweep of `flush` (cold).  The
+    decode step is this read-modify-write plus its per-token inputs and
+    arithmetic, so the ratio of the two rates is how close the decode comes
+    to streaming its state."""
+    import torch
+
+    x = torch.full((n_floats,), 0.5, dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        x.mul_(1.0)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(100):
+        x.mul_(1.0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_s = e0.elapsed_time(e1) / 1e3 / 100
+    pairs = [(ev(), ev()) for _ in range(n_cold)]
+    for s in range(n_cold):
+        flush.sum()
+        pairs[s][0].record(stream)
+        x.mul_(1.0)
+        pairs[s][1].record(stream)
+    torch.cuda.synchronize()
+    cold_s = sorted(a.elapsed_time(b) for a, b in pairs)[n_cold // 2] / 1e3
+    nb = 2 * n_floats * 4
+    del x
+    return dict(note=f"torch in-place multiply of {n_floats * 4 >> 20} MiB fp32 (the batch "
+                     "state's size), bytes read plus written; warm back to back, cold after "
+                     "the same read sweep (median)",
+                warm_us=warm_s * 1e6, cold_us=cold_s * 1e6, warm_GBps=nb / warm_s / 1e9,
+                cold_GBps=nb / cold_s / 1e9)
+
+
 def cold_decode(args):
     """Decode step of the Kaczmarz layer at batch 64 with the state cold: the
     64 MiB state fits in the 256 MiB last-level cache (MALL), so back-to-back
@@ -518,6 +556,8 @@ def cold_decode(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / reps
 
+    rmw = state_rmw_reference(dev, stream, Bd * H * dk * dv, n, flush)
+    del flush
     log("measuring HBM copy / read bandwidth and a bf16 GEMM")
     src = torch.ones(512 << 20, dtype=torch.float32, device=dev)   # 2 GiB
     dst = torch.empty_like(src)
@@ -539,7 +579,9 @@ def cold_decode(args):
         "config": {"workload": "Kaczmarz LA decode step, batch 64, 16 heads, d=128, fp32 state "
                                "from the T=65536 prefill; a 1 GiB read sweep before each cold "
                                "launch"},
-        "warm": warm, "cold": cold, "algorithmic_bytes": db,
+        "warm": warm, "cold": cold, "algorithmic_bytes": db, "state_rmw_reference": rmw,
+        "frac_of_state_rmw": {"warm": warm["GBps_algorithmic"] / rmw["warm_GBps"],
+                              "cold": cold["GBps_algorithmic"] / rmw["cold_GBps"]},
         "measured_peaks": peaks, "git": git_sha(),
     }
     print(json.dumps(out))
@@ -765,6 +807,7 @@ def main():
             pairs[s_][1].record(stream)
         torch.cuda.synchronize()
         cold_us = sorted(a_.elapsed_time(b_) * 1e3 for a_, b_ in pairs)
+        rmw = state_rmw_reference(dev, stream, Bd * H * dk * dv, n_cold, flush)
         del flush
         src = torch.ones(512 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -816,13 +859,16 @@ def main():
             us_per_step=cold_med * 1e6, min_us=cold_us[0], max_us=cold_us[-1],
             GBps=db / cold_med / 1e9, hbm_frac=db / cold_med / PEAK_HBM,
             box_copy_GBps=copy_Bps / 1e9, frac_of_box_copy=db / cold_med / copy_Bps,
-            box_copy_note="torch device copy of 2 GiB, bytes read plus written")
+            box_copy_note="torch device copy of 2 GiB, bytes read plus written",
+            state_rmw_reference=rmw,
+            frac_of_state_rmw=(db / cold_med) / (rmw["cold_GBps"] * 1e9))
     decode = dict(tokens_per_s=Bd / dec_s, us_per_step=dec_s * 1e6,
                   us_per_step_median=med(dec_ms) * 1e3 / Sd,
                   GBps=dec_bw / 1e9, hbm_frac=dec_bw / PEAK_HBM, algorithmic_bytes=db,
                   steps_per_bench_step=Sd, batch=Bd,
                   state_residency="last-level cache (MALL): the 64 MiB state stays in the "
                                   "256 MiB MALL between back-to-back steps",
+                  frac_of_state_rmw_warm=(dec_bw / (rmw["warm_GBps"] * 1e9)) if n_cold else None,
                   cold_state=cold_state)
     t_dec_total = dec_s * Sd
     dominant = "decode" if t_dec_total >= fwd_s else "prefill"
