@@ -559,7 +559,9 @@ template <int CPR, int EPC> __device__ __forceinline__ int swz(int r, int col) {
 // Raw global inputs of one chunk-head, held in registers from the issue of
 // their loads (during the previous chunk-head's arithmetic) to their use.  The
 // loads are unconditional (rows past T read the last valid row) so that the
-// compiler's waits for them stay exact; staging masks those rows.
+// compiler's waits for them stay exact; staging masks those rows.  q is held
+// here only with a channel decay; otherwise each wave loads its own q rows in
+// the matrix-core fragment layout (the kernel's qf).
 template <int V, int DK, int DV, bool RT> struct PrepRaw {
     using VT = VariantTraits<V>;
     static constexpr int NT = kPrep2Threads;
@@ -568,7 +570,8 @@ template <int V, int DK, int DV, bool RT> struct PrepRaw {
     static constexpr int NV = C * VC / NT;                     // v chunks per thread
     static constexpr int NA = VT::kChannelDecay ? C * DK / 4 / NT : 1;
     static_assert(C * KC % NT == 0 && C * VC % NT == 0 && C * DK / 4 % NT == 0, "whole passes");
-    bf16x8 k[NQ], q[NQ], v[NV], vr[RT ? NV : 1];   // vr: the routed value
+    static constexpr int NQR = VT::kChannelDecay ? NQ : 1;   // q chunks held here
+    bf16x8 k[NQ], q[NQR], v[NV], vr[RT ? NV : 1];   // vr: the routed value
     f32x4 eb[VT::kGates ? 2 * NQ : 1], ww[VT::kGates ? 2 * NV : 1];   // erase / write gates
     f32x4 al[NA];                                              // channel-wise alpha
     float a1, be;                                              // scalar alpha, beta / eta
@@ -586,7 +589,8 @@ template <int V, int DK, int DV, bool RT> struct PrepRaw {
             const int idx = tid + n * NT;
             const int r = idx / KC, pc = idx % KC;
             k[n] = *reinterpret_cast<const bf16x8 *>(&kp[tok(r) * DK + 8 * pc]);
-            q[n] = *reinterpret_cast<const bf16x8 *>(&qp[tok(r) * DK + 8 * pc]);
+            if constexpr (VT::kChannelDecay)
+                q[n] = *reinterpret_cast<const bf16x8 *>(&qp[tok(r) * DK + 8 * pc]);
             if constexpr (VT::kGates) {
                 eb[2 * n] = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc]);
                 eb[2 * n + 1] = *reinterpret_cast<const f32x4 *>(&p.erase_b[tok(r) * DK + 8 * pc + 4]);
@@ -639,7 +643,6 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __shared__ float sBeta[C];
     constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
     __shared__ float sEg[kRowDecay ? C : 1], sEgc[kRowDecay ? C : 1];   // e^{g_r}, e^{g_C - g_r}
-    __shared__ float sRq[C];   // 1 / |q_r| with the q/k normalisation
     __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
     __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
     __shared__ float sX[4][16][17];
@@ -673,10 +676,14 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const long T = p.T;
     const int H = (int)p.H;
     const bf16 *q = static_cast<const bf16 *>(p.q);
-    // Work items are the block's chunk-heads, chunk fastest; a workgroup takes
-    // item blockIdx.x first, then every gridDim.x-th item or the next ticket
-    // (blk.ticket), and loads the next item's inputs while it computes the
-    // current one.
+    // Work items are the block's chunk-heads, head fastest: the heads of one
+    // chunk run together, so the 128-byte lines of the per-token gates (laid
+    // out [B, T, H], two tokens of all sixteen heads per line at H = 16) are
+    // fetched once for all of them, and the rows of q, k and v that the
+    // workgroups in flight read are whole token rows of all heads.  A
+    // workgroup takes item blockIdx.x first, then every gridDim.x-th item or
+    // the next ticket (blk.ticket), and loads the next item's inputs while it
+    // computes the current one.
     // Item indices fit in 32 bits (the host keeps B * H * ceil(T / 64) below
     // 2^31), so their split into (chunk, head, batch row) is 32-bit scalar
     // arithmetic.
@@ -685,9 +692,9 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     if (blk.ticket_clear && item == 0 && threadIdx.x == 0) *blk.ticket_clear = 0u;
     if (item >= nitems) return;
     __shared__ unsigned sNext;   // the item after the current one
-    auto chunk_of = [&](unsigned it) { return blk.c0 + (long)(it % nc); };
-    auto head_of = [&](unsigned it) { return (int)((it / nc) % (unsigned)H); };
-    auto row_of = [&](unsigned it) { return (int)((it / nc) / (unsigned)H); };
+    auto chunk_of = [&](unsigned it) { return blk.c0 + (long)((it / (unsigned)H) % nc); };
+    auto head_of = [&](unsigned it) { return (int)(it % (unsigned)H); };
+    auto row_of = [&](unsigned it) { return (int)((it / (unsigned)H) / nc); };
     Raw raw;
     raw.issue(p, chunk_of(item), head_of(item), row_of(item), (int)threadIdx.x);
     // Gram tiles of this wave: row block gR, column blocks gS0 .. gS0+gN-1.
@@ -697,20 +704,30 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     const int gR = wave < 2 ? 3 : (wave < 4 ? 2 : (wave == 4 ? 1 : 0));
     const int gS0 = (wave == 1 || wave == 3) ? 2 : 0;
     const int gN = wave < 6 ? ((wave == 3 || wave == 5) ? 1 : 2) : 0;
-    // q rows of block gR, for phase 2 with scalar decay (L2 hits); rows past
-    // T read the last valid row, whose products only reach rows never stored.
-    // Every wave loads them, so that the loads and their waits are
-    // unconditional.
-    bf16x8 qf[DK / 32];
+    // Without a channel decay, q is read once per item, as the fragments of
+    // the q rows of block qR (lane: row 16 qR + l16, elements 32 ks + 8 lg ..
+    // + 7).  For waves 0-5, qR = gR: the rows phase 2 multiplies.  Waves 6 and
+    // 7, which have no Gram tile, take blocks 1 and 0, so that every row
+    // block is held by two waves, and each wave writes half of its block's
+    // q (.) e^g (fragments 2 qh and 2 qh + 1): the fragments are the only q
+    // the item needs.  The next item's are loaded as soon as phase 2 is done
+    // with the current ones.  Rows past T read the last valid row, whose
+    // products only reach rows never stored.
+    const int qR = wave == 6 ? 1 : (wave == 7 ? 0 : gR);
+    const int qh = (wave == 1 || wave == 3 || wave == 6 || wave == 7) ? 1 : 0;
+    bf16x8 qf[kSplit ? 1 : DK / 32];
     auto load_qf = [&](long c, int h, int b, int l16, int lg) {
         const long t0 = c * C;
         const int last = (int)min((long)C, T - t0) - 1;
-        const int rr = min(16 * gR + l16, last);
+        const int rr = min(16 * qR + l16, last);
         const long row = ((long)b * T + t0 + rr) * H + h;
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
             qf[ks] = *reinterpret_cast<const bf16x8 *>(&q[row * DK + 32 * ks + 8 * lg]);
     };
+    if constexpr (!kSplit)
+        load_qf(chunk_of(item), head_of(item), row_of(item), (int)threadIdx.x & 15,
+                ((int)threadIdx.x & 63) >> 4);
 
     for (;;) {
     // The thread index is re-derived opaquely each item, so that the many
@@ -749,20 +766,19 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 sk += (float)kv[e] * (float)kv[e];
-                sq += (float)raw.q[n][e] * (float)raw.q[n][e];
+                if constexpr (kSplit) sq += (float)raw.q[n][e] * (float)raw.q[n][e];
             }
 #pragma unroll
             for (int off = 1; off < KC; off <<= 1) {
                 sk += __shfl_xor(sk, off, kWave);
-                sq += __shfl_xor(sq, off, kWave);
+                if constexpr (kSplit) sq += __shfl_xor(sq, off, kWave);
             }
             const float rk = rsqrtf(sk + kL2NormEps), rq = rsqrtf(sq + kL2NormEps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kv[e] = (bf16)((float)kv[e] * rk);
-                raw.q[n][e] = (bf16)((float)raw.q[n][e] * rq);
+                if constexpr (kSplit) raw.q[n][e] = (bf16)((float)raw.q[n][e] * rq);
             }
-            if (pc == 0) sRq[r] = rq;
         }
         *reinterpret_cast<bf16x8 *>(&sK[kx(r, 8 * pc)]) = kv;
         if constexpr (VT::kGates) {
@@ -803,6 +819,23 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             }
         }
         *reinterpret_cast<bf16x8 *>(&sV[vx(r, 8 * pc)]) = vv;
+    }
+    if constexpr (!kSplit) {
+        if (l2) {
+            // a fragment row's elements sit in the four lanes l16 + 16 lg
+            float sq = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sq += (float)qf[ks][e] * (float)qf[ks][e];
+            sq += __shfl_xor(sq, 16, kWave);
+            sq += __shfl_xor(sq, 32, kWave);
+            const float rq = rsqrtf(sq + kL2NormEps);
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)qf[ks][e] * rq);
+        }
     }
     if constexpr (VT::kChannelDecay) {
 #pragma unroll
@@ -869,37 +902,33 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     __syncthreads();
 
     // ---- phase 1: element-wise factors ------------------------------------
-    // KLA issues the workspace stores of this phase (q (.) e^g, Kbar^T,
-    // e^{g_C}) after the Gram products: loads and stores share one wait
-    // counter, so a store issued between the Gram operand loads and their
-    // use would be waited for with them.  Elsewhere they go out at once:
-    // with a routed value, for DeltaNet and Gated DeltaNet, and for d_v < d_k,
-    // holding them spills, and a spill reload waits for every load in flight
-    // (the next item's prefetch included); with a channel decay the Gram
-    // products load nothing from global memory, so there is no wait to avoid.
-    constexpr bool kDefer = !RT && V == kKLA && DV >= DK;
-    if constexpr (!kSplit) load_qf(c, h, b, l16, lg);   // for phase 2
-    bf16x8 qo[NQ], kbo[2];
-    float gamo[2];
+    // The workspace stores of this phase (q (.) e^g, Kbar^T, e^{g_C}) go out
+    // at once: the Gram products load nothing from global memory, so no wait
+    // for their operands can be held up by them.
     {
-        // q (.) e^{g}, from registers
+        // q (.) e^{g}, from registers: the row layout with a channel decay,
+        // else half a row block per wave from its q fragments
+        if constexpr (kSplit) {
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int idx = tid + n * NT;
-            if (idx < C * KC) {
+            for (int n = 0; n < NQ; ++n) {
+                const int idx = tid + n * NT;
                 const int r = idx / KC, pc = idx % KC;
                 bf16x8 o;
-                float egr = 1.f;
-                if constexpr (kRowDecay) egr = sEg[r];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float eg = egr;
-                    if constexpr (VT::kChannelDecay) eg = __expf(sG[r][8 * pc + e]);
-                    o[e] = (bf16)((float)raw.q[n][e] * eg);
-                }
-                qo[n] = o;
-                if constexpr (!kDefer)
-                    *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
+                for (int e = 0; e < 8; ++e)
+                    o[e] = (bf16)((float)raw.q[n][e] * __expf(sG[r][8 * pc + e]));
+                *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 8 * pc, DK)) = o;
+            }
+        } else {
+            const int r = 16 * qR + l16;
+            const float egr = kRowDecay ? sEg[r] : 1.f;
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                if (ks / (DK / 64) != qh) continue;
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)qf[ks][e] * egr);
+                *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 32 * ks + 8 * lg, DK)) = o;
             }
         }
         // (a (.) e^{g})^T into LDS and (k (.) e^{g_C - g})^T to the workspace.
@@ -953,13 +982,11 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
                     kb[e] = kk * egc;
                 }
                 store8(&sAt[tx(i, r0)], at);
+                bf16x8 kbo;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kbo[cc][e] = (bf16)kb[e];
-                gamo[cc] = VT::kHasDecay ? __expf(gC) : 1.f;
-                if constexpr (!kDefer) {
-                    *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i, r0, C)) = kbo[cc];
-                    if (r0 == 0) ws.gam[ch * DK + i] = gamo[cc];
-                }
+                for (int e = 0; e < 8; ++e) kbo[e] = (bf16)kb[e];
+                *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i, r0, C)) = kbo;
+                if (r0 == 0) ws.gam[ch * DK + i] = VT::kHasDecay ? __expf(gC) : 1.f;
             }
             // the same elements this thread read, so no other thread races it
             if constexpr (VT::kGates) {
@@ -1081,7 +1108,6 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
             Av[m] = s2 < r ? accA[m] * fa : 0.f;
             Pv[m] = s2 <= r ? accP[m] * f : 0.f;
         }
-        if (l2 && !kSplit) Pv *= sRq[r];   // P used the q rows as stored (kSplit: normalised)
         *reinterpret_cast<f32x4 *>(&sAm[fx(r, 16 * S + 4 * lg)]) = Av;
         store_frag4(ws.P + ch * C * C, r, 16 * S + 4 * lg, C, Pv);
     }
@@ -1097,23 +1123,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         asm volatile("" : "+v"(z));
         *reinterpret_cast<uint2 *>(ws.P + ch * C * C + frag_off<bf16>(r, s2, C)) = make_uint2(z, z);
     }
-    // the phase-1 workspace stores
-    if constexpr (kDefer) {
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        const int idx = tid + n * NT;
-        if (idx < C * KC)
-            *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(idx / KC, 8 * (idx % KC), DK)) =
-                qo[n];
-    }
-    if (tid < DK / 2 * (C / 8)) {
-        const int i0 = 2 * (tid % (DK / 2)), r0 = 8 * (tid / (DK / 2));
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            *reinterpret_cast<bf16x8 *>(ws.Kbt + ch * DK * C + frag_off<bf16>(i0 + cc, r0, C)) = kbo[cc];
-            if (r0 == 0) ws.gam[ch * DK + i0 + cc] = gamo[cc];
-        }
-    }
+    // the q fragments are free: the next item's go out now
+    if constexpr (!kSplit) {
+        const unsigned next = next_item < nitems ? next_item : item;
+        load_qf(chunk_of(next), head_of(next), row_of(next), l16, lg);
     }
     __syncthreads();
 
