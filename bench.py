@@ -280,8 +280,10 @@ def backward_flops_per_chunk_head(dk, dv, c=C, scalar_decay=True):
 def backward(args):
     """Gradient of the chunked forward on the Kaczmarz prefill (B=1, H=16,
     T=65536, d=128, bf16): upstream gradients for o and S_T in, every input
-    gradient out (fp32).  The forward on the same inputs is timed beside it.
-    Prints one JSON line."""
+    gradient out (fp32).  The forward on the same inputs is timed beside it,
+    and so is the training pair that keeps the forward's records for the
+    gradient (gdr_forward_chunked_save, then gdr_backward_chunked_saved in the
+    same workspace) against forward + gradient.  Prints one JSON line."""
     import torch
 
     from gated_delta_rule_85_amd import binding
@@ -333,6 +335,16 @@ def backward(args):
                                                              nfw, sh)))
     bw_s = timed(lambda: binding.check(L.gdr_backward_chunked(ctypes.byref(ba), ctypes.byref(ga),
                                                               ws.data_ptr(), nbw, sh)))
+    fs_s = timed(lambda: binding.check(L.gdr_forward_chunked_save(ctypes.byref(fa), ws.data_ptr(),
+                                                                  nbw, sh)))
+
+    def pair():
+        binding.check(L.gdr_forward_chunked_save(ctypes.byref(fa), ws.data_ptr(), nbw, sh))
+        binding.check(L.gdr_backward_chunked_saved(ctypes.byref(ba), ctypes.byref(ga),
+                                                   ws.data_ptr(), nbw, sh))
+
+    pair_s = timed(pair)
+    plain_pair_s = fw_s + bw_s
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -350,6 +362,13 @@ def backward(args):
                                "S_T; gradients w.r.t. q, k, v, eta, alpha and S_0 in fp32"},
         "backward_ms": bw_s * 1e3, "forward_ms": fw_s * 1e3,
         "backward_over_forward": bw_s / fw_s,
+        "saved": {"note": "gdr_forward_chunked_save then gdr_backward_chunked_saved in one "
+                          "workspace, timed as a pair; the saved gradient alone is the pair "
+                          "minus the saving forward timed by itself",
+                  "forward_save_ms": fs_s * 1e3, "pair_ms": pair_s * 1e3,
+                  "backward_saved_ms": (pair_s - fs_s) * 1e3,
+                  "forward_plus_backward_ms": plain_pair_s * 1e3,
+                  "pair_speedup": plain_pair_s / pair_s},
         "chunk_grad_flops": backward_flops_per_chunk_head(dk, dv) * nch,
         "workspace_bytes": nbw, "outputs_finite": finite, "git": git_sha(),
     }

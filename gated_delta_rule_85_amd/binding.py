@@ -86,6 +86,10 @@ def lib(path: str | None = None):
     L.gdr_backward_workspace_size.restype = ctypes.c_size_t
     L.gdr_backward_chunked.argtypes = [A, G, _vp, ctypes.c_size_t, _vp]
     L.gdr_backward_chunked.restype = ctypes.c_int
+    L.gdr_forward_chunked_save.argtypes = [A, _vp, ctypes.c_size_t, _vp]
+    L.gdr_forward_chunked_save.restype = ctypes.c_int
+    L.gdr_backward_chunked_saved.argtypes = [A, G, _vp, ctypes.c_size_t, _vp]
+    L.gdr_backward_chunked_saved.restype = ctypes.c_int
     L.gdr_status_string.argtypes = [ctypes.c_int]
     L.gdr_status_string.restype = ctypes.c_char_p
     L.gdr_last_error_detail.argtypes = []
@@ -130,6 +134,17 @@ def gdr_backward_chunked(args: GdrArgs, grads: GdrGrads, workspace: int, ws_byte
                          stream: int) -> int:
     return lib().gdr_backward_chunked(ctypes.byref(args), ctypes.byref(grads),
                                       workspace or None, ws_bytes, stream or None)
+
+
+def gdr_forward_chunked_save(args: GdrArgs, workspace: int, ws_bytes: int, stream: int) -> int:
+    return lib().gdr_forward_chunked_save(ctypes.byref(args), workspace or None, ws_bytes,
+                                          stream or None)
+
+
+def gdr_backward_chunked_saved(args: GdrArgs, grads: GdrGrads, workspace: int, ws_bytes: int,
+                               stream: int) -> int:
+    return lib().gdr_backward_chunked_saved(ctypes.byref(args), ctypes.byref(grads),
+                                            workspace or None, ws_bytes, stream or None)
 
 
 def gdr_status_string(status: int) -> str:
@@ -262,13 +277,37 @@ def decode_step(variant: str, q, k, v, state, alpha=None, beta=None, erase_b=Non
     return o
 
 
+def forward_save(variant: str, q, k, v, alpha=None, beta=None, erase_b=None, write_w=None,
+                 eps: float = 0.0, state_in=None, output_state: bool = True, workspace=None,
+                 stream=None):
+    """gdr_forward_chunked_save on device tensors: the forward of a training
+    step.  Returns (o, state_out or None, workspace); pass the same inputs and
+    that workspace to ``backward(..., saved=workspace)``."""
+    import torch
+
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    state_out = (torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+                 if output_state else None)
+    a = make_args(variant, q, k, v, o, alpha, beta, erase_b, write_w, eps, state_in, state_out)
+    need = gdr_backward_workspace_size(a)   # 0 for invalid args: the call below reports why
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check(gdr_forward_chunked_save(a, workspace.data_ptr(), workspace.numel(),
+                                   _stream_handle(stream)))
+    return o, state_out, workspace
+
+
 def backward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None, write_w=None,
              eps: float = 0.0, state_in=None, d_o=None, d_state_out=None,
-             want_state_grad: bool = True, workspace=None, stream=None):
+             want_state_grad: bool = True, workspace=None, stream=None, saved=None):
     """Gradient of the chunked forward on device tensors.  ``d_o`` [B,T,H,dv] (in
     q's dtype) and ``d_state_out`` [B,H,dk,dv] float32 are the upstream gradients
-    (None = zero).  Returns a dict of float32 gradients keyed q, k, v, alpha, beta,
-    erase_b, write_w, state_in (None where the variant takes no such input)."""
+    (None = zero).  ``saved``: the workspace that ``forward_save`` returned for
+    the same inputs (then gdr_backward_chunked_saved runs in it).  Returns a dict
+    of float32 gradients keyed q, k, v, alpha, beta, erase_b, write_w, state_in
+    (None where the variant takes no such input)."""
     import torch
 
     B, T, H, dk = q.shape
@@ -293,6 +332,10 @@ def backward(variant: str, q, k, v, alpha=None, beta=None, erase_b=None, write_w
     g = GdrGrads(_ptr(d_o), _ptr(d_state_out), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
                  _ptr(out["alpha"]), _ptr(out["beta"]), _ptr(out["erase_b"]),
                  _ptr(out["write_w"]), _ptr(out["state_in"]))
+    if saved is not None:
+        check(gdr_backward_chunked_saved(a, g, saved.data_ptr(), saved.numel(),
+                                         _stream_handle(stream)))
+        return out
     need = gdr_backward_workspace_size(a)   # 0 for invalid args: the call below reports why
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

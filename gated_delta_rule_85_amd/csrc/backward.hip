@@ -1223,42 +1223,74 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
     }
 }
 
-template <int V, typename TI, int DK, int DV>
-hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_t st) {
-    char *base = static_cast<char *>(ws);
-    const long NC = (p.T + C - 1) / C, nch = p.B * p.H * NC;
-    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    size_t off = al(forward_states_bytes(p));
-    TI *S_chunks = reinterpret_cast<TI *>(base + off);
-    off += al((size_t)nch * DK * DV * sizeof(TI));
-    TI *D_chunks = reinterpret_cast<TI *>(base + off);
-    off += al((size_t)nch * C * DV * sizeof(TI));
-    TI *dS_chunks = reinterpret_cast<TI *>(base + off);
-    off += al((size_t)nch * DK * DV * sizeof(TI));
-    TI *dD_chunks = reinterpret_cast<TI *>(base + off);
-    off += al((size_t)nch * C * DV * sizeof(TI));
+// The gradient's workspace: the forward's per-chunk factors of every chunk,
+// then the per-chunk records of the two sequential passes and the reverse
+// factors, then the per-chunk gradient workers' scratch.
+template <typename TI, int DK, int DV> struct BwLayout {
+    TI *S_chunks, *D_chunks, *dS_chunks, *dD_chunks;
     RevFactors rf;
-    rf.Kb = base + off;
-    off += al((size_t)nch * C * DK * sizeof(TI));
-    rf.Wt = base + off;
-    off += al((size_t)nch * DK * C * sizeof(TI));
-    rf.X1 = base + off;
-    off += al((size_t)nch * C * DV * sizeof(TI));
-    rf.X2 = base + off;
-    off += al((size_t)nch * DK * DV * sizeof(TI));
-    float *scratch = reinterpret_cast<float *>(base + off);
+    float *scratch;
+    BwLayout(const Problem &p, void *ws) {
+        char *base = static_cast<char *>(ws);
+        const long NC = (p.T + C - 1) / C, nch = p.B * p.H * NC;
+        auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+        size_t off = al(forward_states_bytes(p));
+        S_chunks = reinterpret_cast<TI *>(base + off);
+        off += al((size_t)nch * DK * DV * sizeof(TI));
+        D_chunks = reinterpret_cast<TI *>(base + off);
+        off += al((size_t)nch * C * DV * sizeof(TI));
+        dS_chunks = reinterpret_cast<TI *>(base + off);
+        off += al((size_t)nch * DK * DV * sizeof(TI));
+        dD_chunks = reinterpret_cast<TI *>(base + off);
+        off += al((size_t)nch * C * DV * sizeof(TI));
+        rf.Kb = base + off;
+        off += al((size_t)nch * C * DK * sizeof(TI));
+        rf.Wt = base + off;
+        off += al((size_t)nch * DK * C * sizeof(TI));
+        rf.X1 = base + off;
+        off += al((size_t)nch * C * DV * sizeof(TI));
+        rf.X2 = base + off;
+        off += al((size_t)nch * DK * DV * sizeof(TI));
+        scratch = reinterpret_cast<float *>(base + off);
+    }
+};
+
+// The forward that keeps what its gradient needs: the gradient's states pass
+// (the factors of every chunk, then the scan recording the state and Delta
+// entering each chunk) with the scan also writing o and state_out.
+template <typename TI, int DK, int DV>
+hipError_t forward_save_shape(const Problem &p, void *ws, hipStream_t st) {
+    const BwLayout<TI, DK, DV> L(p, ws);
+    const long NC = (p.T + C - 1) / C;
+    hipError_t e = launch_states_prep(p, ws, 0, (int)NC, false, st);
+    if (e != hipSuccess) return e;
+    return launch_states_scan(p, ws, 0, (int)NC, p.state_in, p.state_out, L.S_chunks, L.D_chunks,
+                              true, st);
+}
+
+template <int V, typename TI, int DK, int DV>
+hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, bool saved, hipStream_t st) {
+    const BwLayout<TI, DK, DV> L(p, ws);
+    const long NC = (p.T + C - 1) / C;
+    TI *const S_chunks = L.S_chunks, *const D_chunks = L.D_chunks;
+    TI *const dS_chunks = L.dS_chunks, *const dD_chunks = L.dD_chunks;
+    const RevFactors rf = L.rf;
+    float *const scratch = L.scratch;
 
     // One pass per kernel over all chunks, in order on `st`.  (Overlapping the
     // sequential passes with the parallel ones on a second stream measured
     // slower: the two kinds of kernel slow each other down more than they
     // overlap.)  The kernels take a block of chunks [c0, c0 + ncb); here the
-    // block is the whole sequence.
+    // block is the whole sequence.  With `saved`, the states pass already ran
+    // as the forward that kept its records in this workspace.
     const ForwardStates f = forward_states_ptrs(p, ws);
-    hipError_t e = launch_states_prep(p, ws, 0, (int)NC, false, st);
-    if (e != hipSuccess) return e;
-    if ((e = launch_states_scan(p, ws, 0, (int)NC, p.state_in, nullptr, S_chunks, D_chunks, st)) !=
-        hipSuccess)
-        return e;
+    hipError_t e = hipSuccess;
+    if (!saved) {
+        if ((e = launch_states_prep(p, ws, 0, (int)NC, false, st)) != hipSuccess) return e;
+        if ((e = launch_states_scan(p, ws, 0, (int)NC, p.state_in, nullptr, S_chunks, D_chunks,
+                                    false, st)) != hipSuccess)
+            return e;
+    }
     const long items = NC * p.B * p.H;
     hipLaunchKernelGGL((bw_prep_kernel<TI, DK, DV>), dim3((unsigned)(items < 16384 ? items : 16384)),
                        dim3(kBpThreads), 0, st, p, f, g, rf, 0L, (int)NC);
@@ -1287,16 +1319,24 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, hipStream_
 }
 
 template <int V, typename TI>
-hipError_t backward_t(const Problem &p, const Grads &g, void *ws, hipStream_t st) {
-    if (p.dk == 128 && p.dv == 128) return backward_shape<V, TI, 128, 128>(p, g, ws, st);
-    if (p.dk == 128 && p.dv == 64) return backward_shape<V, TI, 128, 64>(p, g, ws, st);
-    if (p.dk == 64 && p.dv == 128) return backward_shape<V, TI, 64, 128>(p, g, ws, st);
-    return backward_shape<V, TI, 64, 64>(p, g, ws, st);
+hipError_t backward_t(const Problem &p, const Grads &g, void *ws, bool saved, hipStream_t st) {
+    if (p.dk == 128 && p.dv == 128) return backward_shape<V, TI, 128, 128>(p, g, ws, saved, st);
+    if (p.dk == 128 && p.dv == 64) return backward_shape<V, TI, 128, 64>(p, g, ws, saved, st);
+    if (p.dk == 64 && p.dv == 128) return backward_shape<V, TI, 64, 128>(p, g, ws, saved, st);
+    return backward_shape<V, TI, 64, 64>(p, g, ws, saved, st);
 }
 
 template <int V>
-hipError_t backward_v(const Problem &p, const Grads &g, void *ws, hipStream_t st) {
-    return p.bf16 ? backward_t<V, bf16>(p, g, ws, st) : backward_t<V, float>(p, g, ws, st);
+hipError_t backward_v(const Problem &p, const Grads &g, void *ws, bool saved, hipStream_t st) {
+    return p.bf16 ? backward_t<V, bf16>(p, g, ws, saved, st)
+                  : backward_t<V, float>(p, g, ws, saved, st);
+}
+
+template <typename TI> hipError_t forward_save_t(const Problem &p, void *ws, hipStream_t st) {
+    if (p.dk == 128 && p.dv == 128) return forward_save_shape<TI, 128, 128>(p, ws, st);
+    if (p.dk == 128 && p.dv == 64) return forward_save_shape<TI, 128, 64>(p, ws, st);
+    if (p.dk == 64 && p.dv == 128) return forward_save_shape<TI, 64, 128>(p, ws, st);
+    return forward_save_shape<TI, 64, 64>(p, ws, st);
 }
 
 }  // namespace
@@ -1311,15 +1351,22 @@ size_t backward_workspace_bytes(const Problem &p) {
            kGradSlots * slot;
 }
 
-hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, hipStream_t stream) {
+hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, bool saved,
+                           hipStream_t stream) {
     switch (p.variant) {
-    case kDeltaNet: return backward_v<kDeltaNet>(p, g, workspace, stream);
-    case kGatedDeltaNet: return backward_v<kGatedDeltaNet>(p, g, workspace, stream);
-    case kKDA: return backward_v<kKDA>(p, g, workspace, stream);
-    case kGDN2: return backward_v<kGDN2>(p, g, workspace, stream);
-    case kKLA: return backward_v<kKLA>(p, g, workspace, stream);
+    case kDeltaNet: return backward_v<kDeltaNet>(p, g, workspace, saved, stream);
+    case kGatedDeltaNet: return backward_v<kGatedDeltaNet>(p, g, workspace, saved, stream);
+    case kKDA: return backward_v<kKDA>(p, g, workspace, saved, stream);
+    case kGDN2: return backward_v<kGDN2>(p, g, workspace, saved, stream);
+    case kKLA: return backward_v<kKLA>(p, g, workspace, saved, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_forward_save(const Problem &p, void *workspace, hipStream_t stream) {
+    if (p.variant < kDeltaNet || p.variant > kKLA) return hipErrorInvalidValue;
+    return p.bf16 ? forward_save_t<bf16>(p, workspace, stream)
+                  : forward_save_t<float>(p, workspace, stream);
 }
 
 }  // namespace gdr

@@ -92,6 +92,9 @@ struct Block {
     // the pipelined forward, keeping these partial lines out of the caches
     // leaves them to the next block's factors.
     bool nt_out;
+    // Scan with s_chunks: also write o (and s_out), i.e. the forward that
+    // keeps what its gradient needs; otherwise the states alone.
+    bool with_o = false;
 };
 
 struct WsLayout {
@@ -1346,11 +1349,13 @@ constexpr int kScan2Threads = 512;
 // kOutBurst does.
 constexpr int kOutBurst = 8;
 
-// STATES: instead of the outputs, record the state entering every chunk (fp32)
-// in blk.s_chunks; the output waves then only keep the barrier count.
+// STATES: instead of the outputs, record the state entering every chunk and
+// its Delta (input dtype) in blk.s_chunks and blk.d_chunks; the output waves
+// then only copy them.  SAVE: the outputs and that record both, the output
+// waves copying S_c and Delta_c beside their O_c.
 // A scalar decay's instances keep to 128 registers, so that a prep workgroup
 // fits beside them; a channel decay's never share a unit with a prep.
-template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG>
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG, bool SAVE = false>
 __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
                                                                    Block blk) {
     using M = Mma<TI>;
@@ -1546,6 +1551,17 @@ __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(
                                    Ov[j]);
             }
             pre_pd();
+            if constexpr (SAVE) {
+                // S_c and Delta_c, from the buffers O_c reads, before the
+                // barrier after which the chain overwrites S_c's; issued
+                // after the next chunk's prefetch, so that a wait for those
+                // loads does not wait for these stores.
+                TI *sg = static_cast<TI *>(blk.s_chunks), *dg = static_cast<TI *>(blk.d_chunks);
+                copy_transposed<TI, SW, DK + PT>(sg + (ch0 + c) * (long)DK * DV + col0, DV, sSt[buf],
+                                                 DK, DK, tid - 4 * kWave, 4 * kWave);
+                copy_transposed<TI, SW, C + PT>(dg + (ch0 + c) * (long)C * DV + col0, DV, sDt[buf], C,
+                                                C, tid - 4 * kWave, 4 * kWave);
+            }
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -1744,7 +1760,10 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
         constexpr int NJ = decltype(nj)::value;
         const long nwg = p.B * p.H * (DV / (16 * NJ));
         const long grid = kXcds * ((nwg + kXcds - 1) / kXcds);
-        if (blk.s_chunks)
+        if (blk.s_chunks && blk.with_o)
+            hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, false, false, SG, true>),
+                               dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
+        else if (blk.s_chunks)
             hipLaunchKernelGGL((chunk_scan2_kernel<TI, DK, DEPTH, NJ, true, false, SG>),
                                dim3((unsigned)grid), dim3(kScan2Threads), 0, st, p, w, blk);
         else if (blk.nt_out)
@@ -1899,7 +1918,7 @@ hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc
 
 hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
                               const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
-                              hipStream_t stream) {
+                              bool with_o, hipStream_t stream) {
     return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) {
         using TI = typename decltype(ti)::type;
         constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
@@ -1908,7 +1927,7 @@ hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc
         const Block blk{c0, nc, (int)NC, s_in, s_out,
                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
                         static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr,
-                        false};
+                        false, with_o};
         return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, false, stream);
     });
 }

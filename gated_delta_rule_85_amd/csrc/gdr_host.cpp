@@ -185,6 +185,16 @@ gdr_status check_grads(const gdr_args *a, const gdr_grads *g) {
     return GDR_OK;
 }
 
+// A caller's workspace of `need` bytes: present, 256-byte aligned, large enough.
+gdr_status check_workspace(const void *workspace, size_t ws_bytes, size_t need) {
+    if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return GDR_OK;
+}
+
 gdr::Problem to_problem(const gdr_args *a) {
     gdr::Problem p;
     p.variant = a->variant;
@@ -274,14 +284,46 @@ gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *wor
     p.state_out = nullptr;
     p.delta_out = nullptr;
     const size_t need = gdr::backward_workspace_bytes(p);
-    if (!workspace) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-        return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-    if (ws_bytes < need)
-        return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    if ((s = check_workspace(workspace, ws_bytes, need)) != GDR_OK) return s;
     const gdr::Grads gr{g->d_o, g->d_state_out, g->d_q, g->d_k, g->d_v, g->d_alpha,
                         g->d_beta, g->d_erase_b, g->d_write_w, g->d_state_in};
-    hipError_t e = gdr::launch_backward(p, gr, workspace, reinterpret_cast<hipStream_t>(hip_stream));
+    hipError_t e =
+        gdr::launch_backward(p, gr, workspace, false, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status gdr_forward_chunked_save(const gdr_args *a, void *workspace, size_t ws_bytes,
+                                    void *hip_stream) {
+    gdr_status s = check(a, 0);
+    if (s != GDR_OK) return s;
+    // what the gradient takes, so that the kept records serve it
+    if ((s = check(a, 2)) != GDR_OK) return s;
+    if (a->delta_out)
+        return fail(GDR_ERR_UNSUPPORTED, "gdr_forward_chunked_save takes delta_out = NULL");
+    const gdr::Problem p = to_problem(a);
+    const size_t need = gdr::backward_workspace_bytes(p);
+    if ((s = check_workspace(workspace, ws_bytes, need)) != GDR_OK) return s;
+    hipError_t e = gdr::launch_forward_save(p, workspace, reinterpret_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDR_OK;
+}
+
+gdr_status gdr_backward_chunked_saved(const gdr_args *a, const gdr_grads *g, void *workspace,
+                                      size_t ws_bytes, void *hip_stream) {
+    gdr_status s = check(a, 2);
+    if (s != GDR_OK) return s;
+    if ((s = check_grads(a, g)) != GDR_OK) return s;
+    gdr::Problem p = to_problem(a);
+    p.o = nullptr;
+    p.state_out = nullptr;
+    p.delta_out = nullptr;
+    const size_t need = gdr::backward_workspace_bytes(p);
+    if ((s = check_workspace(workspace, ws_bytes, need)) != GDR_OK) return s;
+    const gdr::Grads gr{g->d_o, g->d_state_out, g->d_q, g->d_k, g->d_v, g->d_alpha,
+                        g->d_beta, g->d_erase_b, g->d_write_w, g->d_state_in};
+    hipError_t e =
+        gdr::launch_backward(p, gr, workspace, true, reinterpret_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(GDR_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GDR_OK;
 }

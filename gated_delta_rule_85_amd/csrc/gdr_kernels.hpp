@@ -62,12 +62,14 @@ ForwardStates forward_states_ptrs(const Problem &p, void *workspace);
 // the factors of the block (prep), then the scan over it from s_in (NULL =
 // zeros) to s_out (NULL = dropped), recording the state entering each chunk
 // ([B*H][nbmax][dk][dv] in s_chunks) and each chunk's Delta = U~ - W S
-// ([B*H][nbmax][C][dv] in d_chunks), both in the input dtype.  No outputs.
+// ([B*H][nbmax][C][dv] in d_chunks), both in the input dtype.  with_o: the
+// scan also writes p.o (the forward that keeps what its gradient needs);
+// otherwise no outputs.
 hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc, bool concurrent,
                               hipStream_t stream);
 hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
                               const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
-                              hipStream_t stream);
+                              bool with_o, hipStream_t stream);
 
 // Gradient of the chunked forward: upstream gradients in, input gradients out.
 struct Grads {
@@ -76,6 +78,13 @@ struct Grads {
     float *d_q, *d_k, *d_v, *d_alpha, *d_beta, *d_erase_b, *d_write_w, *d_state_in;
 };
 size_t backward_workspace_bytes(const Problem &p);
-hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, hipStream_t stream);
+// saved: the workspace already holds the factors and the per-chunk states of
+// p (left by launch_forward_save), so the states pass is skipped.
+hipError_t launch_backward(const Problem &p, const Grads &g, void *workspace, bool saved,
+                           hipStream_t stream);
+// The chunked forward as one pass that leaves in the gradient's workspace the
+// factors of every chunk and the state and Delta entering each (the gradient's
+// states pass, with the outputs written too).
+hipError_t launch_forward_save(const Problem &p, void *workspace, hipStream_t stream);
 
 }  // namespace gdr

@@ -256,6 +256,31 @@ size_t gdr_backward_workspace_size(const gdr_args *a);
 gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *workspace,
                                 size_t ws_bytes, void *hip_stream);
 
+/* The forward of a training step that keeps what its gradient needs.  It
+ * writes o and state_out exactly as gdr_forward_chunked does, computed as one
+ * pass over all chunks, and leaves in `workspace` (256-byte aligned, at least
+ * gdr_backward_workspace_size(a) bytes, owned by the caller) every chunk's
+ * factors of the chunk form and the state and residual entering each chunk:
+ * the first pass gdr_backward_chunked would otherwise recompute.  Besides the
+ * forward's checks, `a` must be valid for the gradient (flags 0, v_route
+ * NULL: GDR_ERR_UNSUPPORTED), and delta_out must be NULL
+ * (GDR_ERR_UNSUPPORTED). */
+gdr_status gdr_forward_chunked_save(const gdr_args *a, void *workspace, size_t ws_bytes,
+                                    void *hip_stream);
+
+/* gdr_backward_chunked without its first pass: it reads the records that
+ * gdr_forward_chunked_save left in `workspace`.  The caller passes the same
+ * `a` (the same inputs, unchanged since) and the same workspace, untouched in
+ * between and ordered after that call (same stream, or synchronised); the
+ * library cannot check this, and results are undefined otherwise.  Results
+ * equal gdr_backward_chunked's, bit for bit except where that call sums per
+ * token with atomic additions of varying order (d_alpha, d_beta, and d_k for
+ * KLA), which differ in their last bits from one call to the next either way.
+ * Same arguments and errors as gdr_backward_chunked; the workspace is
+ * overwritten past the kept records. */
+gdr_status gdr_backward_chunked_saved(const gdr_args *a, const gdr_grads *g, void *workspace,
+                                      size_t ws_bytes, void *hip_stream);
+
 /* Static description of a status code. */
 const char *gdr_status_string(int status);
 

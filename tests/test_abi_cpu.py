@@ -187,6 +187,36 @@ def test_backward_validation(L, variant):
     assert binding.gdr_backward_chunked(a, _grads(variant), 0x100000, n - 1, 0) == 3
 
 
+@pytest.mark.parametrize("variant", list(binding.VARIANTS))
+def test_forward_save_and_saved_backward_validation(L, variant):
+    """The forward that keeps its records takes the forward's arguments (o
+    required) and the gradient's (flags 0, no routed value), no residual
+    output, and the gradient's workspace; the saved gradient validates like
+    gdr_backward_chunked.  Every rejection happens on the host."""
+    a = _args(variant)
+    n = binding.gdr_backward_workspace_size(a)
+    assert n > 0
+    # the forward's own checks
+    assert binding.gdr_forward_chunked_save(_args(variant, o=None), 0x100000, n, 0) == 1
+    assert binding.gdr_forward_chunked_save(_args(variant, o=0x1000), 0x100000, n, 0) == 1  # = q
+    # the gradient's
+    assert binding.gdr_forward_chunked_save(_args(variant, flags=1), 0x100000, n, 0) == 2
+    assert binding.gdr_forward_chunked_save(_args(variant, v_route=0x1c000), 0x100000, n, 0) == 2
+    assert binding.gdr_forward_chunked_save(_args(variant, delta_out=0x1d000), 0x100000, n, 0) == 2
+    # its workspace
+    assert binding.gdr_forward_chunked_save(a, None, n, 0) == 3
+    assert binding.gdr_forward_chunked_save(a, 0x100080, n, 0) == 3
+    assert binding.gdr_forward_chunked_save(a, 0x100000, n - 1, 0) == 3
+    g = _args(variant, o=None, state_out=None)
+    missing = "d_alpha" if variant != "deltanet" else "d_k"
+    assert binding.gdr_backward_chunked_saved(g, _grads(variant, **{missing: None}), 0x100000,
+                                              n, 0) == 1
+    assert binding.gdr_backward_chunked_saved(_args(variant, o=None, flags=1), _grads(variant),
+                                              0x100000, n, 0) == 2
+    assert binding.gdr_backward_chunked_saved(g, _grads(variant), None, n, 0) == 3
+    assert binding.gdr_backward_chunked_saved(g, _grads(variant), 0x100000, n - 1, 0) == 3
+
+
 def test_backward_workspace_grows_with_length(L):
     a1 = _args("kda", o=None, T=64 * 10)
     a2 = _args("kda", o=None, T=64 * 20)
