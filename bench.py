@@ -608,8 +608,11 @@ def cold_decode(args):
 
 def other_workloads(L, dev, sh, steps, warmup):
     """The forward of workloads 1-4 (DeltaNet fp32, Gated DeltaNet, KDA,
-    Gated DeltaNet-2), each timed with HIP events on the launch stream over
-    `steps` back-to-back calls after `warmup` untimed ones."""
+    Gated DeltaNet-2), each timed with HIP events on the launch stream: a HIP
+    graph of `steps` calls replayed (device time per forward, the figure the
+    rates use), and the same calls launched one by one from the host after
+    `warmup` untimed ones (ms_eager: for the smallest workload the host's
+    per-call cost exceeds the device time)."""
     import torch
 
     from gated_delta_rule_85_amd import binding
@@ -638,18 +641,32 @@ def other_workloads(L, dev, sh, steps, warmup):
             L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh)
         e1.record()
         torch.cuda.synchronize()
+        t_eager = e0.elapsed_time(e1) / 1e3 / steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gs = torch.cuda.current_stream().cuda_stream
+            for _ in range(steps):
+                binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, gs))
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 1e3 / steps
+        del graph
         in_bytes = 2 if wl.dtype == "bf16" else 4
         fl = forward_flops_per_head_token(dk, dv) * B * T * H
         fb = forward_bytes_variant(wl.variant, B, T, H, dk, dv, in_bytes)
         peak_mm = PEAK_BF16 if wl.dtype == "bf16" else PEAK_FP32_MATRIX
         res[wl.name] = dict(variant=wl.variant, dtype=wl.dtype, B=B, T=T, H=H, dk=dk, dv=dv,
-                            ms=t * 1e3, tokens_per_s=B * T / t, tflops=fl / t / 1e12,
+                            ms=t * 1e3, ms_eager=t_eager * 1e3, tokens_per_s=B * T / t,
+                            tflops=fl / t / 1e12,
                             mfma_frac=fl / t / peak_mm,
                             mfma_peak_TFLOPs=peak_mm / 1e12, hbm_GBps=fb / t / 1e9,
                             hbm_frac=fb / t / PEAK_HBM, algorithmic_flop=fl,
                             algorithmic_bytes=fb)
-        log(f"{wl.name}: {t * 1e6:.1f} us")
+        log(f"{wl.name}: {t * 1e6:.1f} us (graph replay), {t_eager * 1e6:.1f} us launched one by one")
         del d, o, s_T, ws
     torch.cuda.empty_cache()
     return res

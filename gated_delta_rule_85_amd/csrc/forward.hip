@@ -256,15 +256,31 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(Problem p, WsP
     auto tok = [&](int r) -> long { return ((long)b * T + t0 + r) * H + h; };
 
     // ---- phase 0: row norms, decay prefix sums, per-token write strength -----
-    // One wave per row: |k_r|^2 and |q_r|^2 over the key channels.
-    for (int r = wave; r < C; r += kPrepThreads / kWave) {
+    // |k_r|^2 and |q_r|^2 over the key channels, one wave per row: each wave
+    // issues the loads of all its rows before the first reduction, so that
+    // they wait once instead of once per row.
+    constexpr int kNW = kPrepThreads / kWave, kRPW = C / kNW, kEPL = (DK + kWave - 1) / kWave;
+    float kx[kRPW][kEPL], qx[kRPW][kEPL];
+#pragma unroll
+    for (int n = 0; n < kRPW; ++n) {
+        const int r = wave + kNW * n;
+#pragma unroll
+        for (int e = 0; e < kEPL; ++e) {
+            const int i = lane + kWave * e;
+            const bool ok = r < nvalid && i < DK;
+            kx[n][e] = ok ? to_f32(k[tok(r) * DK + i]) : 0.f;
+            qx[n][e] = ok ? to_f32(q[tok(r) * DK + i]) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kRPW; ++n) {
+        const int r = wave + kNW * n;
         float sk = 0.f, sq = 0.f;
-        if (r < nvalid)
-            for (int i = lane; i < DK; i += kWave) {
-                const float x = to_f32(k[tok(r) * DK + i]), y = to_f32(q[tok(r) * DK + i]);
-                sk += x * x;
-                sq += y * y;
-            }
+#pragma unroll
+        for (int e = 0; e < kEPL; ++e) {
+            sk += kx[n][e] * kx[n][e];
+            sq += qx[n][e] * qx[n][e];
+        }
         sk = wave_sum(sk);
         sq = wave_sum(sq);
         if (lane == 0) {
