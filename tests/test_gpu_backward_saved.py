@@ -82,6 +82,16 @@ def test_saved_path_head_sizes(dk, dv):
     _compare("kla", to_dev(inp), to_dev(up))
 
 
+@pytest.mark.parametrize("T", [1, 64, 65])
+@pytest.mark.parametrize("variant", ["gdn2", "kla"])
+def test_saved_path_short_sequences(variant, T):
+    """One token, one full chunk, and a full chunk plus one token; d = 64."""
+    announce(f"saved forward/gradient {variant} T={T}")
+    inp = make_inputs(variant, 2, T, 2, 64, 64, "bf16", seed=1350 + T, state_scale=0.3)
+    up = make_upstream_grads(2, T, 2, 64, 64, "bf16", seed=1351 + T)
+    _compare(variant, to_dev(inp), to_dev(up))
+
+
 @pytest.mark.parametrize("variant", ["kda", "gated_deltanet"])
 def test_saved_path_where_the_plain_forward_is_pipelined(variant):
     """Long enough (257 / 513 chunks at 4 heads) that gdr_forward_chunked
