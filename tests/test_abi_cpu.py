@@ -28,7 +28,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gdr_forward_chunked", "gdr_decode_step", "gdr_forward_workspace_size",
-              "gdr_check_args", "gdr_status_string", "gdr_last_error_detail"):
+              "gdr_check_args", "gdr_status_string", "gdr_last_error_detail",
+              "gdr_backward_chunked", "gdr_backward_workspace_size", "gdr_forward_chunked_noalloc",
+              "gdr_forward_chunked_save", "gdr_backward_chunked_saved"):
         assert n in names
 
 

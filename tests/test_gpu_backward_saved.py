@@ -92,6 +92,26 @@ def test_saved_path_short_sequences(variant, T):
     _compare(variant, to_dev(inp), to_dev(up))
 
 
+def test_saving_forward_without_final_state():
+    """state_out = NULL: the saving forward still keeps every record the
+    gradient needs (the final state is not one of them)."""
+    announce("saving forward without state_out")
+    inp = make_inputs("gated_deltanet", 1, 140, 2, 128, 128, "bf16", seed=1360, state_scale=0.3)
+    up = make_upstream_grads(1, 140, 2, 128, 128, "bf16", seed=1361)
+    d, du = to_dev(inp), to_dev(up)
+    o_ref, _ = binding.forward("gated_deltanet", d["q"], d["k"], d["v"], **_gates(d))
+    g_ref = binding.backward("gated_deltanet", d["q"], d["k"], d["v"], **_gates(d), d_o=du["d_o"],
+                             d_state_out=du["d_state_out"])
+    o, s, ws = binding.forward_save("gated_deltanet", d["q"], d["k"], d["v"], **_gates(d),
+                                    output_state=False)
+    g = binding.backward("gated_deltanet", d["q"], d["k"], d["v"], **_gates(d), d_o=du["d_o"],
+                         d_state_out=du["d_state_out"], saved=ws)
+    torch.cuda.synchronize()
+    assert s is None and torch.equal(o, o_ref)
+    for name in ("q", "k", "v", "state_in"):
+        assert torch.equal(g[name], g_ref[name]), name
+
+
 @pytest.mark.parametrize("variant", ["kda", "gated_deltanet"])
 def test_saved_path_where_the_plain_forward_is_pipelined(variant):
     """Long enough (257 / 513 chunks at 4 heads) that gdr_forward_chunked
