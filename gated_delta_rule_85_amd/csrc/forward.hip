@@ -1065,11 +1065,15 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         }
     }
     // Every raw register is consumed: the next item's loads go out now and
-    // arrive during phases 2-4 (the last item reloads itself, from L2, so that
-    // the issue is unconditional and the compiler's waits stay exact).
+    // arrive during phases 2-4.  After its last item a workgroup still issues
+    // them, so that the issue is unconditional and the compiler's waits stay
+    // exact; they then read item 0 of the launch, one region that every
+    // workgroup's last prefetch shares and finds in L2 (the workgroup's own
+    // last item has been evicted by then, and re-reading it cost ~18 MB per
+    // 64-chunk block of a pipelined forward).
     const unsigned next_item = sNext;
     {
-        const unsigned next = next_item < nitems ? next_item : item;
+        const unsigned next = next_item < nitems ? next_item : 0u;
         raw.issue(p, chunk_of(next), head_of(next), row_of(next), tid);
     }
     __syncthreads();
@@ -1142,9 +1146,10 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
         asm volatile("" : "+v"(z));
         *reinterpret_cast<uint2 *>(ws.P + ch * C * C + frag_off<bf16>(r, s2, C)) = make_uint2(z, z);
     }
-    // the q fragments are free: the next item's go out now
+    // the q fragments are free: the next item's go out now (item 0's after
+    // the last item, as above)
     if constexpr (!kSplit) {
-        const unsigned next = next_item < nitems ? next_item : item;
+        const unsigned next = next_item < nitems ? next_item : 0u;
         load_qf(chunk_of(next), head_of(next), row_of(next), l16, lg);
     }
     __syncthreads();
