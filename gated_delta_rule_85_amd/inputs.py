@@ -197,6 +197,27 @@ def with_strong_channel_decay(inp, frac=1 / 3, lo=1e-3, hi=0.05, seed=0, log=Fal
     return out
 
 
+def with_strong_scalar_decay(inp, frac=1 / 3, lo=1e-3, hi=0.05, seed=0, log=False):
+    """Replace the scalar decay of ``frac`` of the tokens of every (b, h) by
+    values drawn uniformly from [lo, hi] (with ``log``, uniformly in log(alpha)
+    between log(lo) and log(hi)).  Returns a new dict; the other tensors are
+    shared.  For the variants whose forget gate is one scalar per head and
+    token (Gated DeltaNet, Kaczmarz)."""
+    alpha = inp["alpha"]
+    if alpha is None or alpha.dim() != 3:
+        raise ValueError("needs a scalar decay [B, T, H]")
+    rng = np.random.default_rng(seed)
+    pick = rng.random(tuple(alpha.shape)) < frac
+    if log:
+        strong = np.exp(rng.uniform(np.log(lo), np.log(hi), size=tuple(alpha.shape)))
+    else:
+        strong = rng.uniform(lo, hi, size=tuple(alpha.shape))
+    a = np.where(pick, strong, alpha.numpy().astype(np.float64)).astype(np.float32)
+    out = dict(inp)
+    out["alpha"] = torch.from_numpy(a)
+    return out
+
+
 def make_routed_value(B, T, H, dv, dtype="bf16", seed=0, scale=1.0):
     """A value routed in from another layer, N(0,1) * scale [B,T,H,dv] in ``dtype``."""
     rng = np.random.default_rng(seed)
