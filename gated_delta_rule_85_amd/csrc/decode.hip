@@ -16,7 +16,12 @@
 //     requested before the state (which tends to stay in the last-level
 //     cache between steps);
 //   * the updated state is written from the same registers: S is read once
-//     and written once.
+//     and written once;
+//   * the tile's state is addressed through a buffer descriptor of its own
+//     (wave-uniform base), one per-lane offset and a uniform offset per row
+//     pass, instead of sixteen 64-bit addresses per lane: the kernel stays
+//     within 128 registers, so four waves share a SIMD and a batch-64 step's
+//     4096 tiles are all resident at once.
 #include "gdr_device.hpp"
 
 namespace gdr {
@@ -80,14 +85,15 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
     f32x4 s[PASSES];
     RowVec<TI, DK> kv, qv;
     RowVec<float, DK> av, dv_;
-    TI vr[4], vx[ROUTE ? 4 : 1];   // vx: the routed value
+    // The four value elements as raw 32-bit words (vx: the routed value).
+    static constexpr int VW = (int)sizeof(TI);
+    uint32_t vr[VW], vx[ROUTE ? VW : 1];
     float beta, sdec;
     f32x4 wr;
 
-    __device__ __forceinline__ void load(const Problem &p, long tile, int lane) {
-        const int dv = (int)p.dv, tph = dv / CW;
-        const long bh = tile / tph;
-        const int col0 = (int)(tile % tph) * CW;
+    // bh and col0 are wave-uniform.
+    __device__ __forceinline__ void load(const Problem &p, long bh, int col0, int lane) {
+        const int dv = (int)p.dv;
         const int cg = lane % LPR, r0 = lane / LPR;
         kv.load(static_cast<const TI *>(p.k) + bh * DK, lane);
         qv.load(static_cast<const TI *>(p.q) + bh * DK, lane);
@@ -97,37 +103,57 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
         sdec = (VT::kHasDecay && !VT::kChannelDecay) ? p.alpha[bh] : 1.f;
         const TI *v = static_cast<const TI *>(p.v) + bh * (long)dv + col0 + 4 * cg;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vr[c] = v[c];
+        for (int w = 0; w < VW; ++w) vr[w] = reinterpret_cast<const uint32_t *>(v)[w];
         if constexpr (ROUTE) {
             const TI *x = p.v_route ? static_cast<const TI *>(p.v_route) + bh * (long)dv + col0 + 4 * cg
                                     : v;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vx[c] = x[c];
+            for (int w = 0; w < VW; ++w) vx[w] = reinterpret_cast<const uint32_t *>(x)[w];
         }
         if constexpr (VT::kGates)
             wr = *reinterpret_cast<const f32x4 *>(p.write_w + bh * (long)dv + col0 + 4 * cg);
-        const float *Sin = p.state_in + bh * DK * (long)dv + col0 + 4 * cg;
+        // The token's inputs (cold in the cache) are issued before the state:
+        // the scheduler must not sink them past the state loads.
+        __builtin_amdgcn_sched_barrier(0);
+        const auto rs = make_rsrc(p.state_in + bh * DK * (long)dv + col0);
+        const unsigned voff = (unsigned)(r0 * dv + 4 * cg) * 4u, pass = (unsigned)(RPP * dv) * 4u;
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i)
-            s[i] = *reinterpret_cast<const f32x4 *>(Sin + (long)(r0 + i * RPP) * dv);
+        for (int i = 0; i < PASSES; ++i) {
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * pass, 0);
+            s[i] = __builtin_bit_cast(f32x4, w);
+        }
     }
 
-    __device__ __forceinline__ void finish(const Problem &p, long tile, int lane) {
-        const int dv = (int)p.dv, tph = dv / CW;
-        const long bh = tile / tph;
-        const int col0 = (int)(tile % tph) * CW;
+    __device__ __forceinline__ void finish(const Problem &p, long bh, int col0, int lane) {
+        const int dv = (int)p.dv;
         const int cg = lane % LPR, r0 = lane / LPR;
         // On-load transforms: gates from pre-activations now; the q/k
         // normalisation, a per-token scalar each, after the reductions below.
         constexpr bool rawg = RAWG;
         const float ds = p.decay_scale;
+        // The value words and the write gate are opaque until here, so that
+        // their arithmetic (and the wait for them) cannot be hoisted above the
+        // state loads.
+#pragma unroll
+        for (int w = 0; w < VW; ++w) asm volatile("" : "+v"(vr[w]));
+        if constexpr (ROUTE)
+#pragma unroll
+            for (int w = 0; w < VW; ++w) asm volatile("" : "+v"(vx[w]));
+        if constexpr (VT::kGates)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(wr[c]));
+        auto elem = [](const uint32_t *w, int c) {
+            if constexpr (sizeof(TI) == 4) return __uint_as_float(w[c]);
+            else return __uint_as_float((c & 1) ? (w[c / 2] & 0xffff0000u) : (w[c / 2] << 16));
+        };
         f32x4 u;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) u[c] = to_f32(vr[c]);
+        for (int c = 0; c < 4; ++c) u[c] = elem(vr, c);
         if constexpr (ROUTE)
             if (p.v_route)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) u[c] += to_f32(vx[c]);
+                for (int c = 0; c < 4; ++c) u[c] += elem(vx, c);
         if constexpr (VT::kGates) {
             if constexpr (rawg)
 #pragma unroll
@@ -202,10 +228,14 @@ template <int V, typename TI, int DK, int CW, int FL> struct DecodeTile {
                     for (int c = 0; c < 4; ++c) dp[c] = from_f32<TI>(dl[c]);
                 }
         }
-        float *Sout = p.state_out + bh * DK * (long)dv + col0 + 4 * cg;
+        const auto rs = make_rsrc(p.state_out + bh * DK * (long)dv + col0);
+        const unsigned voff = (unsigned)(r0 * dv + 4 * cg) * 4u, pass = (unsigned)(RPP * dv) * 4u;
 #pragma unroll
-        for (int i = 0; i < PASSES; ++i)
-            *reinterpret_cast<f32x4 *>(Sout + (long)(r0 + i * RPP) * dv) = s[i] + (kr[i] * rk) * dl;
+        for (int i = 0; i < PASSES; ++i) {
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 x = s[i] + (kr[i] * rk) * dl;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, voff, i * pass, 0);
+        }
     }
 };
 
@@ -214,11 +244,17 @@ template <int V, typename TI, int DK, int CW, int WAVES, int FL>
 __global__ __launch_bounds__(WAVES * 64)
 void decode_wave_kernel(Problem p) {
     using Tile = DecodeTile<V, TI, DK, CW, FL>;
-    const long tile = (long)blockIdx.x * WAVES + threadIdx.x / kWave;
+    // The tile index is wave-uniform; d_v is 64 or 128, so a head has 2 or 4
+    // column tiles and the split is a shift.
+    const long tile = (long)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     if (tile >= p.B * p.H * (p.dv / CW)) return;
+    const int sh = p.dv == 128 ? 2 : 1;
+    static_assert(CW == 32, "d_v / CW column tiles per head");
+    const long bh = tile >> sh;
+    const int col0 = (int)(tile & ((1 << sh) - 1)) * CW;
     Tile t;
-    t.load(p, tile, threadIdx.x & (kWave - 1));
-    t.finish(p, tile, threadIdx.x & (kWave - 1));
+    t.load(p, bh, col0, threadIdx.x & (kWave - 1));
+    t.finish(p, bh, col0, threadIdx.x & (kWave - 1));
 }
 
 template <int V, typename TI, int DK>
