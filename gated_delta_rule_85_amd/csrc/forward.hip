@@ -642,10 +642,36 @@ template <int V, int DK, int DV, bool RT> struct PrepRaw {
     }
 };
 
-// RT: a routed value is added to v as it is staged.
+// The prep's LDS tiles (one workgroup's).
+template <int V, int DK, int DV> struct PrepSmem {
+    using VT = VariantTraits<V>;
+    static constexpr int GW = VT::kChannelDecay ? DK : 1;
+    static constexpr int R1 = C * DK * 2 > C * C * 4 ? C * DK * 2 : C * C * 4;   // k   -> T
+    static constexpr int R3 = C * DV * 2 > C * C * 4 ? C * DV * 2 : C * C * 4;   // u   -> A
+    static constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
+    static constexpr bool kSplit = VT::kChannelDecay;
+    static constexpr int NS = VT::kGates ? 2 : 3;
+    alignas(16) char smem1[R1];
+    alignas(16) char smem3[R3];
+    alignas(16) bf16 sAg[VT::kGates ? C * DK : 8];   // b (.) k
+    alignas(16) float sG[C][GW];
+    float sBeta[C];
+    float sEg[kRowDecay ? C : 1], sEgc[kRowDecay ? C : 1];   // e^{g_r}, e^{g_C - g_r}
+    alignas(16) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
+    alignas(16) bf16 sUt[DV * C];   // U^T, [DV][C]
+    float sX[4][16][17];
+    alignas(16) bf16 sSplit[kSplit ? NS : 1][kSplit ? C * DK : 8];   // see prep_body
+    alignas(16) float sM[kSplit ? 6 : 1][kSplit ? DK : 4];
+    unsigned sNext;   // the item after the current one
+};
+
+// The bf16 prep of one workgroup: wg0 is its index among the nwg workgroups
+// of the prep (its first item).  RT: a routed value is added to v as it is
+// staged.
 template <int V, int DK, int DV, bool RT>
-__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
-void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
+__device__ __forceinline__ void prep_body(const Problem &p, const WsPtrs<bf16> &ws, const Block &blk,
+                                          const unsigned wg0, const unsigned nwg,
+                                          PrepSmem<V, DK, DV> &sm) {
     using VT = VariantTraits<V>;
     using M = Mma<bf16>;
     using Raw = PrepRaw<V, DK, DV, RT>;
@@ -653,18 +679,17 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     constexpr int GW = VT::kChannelDecay ? DK : 1;
     constexpr int KC = DK / 8, VC = DV / 8;   // 16-byte chunks per k row / v row
     constexpr int NQ = Raw::NQ, NV = Raw::NV;
-    constexpr int R1 = C * DK * 2 > C * C * 4 ? C * DK * 2 : C * C * 4;   // k   -> T
-    constexpr int R3 = C * DV * 2 > C * C * 4 ? C * DV * 2 : C * C * 4;   // u   -> A
-    __shared__ __attribute__((aligned(16))) char smem1[R1];
-    __shared__ __attribute__((aligned(16))) char smem3[R3];
-    __shared__ __attribute__((aligned(16))) bf16 sAg[VT::kGates ? C * DK : 8];   // b (.) k
-    __shared__ __attribute__((aligned(16))) float sG[C][GW];
-    __shared__ float sBeta[C];
+    auto &smem1 = sm.smem1;
+    auto &smem3 = sm.smem3;
+    auto &sAg = sm.sAg;
+    auto &sG = sm.sG;
+    auto &sBeta = sm.sBeta;
     constexpr bool kRowDecay = VT::kHasDecay && !VT::kChannelDecay;
-    __shared__ float sEg[kRowDecay ? C : 1], sEgc[kRowDecay ? C : 1];   // e^{g_r}, e^{g_C - g_r}
-    __shared__ __attribute__((aligned(16))) bf16 sAt[DK * C];   // (a (.) e^{g})^T, [DK][C]
-    __shared__ __attribute__((aligned(16))) bf16 sUt[DV * C];   // U^T, [DV][C]
-    __shared__ float sX[4][16][17];
+    auto &sEg = sm.sEg;
+    auto &sEgc = sm.sEgc;
+    auto &sAt = sm.sAt;
+    auto &sUt = sm.sUt;
+    auto &sX = sm.sX;
     // Channel decay: the Gram products' split operands, k e^{m - g} (right)
     // and a e^{g - m}, q e^{g - m} (left), with m = (g_{16R} + g_{16R+15}) / 2
     // the reference of the row's own 16-row block R, are formed once per item
@@ -677,8 +702,8 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // such a tile then stay bounded, the right one by 1).
     constexpr bool kSplit = VT::kChannelDecay;
     constexpr int NS = VT::kGates ? 2 : 3;
-    __shared__ __attribute__((aligned(16))) bf16 sSplit[kSplit ? NS : 1][kSplit ? C * DK : 8];
-    __shared__ __attribute__((aligned(16))) float sM[kSplit ? 6 : 1][kSplit ? DK : 4];
+    auto &sSplit = sm.sSplit;
+    auto &sM = sm.sM;
     bf16 *const sKr = sSplit[0];
     bf16 *const sQl = sSplit[kSplit ? NS - 1 : 0];
     bf16 *const sAl = VT::kGates ? sAg : sSplit[kSplit && !VT::kGates ? 1 : 0];
@@ -700,17 +725,17 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     // out [B, T, H], two tokens of all sixteen heads per line at H = 16) are
     // fetched once for all of them, and the rows of q, k and v that the
     // workgroups in flight read are whole token rows of all heads.  A
-    // workgroup takes item blockIdx.x first, then every gridDim.x-th item or
+    // workgroup takes item wg0 first, then every nwg-th item or
     // the next ticket (blk.ticket), and loads the next item's inputs while it
     // computes the current one.
     // Item indices fit in 32 bits (the host keeps B * H * ceil(T / 64) below
     // 2^31), so their split into (chunk, head, batch row) is 32-bit scalar
     // arithmetic.
     const unsigned nc = (unsigned)blk.nc, nitems = nc * (unsigned)(p.H * p.B);
-    unsigned item = blockIdx.x;
+    unsigned item = wg0;
     if (blk.ticket_clear && item == 0 && threadIdx.x == 0) *blk.ticket_clear = 0u;
     if (item >= nitems) return;
-    __shared__ unsigned sNext;   // the item after the current one
+    unsigned &sNext = sm.sNext;
     auto chunk_of = [&](unsigned it) { return blk.c0 + (long)((it / (unsigned)H) % nc); };
     auto head_of = [&](unsigned it) { return (int)(it % (unsigned)H); };
     auto row_of = [&](unsigned it) { return (int)((it / (unsigned)H) / nc); };
@@ -875,7 +900,7 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     }
     if constexpr (VT::kScalarBeta)
         if (tid < C) sBeta[tid] = tid < nvalid ? (rawg ? sigmoid_f(raw.be) : raw.be) : 0.f;
-    if (tid == 0) sNext = blk.ticket ? gridDim.x + (tk - blk.ticket_base) : item + gridDim.x;
+    if (tid == 0) sNext = blk.ticket ? nwg + (tk - blk.ticket_base) : item + nwg;
     __syncthreads();
 
     // ---- gates: decay prefix sums (of the staged logs); KLA step size --------
@@ -1286,6 +1311,13 @@ void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
     }   // items
 }
 
+template <int V, int DK, int DV, bool RT>
+__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
+void chunk_prep_bf16_kernel(Problem p, WsPtrs<bf16> ws, Block blk) {
+    __shared__ PrepSmem<V, DK, DV> sm;
+    prep_body<V, DK, DV, RT>(p, ws, blk, blockIdx.x, gridDim.x, sm);
+}
+
 // ============================================================================
 // chunk_scan, split roles: eight waves per workgroup, which owns NJ 16-column
 // tiles of one head's state.  Waves 0-3 run only the state recurrence
@@ -1376,19 +1408,29 @@ constexpr int kOutBurst = 8;
 // waves copying S_c and Delta_c beside their O_c.
 // A scalar decay's instances keep to 128 registers, so that a prep workgroup
 // fits beside them; a channel decay's never share a unit with a prep.
-template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG, bool SAVE = false>
-__global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
-                                                                   Block blk) {
+// The scan's LDS tiles (one workgroup's).
+template <typename TI, int DK, int NJ, bool STATES> struct ScanSmem {
+    static constexpr int PT = 8;
+    static constexpr int SW = 16 * NJ;   // value columns of the slice
+    alignas(16) TI sSt[2][SW][DK + PT];   // S^T, double-buffered
+    alignas(16) TI sDt[2][SW][C + PT];    // Delta^T, double-buffered
+    // o of the last kOutBurst chunks, written to HBM in one burst (see below)
+    alignas(16) TI sO[STATES ? 1 : kOutBurst][C][SW];
+};
+
+// The scan of one workgroup; wg is its index in the scan's grid.
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG, bool SAVE>
+__device__ __forceinline__ void scan_body(const Problem &p, const WsPtrs<TI> &ws, const Block &blk,
+                                          const unsigned wg, ScanSmem<TI, DK, NJ, STATES> &sm) {
     using M = Mma<TI>;
     using CO = ChainOps<TI, DK, NJ, SG>;
     using OO = OutOps<TI, DK>;
     constexpr int KS_D = CO::KS_D, KS_C = CO::KS_C, NI = CO::NI;
     constexpr int PT = 8;
     constexpr int SW = 16 * NJ;   // value columns of the slice
-    __shared__ __attribute__((aligned(16))) TI sSt[2][SW][DK + PT];   // S^T, double-buffered
-    __shared__ __attribute__((aligned(16))) TI sDt[2][SW][C + PT];    // Delta^T, double-buffered
-    // o of the last kOutBurst chunks, written to HBM in one burst (see below)
-    __shared__ __attribute__((aligned(16))) TI sO[STATES ? 1 : kOutBurst][C][SW];
+    auto &sSt = sm.sSt;
+    auto &sDt = sm.sDt;
+    auto &sO = sm.sO;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -1399,7 +1441,7 @@ __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(
     const int nslice = DV / SW;
     const long nwg = p.B * p.H * nslice;
     const long per_xcd = (nwg + kXcds - 1) / kXcds;
-    const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const long logical = (long)(wg % kXcds) * per_xcd + wg / kXcds;
     if (logical >= nwg) return;
     // The scan is the sequential part: when the next block's prep shares the
     // compute unit, its waves are issued first.
@@ -1627,33 +1669,48 @@ __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(
     }
 }
 
+template <typename TI, int DK, int DEPTH, int NJ, bool STATES, bool NTO, bool SG, bool SAVE = false>
+__global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(Problem p, WsPtrs<TI> ws,
+                                                                   Block blk) {
+    __shared__ ScanSmem<TI, DK, NJ, STATES> sm;
+    scan_body<TI, DK, DEPTH, NJ, STATES, NTO, SG, SAVE>(p, ws, blk, blockIdx.x, sm);
+}
+
+// ============================================================================
+// One launch of the pipelined forward: its first scan_grid workgroups run the
+// scan of block i (o written with streaming stores), the rest the prep of
+// block i + 1 into the other workspace slot.  The two share no data; the
+// scan reads what the previous launch's prep wrote.  Issued in order on one
+// stream, these launches keep every dependency of the pipeline (the prep
+// before the scan of its block, a slot's scan before its next prep, the
+// state carried from block to block), and a launch starts as soon as the one
+// before it ends, where a wait on another stream's event took ~11 us per
+// block.  Workgroups are dispatched in index order, so the scan's take their
+// units first, one per unit; the LDS of the two roles overlays, so the launch
+// asks for the prep's footprint and a prep workgroup still fits beside a
+// scan workgroup.
+static_assert(kScan2Threads == kPrep2Threads, "one workgroup size for both roles");
+template <int V, int DK, int DV, int NJ> union PipeSmem {
+    PrepSmem<V, DK, DV> prep;
+    ScanSmem<bf16, DK, NJ, false> scan;
+};
+template <int V, int DK, int DV, bool RT, int NJ>
+__global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
+void chunk_pipe_kernel(Problem p, WsPtrs<bf16> scan_ws, Block scan_blk, unsigned scan_grid,
+                       WsPtrs<bf16> prep_ws, Block prep_blk) {
+    constexpr bool SG = !VariantTraits<V>::kChannelDecay;
+    __shared__ PipeSmem<V, DK, DV, NJ> sm;
+    if (blockIdx.x < scan_grid)
+        scan_body<bf16, DK, 2, NJ, false, true, SG, false>(p, scan_ws, scan_blk, blockIdx.x, sm.scan);
+    else
+        prep_body<V, DK, DV, RT>(p, prep_ws, prep_blk, blockIdx.x - scan_grid, gridDim.x - scan_grid,
+                                 sm.prep);
+}
+
 // ---- dispatch -----------------------------------------------------------------
 
 
-// Internal helper stream and events of the calling host thread, one set per
-// device, created on first use and kept for the life of the process.
-struct AuxStream {
-    hipStream_t s = nullptr;
-    hipEvent_t start = nullptr, prep[2] = {nullptr, nullptr}, scan[2] = {nullptr, nullptr};
-};
 constexpr int kMaxDevices = 64;
-thread_local AuxStream t_aux[kMaxDevices];
-
-hipError_t aux_stream(AuxStream **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    AuxStream &a = t_aux[dev];
-    if (!a.s) {
-        if ((e = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking)) != hipSuccess) return e;
-        hipEvent_t *evs[] = {&a.start, &a.prep[0], &a.prep[1], &a.scan[0], &a.scan[1]};
-        for (hipEvent_t *ev : evs)
-            if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
-    }
-    *out = &a;
-    return hipSuccess;
-}
 
 // Compute units of the current device, queried once per device.  Threads
 // that race on the first query each store the same value; the atomics make
@@ -1718,32 +1775,39 @@ template <int V, int DK, int DV, bool RT> hipError_t prep_slots(long *slots_out,
     return hipSuccess;
 }
 
+// Workgroups of a bf16 prep over the items of blk.  Persistent workgroups,
+// each looping over chunk-heads with the next one's inputs in flight.  Alone,
+// the grid fills every resident slot; beside a concurrent scan, one workgroup
+// per compute unit, so that a scan workgroup still fits on every unit, plus a
+// second one for each unit the scan leaves free: in whichever order the two
+// grids are placed, every scan workgroup still finds a unit with room.
+template <int V, int DK, int DV>
+hipError_t prep_grid(const Problem &p, const Block &blk, bool concurrent, long *grid) {
+    long slots = 0, cus = 0;
+    hipError_t e = p.v_route ? prep_slots<V, DK, DV, true>(&slots, &cus)
+                             : prep_slots<V, DK, DV, false>(&slots, &cus);
+    if (e != hipSuccess) return e;
+    const long items = (long)blk.nc * p.H * p.B;
+    const long free_cus = cus - scan_workgroups(p, !VariantTraits<V>::kChannelDecay, concurrent, cus);
+    const long extra = free_cus > 0 ? (free_cus < slots - cus ? free_cus : slots - cus) : 0;
+    // A channel-decay prep (one workgroup per unit) never shares a unit with
+    // the scan: beside one it takes just the units the scan leaves free, so
+    // that no workgroup of its static split starts late.
+    long want = slots;
+    if (concurrent)
+        want = VariantTraits<V>::kChannelDecay ? (free_cus > 0 ? free_cus : cus) : cus + extra;
+    *grid = items < want ? items : want;
+    return hipSuccess;
+}
+
 template <int V, typename TI, int DK, int DV>
 hipError_t launch_prep(const Problem &p, const WsPtrs<TI> &w, const Block &blk, bool concurrent,
                        hipStream_t st) {
     if constexpr (sizeof(TI) == 2) {
-        // Persistent workgroups, each looping over chunk-heads with the next
-        // one's inputs in flight.  Alone, the grid fills every resident slot;
-        // beside a concurrent scan, one workgroup per compute unit, so that a
-        // scan workgroup still fits on every unit, plus a second one for each
-        // unit the scan leaves free: in whichever order the two grids are
-        // placed, every scan workgroup still finds a unit with room.
-        long slots = 0, cus = 0;
-        const bool rt = p.v_route != nullptr;
-        hipError_t e = rt ? prep_slots<V, DK, DV, true>(&slots, &cus)
-                          : prep_slots<V, DK, DV, false>(&slots, &cus);
+        long grid = 0;
+        hipError_t e = prep_grid<V, DK, DV>(p, blk, concurrent, &grid);
         if (e != hipSuccess) return e;
-        const long items = (long)blk.nc * p.H * p.B;
-        const long free_cus =
-            cus - scan_workgroups(p, !VariantTraits<V>::kChannelDecay, concurrent, cus);
-        const long extra = free_cus > 0 ? (free_cus < slots - cus ? free_cus : slots - cus) : 0;
-        // A channel-decay prep (one workgroup per unit) never shares a unit
-        // with the scan: beside one it takes just the units the scan leaves
-        // free, so that no workgroup of its static split starts late.
-        long want = slots;
-        if (concurrent)
-            want = VariantTraits<V>::kChannelDecay ? (free_cus > 0 ? free_cus : cus) : cus + extra;
-        const long grid = items < want ? items : want;
+        const bool rt = p.v_route != nullptr;
         if (rt)
             hipLaunchKernelGGL((chunk_prep_bf16_kernel<V, DK, DV, true>), dim3((unsigned)grid),
                                dim3(kPrep2Threads), 0, st, p, w, blk);
@@ -1805,6 +1869,33 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
     return hipGetLastError();
 }
 
+// The scan of block sb and the prep of block pb in one launch
+// (chunk_pipe_kernel), with the grids each would take beside the other.
+template <int V, int DK, int DV>
+hipError_t launch_pipe(const Problem &p, const WsPtrs<bf16> &sw, const Block &sb,
+                       const WsPtrs<bf16> &pw, const Block &pb, hipStream_t st) {
+    long cus = 0, pgrid = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    if ((e = prep_grid<V, DK, DV>(p, pb, true, &pgrid)) != hipSuccess) return e;
+    const bool wide = scan_wide(p, !VariantTraits<V>::kChannelDecay, true, cus);
+    const long nwg = p.B * p.H * (DV / (wide ? 32 : 16));
+    const long sgrid = kXcds * ((nwg + kXcds - 1) / kXcds);
+    const dim3 grid((unsigned)(sgrid + pgrid));
+    auto go = [&](auto nj) {
+        constexpr int NJ = decltype(nj)::value;
+        if (p.v_route)
+            hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, true, NJ>), grid, dim3(kPrep2Threads), 0,
+                               st, p, sw, sb, (unsigned)sgrid, pw, pb);
+        else
+            hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, false, NJ>), grid, dim3(kPrep2Threads), 0,
+                               st, p, sw, sb, (unsigned)sgrid, pw, pb);
+    };
+    if (wide) go(std::integral_constant<int, DV % 32 == 0 ? 2 : 1>{});
+    else go(std::integral_constant<int, 1>{});
+    return hipGetLastError();
+}
+
 template <int V, typename TI, int DK, int DV>
 hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     const Plan q = make_plan(p);
@@ -1817,43 +1908,39 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         if (e != hipSuccess) return e;
         return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, false, stream);
     }
-    // Pipelined: the prep of block i + 1 runs on the helper stream while the
-    // scan of block i runs on the caller's stream; two workspace slots
-    // alternate, and events order each slot's reuse.
-    AuxStream *aux = nullptr;
-    hipError_t e = aux_stream(&aux);
-    if (e != hipSuccess) return e;
+    // Pipelined, on the caller's stream: the prep of block 0 alone (every
+    // resident slot, a fixed stride; it clears the ticket counter that the
+    // later scalar-decay preps draw from, so that the units without a scan
+    // take more items), then one launch per block running the scan of block i
+    // beside the prep of block i + 1 (chunk_pipe_kernel), then the last scan.
+    // Two workspace slots alternate.  A channel-decay prep fills a unit's
+    // registers and never shares one; it runs on the units the scan leaves
+    // free, with a static split, which measured faster.
+    hipError_t e = hipSuccess;
     float *carrier = reinterpret_cast<float *>(base + 2 * q.slot);
-    // The first prep runs alone: every resident slot, a fixed stride, and it
-    // clears the ticket counter that the later ones (beside a scan) draw from.
     unsigned *ticket = reinterpret_cast<unsigned *>(base + 2 * q.slot + q.carrier);
     unsigned ticket_base = 0;
-    if ((e = hipEventRecord(aux->start, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(aux->s, aux->start, 0)) != hipSuccess) return e;
-    for (long i = 0; i < q.nblk; ++i) {
-        const int slot = (int)(i & 1);
-        const WsPtrs<TI> w = ws_ptrs<TI>(p, q.nb, base + slot * q.slot);
+    auto block = [&](long i) {
         const long c0 = i * q.nb;
-        const int nc = (int)min(q.nb, q.NC - c0);
-        // Scalar-decay preps share compute units with the scan and take items
-        // from the ticket counter, so the units without a scan take more of
-        // them.  A channel-decay prep fills a unit's registers and never
-        // shares one; it runs on the units the scan leaves free, with a static
-        // split, which measured faster.
         const bool tickets = i > 0 && !VariantTraits<V>::kChannelDecay;
-        const Block blk{c0, nc, (int)q.nb,
-                        i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
-                        nullptr, nullptr, tickets ? ticket : nullptr, ticket_base,
-                        i == 0 ? ticket : nullptr, true};
-        if (tickets) ticket_base += (unsigned)(nc * p.H * p.B);
-        if (i >= 2 && (e = hipStreamWaitEvent(aux->s, aux->scan[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_prep<V, TI, DK, DV>(p, w, blk, i > 0, aux->s)) != hipSuccess) return e;
-        if ((e = hipEventRecord(aux->prep[slot], aux->s)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(stream, aux->prep[slot], 0)) != hipSuccess) return e;
-        if ((e = launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, true, stream)) !=
-            hipSuccess)
-            return e;
-        if ((e = hipEventRecord(aux->scan[slot], stream)) != hipSuccess) return e;
+        return Block{c0, (int)min(q.nb, q.NC - c0), (int)q.nb,
+                     i == 0 ? p.state_in : carrier, i == q.nblk - 1 ? p.state_out : carrier,
+                     nullptr, nullptr, tickets ? ticket : nullptr, ticket_base,
+                     i == 0 ? ticket : nullptr, true};
+    };
+    auto slot = [&](long i) { return ws_ptrs<TI>(p, q.nb, base + (i & 1) * q.slot); };
+    if ((e = launch_prep<V, TI, DK, DV>(p, slot(0), block(0), false, stream)) != hipSuccess) return e;
+    for (long i = 0; i < q.nblk; ++i) {
+        const Block sb = block(i);
+        if (i + 1 == q.nblk)
+            return launch_scan<TI, DK, DV>(p, slot(i), sb, !VariantTraits<V>::kChannelDecay, true, stream);
+        const Block pb = block(i + 1);
+        if (pb.ticket) ticket_base += (unsigned)(pb.nc * p.H * p.B);
+        if constexpr (sizeof(TI) == 2)
+            e = launch_pipe<V, DK, DV>(p, slot(i), sb, slot(i + 1), pb, stream);
+        else
+            e = hipErrorInvalidValue;   // only bf16 inputs are pipelined
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

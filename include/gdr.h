@@ -47,14 +47,12 @@
  *   - Every tensor pointer is device memory owned by the caller.  The library
  *     never allocates device memory, frees or synchronises; work is enqueued on
  *     the HIP stream passed as `hip_stream` (a hipStream_t; NULL = the null
- *     stream).  A long bf16 prefill (512 chunks or more; 256 for KDA and
- *     GDN-2, and for the others when B * H * dv / 16 is above a quarter and
- *     at most half of the device's compute units) is pipelined over a
- *     second, internal stream, ordered against `hip_stream` with events: the
- *     library creates that stream and five events once per host thread and
- *     device and keeps them for the life of the process.  The call still
- *     behaves as one operation on `hip_stream` (later work on it waits for
- *     all of it), and it can be captured into a HIP graph.
+ *     stream), and only there: a long bf16 prefill (512 chunks or more; 256
+ *     for KDA and GDN-2, and for the others when B * H * dv / 16 is above a
+ *     quarter and at most half of the device's compute units) is pipelined
+ *     in blocks of 64 chunks by launches that each run one block's scan
+ *     beside the next block's prep, in order on `hip_stream`.  Every call can
+ *     be captured into a HIP graph.
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
  *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
@@ -83,9 +81,8 @@
  *     keep no data of their own between them; the library keeps, per device,
  *     its compute-unit count and the resident-workgroup counts of its kernels
  *     (queried once; the workspace size of a call depends on the current
- *     device's unit count), and per host thread and device the internal stream
- *     and events above.  None of these is ever released.  A thread-local
- *     message explains the last failure.
+ *     device's unit count), never released.  A thread-local message explains
+ *     the last failure.
  */
 #ifndef GDR_H
 #define GDR_H

@@ -2,10 +2,9 @@
 entry points may be called concurrently).
 
 Each thread runs pipelined forwards on a stream of its own.  A pipelined
-forward puts its prep on a helper stream that the library keeps per host
-thread and device, ordered against the caller's stream with events, and it
-reads per-device caches (compute units, resident workgroups) that the first
-calls fill.  ctypes releases the interpreter lock during a foreign call, so
+forward runs each block's scan beside the next block's prep in one launch,
+with grids sized from per-device caches (compute units, resident workgroups)
+that the first calls fill.  ctypes releases the interpreter lock during a foreign call, so
 the threads' calls and their device work overlap.  Every result must equal,
 bit for bit, the same call made alone: the forward's arithmetic per chunk and
 per column slice does not depend on which workgroup takes an item."""
