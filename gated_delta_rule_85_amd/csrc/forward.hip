@@ -966,12 +966,19 @@ __device__ __forceinline__ void prep_body(const Problem &p, const WsPtrs<bf16> &
         } else {
             const int r = 16 * qR + l16;
             const float egr = kRowDecay ? sEg[r] : 1.f;
+            // Fragments NH qh .. NH qh + NH - 1 of the row block, selected by
+            // the wave-uniform qh and stored unconditionally: written as
+            // stores under a condition on the fragment index, the compiler
+            // merged them into one store whose data and address it selected
+            // by different tests on the wave index (wrong for d_k = 64).
+            constexpr int NH = DK / 64;
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                if (ks / (DK / 64) != qh) continue;
+            for (int j = 0; j < NH; ++j) {
+                const int ks = qh * NH + j;
+                const bf16x8 src = qh ? qf[NH + j] : qf[j];
                 bf16x8 o;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)qf[ks][e] * egr);
+                for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)src[e] * egr);
                 *reinterpret_cast<bf16x8 *>(ws.Qt + ch * C * DK + frag_off<bf16>(r, 32 * ks + 8 * lg, DK)) = o;
             }
         }
