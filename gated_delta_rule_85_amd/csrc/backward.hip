@@ -21,7 +21,7 @@
 // variant).  The derivation and the kernels are our own.
 //
 // Launches after the forward's own factors and per-chunk states and Deltas
-// (launch_states_prep, launch_states_scan):
+// (launch_states_pass):
 //   bw_prep_kernel        per chunk-head, parallel: P^T dO, Qt^T dO and the
 //                         transposed factors the reverse chain reads.
 //   reverse_chain_kernel  one workgroup per (16 value columns, h, b): the
@@ -1228,6 +1228,9 @@ __global__ __launch_bounds__(kGradThreads, 4) void chunk_grad_kernel(
 // factors, then the per-chunk gradient workers' scratch.
 template <typename TI, int DK, int DV> struct BwLayout {
     TI *S_chunks, *D_chunks, *dS_chunks, *dD_chunks;
+    // dS_chunks is written only by the reverse chain: until then (in the
+    // states pass) it serves as that pass's scratch.
+    size_t dS_bytes;
     RevFactors rf;
     float *scratch;
     BwLayout(const Problem &p, void *ws) {
@@ -1240,7 +1243,8 @@ template <typename TI, int DK, int DV> struct BwLayout {
         D_chunks = reinterpret_cast<TI *>(base + off);
         off += al((size_t)nch * C * DV * sizeof(TI));
         dS_chunks = reinterpret_cast<TI *>(base + off);
-        off += al((size_t)nch * DK * DV * sizeof(TI));
+        dS_bytes = (size_t)nch * DK * DV * sizeof(TI);
+        off += al(dS_bytes);
         dD_chunks = reinterpret_cast<TI *>(base + off);
         off += al((size_t)nch * C * DV * sizeof(TI));
         rf.Kb = base + off;
@@ -1261,11 +1265,8 @@ template <typename TI, int DK, int DV> struct BwLayout {
 template <typename TI, int DK, int DV>
 hipError_t forward_save_shape(const Problem &p, void *ws, hipStream_t st) {
     const BwLayout<TI, DK, DV> L(p, ws);
-    const long NC = (p.T + C - 1) / C;
-    hipError_t e = launch_states_prep(p, ws, 0, (int)NC, false, st);
-    if (e != hipSuccess) return e;
-    return launch_states_scan(p, ws, 0, (int)NC, p.state_in, p.state_out, L.S_chunks, L.D_chunks,
-                              true, st);
+    return launch_states_pass(p, ws, p.state_in, p.state_out, L.S_chunks, L.D_chunks, true,
+                              L.dS_chunks, L.dS_bytes, st);
 }
 
 template <int V, typename TI, int DK, int DV>
@@ -1277,20 +1278,17 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, bool saved
     const RevFactors rf = L.rf;
     float *const scratch = L.scratch;
 
-    // One pass per kernel over all chunks, in order on `st`.  (Overlapping the
-    // sequential passes with the parallel ones on a second stream measured
-    // slower: the two kinds of kernel slow each other down more than they
-    // overlap.)  The kernels take a block of chunks [c0, c0 + ncb); here the
-    // block is the whole sequence.  With `saved`, the states pass already ran
-    // as the forward that kept its records in this workspace.
+    // The states pass (in blocks for long bf16 sequences, as the forward),
+    // then one pass per kernel over all chunks, in order on `st`.
+    // (Overlapping the sequential passes with the parallel ones on a second
+    // stream measured slower: the two kinds of kernel slow each other down
+    // more than they overlap.)  With `saved`, the states pass already ran as
+    // the forward that kept its records in this workspace.
     const ForwardStates f = forward_states_ptrs(p, ws);
     hipError_t e = hipSuccess;
-    if (!saved) {
-        if ((e = launch_states_prep(p, ws, 0, (int)NC, false, st)) != hipSuccess) return e;
-        if ((e = launch_states_scan(p, ws, 0, (int)NC, p.state_in, nullptr, S_chunks, D_chunks,
-                                    false, st)) != hipSuccess)
-            return e;
-    }
+    if (!saved && (e = launch_states_pass(p, ws, p.state_in, nullptr, S_chunks, D_chunks, false,
+                                          dS_chunks, L.dS_bytes, st)) != hipSuccess)
+        return e;
     const long items = NC * p.B * p.H;
     hipLaunchKernelGGL((bw_prep_kernel<TI, DK, DV>), dim3((unsigned)(items < 16384 ? items : 16384)),
                        dim3(kBpThreads), 0, st, p, f, g, rf, 0L, (int)NC);

@@ -1696,19 +1696,24 @@ __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void chunk_scan2_kernel(
 // units first, one per unit; the LDS of the two roles overlays, so the launch
 // asks for the prep's footprint and a prep workgroup still fits beside a
 // scan workgroup.
+// MODE: kPipeForward, the forward (o with streaming stores); kPipeStates, the
+// gradient's states pass (the state and Delta entering each chunk, no o);
+// kPipeSave, both (the forward that keeps its gradient's records).
 static_assert(kScan2Threads == kPrep2Threads, "one workgroup size for both roles");
-template <int V, int DK, int DV, int NJ> union PipeSmem {
+constexpr int kPipeForward = 0, kPipeStates = 1, kPipeSave = 2;
+template <int V, int DK, int DV, int NJ, bool STATES> union PipeSmem {
     PrepSmem<V, DK, DV> prep;
-    ScanSmem<bf16, DK, NJ, false> scan;
+    ScanSmem<bf16, DK, NJ, STATES> scan;
 };
-template <int V, int DK, int DV, bool RT, int NJ>
+template <int V, int DK, int DV, bool RT, int NJ, int MODE>
 __global__ __launch_bounds__(kPrep2Threads, (V == kKDA || V == kGDN2) ? 2 : 4)
 void chunk_pipe_kernel(Problem p, WsPtrs<bf16> scan_ws, Block scan_blk, unsigned scan_grid,
                        WsPtrs<bf16> prep_ws, Block prep_blk) {
     constexpr bool SG = !VariantTraits<V>::kChannelDecay;
-    __shared__ PipeSmem<V, DK, DV, NJ> sm;
+    constexpr bool STATES = MODE == kPipeStates, SAVE = MODE == kPipeSave, NTO = MODE == kPipeForward;
+    __shared__ PipeSmem<V, DK, DV, NJ, STATES> sm;
     if (blockIdx.x < scan_grid)
-        scan_body<bf16, DK, 2, NJ, false, true, SG, false>(p, scan_ws, scan_blk, blockIdx.x, sm.scan);
+        scan_body<bf16, DK, 2, NJ, STATES, NTO, SG, SAVE>(p, scan_ws, scan_blk, blockIdx.x, sm.scan);
     else
         prep_body<V, DK, DV, RT>(p, prep_ws, prep_blk, blockIdx.x - scan_grid, gridDim.x - scan_grid,
                                  sm.prep);
@@ -1877,8 +1882,9 @@ hipError_t launch_scan(const Problem &p, const WsPtrs<TI> &w, const Block &blk, 
 }
 
 // The scan of block sb and the prep of block pb in one launch
-// (chunk_pipe_kernel), with the grids each would take beside the other.
-template <int V, int DK, int DV>
+// (chunk_pipe_kernel), with the grids each would take beside the other.  The
+// states and saving scans take no routed value.
+template <int V, int DK, int DV, int MODE>
 hipError_t launch_pipe(const Problem &p, const WsPtrs<bf16> &sw, const Block &sb,
                        const WsPtrs<bf16> &pw, const Block &pb, hipStream_t st) {
     long cus = 0, pgrid = 0;
@@ -1891,12 +1897,15 @@ hipError_t launch_pipe(const Problem &p, const WsPtrs<bf16> &sw, const Block &sb
     const dim3 grid((unsigned)(sgrid + pgrid));
     auto go = [&](auto nj) {
         constexpr int NJ = decltype(nj)::value;
-        if (p.v_route)
-            hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, true, NJ>), grid, dim3(kPrep2Threads), 0,
-                               st, p, sw, sb, (unsigned)sgrid, pw, pb);
-        else
-            hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, false, NJ>), grid, dim3(kPrep2Threads), 0,
-                               st, p, sw, sb, (unsigned)sgrid, pw, pb);
+        if constexpr (MODE == kPipeForward) {
+            if (p.v_route) {
+                hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, true, NJ, MODE>), grid,
+                                   dim3(kPrep2Threads), 0, st, p, sw, sb, (unsigned)sgrid, pw, pb);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((chunk_pipe_kernel<V, DK, DV, false, NJ, MODE>), grid, dim3(kPrep2Threads),
+                           0, st, p, sw, sb, (unsigned)sgrid, pw, pb);
     };
     if (wide) go(std::integral_constant<int, DV % 32 == 0 ? 2 : 1>{});
     else go(std::integral_constant<int, 1>{});
@@ -1944,7 +1953,7 @@ hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
         const Block pb = block(i + 1);
         if (pb.ticket) ticket_base += (unsigned)(pb.nc * p.H * p.B);
         if constexpr (sizeof(TI) == 2)
-            e = launch_pipe<V, DK, DV>(p, slot(i), sb, slot(i + 1), pb, stream);
+            e = launch_pipe<V, DK, DV, kPipeForward>(p, slot(i), sb, slot(i + 1), pb, stream);
         else
             e = hipErrorInvalidValue;   // only bf16 inputs are pipelined
         if (e != hipSuccess) return e;
@@ -2018,32 +2027,68 @@ ForwardStates forward_states_ptrs(const Problem &p, void *workspace) {
                          reinterpret_cast<const float *>(b + L.gam), NC};
 }
 
-hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc, bool concurrent,
-                              hipStream_t stream) {
-    return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) {
+hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_in, float *s_out,
+                              void *s_chunks, void *d_chunks, bool with_o, void *scratch,
+                              size_t scratch_bytes, hipStream_t stream) {
+    return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) -> hipError_t {
         using TI = typename decltype(ti)::type;
         constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
+        constexpr bool kScalar = !VariantTraits<V>::kChannelDecay;
         const long NC = (p.T + C - 1) / C;
-        const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
-        const Block blk{c0, nc, (int)NC, nullptr, nullptr, nullptr, nullptr, nullptr, 0u, nullptr,
-                        false};
-        return launch_prep<V, TI, DK, DV>(p, w, blk, concurrent, stream);
-    });
-}
-
-hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
-                              const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
-                              bool with_o, hipStream_t stream) {
-    return dispatch_shape(p, [&](auto v, auto ti, auto dk, auto dv) {
-        using TI = typename decltype(ti)::type;
-        constexpr int V = decltype(v)::value, DK = decltype(dk)::value, DV = decltype(dv)::value;
-        const long NC = (p.T + C - 1) / C;
-        const WsPtrs<TI> w = shifted(ws_ptrs<TI>(p, NC, workspace), p, c0);
-        const Block blk{c0, nc, (int)NC, s_in, s_out,
-                        static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
-                        static_cast<TI *>(d_chunks) + c0 * C * (long)DV, nullptr, 0u, nullptr,
-                        false, with_o};
-        return launch_scan<TI, DK, DV>(p, w, blk, !VariantTraits<V>::kChannelDecay, false, stream);
+        const WsPtrs<TI> full = ws_ptrs<TI>(p, NC, workspace);
+        // Every chunk keeps its own factors and records: a block of chunks
+        // [c0, c0 + nc) gets the factor pointers (shifted) and the record
+        // pointers moved by c0, so that the kernels' block-local chunk index
+        // lands on the global one.
+        auto block = [&](long c0, int nc, const float *si, float *so, unsigned *tk, unsigned tb,
+                         unsigned *tclear) {
+            return Block{c0, nc, (int)NC, si, so,
+                         static_cast<TI *>(s_chunks) + c0 * DK * (long)DV,
+                         static_cast<TI *>(d_chunks) + c0 * C * (long)DV, tk, tb, tclear, false,
+                         with_o};
+        };
+        // The forward's choice of when to pipeline, and its blocks.
+        const Plan q = make_plan(p);
+        const size_t carrier_bytes = align256((size_t)p.B * p.H * DK * DV * 4);
+        if constexpr (sizeof(TI) == 2) {
+            if (q.nblk > 1 && scratch && scratch_bytes >= carrier_bytes + 256) {
+                // As the pipelined forward: the prep of block 0 alone (it
+                // clears the ticket counter), then one launch per block with
+                // the scan of block i beside the prep of block i + 1, then the
+                // last scan, all on `stream`; the state is carried between
+                // blocks in fp32 in the scratch.
+                float *carrier = static_cast<float *>(scratch);
+                unsigned *ticket =
+                    reinterpret_cast<unsigned *>(static_cast<char *>(scratch) + carrier_bytes);
+                unsigned ticket_base = 0;
+                auto blk_i = [&](long i) {
+                    const long c0 = i * q.nb;
+                    const bool tickets = i > 0 && kScalar;
+                    return block(c0, (int)min(q.nb, q.NC - c0), i == 0 ? s_in : carrier,
+                                 i == q.nblk - 1 ? s_out : carrier, tickets ? ticket : nullptr,
+                                 ticket_base, i == 0 ? ticket : nullptr);
+                };
+                hipError_t e = launch_prep<V, TI, DK, DV>(p, full, blk_i(0), false, stream);
+                if (e != hipSuccess) return e;
+                for (long i = 0; i < q.nblk; ++i) {
+                    const Block sb = blk_i(i);
+                    const WsPtrs<TI> w = shifted(full, p, sb.c0);
+                    if (i + 1 == q.nblk) return launch_scan<TI, DK, DV>(p, w, sb, kScalar, true, stream);
+                    const Block pb = blk_i(i + 1);
+                    if (pb.ticket) ticket_base += (unsigned)(pb.nc * p.H * p.B);
+                    const WsPtrs<TI> wn = shifted(full, p, pb.c0);
+                    e = with_o ? launch_pipe<V, DK, DV, kPipeSave>(p, w, sb, wn, pb, stream)
+                               : launch_pipe<V, DK, DV, kPipeStates>(p, w, sb, wn, pb, stream);
+                    if (e != hipSuccess) return e;
+                }
+                return hipSuccess;
+            }
+        }
+        hipError_t e = launch_prep<V, TI, DK, DV>(
+            p, full, block(0, (int)NC, nullptr, nullptr, nullptr, 0u, nullptr), false, stream);
+        if (e != hipSuccess) return e;
+        return launch_scan<TI, DK, DV>(p, full, block(0, (int)NC, s_in, s_out, nullptr, 0u, nullptr),
+                                       kScalar, false, stream);
     });
 }
 

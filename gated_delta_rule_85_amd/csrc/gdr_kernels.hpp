@@ -58,18 +58,19 @@ struct ForwardStates {
 };
 size_t forward_states_bytes(const Problem &p);
 ForwardStates forward_states_ptrs(const Problem &p, void *workspace);
-// The gradient's states pass, one block of chunks [c0, c0 + nc) at a time:
-// the factors of the block (prep), then the scan over it from s_in (NULL =
-// zeros) to s_out (NULL = dropped), recording the state entering each chunk
-// ([B*H][nbmax][dk][dv] in s_chunks) and each chunk's Delta = U~ - W S
-// ([B*H][nbmax][C][dv] in d_chunks), both in the input dtype.  with_o: the
-// scan also writes p.o (the forward that keeps what its gradient needs);
-// otherwise no outputs.
-hipError_t launch_states_prep(const Problem &p, void *workspace, long c0, int nc, bool concurrent,
-                              hipStream_t stream);
-hipError_t launch_states_scan(const Problem &p, void *workspace, long c0, int nc,
-                              const float *s_in, float *s_out, void *s_chunks, void *d_chunks,
-                              bool with_o, hipStream_t stream);
+// The gradient's states pass: the factors of every chunk (prep), then the
+// scan from s_in (NULL = zeros) to s_out (NULL = dropped), recording the state
+// entering each chunk ([B*H][NC][dk][dv] in s_chunks) and each chunk's
+// Delta = U~ - W S ([B*H][NC][C][dv] in d_chunks), both in the input dtype.
+// with_o: the scan also writes p.o (the forward that keeps what its gradient
+// needs); otherwise no outputs.  Long bf16 sequences run in blocks of 64
+// chunks as the forward does, each launch running the scan of one block beside
+// the prep of the next; that takes B*H*dk*dv*4 bytes (rounded up to 256) + 256
+// bytes of scratch, free for the duration of the call, for the state carried
+// between blocks and the prep's ticket counter (one pass without it).
+hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_in, float *s_out,
+                              void *s_chunks, void *d_chunks, bool with_o, void *scratch,
+                              size_t scratch_bytes, hipStream_t stream);
 
 // Gradient of the chunked forward: upstream gradients in, input gradients out.
 struct Grads {
