@@ -75,7 +75,7 @@ def test_forward_transforms_head_sizes(variant, dk, dv):
 
 @pytest.mark.parametrize("variant", ["kla", "kda", "gdn2"])
 def test_forward_transforms_pipelined(variant):
-    """514 chunks: the blocked two-stream path, sampled heads."""
+    """514 chunks: the blocked path (one launch per block), sampled heads."""
     _check_forward(variant, "bf16", L2 | RAW, B=1, T=64 * 64 * 8 + 100, H=4, seed=21,
                    heads=[(0, 0), (0, 3)])
 

@@ -270,7 +270,7 @@ def test_forward_pipelined_split_resume():
 
 
 def test_forward_graph_capture_replays():
-    """The two-stream pipelined forward (513 chunks) captured into a HIP graph
+    """The pipelined forward (513 chunks, one launch per block) captured into a HIP graph
     and replayed several times, with other work in between, matches the eager
     result."""
     T = 64 * 64 * 8 + 64

@@ -71,7 +71,7 @@ def test_prefill_residual_and_routed_value(variant, dtype, routed):
 
 @pytest.mark.parametrize("variant", ["kla", "kda"])
 def test_prefill_routing_pipelined(variant):
-    """514 chunks in bf16 (the two-stream blocked path), sampled heads."""
+    """514 chunks in bf16 (the blocked path, one launch per block), sampled heads."""
     B, T, H, d = 1, 64 * 64 * 8 + 77, 4, 128
     inp = make_inputs(variant, B, T, H, d, d, "bf16", seed=41, state_scale=0.1)
     vr = make_routed_value(B, T, H, d, "bf16", seed=42, scale=0.5)
