@@ -193,8 +193,8 @@ gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_byt
  * workspace taken from a static device array of GDR_NOALLOC_WORKSPACE_MAX bytes
  * that the library holds on every device it runs on until the process ends.
  * The call allocates and frees nothing; its first call with a device current
- * looks up that device's array, and like gdr_forward_chunked a pipelined call
- * creates the internal stream and events on a thread's first such call.
+ * looks up that device's array.  Like gdr_forward_chunked it enqueues its
+ * kernels on `hip_stream` only and creates no stream or event.
  * Returns GDR_ERR_WORKSPACE, enqueuing nothing, when
  * gdr_forward_workspace_size(a) exceeds GDR_NOALLOC_WORKSPACE_MAX.  All calls
  * on one device share its array: calls that may overlap on a device (other
