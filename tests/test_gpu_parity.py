@@ -173,12 +173,14 @@ def test_heads_and_batches_are_independent():
 
 # ------------------------------------------------- pipelined (multi-block) forward
 
-@pytest.mark.parametrize("T", [64 * 64 * 8 + 100, 64 * 64 * 2 + 100], ids=["pipelined", "one_pass"])
+@pytest.mark.parametrize("T", [64 * 64 * 8 + 100, 64 * 64 * 8 + 1, 64 * 64 * 2 + 100],
+                         ids=["pipelined", "pipelined_one_token_block", "one_pass"])
 @pytest.mark.parametrize("variant", ["gdn2", "kla", "deltanet"])
 def test_forward_pipelined_blocks(variant, T):
-    """Long bf16 sequences: from 512 chunks on as blocks of 64 chunks on two
-    streams (nine blocks here), below that as one pass (130 chunks); a ragged
-    last chunk and a non-zero initial state."""
+    """Long bf16 sequences: from 512 chunks on as blocks of 64 chunks, one
+    launch per block on the caller's stream (nine blocks here; with T = 32769
+    the last block is a single chunk holding one token), below that as one
+    pass (130 chunks); a ragged last chunk and a non-zero initial state."""
     announce(f"pipelined forward {variant} T={T}")
     inp = make_inputs(variant, 1, T, 2, 128, 128, "bf16", seed=77, state_scale=0.5)
     o, s = gpu_forward(variant, to_dev(inp))
