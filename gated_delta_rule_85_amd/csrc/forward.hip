@@ -170,6 +170,49 @@ Plan make_plan(const Problem &p) {
     return q;
 }
 
+// Sequence-parallel plan.  When the chain's column slices would occupy at
+// most an eighth of the compute units (few heads: B * H * d_v / 16 small),
+// the sequence is cut into segments of L chunks whose chains run side by
+// side: the prep over every chunk; each segment but the last from S = 0 (its
+// local end state N_s) and from the identity with U~ = 0 (its transition M_s,
+// the product of the chunks' maps S -> (Diag(e^{g_C}) - Kbar^T W) S); a short
+// serial combine S_{s+1} = M_s S_s + N_s from the initial state; then every
+// segment's scan from its start state, writing o.  The state update of a chunk
+// is affine in S, so this is the same recurrence.
+struct SegPlan {
+    long nseg = 0;                     // segments (0: the plan is not used)
+    long L = 0;                        // chunks per segment, the last one shorter
+    size_t M = 0, N = 0, S = 0;        // byte offsets: M_s, N_s, start states
+    size_t total = 0;
+};
+constexpr long kSegMinChunks = 32;     // chunks per segment at least
+constexpr long kSegMax = 16;           // segments at most
+
+SegPlan seg_plan(const Problem &p) {
+    SegPlan s;
+    long cus = 0;
+    if (!p.bf16 || device_cus(&cus) != hipSuccess) return s;
+    const long NC = (p.T + C - 1) / C, BH = p.B * p.H;
+    const long slices = BH * (p.dv / 16);
+    if (8 * slices > cus) return s;
+    long nseg = cus / slices;
+    if (nseg > NC / kSegMinChunks) nseg = NC / kSegMinChunks;
+    if (nseg > kSegMax) nseg = kSegMax;
+    if (nseg < 2) return s;
+    const long L = (NC + nseg - 1) / nseg;
+    nseg = (NC + L - 1) / L;
+    if (nseg < 2) return s;
+    size_t o = ws_layout(p, NC).total;
+    s.M = o; o = align256(o + (size_t)(nseg - 1) * BH * p.dk * p.dk * 4);
+    s.N = o; o = align256(o + (size_t)(nseg - 1) * BH * p.dk * p.dv * 4);
+    s.S = o; o = align256(o + (size_t)(nseg - 1) * BH * p.dk * p.dv * 4);
+    if (o > kSinglePassBytes || (p.ws_cap && o > p.ws_cap)) return s;
+    s.nseg = nseg;
+    s.L = L;
+    s.total = o;
+    return s;
+}
+
 // ---- small vector stores ------------------------------------------------------
 
 __device__ __forceinline__ void store8(bf16 *dst, const float *x) {
@@ -1719,6 +1762,174 @@ void chunk_pipe_kernel(Problem p, WsPtrs<bf16> scan_ws, Block scan_blk, unsigned
                                  sm.prep);
 }
 
+// ---- sequence-parallel state pass -------------------------------------------
+// The transitions: segment blockIdx.y of L chunks, for one head and one
+// 16-column tile per workgroup of four waves, either the chain from S = 0 over
+// d_v's columns (N_s) or the chain over the identity's d_k columns with U~
+// taken as zero (M_s).  The chain step is the scan's: Delta = U~ - W S into
+// LDS, then S <- Diag(e^{g_C}) S + Kbar^T Delta, S in fp32 accumulators and a
+// bf16 copy of S^T in LDS as the operand; the next chunk's factors are loaded
+// while the current one is stepped.
+template <int DK, int DV, bool SG>
+__global__ __launch_bounds__(4 * kWave) void seg_transition_kernel(Problem p, WsPtrs<bf16> ws, long NC,
+                                                                  long L, float *Mo, float *No) {
+    using TI = bf16;
+    using M = Mma<TI>;
+    using CO = ChainOps<TI, DK, 1, SG>;
+    constexpr int KS_D = CO::KS_D, KS_C = CO::KS_C, NI = CO::NI;
+    constexpr int PT = 8, NV = DV / 16, NK = DK / 16;
+    __shared__ __attribute__((aligned(16))) TI sSt[2][16][DK + PT];   // S^T
+    __shared__ __attribute__((aligned(16))) TI sDt[2][16][C + PT];    // Delta^T
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const long BH = p.B * p.H;
+    const long nwg = BH * (NV + NK);
+    const long per_xcd = (nwg + kXcds - 1) / kXcds;
+    const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical >= nwg) return;
+    const long bh = logical / (NV + NK);
+    const int r = (int)(logical % (NV + NK));
+    const bool mrole = r >= NV;                  // wave-uniform
+    const int col0 = 16 * (mrole ? r - NV : r);
+    const long seg = blockIdx.y;
+    const long c0 = seg * L, nc = (NC - c0 < L ? NC - c0 : L);
+    const long ch0 = bh * NC + c0, last = nc - 1;
+    auto chunk = [&](long c) { return ch0 + (c < last ? c : last); };
+    // U~ is read for the identity's columns too (from value tile 0, in
+    // bounds) and multiplied by zero there.
+    const int ucol = mrole ? 0 : col0;
+    const float uk = mrole ? 0.f : 1.f;
+    f32x4 S[NI];
+#pragma unroll
+    for (int a = 0; a < NI; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * (w * NI + a) + 4 * lg + m;
+            S[a][m] = (mrole && i == col0 + l16) ? 1.f : 0.f;
+        }
+    auto write_st = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < NI; ++a) store4(&sSt[buf][l16][16 * (w * NI + a) + 4 * lg], S[a]);
+    };
+    write_st(0);
+    __syncthreads();
+    auto step = [&](const CO &op, long c, auto &&pre_update) __attribute__((always_inline)) {
+        const int cur = (int)(c & 1);
+        typename M::frag Sf[KS_D];
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) Sf[ks] = M::load(&sSt[cur][l16][0], ks * M::kK, lane);
+        f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ks += 2) {
+            d0 = M::mma(op.Wf[ks], Sf[ks], d0);
+            if (ks + 1 < KS_D) d1 = M::mma(op.Wf[ks + 1], Sf[ks + 1], d1);
+        }
+        store4(&sDt[cur][l16][16 * w + 4 * lg], uk * to_f32x4(op.U[0]) - (d0 + d1));
+        pre_update();
+        __syncthreads();
+        typename M::frag Df[KS_C];
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(&sDt[cur][l16][0], ks * M::kK, lane);
+#pragma unroll
+        for (int a = 0; a < NI; ++a) {
+            f32x4 acc = S[a] * op.gam[a];
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Kf[a][ks], Df[ks], acc);
+            S[a] = acc;
+        }
+        write_st(cur ^ 1);
+        __syncthreads();
+    };
+    CO A, Bq;
+    A.load_w(ws, chunk(0), DV, ucol, w, lane);
+    A.load_k(ws, chunk(0), w, lane);
+    for (long c = 0; c < nc; c += 2) {
+        Bq.load_w(ws, chunk(c + 1), DV, ucol, w, lane);
+        __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
+        step(A, c, [&] { Bq.load_k(ws, chunk(c + 1), w, lane); });
+        if (c + 1 >= nc) break;
+        A.load_w(ws, chunk(c + 2), DV, ucol, w, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        step(Bq, c + 1, [&] { A.load_k(ws, chunk(c + 2), w, lane); });
+    }
+    const int pitch = mrole ? DK : DV;
+    float *out = (mrole ? Mo + (seg * BH + bh) * (long)DK * DK : No + (seg * BH + bh) * (long)DK * DV) + col0;
+#pragma unroll
+    for (int a = 0; a < NI; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * (w * NI + a) + 4 * lg + m;
+            out[(long)i * pitch + l16] = S[a][m];
+        }
+}
+
+// The combine: for one head and 16 value columns per workgroup, from the
+// initial state (zeros when state_in is NULL), S_{s+1} = M_s S_s + N_s for
+// s = 0 .. nseg - 2, each start state written for its segment's scan.  fp32
+// throughout; a few microseconds per segment.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void seg_combine_kernel(Problem p, long nseg, const float *Mi,
+                                                          const float *Ni, float *Sst) {
+    constexpr int TPR = 256 / DK, CPT = 16 / TPR;   // threads per row, columns per thread
+    __shared__ float sS[DK][16 + 1];
+    const int tid = threadIdx.x;
+    const long BH = p.B * p.H;
+    const long bh = blockIdx.x / (DV / 16);
+    const int col0 = 16 * (int)(blockIdx.x % (DV / 16));
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+        const int i = idx / 16, c = idx % 16;
+        sS[i][c] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + c] : 0.f;
+    }
+    __syncthreads();
+    const int i = tid / TPR, cb = (tid % TPR) * CPT;
+    for (long s = 0; s + 1 < nseg; ++s) {
+        const float *Mr = Mi + ((s * BH + bh) * DK + i) * (long)DK;
+        const float *Nr = Ni + ((s * BH + bh) * DK + i) * (long)DV + col0 + cb;
+        float acc[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] = Nr[c];
+        for (int k = 0; k < DK; ++k) {
+            const float m = Mr[k];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] += m * sS[k][cb + c];
+        }
+        __syncthreads();   // every thread is done reading S_s
+        float *out = Sst + ((s * BH + bh) * DK + i) * (long)DV + col0 + cb;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            sS[i][cb + c] = acc[c];
+            out[c] = acc[c];
+        }
+        __syncthreads();
+    }
+}
+
+// The outputs: segment blockIdx.y's scan (the forward's scan kernel body,
+// 16-column slices) from its start state; only the last segment writes the
+// final state.  blk describes the whole sequence.
+template <int DK, bool SG>
+__global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void seg_scan_kernel(Problem p, WsPtrs<bf16> ws,
+                                                                            Block blk, long L,
+                                                                            const float *Sst) {
+    __shared__ ScanSmem<bf16, DK, 1, false> sm;
+    const long seg = blockIdx.y, nseg = gridDim.y, NC = blk.nc;
+    Block b = blk;
+    b.c0 = seg * L;
+    b.nc = (int)(NC - b.c0 < L ? NC - b.c0 : L);
+    b.s_in = seg == 0 ? blk.s_in : Sst + (seg - 1) * p.B * p.H * DK * p.dv;
+    b.s_out = seg == nseg - 1 ? blk.s_out : nullptr;
+    // the factors of the segment's chunks: every pointer moved by c0 chunks
+    WsPtrs<bf16> w = ws;
+    w.W += b.c0 * C * DK;
+    w.Ut += b.c0 * C * p.dv;
+    w.Qt += b.c0 * C * DK;
+    w.Kbt += b.c0 * C * DK;
+    w.P += b.c0 * C * C;
+    w.gam += b.c0 * DK;
+    scan_body<bf16, DK, 2, 1, false, false, SG, false>(p, w, b, blockIdx.x, sm);
+}
+
 // ---- dispatch -----------------------------------------------------------------
 
 
@@ -1912,8 +2123,40 @@ hipError_t launch_pipe(const Problem &p, const WsPtrs<bf16> &sw, const Block &sb
     return hipGetLastError();
 }
 
+// The sequence-parallel forward (see SegPlan), all on the caller's stream.
+template <int V, int DK, int DV>
+hipError_t launch_segments(const Problem &p, const SegPlan &s, void *ws, hipStream_t st) {
+    constexpr bool SG = !VariantTraits<V>::kChannelDecay;
+    char *base = static_cast<char *>(ws);
+    const long NC = (p.T + C - 1) / C, BH = p.B * p.H;
+    const WsPtrs<bf16> w = ws_ptrs<bf16>(p, NC, base);
+    const Block all{0, (int)NC, (int)NC, p.state_in, p.state_out, nullptr, nullptr, nullptr, 0u, nullptr,
+                    false};
+    hipError_t e = launch_prep<V, bf16, DK, DV>(p, w, all, false, st);
+    if (e != hipSuccess) return e;
+    float *Mo = reinterpret_cast<float *>(base + s.M), *No = reinterpret_cast<float *>(base + s.N);
+    float *Sst = reinterpret_cast<float *>(base + s.S);
+    const long nwg1 = BH * (DV / 16 + DK / 16);
+    hipLaunchKernelGGL((seg_transition_kernel<DK, DV, SG>),
+                       dim3((unsigned)(kXcds * ((nwg1 + kXcds - 1) / kXcds)), (unsigned)(s.nseg - 1)),
+                       dim3(4 * kWave), 0, st, p, w, NC, s.L, Mo, No);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0, st, p,
+                       s.nseg, static_cast<const float *>(Mo), static_cast<const float *>(No), Sst);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const long nwg3 = BH * (DV / 16);
+    hipLaunchKernelGGL((seg_scan_kernel<DK, SG>),
+                       dim3((unsigned)(kXcds * ((nwg3 + kXcds - 1) / kXcds)), (unsigned)s.nseg),
+                       dim3(kScan2Threads), 0, st, p, w, all, s.L, static_cast<const float *>(Sst));
+    return hipGetLastError();
+}
+
 template <int V, typename TI, int DK, int DV>
 hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
+    if constexpr (sizeof(TI) == 2) {
+        const SegPlan s = seg_plan(p);
+        if (s.nseg > 1) return launch_segments<V, DK, DV>(p, s, ws, stream);
+    }
     const Plan q = make_plan(p);
     char *base = static_cast<char *>(ws);
     if (q.nblk == 1) {
@@ -2015,7 +2258,10 @@ hipError_t launch_v(const Problem &p, void *ws, hipStream_t stream) {
 
 }  // namespace
 
-size_t forward_workspace_bytes(const Problem &p) { return make_plan(p).total; }
+size_t forward_workspace_bytes(const Problem &p) {
+    const SegPlan s = seg_plan(p);
+    return s.nseg > 1 ? s.total : make_plan(p).total;
+}
 
 size_t forward_states_bytes(const Problem &p) { return ws_layout(p, (p.T + C - 1) / C).total; }
 

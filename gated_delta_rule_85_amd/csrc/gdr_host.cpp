@@ -246,6 +246,7 @@ gdr_status gdr_forward_chunked_noalloc(const gdr_args *a, void *hip_stream) {
     gdr_status s = check(a, 0);
     if (s != GDR_OK) return s;
     gdr::Problem p = to_problem(a);
+    p.ws_cap = GDR_NOALLOC_WORKSPACE_MAX;
     const size_t need = gdr::forward_workspace_bytes(p);
     if (need > GDR_NOALLOC_WORKSPACE_MAX)
         return fail(GDR_ERR_WORKSPACE,

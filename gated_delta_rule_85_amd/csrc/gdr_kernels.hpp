@@ -39,6 +39,9 @@ struct Problem {
     void *o;
     const void *v_route;   // added to v as it is loaded (NULL = none)
     void *delta_out;       // per-token written residual delta_t (NULL = not written)
+    // The largest forward workspace the caller holds (0 = any size): a plan
+    // that would need more is not taken.
+    size_t ws_cap = 0;
 };
 
 // Decode step (T == 1).  Returns the launch status.

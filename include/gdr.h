@@ -51,7 +51,13 @@
  *     for KDA and GDN-2, and for the others when B * H * dv / 16 is above a
  *     quarter and at most half of the device's compute units) is pipelined
  *     in blocks of 64 chunks by launches that each run one block's scan
- *     beside the next block's prep, in order on `hip_stream`.  Every call can
+ *     beside the next block's prep, in order on `hip_stream`.  A bf16 prefill
+ *     of 64 chunks or more whose B * H * dv / 16 column slices are at most an
+ *     eighth of the compute units runs as 2 to 16 segments whose chains run
+ *     side by side (each segment's transition and local end state, a serial
+ *     combine, then each segment's outputs), the state map of a chunk being
+ *     affine ("Kaczmarz Linear Attention", Implementation: the chunk-wise
+ *     parallel algorithm), when its workspace fits in 1 GiB.  Every call can
  *     be captured into a HIP graph.
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
@@ -180,7 +186,9 @@ size_t gdr_forward_workspace_size(const gdr_args *a);
  * at least gdr_forward_workspace_size(a) bytes.  It holds the per-chunk
  * factors: of every chunk for sequences shorter than 512 chunks of 64 tokens
  * (256 in the cases above; at most 1 GiB; 72.5 KB per chunk and head at
- * dk = dv = 128 in bf16),
+ * dk = dv = 128 in bf16), and for a segmented prefill, with each segment
+ * boundary's transition, local end state and start state (fp32, dk x dk and
+ * twice dk x dv per head);
  * else of two blocks of 64 chunks plus a state carrier and a work counter, so
  * it stops growing with T.  Calls that share a workspace must be ordered on
  * one stream. */
@@ -189,14 +197,19 @@ gdr_status gdr_forward_chunked(const gdr_args *a, void *workspace, size_t ws_byt
 
 /* gdr_forward_chunked for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): the same computation, the same kernels and results, with the
+ * hipMalloc): the same computation, kernels and results, with the
  * workspace taken from a static device array of GDR_NOALLOC_WORKSPACE_MAX bytes
  * that the library holds on every device it runs on until the process ends.
  * The call allocates and frees nothing; its first call with a device current
  * looks up that device's array.  Like gdr_forward_chunked it enqueues its
  * kernels on `hip_stream` only and creates no stream or event.
- * Returns GDR_ERR_WORKSPACE, enqueuing nothing, when
- * gdr_forward_workspace_size(a) exceeds GDR_NOALLOC_WORKSPACE_MAX.  All calls
+ * A segmented prefill (see above) whose workspace would exceed
+ * GDR_NOALLOC_WORKSPACE_MAX runs here pipelined or in one pass instead, so
+ * its results then agree with gdr_forward_chunked's to the forward's
+ * tolerance rather than bit for bit.
+ * Returns GDR_ERR_WORKSPACE, enqueuing nothing, when the plan it takes needs
+ * more than GDR_NOALLOC_WORKSPACE_MAX (for a prefill that gdr_forward_chunked
+ * does not segment: when gdr_forward_workspace_size(a) exceeds it).  All calls
  * on one device share its array: calls that may overlap on a device (other
  * streams, other threads) race and must be ordered by the caller. */
 #define GDR_NOALLOC_WORKSPACE_MAX ((size_t)256 << 20)
@@ -254,8 +267,11 @@ gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *wor
                                 size_t ws_bytes, void *hip_stream);
 
 /* The forward of a training step that keeps what its gradient needs.  It
- * writes o and state_out exactly as gdr_forward_chunked does, computed as one
- * pass over all chunks, and leaves in `workspace` (256-byte aligned, at least
+ * writes o and state_out as gdr_forward_chunked does, computed as one pass
+ * over all chunks (bit for bit the same, except where gdr_forward_chunked
+ * runs in segments, whose chains start from other states and round
+ * differently; both then agree to the forward's tolerance), and leaves in
+ * `workspace` (256-byte aligned, at least
  * gdr_backward_workspace_size(a) bytes, owned by the caller) every chunk's
  * factors of the chunk form and the state and residual entering each chunk:
  * the first pass gdr_backward_chunked would otherwise recompute.  Besides the

@@ -173,16 +173,19 @@ def test_heads_and_batches_are_independent():
 
 # ------------------------------------------------- pipelined (multi-block) forward
 
+@pytest.mark.parametrize("H", [8, 2], ids=["H8", "H2_segmented"])
 @pytest.mark.parametrize("T", [64 * 64 * 8 + 100, 64 * 64 * 8 + 1, 64 * 64 * 2 + 100],
                          ids=["pipelined", "pipelined_one_token_block", "one_pass"])
 @pytest.mark.parametrize("variant", ["gdn2", "kla", "deltanet"])
-def test_forward_pipelined_blocks(variant, T):
-    """Long bf16 sequences: from 512 chunks on as blocks of 64 chunks, one
-    launch per block on the caller's stream (nine blocks here; with T = 32769
-    the last block is a single chunk holding one token), below that as one
-    pass (130 chunks); a ragged last chunk and a non-zero initial state."""
-    announce(f"pipelined forward {variant} T={T}")
-    inp = make_inputs(variant, 1, T, 2, 128, 128, "bf16", seed=77, state_scale=0.5)
+def test_forward_pipelined_blocks(variant, T, H):
+    """Long bf16 sequences at 8 heads: from 512 chunks on as blocks of 64
+    chunks, one launch per block on the caller's stream (nine blocks here;
+    with T = 32769 the last block is a single chunk holding one token), below
+    that as one pass (130 chunks).  At 2 heads the same lengths run as
+    segments whose chains run side by side.  A ragged last chunk and a
+    non-zero initial state."""
+    announce(f"long forward {variant} T={T} H={H}")
+    inp = make_inputs(variant, 1, T, H, 128, 128, "bf16", seed=77, state_scale=0.5)
     o, s = gpu_forward(variant, to_dev(inp))
     o_ref, s_ref = run_oracle(variant, inp)
     e_o = rel_err(o.float().cpu(), o_ref, (0, 2))
@@ -238,7 +241,7 @@ def test_forward_channel_decay_pipelined_wide_scan(variant):
         assert e_o < 2e-2 and e_s < 2e-2
 
 
-@pytest.mark.parametrize("variant,H", [("kda", 4), ("gdn2", 4), ("kla", 16), ("gated_deltanet", 16)])
+@pytest.mark.parametrize("variant,H", [("kda", 8), ("gdn2", 8), ("kla", 16), ("gated_deltanet", 16)])
 def test_forward_pipelined_from_256_chunks(variant, H):
     """Pipelined from 256 chunks on (here 301: five blocks, the last one
     ragged): a channel decay always, a scalar decay when its scan takes half
@@ -255,11 +258,13 @@ def test_forward_pipelined_from_256_chunks(variant, H):
         assert e_o < 2e-2 and e_s < 2e-2
 
 
-def test_forward_pipelined_split_resume():
-    """A pipelined pass (576 chunks) equals the same sequence split in two
-    one-pass calls, the second resuming from the first's final state."""
+@pytest.mark.parametrize("H", [8, 2], ids=["pipelined", "segmented"])
+def test_forward_pipelined_split_resume(H):
+    """A long pass (576 chunks: pipelined at 8 heads, segmented at 2) equals
+    the same sequence split in two calls, the second resuming from the
+    first's final state."""
     T = 64 * 64 * 9
-    inp = make_inputs("gated_deltanet", 1, T, 2, 128, 128, "bf16", seed=79, state_scale=0.2)
+    inp = make_inputs("gated_deltanet", 1, T, H, 128, 128, "bf16", seed=79, state_scale=0.2)
     d = to_dev(inp)
     o_all, s_all = gpu_forward("gated_deltanet", d)
     cut = 64 * 64 * 4 + 64 * 5
@@ -276,7 +281,7 @@ def test_forward_graph_capture_replays():
     and replayed several times, with other work in between, matches the eager
     result."""
     T = 64 * 64 * 8 + 64
-    inp = make_inputs("kla", 1, T, 2, 128, 128, "bf16", seed=81, state_scale=0.3)
+    inp = make_inputs("kla", 1, T, 8, 128, 128, "bf16", seed=81, state_scale=0.3)
     d = to_dev(inp)
     o_ref, s_ref = gpu_forward("kla", d)
     o = torch.empty_like(o_ref)

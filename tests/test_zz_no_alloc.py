@@ -5,13 +5,16 @@ pipelined through the static workspace), then smaller calls in one pass, bf16
 and fp32, scalar and channel decay.  Both entry points run the same kernels on
 the same plan, so their outputs must be bit-identical (a stricter bar than the
 oracle tolerance, which the other parity tests hold the shared kernels to).
-A call whose workspace exceeds the static array is rejected before any work."""
+A call whose workspace exceeds the static array is rejected before any work.
+A few-head prefill that gdr_forward_chunked runs in segments with a workspace
+beyond the static array runs pipelined here instead: the two then agree to
+the forward's tolerance, and the allocation-free result matches the oracle."""
 import pytest
 import torch
 
 from gated_delta_rule_85_amd import binding
 from gated_delta_rule_85_amd.inputs import make_inputs
-from tests.gpu_common import announce, to_dev
+from tests.gpu_common import TOL, announce, rel_err, run_oracle, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -69,3 +72,24 @@ def test_noalloc_rejects_a_workspace_beyond_its_array():
     assert err.value.status == 3 and "static workspace" in str(err.value)
     torch.cuda.synchronize()
     assert not o.any()   # nothing was enqueued
+
+
+def test_noalloc_takes_a_smaller_plan_than_a_large_segmented_one():
+    """Kaczmarz B=1, H=4, T=65536: gdr_forward_chunked runs 1,024 chunks in
+    segments with every chunk's factors (~310 MB); the allocation-free call
+    runs them pipelined through its static array."""
+    T, H = 65536, 4
+    inp = make_inputs("kla", 1, T, H, 128, 128, "bf16", seed=1240, state_scale=0.2)
+    d = to_dev(inp)
+    need = binding.workspace_bytes("kla", d["q"], d["k"], d["v"])
+    announce(f"noalloc fallback: kla B=1 H={H} T={T}, segmented workspace {need / 1e6:.0f} MB")
+    if need <= binding.NOALLOC_WORKSPACE_MAX:
+        pytest.skip("this device segments the prefill within the static array")
+    o, s, o_ref, s_ref = _both("kla", d)
+    tol = TOL[torch.bfloat16]
+    assert rel_err(o.float().cpu(), o_ref.float().cpu(), (0, 2)) < tol
+    assert rel_err(s.cpu(), s_ref.cpu(), (0, 1)) < tol
+    heads = [(0, 1)]
+    o_or, s_or = run_oracle("kla", inp, heads=heads)
+    assert rel_err(o[:, :, 1:2].float().cpu(), o_or[:, :, 1:2], (0, 2)) < tol
+    assert rel_err(s[:, 1:2].cpu(), s_or[:, 1:2], (0, 1)) < tol
