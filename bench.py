@@ -17,6 +17,7 @@ and the CPU oracle timed on a bounded sample of the same work.
     python bench.py --backward [--steps 10] [--warmup 2]
     python bench.py --routing [--steps 20] [--warmup 3]
     python bench.py --cold-decode [--steps 200] [--warmup 1]
+    python bench.py --few-heads [--steps 20] [--warmup 3]
 
 The second form measures the long-context shapes instead (131,072-token
 prefill, single-sequence decode from position 32,768, Kaczmarz LA against Gated
@@ -27,7 +28,9 @@ routing costs on the same Kaczmarz layer: the prefill and the batch-64 decode
 step with a routed value added on load and the per-token written residual
 stored, against the plain calls.  The fifth times single decode launches with
 the state evicted from the last-level cache before each one, beside the same
-launches warm, and measures the box's own copy bandwidth and GEMM rate.
+launches warm, and measures the box's own copy bandwidth and GEMM rate.  The
+sixth times only the prefills with few heads per device (the Kaczmarz layer at
+4 and 2 heads), which the default run also reports as forward_few_heads.
 """
 from __future__ import annotations
 
@@ -606,68 +609,104 @@ def cold_decode(args):
     print(json.dumps(out))
 
 
-def other_workloads(L, dev, sh, steps, warmup):
-    """The forward of workloads 1-4 (DeltaNet fp32, Gated DeltaNet, KDA,
-    Gated DeltaNet-2), each timed with HIP events on the launch stream: a HIP
-    graph of `steps` calls replayed (device time per forward, the figure the
-    rates use), and the same calls launched one by one from the host after
-    `warmup` untimed ones (ms_eager: for the smallest workload the host's
-    per-call cost exceeds the device time)."""
+def _time_forward(L, dev, sh, variant, dtype, d, steps, warmup):
+    """One forward configuration timed with HIP events on the launch stream: a
+    HIP graph of `steps` calls replayed (device time per forward, the figure
+    the rates use), and the same calls launched one by one from the host after
+    `warmup` untimed ones (ms_eager)."""
     import torch
 
     from gated_delta_rule_85_amd import binding
+
+    B, T, H, dk = d["q"].shape
+    dv = d["v"].shape[-1]
+    o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
+    s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    a = binding.make_args(variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"],
+                          d["erase_b"], d["write_w"], d["eps"], None, s_T)
+    binding.check(binding.gdr_check_args(a, 0))
+    n = binding.gdr_forward_workspace_size(a)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    ref = ctypes.byref(a)
+    for _ in range(warmup):
+        binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh)
+    e1.record()
+    torch.cuda.synchronize()
+    t_eager = e0.elapsed_time(e1) / 1e3 / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gs = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, gs))
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    del graph, o, s_T, ws
+    in_bytes = 2 if dtype == "bf16" else 4
+    fl = forward_flops_per_head_token(dk, dv) * B * T * H
+    fb = forward_bytes_variant(variant, B, T, H, dk, dv, in_bytes)
+    peak_mm = PEAK_BF16 if dtype == "bf16" else PEAK_FP32_MATRIX
+    return dict(variant=variant, dtype=dtype, B=B, T=T, H=H, dk=dk, dv=dv,
+                ms=t * 1e3, ms_eager=t_eager * 1e3, tokens_per_s=B * T / t,
+                tflops=fl / t / 1e12, mfma_frac=fl / t / peak_mm,
+                mfma_peak_TFLOPs=peak_mm / 1e12, hbm_GBps=fb / t / 1e9,
+                hbm_frac=fb / t / PEAK_HBM, algorithmic_flop=fl, algorithmic_bytes=fb,
+                workspace_bytes=n)
+
+
+def other_workloads(L, dev, sh, steps, warmup):
+    """The forward of workloads 1-4 (DeltaNet fp32, Gated DeltaNet, KDA,
+    Gated DeltaNet-2), each timed by _time_forward (for the smallest workload
+    the host's per-call cost exceeds the device time, hence ms_eager)."""
+    import torch
+
     from gated_delta_rule_85_amd.inputs import WORKLOADS, make_workload
 
     res = {}
     for wid in (1, 2, 3, 4):
         wl = WORKLOADS[wid]
-        B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
              for k, v in make_workload(wl).items()}
-        o = torch.empty((B, T, H, dv), dtype=d["q"].dtype, device=dev)
-        s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-        a = binding.make_args(wl.variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"],
-                              d["erase_b"], d["write_w"], d["eps"], None, s_T)
-        binding.check(binding.gdr_check_args(a, 0))
-        n = binding.gdr_forward_workspace_size(a)
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-        ref = ctypes.byref(a)
-        for _ in range(warmup):
-            binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh))
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            L.gdr_forward_chunked(ref, ws.data_ptr(), n, sh)
-        e1.record()
-        torch.cuda.synchronize()
-        t_eager = e0.elapsed_time(e1) / 1e3 / steps
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            gs = torch.cuda.current_stream().cuda_stream
-            for _ in range(steps):
-                binding.check(L.gdr_forward_chunked(ref, ws.data_ptr(), n, gs))
-        graph.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 1e3 / steps
-        del graph
-        in_bytes = 2 if wl.dtype == "bf16" else 4
-        fl = forward_flops_per_head_token(dk, dv) * B * T * H
-        fb = forward_bytes_variant(wl.variant, B, T, H, dk, dv, in_bytes)
-        peak_mm = PEAK_BF16 if wl.dtype == "bf16" else PEAK_FP32_MATRIX
-        res[wl.name] = dict(variant=wl.variant, dtype=wl.dtype, B=B, T=T, H=H, dk=dk, dv=dv,
-                            ms=t * 1e3, ms_eager=t_eager * 1e3, tokens_per_s=B * T / t,
-                            tflops=fl / t / 1e12,
-                            mfma_frac=fl / t / peak_mm,
-                            mfma_peak_TFLOPs=peak_mm / 1e12, hbm_GBps=fb / t / 1e9,
-                            hbm_frac=fb / t / PEAK_HBM, algorithmic_flop=fl,
-                            algorithmic_bytes=fb)
-        log(f"{wl.name}: {t * 1e6:.1f} us (graph replay), {t_eager * 1e6:.1f} us launched one by one")
-        del d, o, s_T, ws
+        r = _time_forward(L, dev, sh, wl.variant, wl.dtype, d, steps, warmup)
+        res[wl.name] = r
+        log(f"{wl.name}: {r['ms'] * 1e3:.1f} us (graph replay), {r['ms_eager'] * 1e3:.1f} us "
+            "launched one by one")
+        del d
+    torch.cuda.empty_cache()
+    return res
+
+
+# Prefills with few heads per device (as when the heads are sharded over
+# devices): the Kaczmarz layer of the benchmark at 4 and 2 of its 16 heads,
+# which the library runs as segments whose chains run side by side.
+FEW_HEAD_SHAPES = (("kla", 1, 65536, 4), ("kla", 1, 131072, 2))
+
+
+def few_head_workloads(L, dev, sh, steps, warmup):
+    """The forward of FEW_HEAD_SHAPES (bf16, d = 128, synthetic inputs drawn
+    as the Kaczmarz workload's), each timed by _time_forward."""
+    import torch
+
+    from gated_delta_rule_85_amd.inputs import make_inputs
+
+    res = {}
+    for variant, B, T, H in FEW_HEAD_SHAPES:
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in make_inputs(variant, B, T, H, 128, 128, "bf16", seed=85100 + H).items()}
+        name = f"{variant}_bf16_B{B}_H{H}_T{T}_d128"
+        r = _time_forward(L, dev, sh, variant, "bf16", d, steps, warmup)
+        res[name] = r
+        log(f"{name}: {r['ms'] * 1e3:.1f} us (graph replay)")
+        del d
     torch.cuda.empty_cache()
     return res
 
@@ -693,6 +732,8 @@ def main():
                     help="measure the gradient of the chunked forward on the Kaczmarz prefill")
     ap.add_argument("--routing", action="store_true",
                     help="measure the cost of the cross-layer routing input and output")
+    ap.add_argument("--few-heads", action="store_true",
+                    help="time only the prefills with few heads per device (segmented path)")
     ap.add_argument("--cold-decode", action="store_true",
                     help="time decode launches one by one with the state evicted from the "
                          "last-level cache, and measure the box's copy / GEMM peaks")
@@ -714,6 +755,20 @@ def main():
         return
     if args.cold_decode:
         cold_decode(args)
+        return
+    if args.few_heads:
+        import torch
+
+        from gated_delta_rule_85_amd import binding
+
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        res = few_head_workloads(binding.lib(), dev, torch.cuda.current_stream().cuda_stream,
+                                 steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"metric": "chunked-forward time with few heads per device (ms)",
+                          "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                          "data": "synthetic", "forward_few_heads": res, "git": git_sha()}))
         return
 
     import torch
@@ -859,10 +914,12 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    others = None
+    others = few = None
     if not args.no_extras:
         log("forward of workloads 1-4")
         others = other_workloads(L, dev, sh, steps=20, warmup=3)
+        log("forward with few heads per device")
+        few = few_head_workloads(L, dev, sh, steps=20, warmup=3)
 
     fwd_ms = [t["f0"].elapsed_time(t["f1"]) for t in timers]
     dec_ms = [t["f1"].elapsed_time(t["d1"]) for t in timers]
@@ -959,6 +1016,7 @@ def main():
         "prefill": prefill,
         "decode": decode,
         "forward_other_workloads": others,
+        "forward_few_heads": few,
         "git": git_sha(),
     }
     print(json.dumps(out))

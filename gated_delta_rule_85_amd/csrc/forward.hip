@@ -1866,41 +1866,63 @@ __global__ __launch_bounds__(4 * kWave) void seg_transition_kernel(Problem p, Ws
 
 // The combine: for one head and 16 value columns per workgroup, from the
 // initial state (zeros when state_in is NULL), S_{s+1} = M_s S_s + N_s for
-// s = 0 .. nseg - 2, each start state written for its segment's scan.  fp32
-// throughout; a few microseconds per segment.
+// s = 0 .. nseg - 2, each start state written for its segment's scan.  One
+// wave per 16 rows of S, on fp32 matrix cores (16x16x4: full fp32 products)
+// with M_s and S in LDS; M_{s+1} is loaded into registers while M_s is used.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void seg_combine_kernel(Problem p, long nseg, const float *Mi,
-                                                          const float *Ni, float *Sst) {
-    constexpr int TPR = 256 / DK, CPT = 16 / TPR;   // threads per row, columns per thread
-    __shared__ float sS[DK][16 + 1];
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(4 * DK) void seg_combine_kernel(Problem p, long nseg, const float *Mi,
+                                                             const float *Ni, float *Sst) {
+    using MF = Mma<float>;
+    constexpr int NT = 4 * DK;              // DK / 16 waves
+    constexpr int MP = DK + 4, SP = 16 + 4; // LDS row pitches (fewer bank conflicts)
+    constexpr int NL = DK / 16;             // 16-byte pieces of M per thread
+    __shared__ __attribute__((aligned(16))) float sM[DK][MP];
+    __shared__ float sS[DK][SP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int R = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's 16 rows
+    const int l16 = lane & 15, lg = lane >> 4;
     const long BH = p.B * p.H;
     const long bh = blockIdx.x / (DV / 16);
     const int col0 = 16 * (int)(blockIdx.x % (DV / 16));
-    for (int idx = tid; idx < DK * 16; idx += 256) {
+    for (int idx = tid; idx < DK * 16; idx += NT) {
         const int i = idx / 16, c = idx % 16;
         sS[i][c] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + c] : 0.f;
     }
+    f32x4 mr[NL];
+    auto load_m = [&](long s) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(Mi + (s * BH + bh) * (long)DK * DK);
+#pragma unroll
+        for (int n = 0; n < NL; ++n) mr[n] = src[tid + n * NT];
+    };
+    auto store_m = [&]() {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int e = 4 * (tid + n * NT);
+            *reinterpret_cast<f32x4 *>(&sM[e / DK][e % DK]) = mr[n];
+        }
+    };
+    load_m(0);
+    store_m();
     __syncthreads();
-    const int i = tid / TPR, cb = (tid % TPR) * CPT;
     for (long s = 0; s + 1 < nseg; ++s) {
-        const float *Mr = Mi + ((s * BH + bh) * DK + i) * (long)DK;
-        const float *Nr = Ni + ((s * BH + bh) * DK + i) * (long)DV + col0 + cb;
-        float acc[CPT];
+        const bool next = s + 2 < nseg;   // M_{s+1} is needed
+        if (next) load_m(s + 1);
+        const float *Nt = Ni + (s * BH + bh) * (long)DK * DV + col0;
+        f32x4 acc;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = Nr[c];
-        for (int k = 0; k < DK; ++k) {
-            const float m = Mr[k];
+        for (int m = 0; m < 4; ++m) acc[m] = Nt[(16 * R + 4 * lg + m) * DV + l16];
+#pragma unroll 8
+        for (int k0 = 0; k0 < DK; k0 += 4)
+            acc = MF::mma(sM[16 * R + l16][k0 + lg], sS[k0 + lg][l16], acc);
+        __syncthreads();   // every wave is done reading M_s and S_s
+        float *St = Sst + (s * BH + bh) * (long)DK * DV + col0;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) acc[c] += m * sS[k][cb + c];
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * R + 4 * lg + m;
+            sS[r][l16] = acc[m];
+            St[r * DV + l16] = acc[m];
         }
-        __syncthreads();   // every thread is done reading S_s
-        float *out = Sst + ((s * BH + bh) * DK + i) * (long)DV + col0 + cb;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            sS[i][cb + c] = acc[c];
-            out[c] = acc[c];
-        }
+        if (next) store_m();
         __syncthreads();
     }
 }
@@ -2141,7 +2163,7 @@ hipError_t launch_segments(const Problem &p, const SegPlan &s, void *ws, hipStre
                        dim3((unsigned)(kXcds * ((nwg1 + kXcds - 1) / kXcds)), (unsigned)(s.nseg - 1)),
                        dim3(4 * kWave), 0, st, p, w, NC, s.L, Mo, No);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(4 * DK), 0, st, p,
                        s.nseg, static_cast<const float *>(Mo), static_cast<const float *>(No), Sst);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long nwg3 = BH * (DV / 16);
