@@ -69,6 +69,19 @@ def test_segmented_forward_matches_oracle(variant, H, T):
     assert e_o < TOL[torch.bfloat16] and e_s < TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("B,H,dk,dv,T", [(1, 4, 128, 64, 64 * 64), (2, 2, 64, 64, 64 * 65 + 1),
+                                         (1, 1, 128, 128, 64 * 64 + 1), (2, 1, 64, 128, 64 * 97 + 50)])
+def test_segmented_forward_shapes(B, H, dk, dv, T):
+    """Batch rows, head sizes and the smallest segmented lengths (64 chunks:
+    two segments of 32; 65 chunks: 33 and 32)."""
+    announce(f"segmented forward gated_deltanet B={B} H={H} dk={dk} dv={dv} T={T}")
+    inp = make_inputs("gated_deltanet", B, T, H, dk, dv, "bf16", seed=980 + T % 97, state_scale=0.3)
+    o, s = gpu_forward("gated_deltanet", to_dev(inp))
+    o_ref, s_ref = run_oracle("gated_deltanet", inp)
+    assert rel_err(o.float().cpu(), o_ref, (0, 2)) < TOL[torch.bfloat16]
+    assert rel_err(s.cpu(), s_ref, (0, 1)) < TOL[torch.bfloat16]
+
+
 def test_segmented_forward_zero_initial_state_and_head_sizes():
     """No initial state (the combine starts from zeros), d_k = 64, d_v = 128."""
     T = 64 * 150 + 7
