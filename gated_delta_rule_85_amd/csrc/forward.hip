@@ -1870,8 +1870,8 @@ __global__ __launch_bounds__(4 * kWave) void seg_transition_kernel(Problem p, Ws
 // wave per 16 rows of S, on fp32 matrix cores (16x16x4: full fp32 products)
 // with M_s and S in LDS; M_{s+1} is loaded into registers while M_s is used.
 template <int DK, int DV>
-__global__ __launch_bounds__(4 * DK) void seg_combine_kernel(Problem p, long nseg, const float *Mi,
-                                                             const float *Ni, float *Sst) {
+__global__ __launch_bounds__(4 * DK) void seg_combine_kernel(Problem p, const float *s0, long nseg,
+                                                             const float *Mi, const float *Ni, float *Sst) {
     using MF = Mma<float>;
     constexpr int NT = 4 * DK;              // DK / 16 waves
     constexpr int MP = DK + 4, SP = 16 + 4; // LDS row pitches (fewer bank conflicts)
@@ -1886,7 +1886,7 @@ __global__ __launch_bounds__(4 * DK) void seg_combine_kernel(Problem p, long nse
     const int col0 = 16 * (int)(blockIdx.x % (DV / 16));
     for (int idx = tid; idx < DK * 16; idx += NT) {
         const int i = idx / 16, c = idx % 16;
-        sS[i][c] = p.state_in ? p.state_in[(bh * DK + i) * DV + col0 + c] : 0.f;
+        sS[i][c] = s0 ? s0[(bh * DK + i) * DV + col0 + c] : 0.f;
     }
     f32x4 mr[NL];
     auto load_m = [&](long s) {
@@ -1929,12 +1929,14 @@ __global__ __launch_bounds__(4 * DK) void seg_combine_kernel(Problem p, long nse
 
 // The outputs: segment blockIdx.y's scan (the forward's scan kernel body,
 // 16-column slices) from its start state; only the last segment writes the
-// final state.  blk describes the whole sequence.
-template <int DK, bool SG>
+// final state.  blk describes the whole sequence.  STATES / SAVE: the
+// gradient's records instead of o, or both (see scan_body); the record
+// pointers of blk are moved by the segment's first chunk like the factors.
+template <int DK, bool SG, bool STATES = false, bool SAVE = false>
 __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void seg_scan_kernel(Problem p, WsPtrs<bf16> ws,
                                                                             Block blk, long L,
                                                                             const float *Sst) {
-    __shared__ ScanSmem<bf16, DK, 1, false> sm;
+    __shared__ ScanSmem<bf16, DK, 1, STATES> sm;
     const long seg = blockIdx.y, nseg = gridDim.y, NC = blk.nc;
     Block b = blk;
     b.c0 = seg * L;
@@ -1949,7 +1951,11 @@ __global__ __launch_bounds__(kScan2Threads, SG ? 4 : 2) void seg_scan_kernel(Pro
     w.Kbt += b.c0 * C * DK;
     w.P += b.c0 * C * C;
     w.gam += b.c0 * DK;
-    scan_body<bf16, DK, 2, 1, false, false, SG, false>(p, w, b, blockIdx.x, sm);
+    if constexpr (STATES || SAVE) {
+        b.s_chunks = static_cast<bf16 *>(blk.s_chunks) + b.c0 * DK * p.dv;
+        b.d_chunks = static_cast<bf16 *>(blk.d_chunks) + b.c0 * C * p.dv;
+    }
+    scan_body<bf16, DK, 2, 1, STATES, false, SG, SAVE>(p, w, b, blockIdx.x, sm);
 }
 
 // ---- dispatch -----------------------------------------------------------------
@@ -2146,30 +2152,43 @@ hipError_t launch_pipe(const Problem &p, const WsPtrs<bf16> &sw, const Block &sb
 }
 
 // The sequence-parallel forward (see SegPlan), all on the caller's stream.
-template <int V, int DK, int DV>
-hipError_t launch_segments(const Problem &p, const SegPlan &s, void *ws, hipStream_t st) {
+// `fac` holds the factors of every chunk (ws_layout of all chunks); `seg`
+// the segments' transitions, local end states and start states at the
+// plan's offsets relative to the end of the factors.  MODE: kPipeForward
+// (o), kPipeStates (the gradient's records from s_in, no o), kPipeSave (both).
+template <int V, int DK, int DV, int MODE = kPipeForward>
+hipError_t launch_segments(const Problem &p, const SegPlan &s, void *fac, void *seg, const float *s_in,
+                           float *s_out, void *s_chunks, void *d_chunks, hipStream_t st) {
     constexpr bool SG = !VariantTraits<V>::kChannelDecay;
-    char *base = static_cast<char *>(ws);
     const long NC = (p.T + C - 1) / C, BH = p.B * p.H;
-    const WsPtrs<bf16> w = ws_ptrs<bf16>(p, NC, base);
-    const Block all{0, (int)NC, (int)NC, p.state_in, p.state_out, nullptr, nullptr, nullptr, 0u, nullptr,
-                    false};
+    const WsPtrs<bf16> w = ws_ptrs<bf16>(p, NC, fac);
+    const Block all{0, (int)NC, (int)NC, s_in, s_out, s_chunks, d_chunks, nullptr, 0u, nullptr,
+                    false, MODE == kPipeSave};
     hipError_t e = launch_prep<V, bf16, DK, DV>(p, w, all, false, st);
     if (e != hipSuccess) return e;
-    float *Mo = reinterpret_cast<float *>(base + s.M), *No = reinterpret_cast<float *>(base + s.N);
-    float *Sst = reinterpret_cast<float *>(base + s.S);
+    const size_t base = ws_layout(p, NC).total;
+    char *sb = static_cast<char *>(seg);
+    float *Mo = reinterpret_cast<float *>(sb + (s.M - base)), *No = reinterpret_cast<float *>(sb + (s.N - base));
+    float *Sst = reinterpret_cast<float *>(sb + (s.S - base));
     const long nwg1 = BH * (DV / 16 + DK / 16);
     hipLaunchKernelGGL((seg_transition_kernel<DK, DV, SG>),
                        dim3((unsigned)(kXcds * ((nwg1 + kXcds - 1) / kXcds)), (unsigned)(s.nseg - 1)),
                        dim3(4 * kWave), 0, st, p, w, NC, s.L, Mo, No);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(BH * (DV / 16))), dim3(4 * DK), 0, st, p,
-                       s.nseg, static_cast<const float *>(Mo), static_cast<const float *>(No), Sst);
+                       s_in, s.nseg, static_cast<const float *>(Mo), static_cast<const float *>(No), Sst);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long nwg3 = BH * (DV / 16);
-    hipLaunchKernelGGL((seg_scan_kernel<DK, SG>),
-                       dim3((unsigned)(kXcds * ((nwg3 + kXcds - 1) / kXcds)), (unsigned)s.nseg),
-                       dim3(kScan2Threads), 0, st, p, w, all, s.L, static_cast<const float *>(Sst));
+    const dim3 grid3((unsigned)(kXcds * ((nwg3 + kXcds - 1) / kXcds)), (unsigned)s.nseg);
+    const float *Sc = Sst;
+    if constexpr (MODE == kPipeStates)
+        hipLaunchKernelGGL((seg_scan_kernel<DK, SG, true, false>), grid3, dim3(kScan2Threads), 0, st, p, w,
+                           all, s.L, Sc);
+    else if constexpr (MODE == kPipeSave)
+        hipLaunchKernelGGL((seg_scan_kernel<DK, SG, false, true>), grid3, dim3(kScan2Threads), 0, st, p, w,
+                           all, s.L, Sc);
+    else
+        hipLaunchKernelGGL((seg_scan_kernel<DK, SG>), grid3, dim3(kScan2Threads), 0, st, p, w, all, s.L, Sc);
     return hipGetLastError();
 }
 
@@ -2177,7 +2196,11 @@ template <int V, typename TI, int DK, int DV>
 hipError_t launch_shape(const Problem &p, void *ws, hipStream_t stream) {
     if constexpr (sizeof(TI) == 2) {
         const SegPlan s = seg_plan(p);
-        if (s.nseg > 1) return launch_segments<V, DK, DV>(p, s, ws, stream);
+        if (s.nseg > 1) {
+            char *fac = static_cast<char *>(ws);
+            return launch_segments<V, DK, DV>(p, s, fac, fac + ws_layout(p, (p.T + C - 1) / C).total,
+                                              p.state_in, p.state_out, nullptr, nullptr, stream);
+        }
     }
     const Plan q = make_plan(p);
     char *base = static_cast<char *>(ws);
@@ -2315,7 +2338,18 @@ hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_
                          static_cast<TI *>(d_chunks) + c0 * C * (long)DV, tk, tb, tclear, false,
                          with_o};
         };
-        // The forward's choice of when to pipeline, and its blocks.
+        // The forward's choice of segments, of when to pipeline, and its
+        // blocks.  Segmented, the segments' arrays go to the scratch.
+        if constexpr (sizeof(TI) == 2) {
+            const SegPlan sp = seg_plan(p);
+            const size_t seg_bytes = sp.total - ws_layout(p, NC).total;
+            if (sp.nseg > 1 && scratch && scratch_bytes >= seg_bytes) {
+                return with_o ? launch_segments<V, DK, DV, kPipeSave>(p, sp, workspace, scratch, s_in,
+                                                                      s_out, s_chunks, d_chunks, stream)
+                              : launch_segments<V, DK, DV, kPipeStates>(p, sp, workspace, scratch, s_in,
+                                                                        s_out, s_chunks, d_chunks, stream);
+            }
+        }
         const Plan q = make_plan(p);
         const size_t carrier_bytes = align256((size_t)p.B * p.H * DK * DV * 4);
         if constexpr (sizeof(TI) == 2) {

@@ -267,10 +267,9 @@ gdr_status gdr_backward_chunked(const gdr_args *a, const gdr_grads *g, void *wor
                                 size_t ws_bytes, void *hip_stream);
 
 /* The forward of a training step that keeps what its gradient needs.  It
- * writes o and state_out as gdr_forward_chunked does, computed as one pass
- * over all chunks (bit for bit the same, except where gdr_forward_chunked
- * runs in segments, whose chains start from other states and round
- * differently; both then agree to the forward's tolerance), and leaves in
+ * writes o and state_out exactly as gdr_forward_chunked does (over all
+ * chunks in one pass, or in the same segments as gdr_forward_chunked where
+ * that call runs in segments), and leaves in
  * `workspace` (256-byte aligned, at least
  * gdr_backward_workspace_size(a) bytes, owned by the caller) every chunk's
  * factors of the chunk form and the state and residual entering each chunk:

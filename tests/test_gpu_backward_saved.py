@@ -123,6 +123,19 @@ def test_saved_path_where_the_plain_forward_is_pipelined(variant):
     _compare(variant, to_dev(inp), to_dev(up))
 
 
+@pytest.mark.parametrize("variant", ["kla", "kda"])
+def test_saved_path_where_the_forward_is_segmented(variant):
+    """131 chunks at 4 heads: few enough heads that gdr_forward_chunked runs
+    in segments whose chains run side by side; the saving forward and the
+    gradient's own first pass take the same segments, so o, the final state
+    and the gradients agree bit for bit as elsewhere."""
+    T = 130 * 64 + 9
+    announce(f"saved path, segmented forward: {variant} T={T}")
+    inp = make_inputs(variant, 1, T, 4, 128, 128, "bf16", seed=1325, state_scale=0.3)
+    up = make_upstream_grads(1, T, 4, 128, 128, "bf16", seed=1326)
+    _compare(variant, to_dev(inp), to_dev(up))
+
+
 def test_saved_gradient_against_oracle_and_workspace_reuse():
     """The saved gradient against the float64 oracle, then a second saving
     forward of other inputs in the same workspace: its gradient must follow
