@@ -229,11 +229,21 @@ constexpr int kRevThreads = 512;
 // matrix-core accumulators) backwards over the chunks; waves 4-7 copy each
 // chunk's dS' and dDelta from LDS to the workspace.
 // Chunks c0 + ncb - 1 down to c0; dS enters from ds_in (NULL = zeros) and
-// leaves to ds_out (NULL = dropped).
+// leaves to ds_out (NULL = dropped).  Segmented (L > 0): blockIdx.y is a
+// segment of L chunks (the last one shorter), entering from ds_in for the
+// last segment and from dSend[nseg - 2 - s] for segment s (the combine's
+// order), and only segment 0 writes ds_out.
 template <typename TI, int DK, int DEPTH>
 __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(
     Problem p, const float *gm, RevFactors rf, TI *dS_chunks, TI *dD_chunks, long NC, long c0,
-    int ncb, const float *ds_in, float *ds_out) {
+    int ncb, const float *ds_in, float *ds_out, long L, const float *dSend) {
+    if (L > 0) {
+        const long sg = blockIdx.y, nseg = gridDim.y;
+        c0 = sg * L;
+        ncb = (int)(NC - c0 < L ? NC - c0 : L);
+        if (sg != nseg - 1) ds_in = dSend + (nseg - 2 - sg) * p.B * p.H * DK * p.dv;
+        if (sg != 0) ds_out = nullptr;
+    }
     using M = Mma<TI>;
     using RO = RevOps<TI, DK>;
     constexpr int KS_D = RO::KS_D, KS_C = RO::KS_C, NI = RO::NI;
@@ -346,6 +356,106 @@ __global__ __launch_bounds__(kRevThreads, 4) void reverse_chain_kernel(
             __syncthreads();
         }
     }
+}
+
+// The segmented reverse pass's transitions: segment s = nseg - 1 - blockIdx.y
+// of L chunks (the last one shorter), for one head and one 16-column tile per
+// workgroup of four waves, its chunks in reverse order: either the chain from
+// dS' = 0 over d_v's columns (N, the gradient entering the segment from its
+// own chunks) or the chain over the identity's d_k columns with X1 and X2
+// taken as zero (M, the product of the chunks' maps dS' -> (Diag(e^{g_C}) -
+// W^T Kbar) dS').  The step is the reverse chain's.
+template <int DK, int DV>
+__global__ __launch_bounds__(4 * kWave) void rev_transition_kernel(Problem p, const float *gm,
+                                                                  RevFactors rf, long NC, long L,
+                                                                  long nseg, float *Mo, float *No) {
+    using TI = bf16;
+    using M = Mma<TI>;
+    using RO = RevOps<TI, DK>;
+    constexpr int KS_D = RO::KS_D, KS_C = RO::KS_C, NI = RO::NI;
+    constexpr int PT = 8, NV = DV / 16, NK = DK / 16;
+    __shared__ __attribute__((aligned(16))) TI sSt[2][16][DK + PT];   // dS'^T
+    __shared__ __attribute__((aligned(16))) TI sDt[2][16][C + PT];    // dDelta^T
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const long BH = p.B * p.H;
+    const long nwg = BH * (NV + NK);
+    const long per_xcd = (nwg + kXcds - 1) / kXcds;
+    const long logical = (long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (logical >= nwg) return;
+    const long bh = logical / (NV + NK);
+    const int r = (int)(logical % (NV + NK));
+    const bool mrole = r >= NV;                  // wave-uniform
+    const int col0 = 16 * (mrole ? r - NV : r);
+    const long j = blockIdx.y, sg = nseg - 1 - j;
+    const long c0 = sg * L, nc = (NC - c0 < L ? NC - c0 : L);
+    const long ch0 = bh * NC + c0;
+    auto chunk = [&](long n) { return ch0 + nc - 1 - (n < nc ? n : nc - 1); };
+    // X1 and X2 are read for the identity's columns too (value tile 0, in
+    // bounds) and multiplied by zero there.
+    const int xcol = mrole ? 0 : col0;
+    const float xk = mrole ? 0.f : 1.f;
+    f32x4 S[NI];
+#pragma unroll
+    for (int a = 0; a < NI; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * (w * NI + a) + 4 * lg + m;
+            S[a][m] = (mrole && i == col0 + l16) ? 1.f : 0.f;
+        }
+    auto write_st = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < NI; ++a) store4(&sSt[buf][l16][16 * (w * NI + a) + 4 * lg], S[a]);
+    };
+    write_st(0);
+    __syncthreads();
+    auto step = [&](const RO &op, long n) __attribute__((always_inline)) {
+        const int cur = (int)(n & 1);
+        typename M::frag Sf[KS_D];
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ++ks) Sf[ks] = M::load(&sSt[cur][l16][0], ks * M::kK, lane);
+        f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_D; ks += 2) {
+            d0 = M::mma(op.Kf[ks], Sf[ks], d0);
+            if (ks + 1 < KS_D) d1 = M::mma(op.Kf[ks + 1], Sf[ks + 1], d1);
+        }
+        store4(&sDt[cur][l16][16 * w + 4 * lg], xk * to_f32x4(op.X1) + (d0 + d1));
+        __syncthreads();
+        typename M::frag Df[KS_C];
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) Df[ks] = M::load(&sDt[cur][l16][0], ks * M::kK, lane);
+#pragma unroll
+        for (int a = 0; a < NI; ++a) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(op.Wf[a][ks], Df[ks], acc);
+            S[a] = S[a] * op.gam[a] + xk * to_f32x4(op.X2[a]) - acc;
+        }
+        write_st(cur ^ 1);
+        __syncthreads();
+    };
+    RO A, Bq;
+    A.load(rf, gm, chunk(0), DV, xcol, w, lane);
+    for (long n = 0; n < nc; n += 2) {
+        Bq.load(rf, gm, chunk(n + 1), DV, xcol, w, lane);
+        __builtin_amdgcn_sched_barrier(0);   // issue the prefetch first
+        step(A, n);
+        if (n + 1 >= nc) break;
+        A.load(rf, gm, chunk(n + 2), DV, xcol, w, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        step(Bq, n + 1);
+    }
+    const int pitch = mrole ? DK : DV;
+    float *out = (mrole ? Mo + (j * BH + bh) * (long)DK * DK : No + (j * BH + bh) * (long)DK * DV) + col0;
+#pragma unroll
+    for (int a = 0; a < NI; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * (w * NI + a) + 4 * lg + m;
+            out[(long)i * pitch + l16] = S[a][m];
+        }
 }
 
 // ============================================================================
@@ -1294,12 +1404,40 @@ hipError_t backward_shape(const Problem &p, const Grads &g, void *ws, bool saved
                        dim3(kBpThreads), 0, st, p, f, g, rf, 0L, (int)NC);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long nwg = p.B * p.H * (DV / 16);
+    const unsigned chain_grid = (unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds));
     constexpr int DEPTH = sizeof(TI) == 2 ? 2 : 1;
-    hipLaunchKernelGGL((reverse_chain_kernel<TI, DK, DEPTH>),
-                       dim3((unsigned)(kXcds * ((nwg + kXcds - 1) / kXcds))), dim3(kRevThreads), 0, st,
-                       p, f.gam, rf, dS_chunks, dD_chunks, NC, 0L, (int)NC, g.d_state_out,
-                       g.d_state_in);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // Where the forward runs in segments (few heads), so does the reverse
+    // pass: every segment's transitions side by side, the serial combine
+    // from d_state_out backwards, then every segment's recording chain from
+    // its end state; the segments' arrays in the per-chunk gradient's
+    // scratch, which that kernel only uses later.
+    long SL = 0;   // chunks per segment
+    const long nseg = sizeof(TI) == 2 ? forward_segments(p, &SL) : 0;
+    const long BH = p.B * p.H;
+    const size_t seg_floats = nseg > 1 ? (size_t)(nseg - 1) * BH * DK * (DK + 2 * DV) : 0;
+    const bool rseg = nseg > 1 && seg_floats <= (size_t)kGradSlots * GradSlot<DK>::kFloats;
+    if constexpr (sizeof(TI) == 2) {
+        if (rseg) {
+            float *Mo = scratch, *No = Mo + (nseg - 1) * BH * DK * DK;
+            float *Se = No + (nseg - 1) * BH * DK * DV;
+            const long nwg1 = BH * (DV / 16 + DK / 16);
+            hipLaunchKernelGGL((rev_transition_kernel<DK, DV>),
+                               dim3((unsigned)(kXcds * ((nwg1 + kXcds - 1) / kXcds)), (unsigned)(nseg - 1)),
+                               dim3(4 * kWave), 0, st, p, f.gam, rf, NC, SL, nseg, Mo, No);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_segment_combine(p, g.d_state_out, nseg, Mo, No, Se, st)) != hipSuccess) return e;
+            hipLaunchKernelGGL((reverse_chain_kernel<TI, DK, 2>), dim3(chain_grid, (unsigned)nseg),
+                               dim3(kRevThreads), 0, st, p, f.gam, rf, dS_chunks, dD_chunks, NC, 0L, (int)NC,
+                               g.d_state_out, g.d_state_in, SL, static_cast<const float *>(Se));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    if (!rseg) {
+        hipLaunchKernelGGL((reverse_chain_kernel<TI, DK, DEPTH>), dim3(chain_grid), dim3(kRevThreads), 0, st,
+                           p, f.gam, rf, dS_chunks, dD_chunks, NC, 0L, (int)NC, g.d_state_out,
+                           g.d_state_in, 0L, static_cast<const float *>(nullptr));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)

@@ -2394,6 +2394,28 @@ hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_
     });
 }
 
+long forward_segments(const Problem &p, long *L) {
+    const SegPlan s = seg_plan(p);
+    if (L) *L = s.L;
+    return s.nseg > 1 ? s.nseg : 0;
+}
+
+hipError_t launch_segment_combine(const Problem &p, const float *s0, long nseg, const float *M,
+                                  const float *N, float *Sst, hipStream_t stream) {
+    auto go = [&](auto dk, auto dv) {
+        constexpr int DK = decltype(dk)::value, DV = decltype(dv)::value;
+        hipLaunchKernelGGL((seg_combine_kernel<DK, DV>), dim3((unsigned)(p.B * p.H * (DV / 16))),
+                           dim3(4 * DK), 0, stream, p, s0, nseg, M, N, Sst);
+        return hipGetLastError();
+    };
+    using I = std::integral_constant<int, 128>;
+    using J = std::integral_constant<int, 64>;
+    if (p.dk == 128 && p.dv == 128) return go(I{}, I{});
+    if (p.dk == 128 && p.dv == 64) return go(I{}, J{});
+    if (p.dk == 64 && p.dv == 128) return go(J{}, I{});
+    return go(J{}, J{});
+}
+
 hipError_t launch_forward(const Problem &p, void *workspace, hipStream_t stream) {
     switch (p.variant) {
     case kDeltaNet: return launch_v<kDeltaNet>(p, workspace, stream);

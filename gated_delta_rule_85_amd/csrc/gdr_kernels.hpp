@@ -70,10 +70,22 @@ ForwardStates forward_states_ptrs(const Problem &p, void *workspace);
 // chunks as the forward does, each launch running the scan of one block beside
 // the prep of the next; that takes B*H*dk*dv*4 bytes (rounded up to 256) + 256
 // bytes of scratch, free for the duration of the call, for the state carried
-// between blocks and the prep's ticket counter (one pass without it).
+// between blocks and the prep's ticket counter (one pass without it).  Where
+// the forward runs in segments (forward_segments), so does this pass, its
+// segments' arrays in the scratch.
 hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_in, float *s_out,
                               void *s_chunks, void *d_chunks, bool with_o, void *scratch,
                               size_t scratch_bytes, hipStream_t stream);
+
+// The sequence segments the bf16 forward takes for p (few heads per device:
+// the chain's column slices at most an eighth of the compute units), or 0:
+// the number of segments, each of *L chunks but the last, shorter one.
+long forward_segments(const Problem &p, long *L);
+// The segments' serial combine: from s0 (NULL = zeros), S_{j+1} = M_j S_j + N_j
+// for j = 0 .. nseg - 2, with M [nseg-1][B*H][dk][dk], N and Sst
+// [nseg-1][B*H][dk][dv] (fp32); S_{j+1} is written to Sst[j].
+hipError_t launch_segment_combine(const Problem &p, const float *s0, long nseg, const float *M,
+                                  const float *N, float *Sst, hipStream_t stream);
 
 // Gradient of the chunked forward: upstream gradients in, input gradients out.
 struct Grads {
