@@ -30,7 +30,8 @@ stored, against the plain calls.  The fifth times single decode launches with
 the state evicted from the last-level cache before each one, beside the same
 launches warm, and measures the box's own copy bandwidth and GEMM rate.  The
 sixth times only the prefills with few heads per device (the Kaczmarz layer at
-4 and 2 heads), which the default run also reports as forward_few_heads.
+4 and 2 heads), which the default run also reports as forward_few_heads, and
+their gradients and saving forwards.
 """
 from __future__ import annotations
 
@@ -723,6 +724,65 @@ def _time_noalloc(L, dev, variant, d, steps):
     return e0.elapsed_time(e1) / steps
 
 
+def few_head_gradients(L, dev, sh, steps, warmup):
+    """The gradient of FEW_HEAD_SHAPES' forwards (upstream gradients for o and
+    S_T in, fp32 gradients of q, k, v, eta, alpha and S_0 out) and the saving
+    forward, timed with HIP events on the launch stream after `warmup` calls
+    (ms per call); with few heads both run their chains in segments."""
+    import torch
+
+    from gated_delta_rule_85_amd import binding
+    from gated_delta_rule_85_amd.inputs import make_inputs, make_upstream_grads
+
+    res = {}
+    for variant, B, T, H in FEW_HEAD_SHAPES:
+        dk = dv = 128
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in make_inputs(variant, B, T, H, dk, dv, "bf16", seed=85100 + H).items()}
+        up = {k: v.to(dev) for k, v in make_upstream_grads(B, T, H, dk, dv, "bf16",
+                                                             seed=85200 + H).items()}
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+        s_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        fa = binding.make_args(variant, d["q"], d["k"], d["v"], o, d["alpha"], d["beta"], None,
+                               None, d["eps"], None, s_T)
+        ba = binding.make_args(variant, d["q"], d["k"], d["v"], None, d["alpha"], d["beta"], None,
+                               None, d["eps"], None, None)
+        binding.check(binding.gdr_check_args(fa, 0))
+        nbw = binding.gdr_backward_workspace_size(ba)
+        ws = torch.empty(nbw, dtype=torch.uint8, device=dev)
+        gr = {n: torch.empty(shape, dtype=torch.float32, device=dev) for n, shape in
+              (("q", (B, T, H, dk)), ("k", (B, T, H, dk)), ("v", (B, T, H, dv)),
+               ("alpha", (B, T, H)), ("beta", (B, T, H)), ("s0", (B, H, dk, dv)))}
+        ga = binding.GdrGrads(up["d_o"].data_ptr(), up["d_state_out"].data_ptr(),
+                              gr["q"].data_ptr(), gr["k"].data_ptr(), gr["v"].data_ptr(),
+                              gr["alpha"].data_ptr(), gr["beta"].data_ptr(), None, None,
+                              gr["s0"].data_ptr())
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        name = f"{variant}_bf16_B{B}_H{H}_T{T}_d128"
+        bw = timed(lambda: binding.check(L.gdr_backward_chunked(ctypes.byref(ba), ctypes.byref(ga),
+                                                                ws.data_ptr(), nbw, sh)))
+        fs = timed(lambda: binding.check(L.gdr_forward_chunked_save(ctypes.byref(fa), ws.data_ptr(),
+                                                                    nbw, sh)))
+        res[name] = dict(backward_ms=bw, forward_save_ms=fs, tokens_per_s=B * T / (bw / 1e3),
+                         outputs_finite=all(bool(torch.isfinite(t).all()) for t in gr.values()))
+        log(f"{name}: gradient {bw * 1e3:.1f} us, saving forward {fs * 1e3:.1f} us")
+        del d, up, ws, gr, o, s_T
+        torch.cuda.empty_cache()
+    return res
+
+
 def few_head_workloads(L, dev, sh, steps, warmup):
     """The forward of FEW_HEAD_SHAPES (bf16, d = 128, synthetic inputs drawn
     as the Kaczmarz workload's), each timed by _time_forward.  Where the
@@ -805,12 +865,15 @@ def main():
 
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
-        res = few_head_workloads(binding.lib(), dev, torch.cuda.current_stream().cuda_stream,
-                                 steps=args.steps, warmup=args.warmup)
+        L = binding.lib()
+        sh = torch.cuda.current_stream().cuda_stream
+        res = few_head_workloads(L, dev, sh, steps=args.steps, warmup=args.warmup)
+        grads = few_head_gradients(L, dev, sh, steps=args.steps, warmup=args.warmup)
         print(json.dumps({"metric": "chunked-forward time with few heads per device (ms)",
                           "unit": "ms", "higher_is_better": False, "n_gpus": 1,
                           "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
-                          "data": "synthetic", "forward_few_heads": res, "git": git_sha()}))
+                          "data": "synthetic", "forward_few_heads": res,
+                          "gradient_few_heads": grads, "git": git_sha()}))
         return
 
     import torch

@@ -57,8 +57,9 @@
  *     side by side (each segment's transition and local end state, a serial
  *     combine, then each segment's outputs), the state map of a chunk being
  *     affine ("Kaczmarz Linear Attention", Implementation: the chunk-wise
- *     parallel algorithm), when its workspace fits in 1 GiB.  Every call can
- *     be captured into a HIP graph.
+ *     parallel algorithm), when its workspace fits in 1 GiB; the gradient's
+ *     forward pass and its reverse pass (whose map is affine too) then run in
+ *     the same segments.  Every call can be captured into a HIP graph.
  *   - Layouts are dense row-major:
  *       q, k     [B, T, H, dk]        v, o      [B, T, H, dv]
  *       alpha    GATED_DELTANET, KLA: [B, T, H];  KDA, GDN2: [B, T, H, dk];
