@@ -2342,8 +2342,7 @@ hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_
         // blocks.  Segmented, the segments' arrays go to the scratch.
         if constexpr (sizeof(TI) == 2) {
             const SegPlan sp = seg_plan(p);
-            const size_t seg_bytes = sp.total - ws_layout(p, NC).total;
-            if (sp.nseg > 1 && scratch && scratch_bytes >= seg_bytes) {
+            if (sp.nseg > 1 && scratch && scratch_bytes >= sp.total - ws_layout(p, NC).total) {
                 return with_o ? launch_segments<V, DK, DV, kPipeSave>(p, sp, workspace, scratch, s_in,
                                                                       s_out, s_chunks, d_chunks, stream)
                               : launch_segments<V, DK, DV, kPipeStates>(p, sp, workspace, scratch, s_in,
