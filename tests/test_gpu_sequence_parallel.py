@@ -142,3 +142,31 @@ def test_segmented_forward_is_deterministic_and_replays_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), f"replay {i}: output differs"
         assert torch.equal(s, s_ref), f"replay {i}: state differs"
+
+
+@pytest.mark.parametrize("T,H", [(65536, 4), (131072, 2)])
+def test_segmented_forward_at_full_length_sampled_heads(T, H):
+    """The two few-head Kaczmarz forwards the benchmark times (1,024 chunks in
+    8 segments; 2,048 chunks in 16), on the same inputs (seed 85100 + H) and
+    from a zero state with the workspace passed in, as timed there: every head
+    runs on the GPU, the oracle recomputes the first and the last head over the
+    whole sequence."""
+    if 8 * H * 8 > _cus():
+        pytest.skip("needs at least eight times as many compute units as column slices")
+    announce(f"segmented forward kla B=1 H={H} T={T} (full length), oracle on heads 0 and {H - 1}")
+    inp = dict(make_inputs("kla", 1, T, H, 128, 128, "bf16", seed=85100 + H), state_in=None)
+    d = to_dev(inp)
+    ws = torch.empty(binding.workspace_bytes("kla", d["q"], d["k"], d["v"]), dtype=torch.uint8,
+                     device="cuda")
+    o, s = binding.forward("kla", d["q"], d["k"], d["v"], alpha=d["alpha"], beta=d["beta"],
+                           eps=d["eps"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    heads = [(0, 0), (0, H - 1)]
+    o_ref, s_ref = run_oracle("kla", inp, heads=heads)
+    o_cpu, s_cpu = o.float().cpu().numpy(), s.cpu().numpy()
+    for _, h in heads:
+        e_o = rel_err(o_cpu[:, :, h:h + 1], o_ref[:, :, h:h + 1], (0, 2))
+        e_s = rel_err(s_cpu[:, h:h + 1], s_ref[:, h:h + 1], (0, 1))
+        announce(f"  head {h}: rel_err o={e_o:.3e} S={e_s:.3e}")
+        assert e_o < TOL[torch.bfloat16] and e_s < TOL[torch.bfloat16]
