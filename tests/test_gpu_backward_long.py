@@ -7,7 +7,8 @@ segment by segment from stored states, equal to the plain gradient oracle).
   head's gradient on the GPU, every input's gradient of one sampled head
   compared entry by entry with the oracle.
 * Kimi Delta Attention and Gated DeltaNet-2 at 257 chunks (the last one
-  ragged), one sampled head each.
+  ragged), one sampled head each; with two heads both chains run in segments.
+* The few-head Kaczmarz gradient, B=1, H=4, T=65536, segmented likewise.
 
 Error measure and thresholds as in the other gradient tests: per head,
 max |x - ref| / max |ref|, bf16 inputs 2e-2."""
@@ -77,3 +78,14 @@ def test_backward_257_chunks_channel_decay(variant):
                       state_scale=0.1)
     up = make_upstream_grads(1, T, 2, 128, 128, "bf16", seed=78)
     _check(variant, inp, up, 0, 1)
+
+
+def test_backward_few_heads_segmented_sampled_head():
+    """The few-head Kaczmarz gradient the benchmark times (B=1, H=4,
+    T=65536, its inputs and upstream gradients): 1,024 chunks, both the
+    states pass and the reverse pass in 8 segments; head 3 against the
+    oracle."""
+    announce("gradient kla B=1 H=4 T=65536 (segmented), oracle on head 3")
+    inp = make_inputs("kla", 1, 65536, 4, 128, 128, "bf16", seed=85104)
+    up = make_upstream_grads(1, 65536, 4, 128, 128, "bf16", seed=85204)
+    _check("kla", inp, up, 0, 3)
