@@ -689,7 +689,7 @@ def other_workloads(L, dev, sh, steps, warmup):
 # Prefills with few heads per device (as when the heads are sharded over
 # devices): the Kaczmarz layer of the benchmark at 4 and 2 of its 16 heads,
 # which the library runs as segments whose chains run side by side.
-FEW_HEAD_SHAPES = (("kla", 1, 65536, 4), ("kla", 1, 131072, 2))
+FEW_HEAD_SHAPES = (("kla", 1, 65536, 8), ("kla", 1, 65536, 4), ("kla", 1, 131072, 2))
 
 
 def _time_noalloc(L, dev, variant, d, steps):

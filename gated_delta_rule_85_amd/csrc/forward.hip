@@ -171,7 +171,7 @@ Plan make_plan(const Problem &p) {
 }
 
 // Sequence-parallel plan.  When the chain's column slices would occupy at
-// most an eighth of the compute units (few heads: B * H * d_v / 16 small),
+// most a quarter of the compute units (few heads: B * H * d_v / 16 small),
 // the sequence is cut into segments of L chunks whose chains run side by
 // side: the prep over every chunk; each segment but the last from S = 0 (its
 // local end state N_s) and from the identity with U~ = 0 (its transition M_s,
@@ -194,7 +194,7 @@ SegPlan seg_plan(const Problem &p) {
     if (!p.bf16 || device_cus(&cus) != hipSuccess) return s;
     const long NC = (p.T + C - 1) / C, BH = p.B * p.H;
     const long slices = BH * (p.dv / 16);
-    if (8 * slices > cus) return s;
+    if (4 * slices > cus) return s;
     long nseg = cus / slices;
     if (nseg > NC / kSegMinChunks) nseg = NC / kSegMinChunks;
     if (nseg > kSegMax) nseg = kSegMax;

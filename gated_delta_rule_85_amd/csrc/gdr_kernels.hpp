@@ -78,7 +78,7 @@ hipError_t launch_states_pass(const Problem &p, void *workspace, const float *s_
                               size_t scratch_bytes, hipStream_t stream);
 
 // The sequence segments the bf16 forward takes for p (few heads per device:
-// the chain's column slices at most an eighth of the compute units), or 0:
+// the chain's column slices at most a quarter of the compute units), or 0:
 // the number of segments, each of *L chunks but the last, shorter one.
 long forward_segments(const Problem &p, long *L);
 // The segments' serial combine: from s0 (NULL = zeros), S_{j+1} = M_j S_j + N_j

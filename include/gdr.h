@@ -52,8 +52,8 @@
  *     quarter and at most half of the device's compute units) is pipelined
  *     in blocks of 64 chunks by launches that each run one block's scan
  *     beside the next block's prep, in order on `hip_stream`.  A bf16 prefill
- *     of 64 chunks or more whose B * H * dv / 16 column slices are at most an
- *     eighth of the compute units runs as 2 to 16 segments whose chains run
+ *     of 64 chunks or more whose B * H * dv / 16 column slices are at most a
+ *     quarter of the compute units runs as 2 to 16 segments whose chains run
  *     side by side (each segment's transition and local end state, a serial
  *     combine, then each segment's outputs), the state map of a chunk being
  *     affine ("Kaczmarz Linear Attention", Implementation: the chunk-wise

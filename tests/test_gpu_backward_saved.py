@@ -114,12 +114,12 @@ def test_saving_forward_without_final_state():
 
 @pytest.mark.parametrize("variant", ["kda", "gated_deltanet"])
 def test_saved_path_where_the_plain_forward_is_pipelined(variant):
-    """Long enough (257 / 513 chunks at 8 heads) that gdr_forward_chunked
+    """Long enough (257 / 513 chunks at 16 heads) that gdr_forward_chunked
     runs in 64-chunk blocks; the saving forward is one pass."""
     T = (256 if variant == "kda" else 512) * 64 + 37
     announce(f"saved path, pipelined plain forward: {variant} T={T}")
-    inp = make_inputs(variant, 1, T, 8, 128, 128, "bf16", seed=1320, state_scale=0.3)
-    up = make_upstream_grads(1, T, 8, 128, 128, "bf16", seed=1321)
+    inp = make_inputs(variant, 1, T, 16, 128, 128, "bf16", seed=1320, state_scale=0.3)
+    up = make_upstream_grads(1, T, 16, 128, 128, "bf16", seed=1321)
     _compare(variant, to_dev(inp), to_dev(up))
 
 

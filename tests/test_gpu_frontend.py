@@ -73,10 +73,10 @@ def test_forward_transforms_head_sizes(variant, dk, dv):
     _check_forward(variant, "bf16", L2 | RAW, dk=dk, dv=dv, T=130, seed=11)
 
 
-@pytest.mark.parametrize("H", [8, 4], ids=["pipelined", "segmented"])
+@pytest.mark.parametrize("H", [16, 4], ids=["pipelined", "segmented"])
 @pytest.mark.parametrize("variant", ["kla", "kda", "gdn2"])
 def test_forward_transforms_pipelined(variant, H):
-    """514 chunks, sampled heads: at 8 heads the blocked path (one launch per
+    """514 chunks, sampled heads: at 16 heads the blocked path (one launch per
     block), at 4 heads the segmented one."""
     _check_forward(variant, "bf16", L2 | RAW, B=1, T=64 * 64 * 8 + 100, H=H, seed=21,
                    heads=[(0, 0), (0, H - 1)])

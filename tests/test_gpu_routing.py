@@ -69,10 +69,10 @@ def test_prefill_residual_and_routed_value(variant, dtype, routed):
     assert e_o < tol and e_s < tol and e_d < tol
 
 
-@pytest.mark.parametrize("H", [8, 4], ids=["pipelined", "segmented"])
+@pytest.mark.parametrize("H", [16, 4], ids=["pipelined", "segmented"])
 @pytest.mark.parametrize("variant", ["kla", "kda"])
 def test_prefill_routing_pipelined(variant, H):
-    """514 chunks in bf16, sampled heads: at 8 heads the blocked path (one
+    """514 chunks in bf16, sampled heads: at 16 heads the blocked path (one
     launch per block), at 4 heads the segmented one."""
     B, T, d = 1, 64 * 64 * 8 + 77, 128
     inp = make_inputs(variant, B, T, H, d, d, "bf16", seed=41, state_scale=0.1)

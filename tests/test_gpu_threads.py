@@ -20,9 +20,9 @@ from tests.gpu_common import announce, to_dev
 pytestmark = pytest.mark.gpu
 
 # (variant, B, T, H, seed): KDA from 256 chunks and Gated DeltaNet from 512
-# chunks (at 8 heads) run pipelined, both with a ragged last chunk; KLA at 4
+# chunks (at 16 heads) run pipelined, both with a ragged last chunk; KLA at 4
 # heads runs as segments whose chains run side by side.
-CASES = [("kda", 1, 300 * 64 + 17, 8, 910), ("gated_deltanet", 1, 520 * 64 + 5, 8, 911),
+CASES = [("kda", 1, 300 * 64 + 17, 16, 910), ("gated_deltanet", 1, 520 * 64 + 5, 16, 911),
          ("kla", 1, 530 * 64, 4, 912)]
 
 
