@@ -8,7 +8,8 @@ segment by segment from stored states, equal to the plain gradient oracle).
   compared entry by entry with the oracle.
 * Kimi Delta Attention and Gated DeltaNet-2 at 257 chunks (the last one
   ragged), one sampled head each; with two heads both chains run in segments.
-* The few-head Kaczmarz gradient, B=1, H=4, T=65536, segmented likewise.
+* The few-head Kaczmarz gradient, B=1, H=4, T=65536, and Kimi Delta
+  Attention at 8 heads and 257 chunks, segmented likewise.
 
 Error measure and thresholds as in the other gradient tests: per head,
 max |x - ref| / max |ref|, bf16 inputs 2e-2."""
@@ -89,3 +90,15 @@ def test_backward_few_heads_segmented_sampled_head():
     inp = make_inputs("kla", 1, 65536, 4, 128, 128, "bf16", seed=85104)
     up = make_upstream_grads(1, 65536, 4, 128, 128, "bf16", seed=85204)
     _check("kla", inp, up, 0, 3)
+
+
+def test_backward_eight_heads_segmented_sampled_head():
+    """Kimi Delta Attention at 8 heads (a quarter of the compute units in
+    column slices: both chains in 4 segments), 257 chunks with a ragged last
+    one; head 5 against the oracle."""
+    T = 257 * 64 - 21
+    announce(f"gradient kda B=1 H=8 T={T} (segmented), oracle on head 5")
+    inp = make_inputs("kda", 1, T, 8, 128, 128, "bf16", seed=79, alpha_scale=0.05,
+                      state_scale=0.1)
+    up = make_upstream_grads(1, T, 8, 128, 128, "bf16", seed=80)
+    _check("kda", inp, up, 0, 5)

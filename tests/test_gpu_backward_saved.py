@@ -123,16 +123,16 @@ def test_saved_path_where_the_plain_forward_is_pipelined(variant):
     _compare(variant, to_dev(inp), to_dev(up))
 
 
-@pytest.mark.parametrize("variant", ["kla", "kda"])
-def test_saved_path_where_the_forward_is_segmented(variant):
-    """131 chunks at 4 heads: few enough heads that gdr_forward_chunked runs
-    in segments whose chains run side by side; the saving forward and the
+@pytest.mark.parametrize("variant,H", [("kla", 4), ("kda", 4), ("gdn2", 8)])
+def test_saved_path_where_the_forward_is_segmented(variant, H):
+    """131 chunks at 4 or 8 heads: few enough heads that gdr_forward_chunked
+    runs in segments whose chains run side by side; the saving forward and the
     gradient's own first pass take the same segments, so o, the final state
     and the gradients agree bit for bit as elsewhere."""
     T = 130 * 64 + 9
-    announce(f"saved path, segmented forward: {variant} T={T}")
-    inp = make_inputs(variant, 1, T, 4, 128, 128, "bf16", seed=1325, state_scale=0.3)
-    up = make_upstream_grads(1, T, 4, 128, 128, "bf16", seed=1326)
+    announce(f"saved path, segmented forward: {variant} H={H} T={T}")
+    inp = make_inputs(variant, 1, T, H, 128, 128, "bf16", seed=1325, state_scale=0.3)
+    up = make_upstream_grads(1, T, H, 128, 128, "bf16", seed=1326)
     _compare(variant, to_dev(inp), to_dev(up))
 
 
