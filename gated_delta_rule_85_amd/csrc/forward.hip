@@ -185,7 +185,8 @@ struct SegPlan {
     size_t M = 0, N = 0, S = 0;        // byte offsets: M_s, N_s, start states
     size_t total = 0;
 };
-constexpr long kSegMinChunks = 32;     // chunks per segment at least
+constexpr long kSegMinChunks = 16;     // chunks per segment at least
+constexpr long kSegMinTotal = 64;      // chunks of the sequence at least
 constexpr long kSegMax = 16;           // segments at most
 
 SegPlan seg_plan(const Problem &p) {
@@ -194,7 +195,7 @@ SegPlan seg_plan(const Problem &p) {
     if (!p.bf16 || device_cus(&cus) != hipSuccess) return s;
     const long NC = (p.T + C - 1) / C, BH = p.B * p.H;
     const long slices = BH * (p.dv / 16);
-    if (4 * slices > cus) return s;
+    if (4 * slices > cus || NC < kSegMinTotal) return s;
     long nseg = cus / slices;
     if (nseg > NC / kSegMinChunks) nseg = NC / kSegMinChunks;
     if (nseg > kSegMax) nseg = kSegMax;

@@ -75,7 +75,7 @@ def test_segmented_forward_matches_oracle(variant, H, T):
                                          (1, 1, 128, 128, 64 * 64 + 1), (2, 1, 64, 128, 64 * 97 + 50)])
 def test_segmented_forward_shapes(B, H, dk, dv, T):
     """Batch rows, head sizes and the smallest segmented lengths (64 chunks:
-    two segments of 32; 65 chunks: 33 and 32)."""
+    four segments of 16; 65 chunks: 17, 17, 17 and 14)."""
     announce(f"segmented forward gated_deltanet B={B} H={H} dk={dk} dv={dv} T={T}")
     inp = make_inputs("gated_deltanet", B, T, H, dk, dv, "bf16", seed=980 + T % 97, state_scale=0.3)
     o, s = gpu_forward("gated_deltanet", to_dev(inp))
